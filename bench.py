@@ -1,0 +1,278 @@
+"""Benchmark of the MI355X retention library on one GPU.
+
+Default workload (the `value`): chunkwise retention forward of the multi-scale
+bf16 workload with rotation, B=2, H=8, N=2048, d_k=d_v=64, chunk 64. One step
+is one retention_chunkwise_fwd call over the batch (rotation, intra-chunk
+parallel form, state carry and, when the sequence is split, the segment
+pre-pass and scan), inputs resident in HBM. The other workloads (7B-shaped
+layer, batched decode, long context with the parallel-form crossover, the
+single-head fp32 case) are measured after it and reported under "also".
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+
+Prints one JSON line. Timing uses HIP events on the stream the library
+launches on (torch's current stream).
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "retention fwd tokens/s & MFMA util (chunkwise); decode state-updates/s & HBM GB/s"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3
+
+
+def chunk_alg_bytes(B, H, N, dk, dv, elt=2):
+    """Algorithmic HBM bytes of one chunkwise forward: read q, k, v and write o once."""
+    return B * H * N * elt * (2 * dk + dv + dv)
+
+
+def chunk_alg_flops(B, H, N, dk, dv, C):
+    """Algorithmic FLOPs: causal in-chunk Q K^T and P V, plus Q S and K^T V per token."""
+    return B * H * N * ((C + 1) * (dk + dv) + 4 * dk * dv)
+
+
+def parallel_alg_flops(B, H, N, dk, dv):
+    return B * H * N * (N + 1) * (dk + dv)
+
+
+def decode_alg_bytes(B, H, dk, dv, elt=2):
+    return B * H * (2 * dk * dv * 4 + elt * (2 * dk + dv) + elt * dv)
+
+
+def time_events(fn, steps, warmup):
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps  # ms per step
+
+
+def time_phases(R, q, k, v, kw, steps):
+    """Average duration (ms) of each phase of the chunkwise call, from the
+    four events the library records around its kernels."""
+    import torch
+
+    tot = [0.0, 0.0, 0.0]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for _ in range(steps):
+        R.retention_chunkwise_fwd(q, k, v, events=evs, **kw)
+        torch.cuda.synchronize()
+        for i in range(3):
+            tot[i] += evs[i].elapsed_time(evs[i + 1])
+    return [t / steps for t in tot]
+
+
+def cpu_baseline(q, k, v, theta, H, budget_s):
+    """The fp64 oracle's recurrent form on the host, on a bounded sample of the
+    workload: whole sequences of the first batch entry, repeated until the
+    time budget is used."""
+    import numpy as np
+
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    from oracle import retention as orc
+
+    q64 = q[:1].float().cpu().numpy().astype(np.float64)
+    k64 = k[:1].float().cpu().numpy().astype(np.float64)
+    v64 = v[:1].float().cpu().numpy().astype(np.float64)
+    th = None if theta is None else theta.double().numpy()
+    g = orc.head_gammas(H)
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            orc.recurrent(q64, k64, v64, g, theta=th)
+            reps += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    tokens = reps * q64.shape[2]
+    return {
+        "value": tokens / dt,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"fp64 recurrent oracle, batch entry 0 (H={H}, N={q64.shape[2]}), {reps} repetitions in "
+                  f"{dt:.1f} s, numpy single-threaded",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--quick", action="store_true", help="main workload only")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(sequence and head sharding across GPUs is a design note, not implemented)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import linear_attention_sequence_fwd_amd as R
+    from linear_attention_sequence_fwd_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    R.load_library()
+    dev = "cuda:0"
+
+    # ---------------- main workload
+    name = "msr_bf16_rotary"
+    w = W.WORKLOADS[name]
+    q, k, v, theta = W.make_workload(name, device=dev)
+    kw = dict(chunk=w["chunk"], theta=theta)
+    out = torch.empty_like(v)
+    ws_bytes = R.retention_chunkwise_workspace_size(w["B"], w["H"], w["N"], w["dk"], w["dv"], q.dtype, w["chunk"])
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    kw.update(out=out, workspace=ws)
+    ms = time_events(lambda: R.retention_chunkwise_fwd(q, k, v, **kw), args.steps, args.warmup)
+    phases = time_phases(R, q, k, v, kw, max(20, args.steps // 4))
+    tokens = w["B"] * w["N"]
+    alg_bytes = chunk_alg_bytes(w["B"], w["H"], w["N"], w["dk"], w["dv"])
+    main_ms = phases[2]
+    achieved = alg_bytes / (main_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "multi-scale retention forward, chunkwise: B=2 H=8 N=2048 d_k=d_v=64 bf16, "
+                        "rotary theta_j=10000^(-2j/64), gamma_h=1-2^(-5-h), chunk 64",
+            "global_batch": w["B"],
+            "seq_len": w["N"],
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "chunk_bf16_kernel (main pass)",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "alg_bytes_per_launch": alg_bytes,
+            "kernel_ms": main_ms,
+        },
+        "phase_ms": {"segment_states": phases[0], "segment_scan": phases[1], "main": phases[2]},
+    }
+    result["cpu_baseline"] = cpu_baseline(q.cpu(), k.cpu(), v.cpu(), theta, w["H"], args.cpu_seconds)
+    del q, k, v, out, ws
+    torch.cuda.empty_cache()
+
+    if not args.quick:
+        also = []
+        # ---------------- 7B-shaped layer
+        w = W.WORKLOADS["layer7b_bf16"]
+        q, k, v, _ = W.make_workload("layer7b_bf16", device=dev)
+        out = torch.empty_like(v)
+        kw3 = dict(chunk=w["chunk"], out=out)
+        ms3 = time_events(lambda: R.retention_chunkwise_fwd(q, k, v, **kw3), 10, 3)
+        ph3 = time_phases(R, q, k, v, kw3, 5)
+        fl = chunk_alg_flops(w["B"], w["H"], w["N"], w["dk"], w["dv"], w["chunk"])
+        by = chunk_alg_bytes(w["B"], w["H"], w["N"], w["dk"], w["dv"])
+        also.append({
+            "workload": "7B-shaped layer chunkwise: B=4 H=16 N=8192 d_k=256 d_v=512 bf16, chunk 128",
+            "tokens_per_s": w["B"] * w["N"] / (ms3 * 1e-3), "ms": ms3, "main_kernel_ms": ph3[2],
+            "tflops": fl / (ph3[2] * 1e-3) / 1e12, "mfma_frac": fl / (ph3[2] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "gbs": by / (ph3[2] * 1e-3) / 1e9, "hbm_frac": by / (ph3[2] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        })
+        del q, k, v, out
+        torch.cuda.empty_cache()
+
+        # ---------------- decode
+        w = W.WORKLOADS["decode_bf16"]
+        s0, qs, ks, vs = W.make_decode_workload(device=dev)
+        state = s0.clone()
+        o = torch.empty((w["B"], w["H"], w["dv"]), dtype=torch.bfloat16, device=dev)
+        steps = w["steps"]
+
+        def run_decode():
+            for t in range(steps):
+                R.retention_recurrent_step(qs[t], ks[t], vs[t], state, out=o)
+
+        ms4 = time_events(run_decode, 2, 1) / steps
+        by4 = decode_alg_bytes(w["B"], w["H"], w["dk"], w["dv"])
+        also.append({
+            "workload": "recurrent decode: 64 sequences x H=16, fp32 state 256x512, bf16 q/k/v, 512 steps",
+            "ms_per_step": ms4, "state_updates_per_s": w["B"] * w["H"] / (ms4 * 1e-3),
+            "gbs": by4 / (ms4 * 1e-3) / 1e9, "hbm_frac": by4 / (ms4 * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        })
+        del s0, qs, ks, vs, state, o
+        torch.cuda.empty_cache()
+
+        # ---------------- long context + parallel crossover
+        w = W.WORKLOADS["longctx_bf16"]
+        q, k, v, _ = W.make_workload("longctx_bf16", device=dev)
+        kw5 = dict(chunk=w["chunk"])
+        ms5 = time_events(lambda: R.retention_chunkwise_fwd(q, k, v, **kw5), 10, 3)
+        ph5 = time_phases(R, q, k, v, kw5, 5)
+        by5 = chunk_alg_bytes(w["B"], w["H"], w["N"], w["dk"], w["dv"])
+        fl5 = chunk_alg_flops(w["B"], w["H"], w["N"], w["dk"], w["dv"], w["chunk"])
+        cross = []
+        for n in w["parallel_lengths"]:
+            qn, kn, vn = q[:, :, :n].contiguous(), k[:, :, :n].contiguous(), v[:, :, :n].contiguous()
+            tp = time_events(lambda: R.retention_parallel_fwd(qn, kn, vn), 20, 5)
+            tc = time_events(lambda: R.retention_chunkwise_fwd(qn, kn, vn, chunk=w["chunk"]), 20, 5)
+            pf = parallel_alg_flops(w["B"], w["H"], n, w["dk"], w["dv"])
+            cross.append({"N": n, "parallel_ms": tp, "chunkwise_ms": tc,
+                          "parallel_tflops": pf / (tp * 1e-3) / 1e12})
+        also.append({
+            "workload": "long-context chunkwise: B=1 H=8 N=65536 d_k=d_v=128 bf16, chunk 128",
+            "tokens_per_s": w["B"] * w["N"] / (ms5 * 1e-3), "ms": ms5,
+            "phase_ms": {"segment_states": ph5[0], "segment_scan": ph5[1], "main": ph5[2]},
+            "step_gbs": by5 / (ms5 * 1e-3) / 1e9, "step_hbm_frac": by5 / (ms5 * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "step_tflops": fl5 / (ms5 * 1e-3) / 1e12,
+            "parallel_crossover": cross,
+        })
+        del q, k, v
+        torch.cuda.empty_cache()
+
+        # ---------------- single-head fp32
+        q, k, v, _ = W.make_workload("single_head_f32", device=dev)
+        ms1 = time_events(lambda: R.retention_chunkwise_fwd(q, k, v, chunk=64), 50, 5)
+        msp = time_events(lambda: R.retention_parallel_fwd(q, k, v), 50, 5)
+        also.append({"workload": "single-head fp32 B=1 H=1 N=256 d=64", "chunkwise_ms": ms1, "parallel_ms": msp})
+        result["also"] = also
+
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

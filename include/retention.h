@@ -1,0 +1,165 @@
+/*
+ * retention.h -- C ABI of the MI355X (gfx950) multi-scale retention library.
+ *
+ * Retention per batch b and head h, on query/key rows q'_n, k'_m (after the
+ * optional complex rotation) and value rows v_m:
+ *
+ *     o_n = sum_{m <= n} gamma_h^(n - m) (q'_n . k'_m) v_m
+ *
+ * ("RetNet Guide: Retentive Networks & The Impossible Triangle", sections
+ * "The Parallel Representation", "The Recurrent Representation" and "The
+ * Chunkwise Recurrent Representation"; "How RetNet Combines Parallel Training
+ * and Constant Inference").
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense, row-major, contiguous device buffers owned by the
+ *     caller: q, k [B, H, N, dk]; v, o [B, H, N, dv]; state [B, H, dk, dv].
+ *     Device pointers must be 16-byte aligned.
+ *   - dtype selects the element type of q, k, v and o (RET_F32 or RET_BF16).
+ *     The recurrent state is always float32; accumulation is always float32.
+ *   - gamma: host array of H floats, each in (0, 1], read during the call; NULL
+ *     selects gamma_h = 1 - 2^(-5-h), heads counted from 0 ("RetNet Guide"
+ *     section "3. Multi-Scale Retention (MSR)").
+ *   - theta: host array of dk/2 floats, read during the call, or NULL for no
+ *     rotation. With theta, coordinates (2j, 2j+1) of every query and key row
+ *     are treated as the complex number x_2j + i x_2j+1 and multiplied by
+ *     e^(i n theta_j) at absolute position n ("RetNet Guide" section "2.
+ *     Relative Position via Complex Exponential Phase Rotations"). Angles are
+ *     formed in float64. Values are never rotated.
+ *   - No 1/sqrt(dk) score scale is applied; callers fold it into q.
+ *   - Every call validates all arguments before touching the GPU, launches
+ *     asynchronously on `stream` (a hipStream_t; NULL = the null stream) and
+ *     returns a status. Launch failures reported by hipGetLastError map to
+ *     RET_ERR_HIP; faults inside kernels surface at the caller's next
+ *     synchronisation. The library allocates no device memory and keeps no
+ *     state between calls. Nothing is written when a call returns an error
+ *     found during validation. Checks run in this order, and the first
+ *     failure is returned: NULL pointers, sizes and dtype, gamma and theta
+ *     values, pointer alignment, the implemented set, the workspace.
+ */
+#ifndef RETENTION_H
+#define RETENTION_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RETENTION_ABI_VERSION 1
+#define RETENTION_MAX_HEADS 128 /* H limit (per-head constants travel in kernel arguments) */
+#define RETENTION_MAX_DK 256
+
+typedef enum { RET_F32 = 0, RET_BF16 = 1 } ret_dtype_t;
+
+typedef enum {
+    RET_OK = 0,
+    RET_ERR_NULL = 1,        /* a required pointer is NULL */
+    RET_ERR_SHAPE = 2,       /* a size is < 1, or dk is odd while theta is given */
+    RET_ERR_DTYPE = 3,       /* dtype is not one of ret_dtype_t */
+    RET_ERR_GAMMA = 4,       /* a gamma is not in (0, 1] or not finite, or theta not finite */
+    RET_ERR_UNSUPPORTED = 5, /* valid request outside the implemented set (see each call) */
+    RET_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required */
+    RET_ERR_ALIGN = 7,       /* a device pointer is not 16-byte aligned */
+    RET_ERR_HIP = 8          /* the HIP runtime reported a launch error */
+} ret_status_t;
+
+/*
+ * Parallel form: O = ((Q' K'^T) (.) D) V with D[n, m] = gamma^(n - m) for
+ * n >= m, else 0 ("RetNet Guide" section "1. The Parallel Representation for
+ * High-Throughput Pretraining"). Positions are pos0 .. pos0 + N - 1.
+ * Implemented set: bf16 with dk in {64, 128, 256} and dv a multiple of 64;
+ * f32 with dk <= 128 and dv a multiple of 16 (dk a multiple of 4).
+ * Work is O(N^2) per head; key blocks whose decay underflows float32 for every
+ * entry are skipped (their exact contribution is below float32 resolution).
+ */
+ret_status_t retention_parallel_fwd(const void* q, const void* k, const void* v, void* o,
+                                    int B, int H, int N, int dk, int dv, ret_dtype_t dtype,
+                                    const float* gamma, const float* theta, int64_t pos0,
+                                    void* stream);
+
+/*
+ * Chunkwise recurrent form ("RetNet Guide" section "3. The Chunkwise Recurrent
+ * Representation"): the sequence is cut into chunks of `chunk` tokens (the
+ * last may be shorter). Inside a chunk the parallel form is used; between
+ * chunks a float32 state S [dk, dv] is carried:
+ *     O_X = ((Q_X K_X^T) (.) D) V_X + zeta (.) (Q_X S),   zeta_j = gamma^(j+1)
+ *     S  <- gamma^L S + K_X^T (xi (.) V_X),               xi_j   = gamma^(L-1-j)
+ * (L = chunk length; the xi weights are the in-chunk key decay implied by the
+ * recurrent form). Same result as the parallel form up to rounding.
+ *
+ * state_in:  device float32 [B, H, dk, dv] state before the first token, or
+ *            NULL for zeros. Positions are pos0 .. pos0 + N - 1, so a long
+ *            sequence may be processed in pieces by handing state_out of one
+ *            call to state_in of the next with pos0 advanced.
+ * state_out: device float32 [B, H, dk, dv] receiving the state after the last
+ *            token, or NULL. May alias state_in.
+ * segments:  0 lets the library choose; s >= 1 asks for s sequence segments
+ *            (clamped to the number of chunks). With more than one segment the
+ *            library first builds every segment's end state, then scans them
+ *            with factor gamma^(segment length), then runs all segments in
+ *            parallel; this uses the workspace.
+ * workspace: device buffer of at least retention_chunkwise_workspace_size(...)
+ *            bytes (may be NULL when that size is 0). Contents on entry are
+ *            ignored; contents on return are unspecified.
+ * Implemented set: chunk in {64, 128}; bf16 with dk in {64, 128, 256} and dv a
+ * multiple of 64; f32 with chunk*dk <= 8192, dk a multiple of 4, dv a multiple
+ * of 16.
+ */
+ret_status_t retention_chunkwise_fwd(const void* q, const void* k, const void* v, void* o,
+                                     int B, int H, int N, int dk, int dv, ret_dtype_t dtype,
+                                     int chunk, const float* gamma, const float* theta,
+                                     int64_t pos0, const float* state_in, float* state_out,
+                                     int segments, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
+/*
+ * retention_chunkwise_fwd with a timing hook for profilers and benchmarks:
+ * events points to four hipEvent_t created by the caller, recorded on
+ * `stream` before the segment pre-pass, after it, after the segment scan and
+ * after the main chunk kernel; phases that do not run leave two consecutive
+ * events back to back. Same result and status codes as
+ * retention_chunkwise_fwd (RET_ERR_NULL if an event is missing).
+ */
+ret_status_t retention_chunkwise_fwd_timed(const void* q, const void* k, const void* v, void* o,
+                                           int B, int H, int N, int dk, int dv, ret_dtype_t dtype,
+                                           int chunk, const float* gamma, const float* theta,
+                                           int64_t pos0, const float* state_in, float* state_out,
+                                           int segments, void* workspace, size_t workspace_bytes,
+                                           void* stream, void* const* events);
+
+/*
+ * Bytes of workspace retention_chunkwise_fwd needs for these sizes and this
+ * `segments` request. The value does not depend on N (the segment count is
+ * bounded independently of the sequence length). Returns 0 for sizes the
+ * call would reject.
+ */
+size_t retention_chunkwise_workspace_size(int B, int H, int N, int dk, int dv, ret_dtype_t dtype,
+                                          int chunk, int segments);
+
+/*
+ * One recurrent decode step for one token per sequence ("RetNet Guide" section
+ * "2. The Recurrent Representation for Constant-Memory O(1) Decoding"):
+ *     S <- gamma S + k'^T v ;  o = q' S   (with the updated S)
+ * q, k: [B, H, dk]; v, o: [B, H, dv] in dtype; state: device float32
+ * [B, H, dk, dv], updated in place. pos: device int64 [B] absolute position of
+ * each sequence's token (used only with theta; may be NULL without theta).
+ * Implemented set: dv a multiple of 4 with dv <= 1024, dk <= 4096.
+ */
+ret_status_t retention_recurrent_step(const void* q, const void* k, const void* v, void* o,
+                                      float* state, int B, int H, int dk, int dv,
+                                      ret_dtype_t dtype, const float* gamma, const float* theta,
+                                      const int64_t* pos, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* retention_status_string(ret_status_t status);
+
+/* RETENTION_ABI_VERSION of the built library. */
+int retention_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RETENTION_H */

@@ -1,0 +1,243 @@
+"""MI355X-native multi-scale retention: Python binding of the C ABI.
+
+The functions below share the names of the C entry points declared in
+include/retention.h and only marshal arguments: torch tensors supply device
+memory and the current HIP stream, every step of retention runs in the HIP
+kernels of libretention_mi355x.so. There is no CPU or PyTorch fallback: if
+the library is missing, importing a function raises.
+"""
+
+import ctypes
+import os
+
+__all__ = [
+    "RetentionError",
+    "load_library",
+    "retention_parallel_fwd",
+    "retention_chunkwise_fwd",
+    "retention_chunkwise_fwd_timed",
+    "retention_chunkwise_workspace_size",
+    "retention_recurrent_step",
+    "retention_status_string",
+    "retention_abi_version",
+    "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libretention_mi355x.so")
+
+RET_F32 = 0
+RET_BF16 = 1
+
+_STATUS = {
+    0: "RET_OK",
+    1: "RET_ERR_NULL",
+    2: "RET_ERR_SHAPE",
+    3: "RET_ERR_DTYPE",
+    4: "RET_ERR_GAMMA",
+    5: "RET_ERR_UNSUPPORTED",
+    6: "RET_ERR_WORKSPACE",
+    7: "RET_ERR_ALIGN",
+    8: "RET_ERR_HIP",
+}
+
+_lib = None
+
+
+class RetentionError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        self.code = _STATUS.get(status, str(status))
+        super().__init__(f"{what}: {self.code} ({retention_status_string(status)})")
+
+
+def load_library(path=None):
+    """Load (once) and return the ctypes handle of the HIP library."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build it with `python -m linear_attention_sequence_fwd_amd.build`"
+        )
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz, fp = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+    lib.retention_parallel_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, fp, fp, i64, vp]
+    lib.retention_parallel_fwd.restype = i32
+    lib.retention_chunkwise_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, fp, fp, i64,
+                                            vp, vp, i32, vp, sz, vp]
+    lib.retention_chunkwise_fwd.restype = i32
+    lib.retention_chunkwise_fwd_timed.argtypes = lib.retention_chunkwise_fwd.argtypes + [vp]
+    lib.retention_chunkwise_fwd_timed.restype = i32
+    lib.retention_chunkwise_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
+    lib.retention_chunkwise_workspace_size.restype = sz
+    lib.retention_recurrent_step.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, fp, fp, vp, vp]
+    lib.retention_recurrent_step.restype = i32
+    lib.retention_status_string.argtypes = [i32]
+    lib.retention_status_string.restype = ctypes.c_char_p
+    lib.retention_abi_version.argtypes = []
+    lib.retention_abi_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def retention_status_string(status):
+    return load_library().retention_status_string(int(status)).decode()
+
+
+def retention_abi_version():
+    return int(load_library().retention_abi_version())
+
+
+# ---------------------------------------------------------------- marshalling
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return RET_BF16
+    if t.dtype == torch.float32:
+        return RET_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("retention tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("retention tensors must be contiguous")
+
+
+def _host_floats(vals, n, what):
+    if vals is None:
+        return None, None
+    torch = _torch()
+    if isinstance(vals, torch.Tensor):
+        vals = vals.detach().to("cpu", torch.float32).tolist()
+    vals = [float(x) for x in vals]
+    if len(vals) != n:
+        raise ValueError(f"{what} needs {n} values, got {len(vals)}")
+    arr = (ctypes.c_float * n)(*vals)
+    return arr, ctypes.cast(arr, ctypes.c_void_p)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _raise(status, what):
+    if status != 0:
+        raise RetentionError(status, what)
+
+
+def retention_parallel_fwd(q, k, v, gamma=None, theta=None, pos0=0, out=None, stream=None):
+    """O = ((Q K^T) (.) D) V for q, k [B,H,N,dk] and v [B,H,N,dv] (bf16 or fp32)."""
+    torch = _torch()
+    _check_dev(q, k, v)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=v.dtype, device=v.device)
+    _check_dev(out)
+    _g, g = _host_floats(gamma, H, "gamma")
+    _t, th = _host_floats(theta, dk // 2, "theta")
+    st = load_library().retention_parallel_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, dk, dv, _dtype_code(q), g, th, int(pos0), _stream(stream)
+    )
+    _raise(st, "retention_parallel_fwd")
+    return out
+
+
+def retention_chunkwise_workspace_size(B, H, N, dk, dv, dtype, chunk, segments=0):
+    torch = _torch()
+    code = RET_BF16 if dtype == torch.bfloat16 else RET_F32
+    return int(load_library().retention_chunkwise_workspace_size(B, H, N, dk, dv, code, chunk, segments))
+
+
+def retention_chunkwise_fwd(q, k, v, chunk=64, gamma=None, theta=None, pos0=0, state_in=None,
+                            return_state=False, state_out=None, segments=0, out=None, workspace=None,
+                            stream=None, events=None):
+    """Chunkwise retention forward. Returns o, or (o, state) with return_state.
+
+    state_in / state_out are float32 [B,H,dk,dv] device tensors (state_out may
+    be state_in). The workspace is allocated here from torch's caching
+    allocator when not given. With `events` (four torch.cuda.Event created
+    with enable_timing=True) the call goes through retention_chunkwise_fwd_timed.
+    """
+    torch = _torch()
+    _check_dev(q, k, v, state_in, state_out)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=v.dtype, device=v.device)
+    if return_state and state_out is None:
+        state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=v.device)
+    _check_dev(out)
+    ws_bytes = retention_chunkwise_workspace_size(B, H, N, dk, dv, q.dtype, chunk, segments)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=v.device)
+    _g, g = _host_floats(gamma, H, "gamma")
+    _t, th = _host_floats(theta, dk // 2, "theta")
+    args = [
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, dk, dv, _dtype_code(q), int(chunk), g, th, int(pos0),
+        _ptr(state_in), _ptr(state_out), int(segments), _ptr(workspace),
+        workspace.numel() if workspace is not None else 0, _stream(stream),
+    ]
+    lib = load_library()
+    if events is None:
+        st = lib.retention_chunkwise_fwd(*args)
+        _raise(st, "retention_chunkwise_fwd")
+    else:
+        if len(events) != 4:
+            raise ValueError("events needs four torch.cuda.Event")
+        for e in events:
+            e.record()  # materialise the underlying hipEvent_t
+        evs = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
+        st = lib.retention_chunkwise_fwd_timed(*args, ctypes.cast(evs, ctypes.c_void_p))
+        _raise(st, "retention_chunkwise_fwd_timed")
+    return (out, state_out) if return_state else out
+
+
+def retention_chunkwise_fwd_timed(q, k, v, events, **kw):
+    """retention_chunkwise_fwd recording the four phase events (see the C header)."""
+    return retention_chunkwise_fwd(q, k, v, events=events, **kw)
+
+
+def retention_recurrent_step(q, k, v, state, gamma=None, theta=None, pos=None, out=None, stream=None):
+    """One decode step: state <- gamma state + k^T v (in place); returns o = q state.
+
+    q, k [B,H,dk]; v [B,H,dv]; state float32 [B,H,dk,dv]; pos int64 [B] device
+    tensor of absolute positions (needed with theta).
+    """
+    torch = _torch()
+    _check_dev(q, k, v, state, pos)
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=v.dtype, device=v.device)
+    _check_dev(out)
+    if pos is not None and pos.dtype != torch.int64:
+        raise TypeError("pos must be int64")
+    _g, g = _host_floats(gamma, H, "gamma")
+    _t, th = _host_floats(theta, dk // 2, "theta")
+    st = load_library().retention_recurrent_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state), B, H, dk, dv, _dtype_code(q), g, th, _ptr(pos),
+        _stream(stream),
+    )
+    _raise(st, "retention_recurrent_step")
+    return out

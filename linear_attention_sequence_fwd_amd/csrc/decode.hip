@@ -1,0 +1,125 @@
+// Recurrent decode step: one token per sequence, state updated in place.
+//
+// "RetNet Guide: Retentive Networks & The Impossible Triangle", section "2. The
+// Recurrent Representation for Constant-Memory O(1) Decoding":
+//     S <- gamma S + k^T v ;  o = q S   (the updated S)
+// The step is a pure read-modify-write of the float32 d_k x d_v state, so it
+// is bound by HBM: each state element is read once and written once with
+// 16-byte non-temporal accesses (the state of a large batch does not fit in
+// the caches, and keeping it out of them leaves room for q, k, v). One
+// workgroup owns one (sequence, head); a row of the state is covered by
+// d_v/4 consecutive threads, so a wavefront streams 1 KiB contiguous per
+// access. The output row o = q S' is accumulated per thread over its rows and
+// reduced across row groups in LDS.
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ret {
+
+typedef float f32v4 __attribute__((ext_vector_type(4)));
+
+constexpr int kStepThreads = 256;
+constexpr int kStepMaxDk = 4096;
+
+template <bool BF16>
+__device__ __forceinline__ float load_elem(const void* p, size_t i) {
+    if (BF16) return bf16_to_f32(static_cast<const u16*>(p)[i]);
+    return static_cast<const float*>(p)[i];
+}
+
+template <bool BF16, int UNROLL>
+__global__ __launch_bounds__(kStepThreads) void recurrent_step_kernel(StepArgs a, HeadParams hp) {
+    __shared__ float qs[kStepMaxDk];
+    __shared__ float ks[kStepMaxDk];
+    __shared__ f32v4 red[kStepThreads];
+
+    const int bh = blockIdx.x;
+    const int b = bh / a.H;
+    const int h = bh % a.H;
+    const int tid = threadIdx.x;
+    const float gam = hp.gamma[h];
+
+    // ---- q, k of this (sequence, head) in float32, rotated when asked
+    const size_t qk0 = static_cast<size_t>(bh) * a.dk;
+    if (hp.has_theta) {
+        const double position = static_cast<double>(a.pos[b]);
+        for (int j = tid; j < a.dk / 2; j += kStepThreads) {
+            float c, s;
+            rot_cs(position, hp.theta[j], c, s);
+            const float qr = load_elem<BF16>(a.q, qk0 + 2 * j), qi = load_elem<BF16>(a.q, qk0 + 2 * j + 1);
+            const float kr = load_elem<BF16>(a.k, qk0 + 2 * j), ki = load_elem<BF16>(a.k, qk0 + 2 * j + 1);
+            qs[2 * j] = qr * c - qi * s;
+            qs[2 * j + 1] = qr * s + qi * c;
+            ks[2 * j] = kr * c - ki * s;
+            ks[2 * j + 1] = kr * s + ki * c;
+        }
+    } else {
+        for (int j = tid; j < a.dk; j += kStepThreads) {
+            qs[j] = load_elem<BF16>(a.q, qk0 + j);
+            ks[j] = load_elem<BF16>(a.k, qk0 + j);
+        }
+    }
+    __syncthreads();
+
+    // ---- stream the state: thread (rg, c4) owns columns 4*c4..4*c4+3 of rows rg, rg+RG, ...
+    const int tpr = a.dv / 4;
+    const int rgs = kStepThreads / tpr;
+    const int rg = tid / tpr;
+    const int c4 = tid % tpr;
+    f32v4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (rg < rgs) {
+        const size_t v0 = static_cast<size_t>(bh) * a.dv + 4 * c4;
+        const f32v4 vv = {load_elem<BF16>(a.v, v0), load_elem<BF16>(a.v, v0 + 1), load_elem<BF16>(a.v, v0 + 2),
+                          load_elem<BF16>(a.v, v0 + 3)};
+        f32v4* S = reinterpret_cast<f32v4*>(a.state + static_cast<size_t>(bh) * a.dk * a.dv) + c4;
+        const size_t row_stride = static_cast<size_t>(tpr);
+        int i = rg;
+        for (; i + (UNROLL - 1) * rgs < a.dk; i += UNROLL * rgs) {
+            f32v4 s[UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) s[u] = __builtin_nontemporal_load(S + (i + u * rgs) * row_stride);
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int row = i + u * rgs;
+                const float kk = ks[row], qq = qs[row];
+                s[u] = gam * s[u] + kk * vv;
+                acc += qq * s[u];
+                __builtin_nontemporal_store(s[u], S + row * row_stride);
+            }
+        }
+        for (; i < a.dk; i += rgs) {
+            f32v4 s = __builtin_nontemporal_load(S + i * row_stride);
+            s = gam * s + ks[i] * vv;
+            acc += qs[i] * s;
+            __builtin_nontemporal_store(s, S + i * row_stride);
+        }
+    }
+    red[tid] = acc;
+    __syncthreads();
+
+    // ---- reduce over row groups and write o
+    if (tid < tpr) {
+        f32v4 o = red[tid];
+        for (int g = 1; g < rgs; ++g) o += red[g * tpr + tid];
+        const size_t o0 = static_cast<size_t>(bh) * a.dv + 4 * tid;
+        if (BF16) {
+            u16* op = static_cast<u16*>(a.o) + o0;
+            *reinterpret_cast<uint2*>(op) = make_uint2(pack2_bf16(o[0], o[1]), pack2_bf16(o[2], o[3]));
+        } else {
+            *reinterpret_cast<f32v4*>(static_cast<float*>(a.o) + o0) = o;
+        }
+    }
+}
+
+hipError_t launch_recurrent_step(const StepArgs& a, const HeadParams& hp, hipStream_t st) {
+    if (a.dk > kStepMaxDk || a.dv % 4 != 0 || a.dv / 4 > kStepThreads) return hipErrorInvalidValue;
+    dim3 grid(a.B * a.H), block(kStepThreads);
+    if (a.bf16)
+        recurrent_step_kernel<true, 8><<<grid, block, 0, st>>>(a, hp);
+    else
+        recurrent_step_kernel<false, 8><<<grid, block, 0, st>>>(a, hp);
+    return hipGetLastError();
+}
+
+}  // namespace ret

@@ -1,0 +1,48 @@
+// Scan of per-segment end states for the segmented chunkwise forward.
+//
+// "RetNet Guide: Retentive Networks & The Impossible Triangle", section "3. The
+// Chunkwise Recurrent Representation": the state carried from one chunk to the
+// next is decayed by gamma^L and gains the chunk's own contribution. Applied
+// to runs of chunks (segments), the start state of segment s is
+//     S_in(s) = gamma^seg_len S_in(s-1) + T_(s-1)
+// with T_(s-1) the end state of segment s-1 built from a zero state.
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ret {
+
+// Exclusive scan of segment end states with factor gamma^seg_len, in place.
+// Slot 0 receives the initial state (state_in or zeros); slot s >= 1 holds the
+// end state of segment s-1 built from zero and is replaced by the state at
+// the start of segment s. One thread owns four consecutive state elements and
+// walks the segments in order; a wavefront covers 256 contiguous elements.
+__global__ __launch_bounds__(256) void segment_scan_kernel(float* ws, const float* state_in, int H, int nseg,
+                                                           int per_bh, int seg_len, HeadParams hp) {
+    const int bh = blockIdx.y;
+    const int e4 = blockIdx.x * blockDim.x + threadIdx.x;
+    if (e4 * 4 >= per_bh) return;
+    const float gL = gamma_pow(log2_gamma(hp.gamma[bh % H]), seg_len);
+    float4* w = reinterpret_cast<float4*>(ws + static_cast<size_t>(bh) * nseg * per_bh) + e4;
+    const size_t stride = per_bh / 4;
+    float4 acc = state_in ? reinterpret_cast<const float4*>(state_in + static_cast<size_t>(bh) * per_bh)[e4]
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+    w[0] = acc;
+    for (int s = 1; s < nseg; ++s) {
+        const float4 t = w[s * stride];
+        acc.x = gL * acc.x + t.x;
+        acc.y = gL * acc.y + t.y;
+        acc.z = gL * acc.z + t.z;
+        acc.w = gL * acc.w + t.w;
+        w[s * stride] = acc;
+    }
+}
+
+hipError_t launch_segment_scan(const ChunkArgs& a, const HeadParams& hp, hipStream_t st) {
+    const int per_bh = a.dk * a.dv;
+    dim3 grid((per_bh / 4 + 255) / 256, a.B * a.H);
+    segment_scan_kernel<<<grid, dim3(256), 0, st>>>(a.ws, a.state_in, a.H, a.nseg, per_bh, a.seg_len, hp);
+    return hipGetLastError();
+}
+
+}  // namespace ret

@@ -1,0 +1,173 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function include/retention.h declares,
+and reject bad arguments with the documented status codes before any HIP
+call: every call here fails validation, so nothing reaches the GPU.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "retention.h")
+PKG = os.path.join(ROOT, "linear_attention_sequence_fwd_amd")
+
+OK, NULL, SHAPE, DTYPE, GAMMA, UNSUP, WS, ALIGN = 0, 1, 2, 3, 4, 5, 6, 7
+F32, BF16 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import linear_attention_sequence_fwd_amd as ret
+
+    if not os.path.exists(ret.LIB_PATH):
+        from linear_attention_sequence_fwd_amd import build
+
+        build.build(verbose=False)
+    return ret.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(retention_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("retention_parallel_fwd", "retention_chunkwise_fwd", "retention_recurrent_step",
+              "retention_chunkwise_workspace_size", "retention_status_string", "retention_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.retention_abi_version() == 1
+    for s in range(9):
+        assert len(lib.retention_status_string(s)) > 0
+    assert lib.retention_status_string(123) == b"unknown status"
+
+
+A = 0x10000  # fake, 16-byte aligned device address: validation never dereferences it
+
+
+def chunk(lib, **kw):
+    a = dict(q=A, k=A, v=A, o=A, B=1, H=2, N=100, dk=64, dv=64, dtype=BF16, chunk=64, gamma=None,
+             theta=None, pos0=0, state_in=None, state_out=None, segments=0, ws=None, ws_bytes=0)
+    a.update(kw)
+    return lib.retention_chunkwise_fwd(a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], a["N"], a["dk"],
+                                       a["dv"], a["dtype"], a["chunk"], a["gamma"], a["theta"], a["pos0"],
+                                       a["state_in"], a["state_out"], a["segments"], a["ws"], a["ws_bytes"],
+                                       None)
+
+
+def par(lib, **kw):
+    a = dict(q=A, k=A, v=A, o=A, B=1, H=2, N=100, dk=64, dv=64, dtype=BF16, gamma=None, theta=None, pos0=0)
+    a.update(kw)
+    return lib.retention_parallel_fwd(a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], a["N"], a["dk"], a["dv"],
+                                      a["dtype"], a["gamma"], a["theta"], a["pos0"], None)
+
+
+def step(lib, **kw):
+    a = dict(q=A, k=A, v=A, o=A, state=A, B=1, H=2, dk=64, dv=64, dtype=BF16, gamma=None, theta=None, pos=None)
+    a.update(kw)
+    return lib.retention_recurrent_step(a["q"], a["k"], a["v"], a["o"], a["state"], a["B"], a["H"], a["dk"],
+                                        a["dv"], a["dtype"], a["gamma"], a["theta"], a["pos"], None)
+
+
+def floats(*x):
+    arr = (ctypes.c_float * len(x))(*x)
+    return ctypes.cast(arr, ctypes.c_void_p), arr
+
+
+def test_null_pointers(lib):
+    for key in ("q", "k", "v", "o"):
+        assert chunk(lib, **{key: None}) == NULL
+        assert par(lib, **{key: None}) == NULL
+        assert step(lib, **{key: None}) == NULL
+    assert step(lib, state=None) == NULL
+    th, _keep = floats(*([1.0] * 32))
+    assert step(lib, theta=th, pos=None) == NULL
+
+
+def test_bad_shapes_and_dtype(lib):
+    for key in ("B", "H", "N", "dk", "dv"):
+        assert chunk(lib, **{key: 0}) == SHAPE
+        assert par(lib, **{key: -1}) == SHAPE
+    assert chunk(lib, dtype=7) == DTYPE
+    assert step(lib, dtype=-1) == DTYPE
+    th, _keep = floats(*([1.0] * 32))
+    assert chunk(lib, dk=63, theta=th, dtype=F32) == SHAPE
+    assert chunk(lib, segments=-1) == SHAPE
+
+
+def test_gamma_and_theta_validation(lib):
+    for bad in (0.0, -0.5, 1.5, float("nan"), float("inf")):
+        g, _keep = floats(0.9, bad)
+        assert chunk(lib, gamma=g) == GAMMA
+        assert par(lib, gamma=g) == GAMMA
+        assert step(lib, gamma=g) == GAMMA
+    th, _keep = floats(*([1.0] * 31 + [float("nan")]))
+    assert chunk(lib, theta=th) == GAMMA
+
+
+def test_unsupported_sets(lib):
+    assert chunk(lib, chunk=32) == UNSUP
+    assert chunk(lib, chunk=100) == UNSUP
+    assert chunk(lib, dk=96) == UNSUP          # bf16 dk outside {64,128,256}
+    assert chunk(lib, dv=96) == UNSUP          # bf16 dv not a multiple of 64
+    assert chunk(lib, dtype=F32, dk=256, chunk=64) == UNSUP  # f32 chunk*dk > 8192
+    assert chunk(lib, H=129) == UNSUP
+    th, _keep = floats(*([1.0] * 256))
+    assert chunk(lib, dk=512, theta=th, dtype=F32) == UNSUP
+    assert par(lib, dtype=F32, dk=256) == UNSUP
+    assert step(lib, dv=1028) == UNSUP
+    assert step(lib, dv=6) == UNSUP
+
+
+def test_alignment(lib):
+    assert chunk(lib, q=A + 2) == ALIGN
+    assert chunk(lib, state_in=A + 4) == ALIGN
+    assert par(lib, o=A + 8) == ALIGN
+    assert step(lib, state=A + 4) == ALIGN
+
+
+def test_workspace_contract(lib):
+    # few heads: the library splits the sequence and needs a workspace
+    need = lib.retention_chunkwise_workspace_size(1, 2, 4096, 64, 64, BF16, 64, 0)
+    assert need > 0
+    assert chunk(lib, N=4096, ws=None, ws_bytes=0) == WS
+    assert chunk(lib, N=4096, ws=A, ws_bytes=need - 1) == WS
+    # invalid sizes report 0
+    assert lib.retention_chunkwise_workspace_size(1, 2, 4096, 64, 64, BF16, 33, 0) == 0
+    assert lib.retention_chunkwise_workspace_size(0, 2, 4096, 64, 64, BF16, 64, 0) == 0
+    # many heads: no split, no workspace
+    assert lib.retention_chunkwise_workspace_size(4, 16, 8192, 256, 512, BF16, 128, 0) == 0
+
+
+@pytest.mark.parametrize("cfg", [(1, 8, 64, 64, BF16, 64), (1, 8, 128, 128, BF16, 128), (2, 8, 64, 64, F32, 64),
+                                 (1, 1, 64, 64, F32, 64)])
+def test_workspace_does_not_depend_on_length(lib, cfg):
+    """The resident state of the method does not grow with context ("Retentive
+    Networks (RetNet)" implementer checklist); neither does this workspace."""
+    B, H, dk, dv, dt, C = cfg
+    sizes = {lib.retention_chunkwise_workspace_size(B, H, N, dk, dv, dt, C, 0) for N in (1024, 8192, 65536, 1 << 20)}
+    assert len(sizes) == 1
+
+
+def test_product_path_never_touches_the_oracle():
+    imp = re.compile(r"^\s*(from\s+oracle\b|import\s+oracle\b|from\s+\.+oracle\b)", re.M)
+    inc = re.compile(r'#\s*include\s*[<"][^>"]*oracle', re.M)
+    for dirpath, _, files in os.walk(PKG):
+        for f in files:
+            path = os.path.join(dirpath, f)
+            if f.endswith(".py"):
+                assert not imp.search(open(path).read()), path
+            elif f.endswith((".hip", ".hpp", ".cpp", ".h")):
+                assert not inc.search(open(path).read()), path

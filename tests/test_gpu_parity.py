@@ -1,0 +1,335 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 oracle.
+
+Small cases compare every output element and the carried state; they span
+several tiles and end in a ragged chunk. The full-size workloads run exactly
+as the benchmark launches them and are compared on sampled heads the oracle
+recomputes one by one. Tolerances (relative L2, tensor-wide and per head):
+1e-5 for float32 inputs, 2e-2 for bf16 inputs with float32 accumulation.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_sequence_fwd_amd as R
+from linear_attention_sequence_fwd_amd import workloads as W
+from oracle import retention as orc
+
+from helpers import BF16_TOL, F32_TOL, assert_close, to64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    R.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _inputs(B, H, N, dk, dv, dtype, seed):
+    q, k, v = W.make_qkv(B, H, N, dk, dv, dtype, seed, device="cpu")
+    return q, k, v
+
+
+def _gammas_for(H, gamma):
+    return orc.head_gammas(H) if gamma is None else np.asarray(gamma, dtype=np.float64)
+
+
+# ------------------------------------------------------------ single-head fp32 workload
+
+
+def test_single_head_f32_all_forms():
+    w = W.WORKLOADS["single_head_f32"]
+    q, k, v, _ = W.make_workload("single_head_f32", device="cpu")
+    ref, ref_s = orc.recurrent(to64(q), to64(k), to64(v), orc.head_gammas(1))
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o_par = R.retention_parallel_fwd(qd, kd, vd)
+    o_chk, s_chk = R.retention_chunkwise_fwd(qd, kd, vd, chunk=w["chunk"], return_state=True)
+    state = torch.zeros((1, 1, 64, 64), dtype=torch.float32, device=DEV)
+    outs = []
+    for n in range(w["N"]):
+        outs.append(R.retention_recurrent_step(qd[:, :, n].contiguous(), kd[:, :, n].contiguous(),
+                                               vd[:, :, n].contiguous(), state))
+    o_rec = torch.stack(outs, dim=2)
+    torch.cuda.synchronize()
+    assert_close(to64(o_par), ref, F32_TOL, "parallel")
+    assert_close(to64(o_chk), ref, F32_TOL, "chunkwise")
+    assert_close(to64(s_chk), ref_s, F32_TOL, "chunkwise state")
+    assert_close(to64(o_rec), ref, F32_TOL, "recurrent")
+    assert_close(to64(state), ref_s, F32_TOL, "recurrent state")
+
+
+# ------------------------------------------------------------ small bf16 chunkwise, many shapes
+
+BF16_CHUNK_CASES = [
+    # B, H, N, dk, dv, chunk, rotary, state_in, segments
+    (2, 3, 300, 64, 64, 64, False, False, 0),
+    (1, 2, 333, 128, 128, 128, True, True, 0),
+    (2, 2, 257, 256, 128, 128, False, True, 0),
+    (1, 2, 200, 256, 192, 64, True, False, 0),
+    (2, 3, 640, 64, 128, 64, True, True, 3),
+    (1, 1, 1000, 128, 64, 128, False, True, 4),
+    (1, 2, 1, 64, 64, 64, True, True, 0),
+    (1, 2, 63, 128, 128, 128, False, False, 0),
+    (1, 1, 4100, 64, 64, 64, True, True, 0),
+]
+
+
+@pytest.mark.parametrize("case", BF16_CHUNK_CASES, ids=lambda c: "B{}H{}N{}dk{}dv{}C{}rot{}st{}seg{}".format(*c))
+def test_chunkwise_bf16_small(case):
+    B, H, N, dk, dv, C, rot, st, seg = case
+    q, k, v = _inputs(B, H, N, dk, dv, torch.bfloat16, seed=N + dk + dv)
+    theta = W.rotary_theta(dk) if rot else None
+    s0 = torch.randn((B, H, dk, dv), generator=torch.Generator().manual_seed(7)) * 0.1 if st else None
+    pos0 = 17 if rot else 0
+    ref, ref_s = orc.recurrent(to64(q), to64(k), to64(v), orc.head_gammas(H),
+                               theta=None if theta is None else to64(theta), pos0=pos0,
+                               state0=None if s0 is None else to64(s0))
+    o, s = R.retention_chunkwise_fwd(q.to(DEV), k.to(DEV), v.to(DEV), chunk=C, theta=theta, pos0=pos0,
+                                     state_in=None if s0 is None else s0.to(DEV), return_state=True,
+                                     segments=seg)
+    torch.cuda.synchronize()
+    assert_close(to64(o), ref, BF16_TOL, "O")
+    assert_close(to64(s), ref_s, BF16_TOL, "state")
+
+
+# ------------------------------------------------------------ small bf16 parallel
+
+BF16_PAR_CASES = [
+    (2, 3, 300, 64, 64, False),
+    (1, 2, 513, 128, 128, True),
+    (1, 2, 260, 256, 128, False),
+    (1, 2, 130, 256, 192, True),
+    (1, 1, 1, 64, 64, False),
+]
+
+
+@pytest.mark.parametrize("case", BF16_PAR_CASES, ids=lambda c: "B{}H{}N{}dk{}dv{}rot{}".format(*c))
+def test_parallel_bf16_small(case):
+    B, H, N, dk, dv, rot = case
+    q, k, v = _inputs(B, H, N, dk, dv, torch.bfloat16, seed=3 * N + dk)
+    theta = W.rotary_theta(dk) if rot else None
+    ref = orc.parallel(to64(q), to64(k), to64(v), orc.head_gammas(H),
+                       theta=None if theta is None else to64(theta), pos0=5)
+    o = R.retention_parallel_fwd(q.to(DEV), k.to(DEV), v.to(DEV), theta=theta, pos0=5)
+    torch.cuda.synchronize()
+    assert_close(to64(o), ref, BF16_TOL, "O")
+
+
+# ------------------------------------------------------------ float32 paths
+
+F32_CASES = [
+    # B, H, N, dk, dv, chunk, rotary, state_in
+    (2, 2, 150, 16, 48, 64, True, True),
+    (1, 3, 300, 64, 64, 128, False, False),
+    (1, 2, 129, 128, 16, 64, True, True),
+    (2, 1, 77, 32, 128, 128, False, True),
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=lambda c: "B{}H{}N{}dk{}dv{}C{}rot{}st{}".format(*c))
+def test_f32_chunkwise_and_parallel(case):
+    B, H, N, dk, dv, C, rot, st = case
+    q, k, v = _inputs(B, H, N, dk, dv, torch.float32, seed=N + 11)
+    theta = W.rotary_theta(dk) if rot else None
+    s0 = torch.randn((B, H, dk, dv), generator=torch.Generator().manual_seed(3)) * 0.1 if st else None
+    th64 = None if theta is None else to64(theta)
+    ref, ref_s = orc.recurrent(to64(q), to64(k), to64(v), orc.head_gammas(H), theta=th64, pos0=3,
+                               state0=None if s0 is None else to64(s0))
+    o, s = R.retention_chunkwise_fwd(q.to(DEV), k.to(DEV), v.to(DEV), chunk=C, theta=theta, pos0=3,
+                                     state_in=None if s0 is None else s0.to(DEV), return_state=True)
+    o_seg = R.retention_chunkwise_fwd(q.to(DEV), k.to(DEV), v.to(DEV), chunk=C, theta=theta, pos0=3,
+                                      state_in=None if s0 is None else s0.to(DEV), segments=2)
+    ref_p = orc.parallel(to64(q), to64(k), to64(v), orc.head_gammas(H), theta=th64, pos0=3)
+    if dk <= 128:
+        o_par = R.retention_parallel_fwd(q.to(DEV), k.to(DEV), v.to(DEV), theta=theta, pos0=3)
+    torch.cuda.synchronize()
+    assert_close(to64(o), ref, F32_TOL, "chunkwise O")
+    assert_close(to64(s), ref_s, F32_TOL, "chunkwise state")
+    assert_close(to64(o_seg), ref, F32_TOL, "segmented O")
+    if dk <= 128:
+        assert_close(to64(o_par), ref_p, F32_TOL, "parallel O")
+
+
+# ------------------------------------------------------------ decode steps
+
+
+@pytest.mark.parametrize("dtype,rot", [(torch.bfloat16, False), (torch.bfloat16, True), (torch.float32, True)])
+def test_recurrent_step_small(dtype, rot):
+    B, H, dk, dv, steps = 3, 2, 64, 96, 5
+    s0, qs, ks, vs = W.make_decode(B, H, dk, dv, dtype, steps, 0.01, seed=9)
+    theta = W.rotary_theta(dk) if rot else None
+    pos = torch.tensor([0, 77, 4000], dtype=torch.int64)
+    g = orc.head_gammas(H)
+    S = to64(s0)
+    state = s0.to(DEV)
+    tol = BF16_TOL if dtype == torch.bfloat16 else F32_TOL
+    for t in range(steps):
+        o_ref, S = orc.decode_step(to64(qs[t]), to64(ks[t]), to64(vs[t]), S, g,
+                                   theta=None if theta is None else to64(theta),
+                                   pos=(pos + t).numpy() if rot else None)
+        o = R.retention_recurrent_step(qs[t].to(DEV), ks[t].to(DEV), vs[t].to(DEV), state, theta=theta,
+                                       pos=(pos + t).to(DEV) if rot else None)
+        torch.cuda.synchronize()
+        assert_close(to64(o), o_ref, tol, f"o step {t}")
+    assert_close(to64(state), S, tol, "final state")
+
+
+# ------------------------------------------------------------ the full-size workloads
+
+
+def test_msr_bf16_rotary_full():
+    """Multi-scale bf16 workload with rotation, every element."""
+    w = W.WORKLOADS["msr_bf16_rotary"]
+    q, k, v, theta = W.make_workload("msr_bf16_rotary", device="cpu")
+    ref, ref_s = orc.recurrent(to64(q), to64(k), to64(v), orc.head_gammas(w["H"]), theta=to64(theta))
+    o, s = R.retention_chunkwise_fwd(q.to(DEV), k.to(DEV), v.to(DEV), chunk=w["chunk"], theta=theta,
+                                     return_state=True)
+    torch.cuda.synchronize()
+    assert_close(to64(o), ref, BF16_TOL, "O")
+    assert_close(to64(s), ref_s, BF16_TOL, "state")
+
+
+def _sampled_heads_check(q, k, v, o, s, H, heads, theta=None):
+    for (b, h) in heads:
+        ref, ref_s = orc.recurrent(to64(q[b:b + 1, h:h + 1]), to64(k[b:b + 1, h:h + 1]),
+                                   to64(v[b:b + 1, h:h + 1]), orc.head_gammas(H)[h:h + 1],
+                                   theta=theta)
+        assert_close(to64(o[b:b + 1, h:h + 1]), ref, BF16_TOL, f"O head {(b, h)}")
+        if s is not None:
+            assert_close(to64(s[b:b + 1, h:h + 1]), ref_s, BF16_TOL, f"state head {(b, h)}")
+
+
+def test_layer7b_full_sampled_heads():
+    w = W.WORKLOADS["layer7b_bf16"]
+    q, k, v, _ = W.make_workload("layer7b_bf16", device=DEV)
+    o, s = R.retention_chunkwise_fwd(q, k, v, chunk=w["chunk"], return_state=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()
+    _sampled_heads_check(q, k, v, o, s, w["H"], heads=[(0, 0), (3, 15), (2, 7)])
+
+
+def test_longctx_full_sampled_heads():
+    w = W.WORKLOADS["longctx_bf16"]
+    q, k, v, _ = W.make_workload("longctx_bf16", device=DEV)
+    o, s = R.retention_chunkwise_fwd(q, k, v, chunk=w["chunk"], return_state=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()
+    _sampled_heads_check(q, k, v, o, s, w["H"], heads=[(0, 0), (0, 7)])
+
+
+def test_longctx_parallel_crossover_lengths_sampled():
+    w = W.WORKLOADS["longctx_bf16"]
+    q, k, v, _ = W.make_workload("longctx_bf16", device=DEV)
+    for n in w["parallel_lengths"]:
+        qn, kn, vn = q[:, :, :n].contiguous(), k[:, :, :n].contiguous(), v[:, :, :n].contiguous()
+        o_par = R.retention_parallel_fwd(qn, kn, vn)
+        o_chk = R.retention_chunkwise_fwd(qn, kn, vn, chunk=w["chunk"])
+        torch.cuda.synchronize()
+        for h in (1, 6):
+            ref = orc.parallel(to64(qn[:, h:h + 1]), to64(kn[:, h:h + 1]), to64(vn[:, h:h + 1]),
+                               orc.head_gammas(w["H"])[h:h + 1])
+            assert_close(to64(o_par[:, h:h + 1]), ref, BF16_TOL, f"parallel N={n} head {h}")
+            assert_close(to64(o_chk[:, h:h + 1]), ref, BF16_TOL, f"chunkwise N={n} head {h}")
+
+
+def test_decode_full_512_steps_sampled_heads():
+    w = W.WORKLOADS["decode_bf16"]
+    s0, qs, ks, vs = W.make_decode_workload(device=DEV)
+    state = s0.clone()
+    heads = [(0, 0), (17, 9), (63, 15)]
+    H = w["H"]
+    S = {bh: to64(s0[bh[0], bh[1]])[None, None] for bh in heads}
+    g = orc.head_gammas(H)
+    outs = {bh: [] for bh in heads}
+    refs = {bh: [] for bh in heads}
+    for t in range(w["steps"]):
+        o = R.retention_recurrent_step(qs[t], ks[t], vs[t], state)
+        for (b, h) in heads:
+            outs[(b, h)].append(o[b, h].float())
+    torch.cuda.synchronize()
+    qs_c, ks_c, vs_c = qs.cpu(), ks.cpu(), vs.cpu()
+    for (b, h) in heads:
+        St = S[(b, h)]
+        for t in range(w["steps"]):
+            o_ref, St = orc.decode_step(to64(qs_c[t, b:b + 1, h:h + 1]), to64(ks_c[t, b:b + 1, h:h + 1]),
+                                        to64(vs_c[t, b:b + 1, h:h + 1]), St, g[h:h + 1])
+            refs[(b, h)].append(o_ref[0, 0])
+        got = torch.stack(outs[(b, h)]).cpu().numpy().astype(np.float64)
+        assert_close(got, np.stack(refs[(b, h)]), BF16_TOL, f"o over 512 steps, head {(b, h)}", per_head_axes=0)
+        assert_close(to64(state[b, h]), St[0, 0], BF16_TOL, f"final state head {(b, h)}", per_head_axes=0)
+
+
+# ------------------------------------------------------------ edge cases and properties
+
+
+def test_future_inf_key_does_not_leak():
+    """The causal mask is a select: an infinite key at the last position must
+    not turn earlier outputs into NaN (Inf * 0 would)."""
+    B, H, N, dk, dv = 1, 2, 200, 64, 64
+    q, k, v = _inputs(B, H, N, dk, dv, torch.bfloat16, seed=21)
+    k_bad = k.clone()
+    k_bad[:, :, -1, :] = float("inf")
+    for fn in (lambda a, b, c: R.retention_chunkwise_fwd(a, b, c, chunk=64),
+               lambda a, b, c: R.retention_parallel_fwd(a, b, c)):
+        good = fn(q.to(DEV), k.to(DEV), v.to(DEV))
+        bad = fn(q.to(DEV), k_bad.to(DEV), v.to(DEV))
+        torch.cuda.synchronize()
+        assert torch.equal(good[:, :, :-1], bad[:, :, :-1])
+
+
+def test_repeatable_bitwise():
+    q, k, v = _inputs(2, 4, 1000, 128, 128, torch.bfloat16, seed=5)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    a = R.retention_chunkwise_fwd(qd, kd, vd, chunk=128)
+    b = R.retention_chunkwise_fwd(qd, kd, vd, chunk=128)
+    c = R.retention_parallel_fwd(qd, kd, vd)
+    d = R.retention_parallel_fwd(qd, kd, vd)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(c, d)
+
+
+def test_state_in_out_alias_and_handoff():
+    B, H, N, dk, dv = 1, 2, 500, 128, 128
+    q, k, v = _inputs(B, H, N, dk, dv, torch.bfloat16, seed=33)
+    theta = W.rotary_theta(dk)
+    ref, ref_s = orc.recurrent(to64(q), to64(k), to64(v), orc.head_gammas(H), theta=to64(theta))
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    n1 = 200
+    state = torch.zeros((B, H, dk, dv), dtype=torch.float32, device=DEV)
+    o1 = R.retention_chunkwise_fwd(qd[:, :, :n1].contiguous(), kd[:, :, :n1].contiguous(),
+                                   vd[:, :, :n1].contiguous(), chunk=128, theta=theta, state_in=state,
+                                   state_out=state)
+    o2 = R.retention_chunkwise_fwd(qd[:, :, n1:].contiguous(), kd[:, :, n1:].contiguous(),
+                                   vd[:, :, n1:].contiguous(), chunk=128, theta=theta, pos0=n1, state_in=state,
+                                   state_out=state, segments=3)
+    torch.cuda.synchronize()
+    assert_close(np.concatenate([to64(o1), to64(o2)], axis=2), ref, BF16_TOL, "handed-off O")
+    assert_close(to64(state), ref_s, BF16_TOL, "handed-off state")
+
+
+@pytest.mark.parametrize("gammas", [[1.0, 0.99], [0.5, 0.75], [0.9, 0.999999]])
+def test_custom_gammas(gammas):
+    B, H, N, dk, dv = 1, 2, 300, 64, 64
+    q, k, v = _inputs(B, H, N, dk, dv, torch.bfloat16, seed=44)
+    g = np.asarray(gammas, dtype=np.float32).astype(np.float64)
+    ref = orc.parallel(to64(q), to64(k), to64(v), g)
+    for o in (R.retention_chunkwise_fwd(q.to(DEV), k.to(DEV), v.to(DEV), chunk=64, gamma=list(g)),
+              R.retention_chunkwise_fwd(q.to(DEV), k.to(DEV), v.to(DEV), chunk=64, gamma=list(g), segments=2),
+              R.retention_parallel_fwd(q.to(DEV), k.to(DEV), v.to(DEV), gamma=list(g))):
+        torch.cuda.synchronize()
+        assert_close(to64(o), ref, BF16_TOL, f"gammas {gammas}")
+
+
+def test_segment_count_invariance_full_msr():
+    w = W.WORKLOADS["msr_bf16_rotary"]
+    q, k, v, theta = W.make_workload("msr_bf16_rotary", device=DEV)
+    outs = [R.retention_chunkwise_fwd(q, k, v, chunk=w["chunk"], theta=theta, segments=s) for s in (1, 5, 0)]
+    torch.cuda.synchronize()
+    base = to64(outs[0])
+    for o in outs[1:]:
+        assert_close(to64(o), base, 5e-3, "segments vs single pass")
