@@ -10,14 +10,18 @@
 //
 // One workgroup owns one (batch, head, value tile, sequence segment) and walks
 // the segment's chunks in order. Per chunk it runs four contractions on
-// v_mfma_f32_16x16x32_bf16:
-//   G4  S      = gamma^L S + Kx^T V   (Kx = keys scaled by xi; S in AGPR/VGPR accumulators)
+// v_mfma_f32_16x16x32_bf16, in this order:
+//   G3  O^T    = S^T Q^T, scaled by zeta   (the previous chunk's state, bf16 copy in LDS)
+//   G4  S      = gamma^L S + Kx^T V   (Kx = keys scaled by xi; S in float32 accumulators)
 //   G1  P^T    = K Q^T, masked by D (D generated in registers)
-//   G3  O^T    = S^T Q^T, scaled by zeta   (reads the previous chunk's state)
 //   G2  O^T   += V^T P^T
-// Each wave owns two 16-row blocks of the chunk (rows w and NRB-1-w, which
-// balances the causal work) and a band of rows of S. The state is kept in
-// float32 accumulators; a bf16 copy of it lives in LDS for G3.
+// G3 runs before G4 so that the bf16 copy of the new state can be written
+// straight after G4, without keeping a converted copy of S alive across G1/G2.
+// Each wave owns one 16-row block of the chunk (paired so that the two waves
+// sharing a SIMD carry equal causal work) and a grid cell of S tiles. The state
+// is kept in float32 accumulators; a bf16 copy of it lives in LDS for G3.
+// With C/16 waves per workgroup (8 for 128-token chunks) two waves share each
+// SIMD, so one wave's LDS and HBM waits overlap the other's MFMAs.
 //
 // LDS (bf16, 16-byte units XOR-swizzled against bank conflicts):
 //   kbuf  keys of the chunk, first as K^T scaled by xi (for G4) and then as K
@@ -34,27 +38,59 @@
 
 namespace ret {
 
+// Split of the (DK/16) x (DVT/16) state tiles over the waves: NG column
+// groups times NW/NG row groups, chosen to minimise the LDS fragment reads of
+// G4 per wave (proportional to row tiles + column tiles).
+constexpr int pick_state_col_groups(int tm, int tn, int nw) {
+    int best = 1, best_cost = 1 << 30;
+    for (int ng = 1; ng <= nw; ng *= 2) {
+        const int mg = nw / ng;
+        if (nw % ng != 0 || tn % ng != 0 || tm % mg != 0) continue;
+        const int cost = tm / mg + tn / ng;
+        if (cost < best_cost) {
+            best_cost = cost;
+            best = ng;
+        }
+    }
+    return best;
+}
+
 template <int DK, int DVT, int C>
 struct ChunkGeo {
-    static constexpr int NW = C / 32;         // waves per workgroup
+    static constexpr int NW = C / 16;         // waves per workgroup: one 16-row block of the chunk each
     static constexpr int NTHR = NW * 64;
-    static constexpr int NRB = C / 16;        // 16-row blocks in a chunk
     static constexpr int KSQ = DK / 32;       // 32-wide contraction steps over dk
     static constexpr int KST = C / 32;        // 32-wide contraction steps over tokens
-    static constexpr int MT = DK / 16 / NW;   // 16-row tiles of S per wave
-    static constexpr int NTV = DVT / 16;      // 16-column tiles of the value tile
-    static constexpr int KB = (C / 8) * (DK / 8);   // 8x8 key blocks per chunk
-    static constexpr int VB = (C / 8) * (DVT / 8);  // 8x8 value blocks per chunk
+    static constexpr int TM = DK / 16;        // 16-row tiles of S
+    static constexpr int NTV = DVT / 16;      // 16-column tiles of S and O
+    static constexpr int NG = pick_state_col_groups(TM, NTV, NW);
+    static constexpr int MG = NW / NG;
+    static constexpr int MT = TM / MG;        // S row tiles per wave
+    static constexpr int NT = NTV / NG;       // S column tiles per wave
+    static constexpr int BWK = stage_width(C, DK, NTHR);   // staging block widths
+    static constexpr int BWV = stage_width(C, DVT, NTHR);
+    static constexpr int KB = (C / 8) * (DK / BWK);   // key staging blocks per chunk
+    static constexpr int VB = (C / 8) * (DVT / BWV);  // value staging blocks per chunk
     static constexpr int KPT = (KB + NTHR - 1) / NTHR;
     static constexpr int VPT = (VB + NTHR - 1) / NTHR;
     static_assert(C == 64 || C == 128, "chunk");
     static_assert(DK % 64 == 0 && DVT % 64 == 0, "tile sizes");
-    static_assert(MT >= 1 && MT * NTV <= 32, "state accumulators per wave");
+    static_assert(MG * MT == TM && NG * NT == NTV, "state split");
 };
 
+// Row block owned by wave w: waves w and w + NW/2 (which the dispatcher puts
+// on the same SIMD) get blocks b and NW-1-b, so the causal work per SIMD is
+// the same for every SIMD.
+template <int NW>
+__device__ __forceinline__ int wave_row_block(int w) {
+    return w < NW / 2 ? w : (3 * NW / 2 - 1) - w;
+}
+
 template <int DK, int DVT, int C, bool STATE_ONLY>
-__global__ __launch_bounds__((C / 32) * 64) void chunk_bf16_kernel(ChunkArgs a, HeadParams hp) {
+__global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, HeadParams hp) {
     using G = ChunkGeo<DK, DVT, C>;
+    constexpr int UK = DK / 8;  // 16-byte units in a row of K (row-major) and of S^T
+    constexpr int UC = C / 8;   // 16-byte units in a row of K^T and V^T
     __shared__ __attribute__((aligned(16))) u16 kbuf[C * DK];
     __shared__ __attribute__((aligned(16))) u16 vbuf[DVT * C];
     __shared__ __attribute__((aligned(16))) u16 sbuf[STATE_ONLY ? 8 : DVT * DK];
@@ -87,11 +123,12 @@ __global__ __launch_bounds__((C / 32) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     const u16* Vg = a.v + tok0 * a.dv + vt * DVT;
     u16* Og = a.o + tok0 * a.dv + vt * DVT;
 
-    const int d_base = wave * G::MT * 16;  // first S row owned by this wave
-    const int rbs[2] = {wave, G::NRB - 1 - wave};
+    const int rb = wave_row_block<G::NW>(wave);      // this wave's 16 chunk rows
+    const int d_base = (wave % G::MG) * G::MT * 16;  // this wave's S rows ...
+    const int c_base = (wave / G::MG) * G::NT * 16;  // ... and S columns (within the value tile)
 
     // ---- initial state
-    f32x4 sacc[G::MT][G::NTV];
+    f32x4 sacc[G::MT][G::NT];
     const float* s_src = nullptr;
     if (!STATE_ONLY) {
         if (a.nseg > 1)
@@ -102,26 +139,29 @@ __global__ __launch_bounds__((C / 32) * 64) void chunk_bf16_kernel(ChunkArgs a, 
 #pragma unroll
     for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < G::NTV; ++nt)
+        for (int nt = 0; nt < G::NT; ++nt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int d = d_base + mt * 16 + grp * 4 + r;
-                const int c = vt * DVT + nt * 16 + l16;
+                const int c = vt * DVT + c_base + nt * 16 + l16;
                 sacc[mt][nt][r] = s_src ? s_src[static_cast<size_t>(d) * a.dv + c] : 0.0f;
             }
     bool have_state = (s_src != nullptr);
-    if (!STATE_ONLY && have_state) {
+
+    // bf16 copy of this wave's state tiles into S^T (row = value column, 4 consecutive dk)
+    auto write_state_copy = [&](int l16_, int grp_) {
 #pragma unroll
         for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < G::NTV; ++nt) {
-                const int d = d_base + mt * 16 + grp * 4;
-                const int c = nt * 16 + l16;
-                uint2 w = make_uint2(pack2_bf16(sacc[mt][nt][0], sacc[mt][nt][1]),
-                                     pack2_bf16(sacc[mt][nt][2], sacc[mt][nt][3]));
-                *reinterpret_cast<uint2*>(&sbuf[sidx<DK>(c, d)]) = w;
+            for (int nt = 0; nt < G::NT; ++nt) {
+                const int d = d_base + mt * 16 + grp_ * 4;
+                const int c = c_base + nt * 16 + l16_;
+                const uint2 w = make_uint2(pack2_bf16(sacc[mt][nt][0], sacc[mt][nt][1]),
+                                           pack2_bf16(sacc[mt][nt][2], sacc[mt][nt][3]));
+                *reinterpret_cast<uint2*>(&sbuf[swz<UK>(c, d >> 3) + (d & 7)]) = w;
             }
-    }
+    };
+    if (!STATE_ONLY && have_state) write_state_copy(l16, grp);
 
     // ---- per-lane decay constants
     // D[i][j] = gamma^(i-j) with i = 16 rb + l16, j = 16 jt + 4 grp + r:
@@ -129,101 +169,126 @@ __global__ __launch_bounds__((C / 32) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     float dlane[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) dlane[r] = exp2f(static_cast<float>(l16 - 4 * grp - r) * lg2f);
-    const float zeta0 = exp2f(static_cast<float>(16 * rbs[0] + l16 + 1) * lg2f);
-    const float zeta1 = exp2f(static_cast<float>(16 * rbs[1] + l16 + 1) * lg2f);
+    const float zeta = exp2f(static_cast<float>(16 * rb + l16 + 1) * lg2f);
     const float gC = gamma_pow(lg2, C);
 
     // ---- prefetch the first chunk
-    uint4 kr[G::KPT][8];
-    uint4 vr[G::VPT][8];
-    uint4 qf[2][G::KSQ];
+    BlockRows<G::BWK> kr[G::KPT];
+    BlockRows<G::BWV> vr[G::VPT];
+    uint4 qf[G::KSQ];
+    auto load_q = [&](int t, int Lq) {
+        const int row = rb * 16 + l16;
+        const u16* p = Qg + static_cast<size_t>(t + row) * DK + grp * 8;
+#pragma unroll
+        for (int s = 0; s < G::KSQ; ++s)
+            qf[s] = row < Lq ? *reinterpret_cast<const uint4*>(p + s * 32) : make_uint4(0, 0, 0, 0);
+    };
     {
         const int L0 = min(C, t_end - t_begin);
-        load_blocks<DK, G::KB, G::KPT, G::NTHR>(kr, Kg + static_cast<size_t>(t_begin) * DK, DK, L0, tid);
-        load_blocks<DVT, G::VB, G::VPT, G::NTHR>(vr, Vg + static_cast<size_t>(t_begin) * a.dv, a.dv, L0, tid);
-        if (!STATE_ONLY) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int row = rbs[i] * 16 + l16;
-#pragma unroll
-                for (int s = 0; s < G::KSQ; ++s)
-                    qf[i][s] = row < L0 ? *reinterpret_cast<const uint4*>(Qg + static_cast<size_t>(t_begin + row) * DK + s * 32 + grp * 8)
-                                        : make_uint4(0, 0, 0, 0);
-            }
-        }
+        load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR>(kr, Kg + static_cast<size_t>(t_begin) * DK, DK, L0, tid);
+        load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR>(vr, Vg + static_cast<size_t>(t_begin) * a.dv, a.dv, L0, tid);
+        if (!STATE_ONLY) load_q(t_begin, L0);
     }
 
     for (int ch = 0; ch < nch; ++ch) {
-        // Per-iteration copies the compiler cannot prove loop-invariant: LDS
-        // addresses and decay factors are recomputed each chunk (a few VALU
-        // ops under the MFMAs) instead of being hoisted and held in registers.
-        int lane_it = lane;
+        // Per-iteration copies the compiler cannot prove loop-invariant: the
+        // block-write addresses and the decay factors are recomputed each
+        // chunk (a few VALU ops under the MFMAs) instead of being hoisted out
+        // of the loop and held in registers for its whole length.
+        int tid_it = tid;
         float lg2_it = lg2f;
-        asm volatile("" : "+v"(lane_it), "+v"(lg2_it));
-        const int l16 = lane_it & 15;
-        const int grp = lane_it >> 4;
-        const float lg2f = lg2_it;
+        asm volatile("" : "+v"(tid_it), "+v"(lg2_it));
+        const float lg2c = lg2_it;
+        const int l16c = tid_it & 15;
+        const int grpc = (tid_it & 63) >> 4;
         const int t0 = t_begin + ch * C;
         const int L = min(C, t_end - t0);
         const bool has_next = (ch + 1) < nch;
         const int t1 = t0 + C;
         const int L1 = has_next ? min(C, t_end - t1) : 0;
 
-        // ---- 1. rotate keys; K^T (scaled by xi) and V^T into LDS
+        // ---- 1. rotate keys; K^T (scaled by xi) and V^T into LDS; rotate queries
 #pragma unroll
         for (int u = 0; u < G::KPT; ++u) {
-            const int idx = tid + u * G::NTHR;
+            const int idx = tid_it + u * G::NTHR;
             if (idx < G::KB) {
                 int tb, cb;
-                block_coords<DK>(idx, tb, cb);
+                block_coords<DK, G::BWK>(idx, tb, cb);
                 if (hp.has_theta) {
 #pragma unroll
                     for (int q = 0; q < 8; ++q)
                         if (tb * 8 + q < L)
-                            kr[u][q] = rotate8_bf16(kr[u][q], hp, cb * 4,
-                                                    static_cast<double>(a.pos0 + t0 + tb * 8 + q));
+                            rotate_row<G::BWK>(kr[u].w[q], hp, cb * (G::BWK / 2),
+                                               static_cast<double>(a.pos0 + t0 + tb * 8 + q));
                 }
                 float xi[8];
 #pragma unroll
-                for (int q = 0; q < 8; ++q) xi[q] = exp2f(static_cast<float>(L - 1 - tb * 8 - q) * lg2f);
+                for (int q = 0; q < 8; ++q) xi[q] = exp2f(static_cast<float>(L - 1 - tb * 8 - q) * lg2c);
 #pragma unroll
-                for (int c = 0; c < 8; ++c) {
+                for (int c = 0; c < G::BWK; ++c) {
                     uint32_t w[4];
 #pragma unroll
                     for (int p = 0; p < 4; ++p) {
-                        const float lo = bf16_to_f32(static_cast<u16>(elem16(kr[u][2 * p], c))) * xi[2 * p];
-                        const float hi = bf16_to_f32(static_cast<u16>(elem16(kr[u][2 * p + 1], c))) * xi[2 * p + 1];
+                        const float lo = bf16_to_f32(static_cast<u16>(elem16(kr[u].w[2 * p], c))) * xi[2 * p];
+                        const float hi = bf16_to_f32(static_cast<u16>(elem16(kr[u].w[2 * p + 1], c))) * xi[2 * p + 1];
                         w[p] = pack2_bf16(lo, hi);
                     }
-                    *reinterpret_cast<uint4*>(&kbuf[tidx<C>(cb * 8 + c, tb * 8)]) = make_uint4(w[0], w[1], w[2], w[3]);
+                    *reinterpret_cast<uint4*>(&kbuf[swz<UC>(cb * G::BWK + c, tb)]) = make_uint4(w[0], w[1], w[2], w[3]);
                 }
             }
         }
 #pragma unroll
         for (int u = 0; u < G::VPT; ++u) {
-            const int idx = tid + u * G::NTHR;
+            const int idx = tid_it + u * G::NTHR;
             if (idx < G::VB) {
                 int tb, cb;
-                block_coords<DVT>(idx, tb, cb);
+                block_coords<DVT, G::BWV>(idx, tb, cb);
 #pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    uint32_t w[4];
-#pragma unroll
-                    for (int p = 0; p < 4; ++p)
-                        w[p] = elem16(vr[u][2 * p], c) | (elem16(vr[u][2 * p + 1], c) << 16);
-                    *reinterpret_cast<uint4*>(&vbuf[tidx<C>(cb * 8 + c, tb * 8)]) = make_uint4(w[0], w[1], w[2], w[3]);
-                }
+                for (int c = 0; c < G::BWV; ++c)
+                    *reinterpret_cast<uint4*>(&vbuf[swz<UC>(cb * G::BWV + c, tb)]) = block_column(vr[u], c);
             }
         }
-        __syncthreads();  // A
+        if (!STATE_ONLY && hp.has_theta) {
+            const int row = rb * 16 + l16;
+            if (row < L) {
+#pragma unroll
+                for (int s = 0; s < G::KSQ; ++s)
+                    qf[s] = rotate8_bf16(qf[s], hp, s * 16 + grp * 4, static_cast<double>(a.pos0 + t0 + row));
+            }
+        }
+        __syncthreads();  // A: K^T, V^T written
 
-        // ---- 2. G4: S = gamma^L S + Kx^T V
+        // ---- 2. G3: O^T = S^T Q^T with the previous chunk's state, times zeta
+        f32x4 oacc[G::NTV];
+        if (!STATE_ONLY) {
+#pragma unroll
+            for (int nt = 0; nt < G::NTV; ++nt) oacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (have_state) {
+                const FragAddr<UK> fa_s(l16c, grpc);  // S^T rows 16 nt + l16, dk 32 s + 8 grp
+#pragma unroll
+                for (int nt = 0; nt < G::NTV; ++nt) {
+#pragma unroll
+                    for (int s = 0; s < G::KSQ; ++s) {
+                        const uint4 af = *reinterpret_cast<const uint4*>(&sbuf[fa_s.at(nt, s)]);
+                        oacc[nt] = mfma16x16x32(af, qf[s], oacc[nt]);
+                    }
+                }
+#pragma unroll
+                for (int nt = 0; nt < G::NTV; ++nt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) oacc[nt][r] *= zeta;
+            }
+        }
+
+        // ---- 3. G4: S = gamma^L S + Kx^T V on this wave's tiles
         {
             const float gL = (L == C) ? gC : gamma_pow(lg2, L);
+            const FragAddr<UC> fa_kt(d_base + l16c, grpc);  // K^T rows d_base + 16 mt + l16, tokens 32 t + 8 grp
+            const FragAddr<UC> fa_vt(c_base + l16c, grpc);  // V^T rows c_base + 16 nt + l16, tokens 32 t + 8 grp
 #pragma unroll
             for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < G::NTV; ++nt)
+                for (int nt = 0; nt < G::NT; ++nt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) sacc[mt][nt][r] *= gL;
 #pragma unroll
@@ -231,186 +296,128 @@ __global__ __launch_bounds__((C / 32) * 64) void chunk_bf16_kernel(ChunkArgs a, 
                 if (t * 32 < L) {
                     uint4 af[G::MT];
 #pragma unroll
-                    for (int mt = 0; mt < G::MT; ++mt)
-                        af[mt] = *reinterpret_cast<const uint4*>(&kbuf[tidx<C>(d_base + mt * 16 + l16, t * 32 + grp * 8)]);
+                    for (int mt = 0; mt < G::MT; ++mt) af[mt] = *reinterpret_cast<const uint4*>(&kbuf[fa_kt.at(mt, t)]);
 #pragma unroll
-                    for (int nt = 0; nt < G::NTV; ++nt) {
-                        const uint4 bfr = *reinterpret_cast<const uint4*>(&vbuf[tidx<C>(nt * 16 + l16, t * 32 + grp * 8)]);
+                    for (int nt = 0; nt < G::NT; ++nt) {
+                        const uint4 bfr = *reinterpret_cast<const uint4*>(&vbuf[fa_vt.at(nt, t)]);
 #pragma unroll
                         for (int mt = 0; mt < G::MT; ++mt) sacc[mt][nt] = mfma16x16x32(af[mt], bfr, sacc[mt][nt]);
                     }
                 }
-                __builtin_amdgcn_sched_barrier(0);
             }
         }
 
         if (STATE_ONLY) {
             __syncthreads();  // everyone done reading kbuf / vbuf
             if (has_next) {
-                load_blocks<DK, G::KB, G::KPT, G::NTHR>(kr, Kg + static_cast<size_t>(t1) * DK, DK, L1, tid);
-                load_blocks<DVT, G::VB, G::VPT, G::NTHR>(vr, Vg + static_cast<size_t>(t1) * a.dv, a.dv, L1, tid);
+                load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR>(kr, Kg + static_cast<size_t>(t1) * DK, DK, L1, tid);
+                load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR>(vr, Vg + static_cast<size_t>(t1) * a.dv, a.dv, L1, tid);
             }
             continue;
         }
 
-        __syncthreads();  // B: K^T reads done
+        __syncthreads();  // B: S^T and K^T reads done
 
-        // ---- 3. K row-major into LDS; prefetch next chunk's keys and values
+        // ---- 4. new bf16 state copy, K row-major into LDS, prefetch next keys/values
+        write_state_copy(l16c, grpc);
+        have_state = true;
 #pragma unroll
         for (int u = 0; u < G::KPT; ++u) {
-            const int idx = tid + u * G::NTHR;
+            const int idx = tid_it + u * G::NTHR;
             if (idx < G::KB) {
                 int tb, cb;
-                block_coords<DK>(idx, tb, cb);
+                block_coords<DK, G::BWK>(idx, tb, cb);
 #pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    *reinterpret_cast<uint4*>(&kbuf[kidx_rm<DK>(tb * 8 + q, cb * 8)]) = kr[u][q];
+                for (int q = 0; q < 8; ++q) {
+                    if constexpr (G::BWK == 8) {
+                        *reinterpret_cast<uint4*>(&kbuf[swz<UK>(tb * 8 + q, cb)]) =
+                            make_uint4(kr[u].w[q][0], kr[u].w[q][1], kr[u].w[q][2], kr[u].w[q][3]);
+                    } else {
+                        *reinterpret_cast<uint2*>(&kbuf[swz<UK>(tb * 8 + q, cb >> 1) + 4 * (cb & 1)]) =
+                            make_uint2(kr[u].w[q][0], kr[u].w[q][1]);
+                    }
+                }
             }
         }
         if (has_next) {
-            load_blocks<DK, G::KB, G::KPT, G::NTHR>(kr, Kg + static_cast<size_t>(t1) * DK, DK, L1, tid);
-            load_blocks<DVT, G::VB, G::VPT, G::NTHR>(vr, Vg + static_cast<size_t>(t1) * a.dv, a.dv, L1, tid);
+            load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR>(kr, Kg + static_cast<size_t>(t1) * DK, DK, L1, tid);
+            load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR>(vr, Vg + static_cast<size_t>(t1) * a.dv, a.dv, L1, tid);
         }
-        // rotate this chunk's queries while the writes settle
-        if (hp.has_theta) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int row = rbs[i] * 16 + l16;
-                if (row < L) {
-#pragma unroll
-                    for (int s = 0; s < G::KSQ; ++s)
-                        qf[i][s] = rotate8_bf16(qf[i][s], hp, s * 16 + grp * 4,
-                                                static_cast<double>(a.pos0 + t0 + row));
-                }
-            }
-        }
-        __syncthreads();  // C
+        __syncthreads();  // C: K row-major written
 
-        // ---- 4. G1: P^T = K Q^T, decay mask in registers, one 32-token step at
-        //         a time, packed straight into bf16 B operands for G2
-        const int rb_max = rbs[1];  // rbs[1] >= rbs[0]
-        uint4 pf[2][G::KST];
+        // ---- 5. G1: P^T = K Q^T for this wave's rows, decay mask in registers,
+        //         one 32-token step at a time, packed into bf16 B operands for G2.
+        //         Steps entirely above the diagonal are skipped (one uniform
+        //         branch per step); inside a step both 16-key halves run and
+        //         the mask zeroes what lies above the diagonal.
+        uint4 pf[G::KST];
+        {
+            const FragAddr<UK> fa_k(l16c, grpc);  // K rows 16 jt + l16, dk 32 s + 8 grp
 #pragma unroll
-        for (int t = 0; t < G::KST; ++t) {
-            f32x4 pa[2][2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) pa[i][0] = pa[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int jt = 2 * t + hh;
-                if (jt <= rb_max && jt * 16 < L) {
+            for (int t = 0; t < G::KST; ++t) {
+                pf[t] = make_uint4(0, 0, 0, 0);
+                if (2 * t <= rb) {
+                    f32x4 pa[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
                     for (int s = 0; s < G::KSQ; ++s) {
-                        const uint4 af = *reinterpret_cast<const uint4*>(&kbuf[kidx_rm<DK>(jt * 16 + l16, s * 32 + grp * 8)]);
 #pragma unroll
-                        for (int i = 0; i < 2; ++i)
-                            if (jt <= rbs[i]) pa[i][hh] = mfma16x16x32(af, qf[i][s], pa[i][hh]);
+                        for (int hh = 0; hh < 2; ++hh) {
+                            const uint4 af = *reinterpret_cast<const uint4*>(&kbuf[fa_k.at(2 * t + hh, s)]);
+                            pa[hh] = mfma16x16x32(af, qf[s], pa[hh]);
+                        }
                     }
-                }
-            }
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int delta = rb - (2 * t + hh);
+                        const float blk = exp2f(static_cast<float>(16 * delta) * lg2c);
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int delta = rbs[i] - (2 * t + hh);
-                    const float blk = exp2f(static_cast<float>(16 * delta) * lg2f);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        float val = 0.0f;
-                        if (delta > 0 || (delta == 0 && l16 >= 4 * grp + r)) val = pa[i][hh][r] * (dlane[r] * blk);
-                        pa[i][hh][r] = val;
+                        for (int r = 0; r < 4; ++r) {
+                            float val = 0.0f;
+                            if (delta > 0 || (delta == 0 && l16 >= 4 * grp + r)) val = pa[hh][r] * (dlane[r] * blk);
+                            pa[hh][r] = val;
+                        }
                     }
+                    pf[t] = make_uint4(pack2_bf16(pa[0][0], pa[0][1]), pack2_bf16(pa[0][2], pa[0][3]),
+                                       pack2_bf16(pa[1][0], pa[1][1]), pack2_bf16(pa[1][2], pa[1][3]));
                 }
-                pf[i][t] = make_uint4(pack2_bf16(pa[i][0][0], pa[i][0][1]), pack2_bf16(pa[i][0][2], pa[i][0][3]),
-                                      pack2_bf16(pa[i][1][0], pa[i][1][1]), pack2_bf16(pa[i][1][2], pa[i][1][3]));
             }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-
-        // ---- 5. G3: O^T = S^T Q^T (previous state), times zeta
-        f32x4 oacc[2][G::NTV];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int nt = 0; nt < G::NTV; ++nt) oacc[i][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (have_state) {
-#pragma unroll
-            for (int nt = 0; nt < G::NTV; ++nt) {
-#pragma unroll
-                for (int s = 0; s < G::KSQ; ++s) {
-                    const uint4 af = *reinterpret_cast<const uint4*>(&sbuf[sidx<DK>(nt * 16 + l16, s * 32 + grp * 8)]);
-#pragma unroll
-                    for (int i = 0; i < 2; ++i) oacc[i][nt] = mfma16x16x32(af, qf[i][s], oacc[i][nt]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-#pragma unroll
-            for (int nt = 0; nt < G::NTV; ++nt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    oacc[0][nt][r] *= zeta0;
-                    oacc[1][nt][r] *= zeta1;
-                }
         }
 
         // ---- prefetch next chunk's queries (qf is dead for this chunk now)
-        if (has_next) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int row = rbs[i] * 16 + l16;
-#pragma unroll
-                for (int s = 0; s < G::KSQ; ++s)
-                    qf[i][s] = row < L1 ? *reinterpret_cast<const uint4*>(Qg + static_cast<size_t>(t1 + row) * DK + s * 32 + grp * 8)
-                                        : make_uint4(0, 0, 0, 0);
-            }
-        }
+        if (has_next) load_q(t1, L1);
 
         // ---- 6. G2: O^T += V^T P^T
+        {
+            const FragAddr<UC> fa_v2a(l16c, grpc >> 1);        // V^T tokens 32 t + 4 grp .. +3
+            const FragAddr<UC> fa_v2b(l16c, 2 + (grpc >> 1));  // V^T tokens 32 t + 16 + 4 grp .. +3
+            const int v2half = 4 * (grpc & 1);
 #pragma unroll
-        for (int t = 0; t < G::KST; ++t) {
-            if (2 * t <= rb_max && t * 32 < L) {
+            for (int t = 0; t < G::KST; ++t) {
+                if (2 * t <= rb) {
 #pragma unroll
-                for (int nt = 0; nt < G::NTV; ++nt) {
-                    const int row = nt * 16 + l16;
-                    const uint2 lo = *reinterpret_cast<const uint2*>(&vbuf[tidx<C>(row, t * 32 + grp * 4)]);
-                    const uint2 hi = *reinterpret_cast<const uint2*>(&vbuf[tidx<C>(row, t * 32 + 16 + grp * 4)]);
-                    const uint4 af = make_uint4(lo.x, lo.y, hi.x, hi.y);
-#pragma unroll
-                    for (int i = 0; i < 2; ++i)
-                        if (2 * t <= rbs[i]) oacc[i][nt] = mfma16x16x32(af, pf[i][t], oacc[i][nt]);
+                    for (int nt = 0; nt < G::NTV; ++nt) {
+                        const uint2 lo = *reinterpret_cast<const uint2*>(&vbuf[fa_v2a.at(nt, t) + v2half]);
+                        const uint2 hi = *reinterpret_cast<const uint2*>(&vbuf[fa_v2b.at(nt, t) + v2half]);
+                        oacc[nt] = mfma16x16x32(make_uint4(lo.x, lo.y, hi.x, hi.y), pf[t], oacc[nt]);
+                    }
                 }
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
 
         // ---- 7. store O (bf16)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int row = rbs[i] * 16 + l16;
+        {
+            const int row = rb * 16 + l16;
             if (row < L) {
-                u16* orow = Og + static_cast<size_t>(t0 + row) * a.dv;
+                u16* orow = Og + static_cast<size_t>(t0 + row) * a.dv + grp * 4;
 #pragma unroll
                 for (int nt = 0; nt < G::NTV; ++nt) {
-                    const uint2 w = make_uint2(pack2_bf16(oacc[i][nt][0], oacc[i][nt][1]),
-                                               pack2_bf16(oacc[i][nt][2], oacc[i][nt][3]));
-                    *reinterpret_cast<uint2*>(orow + nt * 16 + grp * 4) = w;
+                    const uint2 w = make_uint2(pack2_bf16(oacc[nt][0], oacc[nt][1]),
+                                               pack2_bf16(oacc[nt][2], oacc[nt][3]));
+                    *reinterpret_cast<uint2*>(orow + nt * 16) = w;
                 }
             }
         }
-        __syncthreads();  // D: reads of kbuf, vbuf, sbuf done
-
-        // ---- 8. bf16 copy of the new state for the next chunk's G3
-#pragma unroll
-        for (int mt = 0; mt < G::MT; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < G::NTV; ++nt) {
-                const int d = d_base + mt * 16 + grp * 4;
-                const int c = nt * 16 + l16;
-                const uint2 w = make_uint2(pack2_bf16(sacc[mt][nt][0], sacc[mt][nt][1]),
-                                           pack2_bf16(sacc[mt][nt][2], sacc[mt][nt][3]));
-                *reinterpret_cast<uint2*>(&sbuf[sidx<DK>(c, d)]) = w;
-            }
-        have_state = true;
+        __syncthreads();  // D: reads of kbuf and vbuf done before the next chunk's writes
     }
 
     // ---- final state
@@ -423,11 +430,11 @@ __global__ __launch_bounds__((C / 32) * 64) void chunk_bf16_kernel(ChunkArgs a, 
 #pragma unroll
         for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < G::NTV; ++nt)
+            for (int nt = 0; nt < G::NT; ++nt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int d = d_base + mt * 16 + grp * 4 + r;
-                    const int c = vt * DVT + nt * 16 + l16;
+                    const int c = vt * DVT + c_base + nt * 16 + l16;
                     s_dst[static_cast<size_t>(d) * a.dv + c] = sacc[mt][nt][r];
                 }
     }

@@ -6,8 +6,9 @@
 // D[n][m] = gamma^(n-m) for n >= m and 0 otherwise.
 //
 // The N x N score matrix is never formed in memory. One workgroup owns one
-// block of BQ query rows (one head, one value tile) and walks the key blocks
-// from its own (diagonal) block backwards. For each key block it forms
+// block of BQ query rows (one head, one value tile; one 16-row block per wave)
+// and walks the key blocks from its own (diagonal) block backwards. For each
+// key block it forms
 // P^T = K Q^T on v_mfma_f32_16x16x32_bf16, multiplies by D generated in
 // registers (a per-lane factor times a per-block factor), and accumulates
 // O^T += V^T P^T. There is no softmax, so nothing is rescaled between blocks.
@@ -23,21 +24,24 @@ namespace ret {
 
 template <int DK, int DVT, int BQ>
 struct ParGeo {
-    static constexpr int NW = BQ / 32;
+    static constexpr int NW = BQ / 16;  // waves: one 16-row block of the query block each
     static constexpr int NTHR = NW * 64;
-    static constexpr int NRB = BQ / 16;
     static constexpr int KSQ = DK / 32;
     static constexpr int KST = BQ / 32;
     static constexpr int NTV = DVT / 16;
-    static constexpr int KB = (BQ / 8) * (DK / 8);
-    static constexpr int VB = (BQ / 8) * (DVT / 8);
+    static constexpr int BWK = stage_width(BQ, DK, NTHR);
+    static constexpr int BWV = stage_width(BQ, DVT, NTHR);
+    static constexpr int KB = (BQ / 8) * (DK / BWK);
+    static constexpr int VB = (BQ / 8) * (DVT / BWV);
     static constexpr int KPT = (KB + NTHR - 1) / NTHR;
     static constexpr int VPT = (VB + NTHR - 1) / NTHR;
 };
 
 template <int DK, int DVT, int BQ>
-__global__ __launch_bounds__((BQ / 32) * 64) void parallel_bf16_kernel(ParallelArgs a, HeadParams hp) {
+__global__ __launch_bounds__((BQ / 16) * 64) void parallel_bf16_kernel(ParallelArgs a, HeadParams hp) {
     using G = ParGeo<DK, DVT, BQ>;
+    constexpr int UK = DK / 8;
+    constexpr int UC = BQ / 8;
     __shared__ __attribute__((aligned(16))) u16 kbuf[BQ * DK];
     __shared__ __attribute__((aligned(16))) u16 vbuf[DVT * BQ];
 
@@ -65,7 +69,8 @@ __global__ __launch_bounds__((BQ / 32) * 64) void parallel_bf16_kernel(ParallelA
     const u16* Vg = a.v + tok0 * a.dv + vt * DVT;
     u16* Og = a.o + tok0 * a.dv + vt * DVT;
 
-    const int rbs[2] = {wave, G::NRB - 1 - wave};
+    // row block of this wave; the two waves sharing a SIMD get blocks b and NW-1-b
+    const int rb = wave < G::NW / 2 ? wave : (3 * G::NW / 2 - 1) - wave;
     const int q0 = qb * BQ;
     const int Lq = min(BQ, a.N - q0);
 
@@ -75,26 +80,23 @@ __global__ __launch_bounds__((BQ / 32) * 64) void parallel_bf16_kernel(ParallelA
 #pragma unroll
     for (int r = 0; r < 4; ++r) dlane[r] = exp2f(static_cast<float>(l16 - 4 * grp - r) * lg2f);
 
-    // queries of this block, rotated, in MFMA operand registers
-    uint4 qf[2][G::KSQ];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int row = rbs[i] * 16 + l16;
+    // queries of this wave's rows, rotated, in MFMA operand registers
+    uint4 qf[G::KSQ];
+    {
+        const int row = rb * 16 + l16;
+        const u16* p = Qg + static_cast<size_t>(q0 + row) * DK + grp * 8;
 #pragma unroll
         for (int s = 0; s < G::KSQ; ++s) {
-            uint4 x = row < Lq ? *reinterpret_cast<const uint4*>(Qg + static_cast<size_t>(q0 + row) * DK + s * 32 + grp * 8)
-                               : make_uint4(0, 0, 0, 0);
+            uint4 x = row < Lq ? *reinterpret_cast<const uint4*>(p + s * 32) : make_uint4(0, 0, 0, 0);
             if (hp.has_theta && row < Lq)
                 x = rotate8_bf16(x, hp, s * 16 + grp * 4, static_cast<double>(a.pos0 + q0 + row));
-            qf[i][s] = x;
+            qf[s] = x;
         }
     }
 
-    f32x4 oacc[2][G::NTV];
+    f32x4 oacc[G::NTV];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int nt = 0; nt < G::NTV; ++nt) oacc[i][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < G::NTV; ++nt) oacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // number of key blocks with any entry of D above float32 underflow:
     // block qb - m has its largest decay gamma^(m BQ - BQ + 1)
@@ -105,133 +107,118 @@ __global__ __launch_bounds__((BQ / 32) * 64) void parallel_bf16_kernel(ParallelA
         nkb = min(nkb, mmax + 1);
     }
 
-    uint4 kr[G::KPT][8];
-    uint4 vr[G::VPT][8];
-    load_blocks<DK, G::KB, G::KPT, G::NTHR>(kr, Kg + static_cast<size_t>(q0) * DK, DK, Lq, tid);
-    load_blocks<DVT, G::VB, G::VPT, G::NTHR>(vr, Vg + static_cast<size_t>(q0) * a.dv, a.dv, Lq, tid);
+    BlockRows<G::BWK> kr[G::KPT];
+    BlockRows<G::BWV> vr[G::VPT];
+    load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR>(kr, Kg + static_cast<size_t>(q0) * DK, DK, Lq, tid);
+    load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR>(vr, Vg + static_cast<size_t>(q0) * a.dv, a.dv, Lq, tid);
 
     for (int m = 0; m < nkb; ++m) {
-        // Per-iteration copies the compiler cannot prove loop-invariant (see the
-        // chunkwise kernel): addresses and decay factors are recomputed per block.
-        int lane_it = lane;
+        // Per-iteration copies the compiler cannot prove loop-invariant: block
+        // write addresses and decay factors are recomputed per key block rather
+        // than held in registers across the loop.
+        int tid_it = tid;
         float lg2_it = lg2f;
-        asm volatile("" : "+v"(lane_it), "+v"(lg2_it));
-        const int l16 = lane_it & 15;
-        const int grp = lane_it >> 4;
-        const float lg2f = lg2_it;
+        asm volatile("" : "+v"(tid_it), "+v"(lg2_it));
+        const float lg2c = lg2_it;
+        const int l16c = tid_it & 15;
+        const int grpc = (tid_it & 63) >> 4;
         const int kb = qb - m;
         const int k0 = kb * BQ;
         const int Lk = min(BQ, a.N - k0);
         const bool diag = (m == 0);
 
-        // keys row-major and V^T into LDS
+        // keys row-major (rotated) and V^T into LDS
 #pragma unroll
         for (int u = 0; u < G::KPT; ++u) {
-            const int idx = tid + u * G::NTHR;
+            const int idx = tid_it + u * G::NTHR;
             if (idx < G::KB) {
                 int tb, cb;
-                block_coords<DK>(idx, tb, cb);
+                block_coords<DK, G::BWK>(idx, tb, cb);
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
-                    uint4 x = kr[u][q];
                     if (hp.has_theta && tb * 8 + q < Lk)
-                        x = rotate8_bf16(x, hp, cb * 4, static_cast<double>(a.pos0 + k0 + tb * 8 + q));
-                    *reinterpret_cast<uint4*>(&kbuf[kidx_rm<DK>(tb * 8 + q, cb * 8)]) = x;
+                        rotate_row<G::BWK>(kr[u].w[q], hp, cb * (G::BWK / 2),
+                                           static_cast<double>(a.pos0 + k0 + tb * 8 + q));
+                    if constexpr (G::BWK == 8) {
+                        *reinterpret_cast<uint4*>(&kbuf[swz<UK>(tb * 8 + q, cb)]) =
+                            make_uint4(kr[u].w[q][0], kr[u].w[q][1], kr[u].w[q][2], kr[u].w[q][3]);
+                    } else {
+                        *reinterpret_cast<uint2*>(&kbuf[swz<UK>(tb * 8 + q, cb >> 1) + 4 * (cb & 1)]) =
+                            make_uint2(kr[u].w[q][0], kr[u].w[q][1]);
+                    }
                 }
             }
         }
 #pragma unroll
         for (int u = 0; u < G::VPT; ++u) {
-            const int idx = tid + u * G::NTHR;
+            const int idx = tid_it + u * G::NTHR;
             if (idx < G::VB) {
                 int tb, cb;
-                block_coords<DVT>(idx, tb, cb);
+                block_coords<DVT, G::BWV>(idx, tb, cb);
 #pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    uint32_t w[4];
-#pragma unroll
-                    for (int p = 0; p < 4; ++p) w[p] = elem16(vr[u][2 * p], c) | (elem16(vr[u][2 * p + 1], c) << 16);
-                    *reinterpret_cast<uint4*>(&vbuf[tidx<BQ>(cb * 8 + c, tb * 8)]) = make_uint4(w[0], w[1], w[2], w[3]);
-                }
+                for (int c = 0; c < G::BWV; ++c)
+                    *reinterpret_cast<uint4*>(&vbuf[swz<UC>(cb * G::BWV + c, tb)]) = block_column(vr[u], c);
             }
         }
         __syncthreads();
 
         if (m + 1 < nkb) {
             const int kn = (kb - 1) * BQ;
-            load_blocks<DK, G::KB, G::KPT, G::NTHR>(kr, Kg + static_cast<size_t>(kn) * DK, DK, BQ, tid);
-            load_blocks<DVT, G::VB, G::VPT, G::NTHR>(vr, Vg + static_cast<size_t>(kn) * a.dv, a.dv, BQ, tid);
+            load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR>(kr, Kg + static_cast<size_t>(kn) * DK, DK, BQ, tid);
+            load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR>(vr, Vg + static_cast<size_t>(kn) * a.dv, a.dv, BQ, tid);
         }
 
         const float blkf = gamma_pow(lg2, static_cast<double>(q0 - k0));
-        f32x4 pacc[2][G::NRB];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int jt = 0; jt < G::NRB; ++jt) pacc[i][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int jt = 0; jt < G::NRB; ++jt) {
-            if ((!diag || jt <= rbs[1]) && jt * 16 < Lk) {
-#pragma unroll
-                for (int s = 0; s < G::KSQ; ++s) {
-                    const uint4 af = *reinterpret_cast<const uint4*>(&kbuf[kidx_rm<DK>(jt * 16 + l16, s * 32 + grp * 8)]);
-#pragma unroll
-                    for (int i = 0; i < 2; ++i)
-                        if (!diag || jt <= rbs[i]) pacc[i][jt] = mfma16x16x32(af, qf[i][s], pacc[i][jt]);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        uint4 pf[2][G::KST];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-#pragma unroll
-            for (int jt = 0; jt < G::NRB; ++jt) {
-                const int delta = rbs[i] - jt;
-                const float blk = exp2f(static_cast<float>(16 * delta) * lg2f) * blkf;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float val = 0.0f;
-                    const bool keep = !diag || delta > 0 || (delta == 0 && l16 >= 4 * grp + r);
-                    if (keep) val = pacc[i][jt][r] * (dlane[r] * blk);
-                    pacc[i][jt][r] = val;
-                }
-            }
-#pragma unroll
-            for (int t = 0; t < G::KST; ++t)
-                pf[i][t] = make_uint4(pack2_bf16(pacc[i][2 * t][0], pacc[i][2 * t][1]),
-                                      pack2_bf16(pacc[i][2 * t][2], pacc[i][2 * t][3]),
-                                      pack2_bf16(pacc[i][2 * t + 1][0], pacc[i][2 * t + 1][1]),
-                                      pack2_bf16(pacc[i][2 * t + 1][2], pacc[i][2 * t + 1][3]));
-        }
+        const FragAddr<UK> fa_k(l16c, grpc);
+        const FragAddr<UC> fa_v2a(l16c, grpc >> 1);
+        const FragAddr<UC> fa_v2b(l16c, 2 + (grpc >> 1));
+        const int v2half = 4 * (grpc & 1);
 #pragma unroll
         for (int t = 0; t < G::KST; ++t) {
-            if ((!diag || 2 * t <= rbs[1]) && t * 32 < Lk) {
+            // on the diagonal block, steps above this wave's rows are skipped
+            if ((!diag || 2 * t <= rb) && t * 32 < Lk) {
+                f32x4 pa[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+                for (int s = 0; s < G::KSQ; ++s) {
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const uint4 af = *reinterpret_cast<const uint4*>(&kbuf[fa_k.at(2 * t + hh, s)]);
+                        pa[hh] = mfma16x16x32(af, qf[s], pa[hh]);
+                    }
+                }
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int delta = rb - (2 * t + hh);
+                    const float blk = exp2f(static_cast<float>(16 * delta) * lg2c) * blkf;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float val = 0.0f;
+                        const bool keep = !diag || delta > 0 || (delta == 0 && l16 >= 4 * grp + r);
+                        if (keep) val = pa[hh][r] * (dlane[r] * blk);
+                        pa[hh][r] = val;
+                    }
+                }
+                const uint4 pf = make_uint4(pack2_bf16(pa[0][0], pa[0][1]), pack2_bf16(pa[0][2], pa[0][3]),
+                                            pack2_bf16(pa[1][0], pa[1][1]), pack2_bf16(pa[1][2], pa[1][3]));
 #pragma unroll
                 for (int nt = 0; nt < G::NTV; ++nt) {
-                    const int row = nt * 16 + l16;
-                    const uint2 lo = *reinterpret_cast<const uint2*>(&vbuf[tidx<BQ>(row, t * 32 + grp * 4)]);
-                    const uint2 hi = *reinterpret_cast<const uint2*>(&vbuf[tidx<BQ>(row, t * 32 + 16 + grp * 4)]);
-                    const uint4 af = make_uint4(lo.x, lo.y, hi.x, hi.y);
-#pragma unroll
-                    for (int i = 0; i < 2; ++i)
-                        if (!diag || 2 * t <= rbs[i]) oacc[i][nt] = mfma16x16x32(af, pf[i][t], oacc[i][nt]);
+                    const uint2 lo = *reinterpret_cast<const uint2*>(&vbuf[fa_v2a.at(nt, t) + v2half]);
+                    const uint2 hi = *reinterpret_cast<const uint2*>(&vbuf[fa_v2b.at(nt, t) + v2half]);
+                    oacc[nt] = mfma16x16x32(make_uint4(lo.x, lo.y, hi.x, hi.y), pf, oacc[nt]);
                 }
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
     }
 
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int row = rbs[i] * 16 + l16;
+    {
+        const int row = rb * 16 + l16;
         if (row < Lq) {
-            u16* orow = Og + static_cast<size_t>(q0 + row) * a.dv;
+            u16* orow = Og + static_cast<size_t>(q0 + row) * a.dv + grp * 4;
 #pragma unroll
             for (int nt = 0; nt < G::NTV; ++nt)
-                *reinterpret_cast<uint2*>(orow + nt * 16 + grp * 4) =
-                    make_uint2(pack2_bf16(oacc[i][nt][0], oacc[i][nt][1]), pack2_bf16(oacc[i][nt][2], oacc[i][nt][3]));
+                *reinterpret_cast<uint2*>(orow + nt * 16) =
+                    make_uint2(pack2_bf16(oacc[nt][0], oacc[nt][1]), pack2_bf16(oacc[nt][2], oacc[nt][3]));
         }
     }
 }

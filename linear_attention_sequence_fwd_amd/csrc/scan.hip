@@ -28,13 +28,25 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* ws, const floa
     float4 acc = state_in ? reinterpret_cast<const float4*>(state_in + static_cast<size_t>(bh) * per_bh)[e4]
                           : make_float4(0.f, 0.f, 0.f, 0.f);
     w[0] = acc;
-    for (int s = 1; s < nseg; ++s) {
-        const float4 t = w[s * stride];
-        acc.x = gL * acc.x + t.x;
-        acc.y = gL * acc.y + t.y;
-        acc.z = gL * acc.z + t.z;
-        acc.w = gL * acc.w + t.w;
-        w[s * stride] = acc;
+    // Loads are issued in batches ahead of the dependent updates so several
+    // segments are in flight per thread (the slots are disjoint from the
+    // ones being written, but the compiler cannot prove it).
+    constexpr int kBatch = 8;
+    for (int s0 = 1; s0 < nseg; s0 += kBatch) {
+        float4 t[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+            if (s0 + j < nseg) t[j] = w[(s0 + j) * stride];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            if (s0 + j < nseg) {
+                acc.x = gL * acc.x + t[j].x;
+                acc.y = gL * acc.y + t[j].y;
+                acc.z = gL * acc.z + t[j].z;
+                acc.w = gL * acc.w + t[j].w;
+                w[(s0 + j) * stride] = acc;
+            }
+        }
     }
 }
 

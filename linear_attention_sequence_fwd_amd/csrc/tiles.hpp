@@ -5,61 +5,122 @@
 
 namespace ret {
 
-// ---------------------------------------------------------------- LDS index maps
+// ---------------------------------------------------------------- LDS layouts
+//
+// Every LDS tile is a row-major [rows][U*8] bf16 array whose 16-byte units
+// are XOR-swizzled per row: unit u of row r is stored at u ^ (r mod W),
+// W = min(U, 16). Sixteen consecutive rows therefore spread one column of
+// units over 16 different bank groups, so MFMA fragment reads (16 rows, one
+// unit each) and the transposing block writes are free of bank conflicts.
+//
+// Because the swizzle depends only on r mod 16, a fragment read at row
+// r0 + 16a + l16 and unit 4b + w (a, b unrolled loop indices; l16, w per lane)
+// lands at  base[b mod 4] + 16a*U*8 + (b/4)*32*... : four per-lane base
+// addresses plus compile-time offsets. Fragment reads then need no address
+// arithmetic inside the unrolled loops, which keeps register pressure down.
 
-// K row-major [C][DK]: unit (d/8) of row j is XOR-ed with (j + j/8) mod 8, so
-// that both the block writes (8 rows of one block column) and the G1 reads
-// (16 consecutive rows) spread over banks.
-template <int DK>
-__device__ __forceinline__ int kidx_rm(int j, int d) {
-    return j * DK + ((((d >> 3) ^ ((j + (j >> 3)) & 7))) << 3) + (d & 7);
-}
-// Transposed [rows][C] (K^T and V^T): unit (token/8) XOR-ed with row mod 8.
-template <int C>
-__device__ __forceinline__ int tidx(int row, int j) {
-    return row * C + ((((j >> 3) ^ (row & 7))) << 3) + (j & 7);
-}
-// S^T [DVT][DK]: unit (d/8) XOR-ed with column mod 8.
-template <int DK>
-__device__ __forceinline__ int sidx(int c, int d) {
-    return c * DK + ((((d >> 3) ^ (c & 7))) << 3) + (d & 7);
+template <int U>
+__device__ __forceinline__ int swz(int row, int unit) {
+    constexpr int W = U < 16 ? U : 16;
+    return row * (U * 8) + ((unit ^ (row & (W - 1))) << 3);
 }
 
-// Element e (0..7) of 8 packed bf16, as raw 16 bits.
-__device__ __forceinline__ uint32_t elem16(const uint4& x, int e) {
-    const uint32_t w = (e >> 1) == 0 ? x.x : (e >> 1) == 1 ? x.y : (e >> 1) == 2 ? x.z : x.w;
+// Per-lane bases for fragment reads of 16-byte unit 4b + w (w in 0..3) at rows
+// row_lane + 16a.  at(a, b) returns the element offset for compile-time a, b.
+template <int U>
+struct FragAddr {
+    int base[4];
+    __device__ __forceinline__ FragAddr(int row_lane, int w) {
+        constexpr int W = U < 16 ? U : 16;
+        const int x = row_lane & (W - 1);
+        const int y = x >> 2;
+        const int z = w ^ (x & 3);
+#pragma unroll
+        for (int b0 = 0; b0 < 4; ++b0) base[b0] = row_lane * (U * 8) + z * 8 + 32 * (b0 ^ y);
+    }
+    __device__ __forceinline__ int at(int a, int b) const { return base[b & 3] + a * 16 * (U * 8) + (b >> 2) * 128; }
+};
+
+// Element e of bf16 values packed two per dword, as raw 16 bits.
+template <int NW32>
+__device__ __forceinline__ uint32_t elem16(const uint32_t (&x)[NW32], int e) {
+    const uint32_t w = x[e >> 1];
     return (e & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
-// 8x8 block index -> (token block, column block). Eight consecutive indices
-// walk down the token blocks of one column block, so a wave's 64 lanes cover
-// 8 token blocks x 8 column blocks: every row it touches is read as 128
-// contiguous bytes, and the transposed LDS writes of the 8 lanes that share a
-// column block land in different banks.
-template <int D>
+// Staging blocks: 8 tokens x BW columns (BW = 8 or 4), each row held as BW/2
+// dwords. Block index -> (token block, column block): eight consecutive
+// indices walk down the token blocks of one column block, so a wave's 64 lanes
+// read 8 token blocks x 8 column blocks (each row it touches as 8*BW*2
+// contiguous bytes), and the transposed LDS writes of the 8 lanes that share
+// a column block land in different units of the same row.
+template <int D, int BW>
 __device__ __forceinline__ void block_coords(int idx, int& tb, int& cb) {
     const int rest = idx >> 3;
-    cb = rest % (D / 8);
-    tb = (idx & 7) + 8 * (rest / (D / 8));
+    cb = rest % (D / BW);
+    tb = (idx & 7) + 8 * (rest / (D / BW));
 }
 
-template <int D, int NBLK, int PT, int NTHR>
-__device__ __forceinline__ void load_blocks(uint4 (&r)[PT][8], const u16* base, int ld, int valid,
-                                            int tid) {
+template <int BW>
+struct BlockRows {
+    uint32_t w[8][BW / 2];
+};
+
+template <int D, int BW, int NBLK, int PT, int NTHR>
+__device__ __forceinline__ void load_blocks(BlockRows<BW> (&r)[PT], const u16* base, int ld, int valid, int tid) {
+    // Row pointers are wave-uniform (base + row * ld); the per-lane part is a
+    // 32-bit byte offset, so each row load needs one shared offset register
+    // and a scalar base instead of its own 64-bit address.
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
         const int idx = tid + u * NTHR;
         int tb, cb;
-        block_coords<D>(idx < NBLK ? idx : 0, tb, cb);
+        block_coords<D, BW>(idx < NBLK ? idx : 0, tb, cb);
+        const uint32_t lane_off = static_cast<uint32_t>((tb * 8 * ld + cb * BW) * 2);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const int row = tb * 8 + q;
-            if (idx < NBLK && row < valid)
-                r[u][q] = *reinterpret_cast<const uint4*>(base + static_cast<size_t>(row) * ld + cb * 8);
-            else
-                r[u][q] = make_uint4(0, 0, 0, 0);
+            const char* rowq = reinterpret_cast<const char*>(base + static_cast<size_t>(q) * ld) + lane_off;
+            const bool ok = idx < NBLK && row < valid;
+            if constexpr (BW == 8) {
+                const uint4 x = ok ? *reinterpret_cast<const uint4*>(rowq) : make_uint4(0, 0, 0, 0);
+                r[u].w[q][0] = x.x;
+                r[u].w[q][1] = x.y;
+                r[u].w[q][2] = x.z;
+                r[u].w[q][3] = x.w;
+            } else {
+                const uint2 x = ok ? *reinterpret_cast<const uint2*>(rowq) : make_uint2(0, 0);
+                r[u].w[q][0] = x.x;
+                r[u].w[q][1] = x.y;
+            }
         }
     }
 }
+
+// Column c of a staged block: 8 consecutive tokens, packed as one uint4.
+template <int BW>
+__device__ __forceinline__ uint4 block_column(const BlockRows<BW>& b, int c) {
+    uint32_t w[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) w[p] = elem16(b.w[2 * p], c) | (elem16(b.w[2 * p + 1], c) << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Rotate the complex pairs of one staged row in place (BW/2 pairs, first
+// frequency index j0) at absolute position `position`.
+template <int BW>
+__device__ __forceinline__ void rotate_row(uint32_t (&w)[BW / 2], const HeadParams& hp, int j0, double position) {
+#pragma unroll
+    for (int p = 0; p < BW / 2; ++p) {
+        float c, s;
+        rot_cs_fast(position, hp.theta[j0 + p], c, s);
+        const float re = lo_bf16(w[p]), im = hi_bf16(w[p]);
+        w[p] = pack2_bf16(re * c - im * s, re * s + im * c);
+    }
+}
+
+// Staging block width: 8x8 blocks when there are at least as many as
+// threads, else 8x4 blocks (half the registers per thread).
+constexpr int stage_width(int rows, int cols, int nthr) { return (rows / 8) * (cols / 8) >= nthr ? 8 : 4; }
 
 }  // namespace ret
