@@ -65,18 +65,49 @@ def time_events(fn, steps, warmup):
 
 
 def time_phases(R, q, k, v, kw, steps):
-    """Average duration (ms) of each phase of the chunkwise call, from the
-    four events the library records around its kernels."""
+    """Average duration (ms) of each kernel of the chunkwise call (segment
+    pre-pass, segment scan, main pass), from start/stop events the library
+    records around each kernel's execution (hipExtLaunchKernelGGL)."""
     import torch
 
-    tot = [0.0, 0.0, 0.0]
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    for _ in range(steps):
+    sets = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    for evs in sets:
         R.retention_chunkwise_fwd(q, k, v, events=evs, **kw)
-        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    tot = [0.0, 0.0, 0.0]
+    for evs in sets:
         for i in range(3):
-            tot[i] += evs[i].elapsed_time(evs[i + 1])
+            tot[i] += evs[2 * i].elapsed_time(evs[2 * i + 1])
     return [t / steps for t in tot]
+
+
+def time_graph(fn, steps, warmup, per_graph=20):
+    """Per-step time with the step captured in a HIP graph (per_graph steps per
+    graph) and replayed, so host launch overhead is not in the measurement."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(max(warmup, 3)):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // per_graph)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / (reps * per_graph)
 
 
 def cpu_baseline(q, k, v, theta, H, budget_s):
@@ -122,12 +153,53 @@ def cpu_baseline(q, k, v, theta, H, budget_s):
     }
 
 
+def run_only(name, steps, warmup, dev):
+    """One workload, timed with events; prints a short JSON line."""
+    import torch
+
+    import linear_attention_sequence_fwd_amd as R
+    from linear_attention_sequence_fwd_amd import workloads as W
+
+    if name == "copy":
+        # plain device copy of a known size: calibrates HBM byte counters
+        src = torch.ones(256 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        ms = time_events(lambda: dst.copy_(src), steps, warmup)
+        print(json.dumps({"workload": "copy 1 GiB -> 1 GiB", "ms_per_call": ms, "bytes_read": src.numel() * 4,
+                          "bytes_written": dst.numel() * 4}))
+        return
+    key = {"msr": "msr_bf16_rotary", "layer7b": "layer7b_bf16", "decode": "decode_bf16",
+           "longctx": "longctx_bf16", "single": "single_head_f32"}[name]
+    w = W.WORKLOADS[key]
+    if name == "decode":
+        s0, qs, ks, vs = W.make_decode_workload(device=dev, steps=steps + warmup)
+        o = torch.empty((w["B"], w["H"], w["dv"]), dtype=w["dtype"], device=dev)
+        it = iter(range(steps + warmup))
+
+        def fn():
+            t = next(it)
+            R.retention_recurrent_step(qs[t], ks[t], vs[t], s0, out=o)
+    else:
+        q, k, v, theta = W.make_workload(key, device=dev)
+        out = torch.empty_like(v)
+        ws_bytes = R.retention_chunkwise_workspace_size(w["B"], w["H"], w["N"], w["dk"], w["dv"], q.dtype,
+                                                        w["chunk"])
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+
+        def fn():
+            R.retention_chunkwise_fwd(q, k, v, chunk=w["chunk"], theta=theta, out=out, workspace=ws)
+    ms = time_events(fn, steps, warmup)
+    print(json.dumps({"workload": key, "ms_per_call": ms, "steps": steps}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--quick", action="store_true", help="main workload only")
+    ap.add_argument("--only", choices=["msr", "layer7b", "decode", "longctx", "single", "copy"],
+                    help="time one workload only (no CPU baseline); for profilers")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -143,17 +215,22 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     R.load_library()
     dev = "cuda:0"
+    if args.only:
+        run_only(args.only, args.steps, args.warmup, dev)
+        return
 
     # ---------------- main workload
     name = "msr_bf16_rotary"
     w = W.WORKLOADS[name]
     q, k, v, theta = W.make_workload(name, device=dev)
-    kw = dict(chunk=w["chunk"], theta=theta)
+    kw = dict(chunk=w["chunk"], theta=R.HostFloats(theta))
     out = torch.empty_like(v)
     ws_bytes = R.retention_chunkwise_workspace_size(w["B"], w["H"], w["N"], w["dk"], w["dv"], q.dtype, w["chunk"])
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     kw.update(out=out, workspace=ws)
-    ms = time_events(lambda: R.retention_chunkwise_fwd(q, k, v, **kw), args.steps, args.warmup)
+    step = lambda: R.retention_chunkwise_fwd(q, k, v, **kw)  # noqa: E731
+    ms_eager = time_events(step, args.steps, args.warmup)
+    ms = time_graph(step, args.steps, args.warmup)
     phases = time_phases(R, q, k, v, kw, max(20, args.steps // 4))
     tokens = w["B"] * w["N"]
     alg_bytes = chunk_alg_bytes(w["B"], w["H"], w["N"], w["dk"], w["dv"])
@@ -191,6 +268,9 @@ def main():
             "kernel_ms": main_ms,
         },
         "phase_ms": {"segment_states": phases[0], "segment_scan": phases[1], "main": phases[2]},
+        "timing": "ms_per_step from HIP-graph replay of the step (20 steps per graph); "
+                  "eager_ms_per_step launches each call from Python",
+        "eager_ms_per_step": ms_eager,
     }
     result["cpu_baseline"] = cpu_baseline(q.cpu(), k.cpu(), v.cpu(), theta, w["H"], args.cpu_seconds)
     del q, k, v, out, ws

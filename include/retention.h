@@ -116,10 +116,11 @@ ret_status_t retention_chunkwise_fwd(const void* q, const void* k, const void* v
 
 /*
  * retention_chunkwise_fwd with a timing hook for profilers and benchmarks:
- * events points to four hipEvent_t created by the caller, recorded on
- * `stream` before the segment pre-pass, after it, after the segment scan and
- * after the main chunk kernel; phases that do not run leave two consecutive
- * events back to back. Same result and status codes as
+ * events points to six hipEvent_t created by the caller, a start/stop pair for
+ * each phase in order: segment pre-pass, segment scan, main chunk kernel. Each
+ * pair brackets that kernel's execution on `stream` (recorded by the launch
+ * itself, so host submission gaps are not included); a phase that does not
+ * run records its pair back to back. Same result and status codes as
  * retention_chunkwise_fwd (RET_ERR_NULL if an event is missing).
  */
 ret_status_t retention_chunkwise_fwd_timed(const void* q, const void* k, const void* v, void* o,

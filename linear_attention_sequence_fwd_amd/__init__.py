@@ -12,6 +12,7 @@ import os
 
 __all__ = [
     "RetentionError",
+    "HostFloats",
     "load_library",
     "retention_parallel_fwd",
     "retention_chunkwise_fwd",
@@ -117,17 +118,32 @@ def _check_dev(*ts):
             raise ValueError("retention tensors must be contiguous")
 
 
+class HostFloats:
+    """A host float array marshalled once for repeated calls (gamma or theta).
+
+    Passing one of these instead of a list or tensor skips the per-call
+    conversion, which matters for launch-bound callers."""
+
+    def __init__(self, vals):
+        torch = _torch()
+        if isinstance(vals, torch.Tensor):
+            vals = vals.detach().to("cpu", torch.float32).tolist()
+        self.values = [float(x) for x in vals]
+        self.array = (ctypes.c_float * len(self.values))(*self.values)
+        self.pointer = ctypes.cast(self.array, ctypes.c_void_p)
+
+    def __len__(self):
+        return len(self.values)
+
+
 def _host_floats(vals, n, what):
     if vals is None:
         return None, None
-    torch = _torch()
-    if isinstance(vals, torch.Tensor):
-        vals = vals.detach().to("cpu", torch.float32).tolist()
-    vals = [float(x) for x in vals]
+    if not isinstance(vals, HostFloats):
+        vals = HostFloats(vals)
     if len(vals) != n:
         raise ValueError(f"{what} needs {n} values, got {len(vals)}")
-    arr = (ctypes.c_float * n)(*vals)
-    return arr, ctypes.cast(arr, ctypes.c_void_p)
+    return vals, vals.pointer
 
 
 def _ptr(t):
@@ -176,8 +192,10 @@ def retention_chunkwise_fwd(q, k, v, chunk=64, gamma=None, theta=None, pos0=0, s
 
     state_in / state_out are float32 [B,H,dk,dv] device tensors (state_out may
     be state_in). The workspace is allocated here from torch's caching
-    allocator when not given. With `events` (four torch.cuda.Event created
-    with enable_timing=True) the call goes through retention_chunkwise_fwd_timed.
+    allocator when not given. With `events` (six torch.cuda.Event created
+    with enable_timing=True: start/stop of the segment pre-pass, the segment
+    scan and the main kernel) the call goes through
+    retention_chunkwise_fwd_timed.
     """
     torch = _torch()
     _check_dev(q, k, v, state_in, state_out)
@@ -203,18 +221,18 @@ def retention_chunkwise_fwd(q, k, v, chunk=64, gamma=None, theta=None, pos0=0, s
         st = lib.retention_chunkwise_fwd(*args)
         _raise(st, "retention_chunkwise_fwd")
     else:
-        if len(events) != 4:
-            raise ValueError("events needs four torch.cuda.Event")
+        if len(events) != 6:
+            raise ValueError("events needs six torch.cuda.Event")
         for e in events:
             e.record()  # materialise the underlying hipEvent_t
-        evs = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
+        evs = (ctypes.c_void_p * 6)(*[e.cuda_event for e in events])
         st = lib.retention_chunkwise_fwd_timed(*args, ctypes.cast(evs, ctypes.c_void_p))
         _raise(st, "retention_chunkwise_fwd_timed")
     return (out, state_out) if return_state else out
 
 
 def retention_chunkwise_fwd_timed(q, k, v, events, **kw):
-    """retention_chunkwise_fwd recording the four phase events (see the C header)."""
+    """retention_chunkwise_fwd recording the six phase events (see the C header)."""
     return retention_chunkwise_fwd(q, k, v, events=events, **kw)
 
 

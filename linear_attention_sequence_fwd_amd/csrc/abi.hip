@@ -198,7 +198,9 @@ ret_status_t retention_chunkwise_fwd_timed(const void* q, const void* k, const v
                                            const float* theta, int64_t pos0, const float* state_in,
                                            float* state_out, int segments, void* workspace,
                                            size_t workspace_bytes, void* stream, void* const* events) {
-    if (!events || !events[0] || !events[1] || !events[2] || !events[3]) return RET_ERR_NULL;
+    if (!events) return RET_ERR_NULL;
+    for (int i = 0; i < 6; ++i)
+        if (!events[i]) return RET_ERR_NULL;
     return chunkwise_impl(q, k, v, o, B, H, N, dk, dv, dtype, chunk, gamma, theta, pos0, state_in, state_out,
                           segments, workspace, workspace_bytes, stream, events);
 }

@@ -23,6 +23,10 @@
 // With C/16 waves per workgroup (8 for 128-token chunks) two waves share each
 // SIMD, so one wave's LDS and HBM waits overlap the other's MFMAs.
 //
+// Keys and values are staged token-permuted inside each 32-token group (see
+// staged_token), so a 16-byte unit of K^T / V^T holds the 8 tokens a lane
+// group contracts over in both G4 and G2.
+//
 // LDS (bf16, 16-byte units XOR-swizzled against bank conflicts):
 //   kbuf  keys of the chunk, first as K^T scaled by xi (for G4) and then as K
 //         row-major (for G1)
@@ -168,8 +172,8 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     //        = gamma^(l16 - 4 grp - r) * gamma^(16 (rb - jt)).
     float dlane[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dlane[r] = exp2f(static_cast<float>(l16 - 4 * grp - r) * lg2f);
-    const float zeta = exp2f(static_cast<float>(16 * rb + l16 + 1) * lg2f);
+    for (int r = 0; r < 4; ++r) dlane[r] = fast_exp2(static_cast<float>(l16 - 4 * grp - r) * lg2f);
+    const float zeta = fast_exp2(static_cast<float>(16 * rb + l16 + 1) * lg2f);
     const float gC = gamma_pow(lg2, C);
 
     // ---- prefetch the first chunk
@@ -217,13 +221,13 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
                 if (hp.has_theta) {
 #pragma unroll
                     for (int q = 0; q < 8; ++q)
-                        if (tb * 8 + q < L)
+                        if (staged_token(tb, q) < L)
                             rotate_row<G::BWK>(kr[u].w[q], hp, cb * (G::BWK / 2),
-                                               static_cast<double>(a.pos0 + t0 + tb * 8 + q));
+                                               static_cast<double>(a.pos0 + t0 + staged_token(tb, q)));
                 }
                 float xi[8];
 #pragma unroll
-                for (int q = 0; q < 8; ++q) xi[q] = exp2f(static_cast<float>(L - 1 - tb * 8 - q) * lg2c);
+                for (int q = 0; q < 8; ++q) xi[q] = fast_exp2(static_cast<float>(L - 1 - staged_token(tb, q)) * lg2c);
 #pragma unroll
                 for (int c = 0; c < G::BWK; ++c) {
                     uint32_t w[4];
@@ -329,11 +333,12 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
                 block_coords<DK, G::BWK>(idx, tb, cb);
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
+                    const int row = staged_token(tb, q);
                     if constexpr (G::BWK == 8) {
-                        *reinterpret_cast<uint4*>(&kbuf[swz<UK>(tb * 8 + q, cb)]) =
+                        *reinterpret_cast<uint4*>(&kbuf[swz<UK>(row, cb)]) =
                             make_uint4(kr[u].w[q][0], kr[u].w[q][1], kr[u].w[q][2], kr[u].w[q][3]);
                     } else {
-                        *reinterpret_cast<uint2*>(&kbuf[swz<UK>(tb * 8 + q, cb >> 1) + 4 * (cb & 1)]) =
+                        *reinterpret_cast<uint2*>(&kbuf[swz<UK>(row, cb >> 1) + 4 * (cb & 1)]) =
                             make_uint2(kr[u].w[q][0], kr[u].w[q][1]);
                     }
                 }
@@ -369,7 +374,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
 #pragma unroll
                     for (int hh = 0; hh < 2; ++hh) {
                         const int delta = rb - (2 * t + hh);
-                        const float blk = exp2f(static_cast<float>(16 * delta) * lg2c);
+                        const float blk = fast_exp2(static_cast<float>(16 * delta) * lg2c);
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             float val = 0.0f;
@@ -388,17 +393,16 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
 
         // ---- 6. G2: O^T += V^T P^T
         {
-            const FragAddr<UC> fa_v2a(l16c, grpc >> 1);        // V^T tokens 32 t + 4 grp .. +3
-            const FragAddr<UC> fa_v2b(l16c, 2 + (grpc >> 1));  // V^T tokens 32 t + 16 + 4 grp .. +3
-            const int v2half = 4 * (grpc & 1);
+            // V^T rows 16 nt + l16, staged unit 4 t + grp: tokens 32 t + 4 grp + {0..3, 16..19},
+            // the order in which pf holds this lane group's scores
+            const FragAddr<UC> fa_v(l16c, grpc);
 #pragma unroll
             for (int t = 0; t < G::KST; ++t) {
                 if (2 * t <= rb) {
 #pragma unroll
                     for (int nt = 0; nt < G::NTV; ++nt) {
-                        const uint2 lo = *reinterpret_cast<const uint2*>(&vbuf[fa_v2a.at(nt, t) + v2half]);
-                        const uint2 hi = *reinterpret_cast<const uint2*>(&vbuf[fa_v2b.at(nt, t) + v2half]);
-                        oacc[nt] = mfma16x16x32(make_uint4(lo.x, lo.y, hi.x, hi.y), pf[t], oacc[nt]);
+                        const uint4 af = *reinterpret_cast<const uint4*>(&vbuf[fa_v.at(nt, t)]);
+                        oacc[nt] = mfma16x16x32(af, pf[t], oacc[nt]);
                     }
                 }
             }
@@ -444,16 +448,17 @@ template <int DK, int DVT, int C>
 static hipError_t run_chunk_bf16(const ChunkArgs& a, const HeadParams& hp, hipStream_t st, hipEvent_t* ev) {
     using G = ChunkGeo<DK, DVT, C>;
     const int bhv = a.B * a.H * a.nvt;
-    if (ev) (void)hipEventRecord(ev[0], st);
-    if (a.nseg > 1) chunk_bf16_kernel<DK, DVT, C, true><<<dim3(bhv * (a.nseg - 1)), dim3(G::NTHR), 0, st>>>(a, hp);
-    if (ev) (void)hipEventRecord(ev[1], st);
     if (a.nseg > 1) {
-        const hipError_t e = launch_segment_scan(a, hp, st);
+        launch_timed(chunk_bf16_kernel<DK, DVT, C, true>, dim3(bhv * (a.nseg - 1)), dim3(G::NTHR), 0, st, ev, a,
+                     hp);
+        const hipError_t e = launch_segment_scan(a, hp, st, ev ? ev + 2 : nullptr);
         if (e != hipSuccess) return e;
+    } else {
+        record_empty_phase(st, ev);
+        record_empty_phase(st, ev ? ev + 2 : nullptr);
     }
-    if (ev) (void)hipEventRecord(ev[2], st);
-    chunk_bf16_kernel<DK, DVT, C, false><<<dim3(bhv * a.nseg), dim3(G::NTHR), 0, st>>>(a, hp);
-    if (ev) (void)hipEventRecord(ev[3], st);
+    launch_timed(chunk_bf16_kernel<DK, DVT, C, false>, dim3(bhv * a.nseg), dim3(G::NTHR), 0, st,
+                 ev ? ev + 4 : nullptr, a, hp);
     return hipGetLastError();
 }
 

@@ -62,6 +62,11 @@ __device__ __forceinline__ float gamma_pow(double lg2, double n) {
     return static_cast<float>(exp2(lg2 * n));
 }
 
+// 2^x on the hardware transcendental unit (one instruction; results below
+// the float32 normal range flush toward zero, which only affects decay
+// factors far below any retained contribution).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // ---------------------------------------------------------------- rotation
 
 // cos/sin of position * theta with the product and the reduction to

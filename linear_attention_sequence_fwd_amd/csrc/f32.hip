@@ -157,16 +157,16 @@ hipError_t launch_chunk_f32(const ChunkArgs& a, const HeadParams& hp, int dvt, h
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     const int bhv = a.B * a.H * a.nvt;
-    if (ev) (void)hipEventRecord(ev[0], st);
-    if (a.nseg > 1) chunk_f32_kernel<true><<<dim3(bhv * (a.nseg - 1)), dim3(kF32Threads), lds, st>>>(a, hp, dvt);
-    if (ev) (void)hipEventRecord(ev[1], st);
     if (a.nseg > 1) {
-        e = launch_segment_scan(a, hp, st);
+        launch_timed(chunk_f32_kernel<true>, dim3(bhv * (a.nseg - 1)), dim3(kF32Threads), lds, st, ev, a, hp, dvt);
+        e = launch_segment_scan(a, hp, st, ev ? ev + 2 : nullptr);
         if (e != hipSuccess) return e;
+    } else {
+        record_empty_phase(st, ev);
+        record_empty_phase(st, ev ? ev + 2 : nullptr);
     }
-    if (ev) (void)hipEventRecord(ev[2], st);
-    chunk_f32_kernel<false><<<dim3(bhv * a.nseg), dim3(kF32Threads), lds, st>>>(a, hp, dvt);
-    if (ev) (void)hipEventRecord(ev[3], st);
+    launch_timed(chunk_f32_kernel<false>, dim3(bhv * a.nseg), dim3(kF32Threads), lds, st, ev ? ev + 4 : nullptr, a,
+                 hp, dvt);
     return hipGetLastError();
 }
 

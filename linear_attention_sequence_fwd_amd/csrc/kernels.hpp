@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 
 namespace ret {
@@ -46,14 +48,35 @@ struct StepArgs {
     int bf16;
 };
 
-// Optional timing hook: when ev is not null, ev[0..3] are recorded on the
-// stream before the segment pre-pass, after it, after the segment scan and
-// after the main chunk kernel (phases that do not run record back-to-back).
+// Optional timing hook: when ev is not null it holds six events, a start/stop
+// pair per phase (segment pre-pass, segment scan, main chunk kernel), each pair
+// recorded by the launch itself around that kernel's execution
+// (hipExtLaunchKernelGGL); a phase that does not run records its pair back to
+// back.
 hipError_t launch_chunk_bf16(const ChunkArgs& a, const HeadParams& hp, int dvt, hipStream_t st, hipEvent_t* ev);
 hipError_t launch_chunk_f32(const ChunkArgs& a, const HeadParams& hp, int dvt, hipStream_t st, hipEvent_t* ev);
 hipError_t launch_parallel_bf16(const ParallelArgs& a, const HeadParams& hp, int dvt, hipStream_t st);
 hipError_t launch_parallel_f32(const ParallelArgs& a, const HeadParams& hp, int dvt, hipStream_t st);
 hipError_t launch_recurrent_step(const StepArgs& a, const HeadParams& hp, hipStream_t st);
-hipError_t launch_segment_scan(const ChunkArgs& a, const HeadParams& hp, hipStream_t st);
+hipError_t launch_segment_scan(const ChunkArgs& a, const HeadParams& hp, hipStream_t st, hipEvent_t* ev);
+
+// Launch `kernel` with the given configuration; with events, bracket its
+// execution with ev[0] / ev[1].
+template <typename... KArgs, typename... Args>
+inline void launch_timed(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t st,
+                         hipEvent_t* ev, Args... args) {
+    if (ev)
+        hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, ev[0], ev[1], 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, shmem, st, args...);
+}
+
+// Record a phase that does not run (start and stop back to back).
+inline void record_empty_phase(hipStream_t st, hipEvent_t* ev) {
+    if (ev) {
+        (void)hipEventRecord(ev[0], st);
+        (void)hipEventRecord(ev[1], st);
+    }
+}
 
 }  // namespace ret

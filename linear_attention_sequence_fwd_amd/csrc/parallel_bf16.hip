@@ -78,7 +78,7 @@ __global__ __launch_bounds__((BQ / 16) * 64) void parallel_bf16_kernel(ParallelA
     //   = dlane[r] * gamma^(16 (rb - jt)) * gamma^(q0 - k0), the last factor in float64
     float dlane[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dlane[r] = exp2f(static_cast<float>(l16 - 4 * grp - r) * lg2f);
+    for (int r = 0; r < 4; ++r) dlane[r] = fast_exp2(static_cast<float>(l16 - 4 * grp - r) * lg2f);
 
     // queries of this wave's rows, rotated, in MFMA operand registers
     uint4 qf[G::KSQ];
@@ -136,14 +136,14 @@ __global__ __launch_bounds__((BQ / 16) * 64) void parallel_bf16_kernel(ParallelA
                 block_coords<DK, G::BWK>(idx, tb, cb);
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
-                    if (hp.has_theta && tb * 8 + q < Lk)
-                        rotate_row<G::BWK>(kr[u].w[q], hp, cb * (G::BWK / 2),
-                                           static_cast<double>(a.pos0 + k0 + tb * 8 + q));
+                    const int row = staged_token(tb, q);
+                    if (hp.has_theta && row < Lk)
+                        rotate_row<G::BWK>(kr[u].w[q], hp, cb * (G::BWK / 2), static_cast<double>(a.pos0 + k0 + row));
                     if constexpr (G::BWK == 8) {
-                        *reinterpret_cast<uint4*>(&kbuf[swz<UK>(tb * 8 + q, cb)]) =
+                        *reinterpret_cast<uint4*>(&kbuf[swz<UK>(row, cb)]) =
                             make_uint4(kr[u].w[q][0], kr[u].w[q][1], kr[u].w[q][2], kr[u].w[q][3]);
                     } else {
-                        *reinterpret_cast<uint2*>(&kbuf[swz<UK>(tb * 8 + q, cb >> 1) + 4 * (cb & 1)]) =
+                        *reinterpret_cast<uint2*>(&kbuf[swz<UK>(row, cb >> 1) + 4 * (cb & 1)]) =
                             make_uint2(kr[u].w[q][0], kr[u].w[q][1]);
                     }
                 }
@@ -170,9 +170,7 @@ __global__ __launch_bounds__((BQ / 16) * 64) void parallel_bf16_kernel(ParallelA
 
         const float blkf = gamma_pow(lg2, static_cast<double>(q0 - k0));
         const FragAddr<UK> fa_k(l16c, grpc);
-        const FragAddr<UC> fa_v2a(l16c, grpc >> 1);
-        const FragAddr<UC> fa_v2b(l16c, 2 + (grpc >> 1));
-        const int v2half = 4 * (grpc & 1);
+        const FragAddr<UC> fa_v(l16c, grpc);  // V^T staged unit 4 t + grp (see staged_token)
 #pragma unroll
         for (int t = 0; t < G::KST; ++t) {
             // on the diagonal block, steps above this wave's rows are skipped
@@ -189,7 +187,7 @@ __global__ __launch_bounds__((BQ / 16) * 64) void parallel_bf16_kernel(ParallelA
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     const int delta = rb - (2 * t + hh);
-                    const float blk = exp2f(static_cast<float>(16 * delta) * lg2c) * blkf;
+                    const float blk = fast_exp2(static_cast<float>(16 * delta) * lg2c) * blkf;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         float val = 0.0f;
@@ -202,9 +200,8 @@ __global__ __launch_bounds__((BQ / 16) * 64) void parallel_bf16_kernel(ParallelA
                                             pack2_bf16(pa[1][0], pa[1][1]), pack2_bf16(pa[1][2], pa[1][3]));
 #pragma unroll
                 for (int nt = 0; nt < G::NTV; ++nt) {
-                    const uint2 lo = *reinterpret_cast<const uint2*>(&vbuf[fa_v2a.at(nt, t) + v2half]);
-                    const uint2 hi = *reinterpret_cast<const uint2*>(&vbuf[fa_v2b.at(nt, t) + v2half]);
-                    oacc[nt] = mfma16x16x32(make_uint4(lo.x, lo.y, hi.x, hi.y), pf, oacc[nt]);
+                    const uint4 af = *reinterpret_cast<const uint4*>(&vbuf[fa_v.at(nt, t)]);
+                    oacc[nt] = mfma16x16x32(af, pf, oacc[nt]);
                 }
             }
         }

@@ -49,16 +49,26 @@ __device__ __forceinline__ uint32_t elem16(const uint32_t (&x)[NW32], int e) {
 }
 
 // Staging blocks: 8 tokens x BW columns (BW = 8 or 4), each row held as BW/2
-// dwords. Block index -> (token block, column block): eight consecutive
-// indices walk down the token blocks of one column block, so a wave's 64 lanes
-// read 8 token blocks x 8 column blocks (each row it touches as 8*BW*2
-// contiguous bytes), and the transposed LDS writes of the 8 lanes that share
-// a column block land in different units of the same row.
+// dwords; the 8 tokens of block tb are staged_token(tb, 0..7). Block index ->
+// (token block, column block): eight consecutive indices walk down the token
+// blocks of one column block, so a wave's 64 lanes read 8 token blocks x 8
+// column blocks (each row it touches as BW*2 contiguous bytes per lane), and
+// the transposed LDS writes of the 8 lanes that share a column block land in
+// different units of the same row.
 template <int D, int BW>
 __device__ __forceinline__ void block_coords(int idx, int& tb, int& cb) {
     const int rest = idx >> 3;
     cb = rest % (D / BW);
     tb = (idx & 7) + 8 * (rest / (D / BW));
+}
+
+// Token order inside staged 32-token groups. Staging block tb covers tokens
+// 32*(tb/4) + 4*(tb%4) + {0,1,2,3, 16,17,18,19}, in that order, so one 16-byte
+// unit of a transposed (token-contiguous) LDS row holds exactly the 8 tokens
+// that one MFMA lane group contracts over when the other operand is a pair of
+// 16x16 accumulator tiles (rows 4g..4g+3 of tile 2t and of tile 2t+1).
+__device__ __forceinline__ int staged_token(int tb, int q) {
+    return 32 * (tb >> 2) + 4 * (tb & 3) + (q < 4 ? q : 12 + q);
 }
 
 template <int BW>
@@ -76,12 +86,13 @@ __device__ __forceinline__ void load_blocks(BlockRows<BW> (&r)[PT], const u16* b
         const int idx = tid + u * NTHR;
         int tb, cb;
         block_coords<D, BW>(idx < NBLK ? idx : 0, tb, cb);
-        const uint32_t lane_off = static_cast<uint32_t>((tb * 8 * ld + cb * BW) * 2);
+        const int tok0 = staged_token(tb, 0);
+        const uint32_t lane_off = static_cast<uint32_t>((tok0 * ld + cb * BW) * 2);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            const int row = tb * 8 + q;
-            const char* rowq = reinterpret_cast<const char*>(base + static_cast<size_t>(q) * ld) + lane_off;
-            const bool ok = idx < NBLK && row < valid;
+            const int dq = staged_token(0, q);  // token offset of row q inside the block
+            const char* rowq = reinterpret_cast<const char*>(base + static_cast<size_t>(dq) * ld) + lane_off;
+            const bool ok = idx < NBLK && tok0 + dq < valid;
             if constexpr (BW == 8) {
                 const uint4 x = ok ? *reinterpret_cast<const uint4*>(rowq) : make_uint4(0, 0, 0, 0);
                 r[u].w[q][0] = x.x;

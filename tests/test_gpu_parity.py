@@ -333,3 +333,33 @@ def test_segment_count_invariance_full_msr():
     base = to64(outs[0])
     for o in outs[1:]:
         assert_close(to64(o), base, 5e-3, "segments vs single pass")
+
+
+def test_graph_replay_matches_eager():
+    """The benchmark replays the step from a HIP graph: every replay, with
+    eager work in between, must reproduce the eager result bit for bit."""
+    w = W.WORKLOADS["msr_bf16_rotary"]
+    q, k, v, theta = W.make_workload("msr_bf16_rotary", device=DEV)
+    th = R.HostFloats(theta)
+    nbytes = R.retention_chunkwise_workspace_size(w["B"], w["H"], w["N"], w["dk"], w["dv"], q.dtype, w["chunk"])
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=DEV)
+    ws2 = torch.empty_like(ws)
+    eager = R.retention_chunkwise_fwd(q, k, v, chunk=w["chunk"], theta=th, workspace=ws)
+    out = torch.empty_like(eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        R.retention_chunkwise_fwd(q, k, v, chunk=w["chunk"], theta=th, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        R.retention_chunkwise_fwd(q, k, v, chunk=w["chunk"], theta=th, out=out, workspace=ws)
+    for _ in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+        other = R.retention_chunkwise_fwd(q, k, v, chunk=w["chunk"], theta=th, workspace=ws2, segments=3)
+        torch.cuda.synchronize()
+        assert torch.isfinite(other).all()
