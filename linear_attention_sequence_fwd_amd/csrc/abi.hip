@@ -18,7 +18,7 @@ namespace {
 using ret::HeadParams;
 
 constexpr size_t kMaxLdsBytes = 160 * 1024;
-constexpr int kTargetBlocks = 512;  // two workgroups per compute unit
+constexpr int kTargetBlocks = 256;  // one workgroup per compute unit
 constexpr int kMaxSegments = 4096;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

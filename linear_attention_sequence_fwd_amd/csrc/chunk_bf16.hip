@@ -131,6 +131,25 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     const int d_base = (wave % G::MG) * G::MT * 16;  // this wave's S rows ...
     const int c_base = (wave / G::MG) * G::NT * 16;  // ... and S columns (within the value tile)
 
+    // ---- prefetch the first chunk (issued before the initial-state loads so the
+    //      two HBM round trips overlap)
+    BlockRows<G::BWK> kr[G::KPT];
+    BlockRows<G::BWV> vr[G::VPT];
+    uint4 qf[G::KSQ];
+    auto load_q = [&](int t, int Lq) {
+        const int row = rb * 16 + l16;
+        const u16* p = Qg + static_cast<size_t>(t + row) * DK + grp * 8;
+#pragma unroll
+        for (int s = 0; s < G::KSQ; ++s)
+            qf[s] = row < Lq ? *reinterpret_cast<const uint4*>(p + s * 32) : make_uint4(0, 0, 0, 0);
+    };
+    {
+        const int L0 = min(C, t_end - t_begin);
+        load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR>(kr, Kg + static_cast<size_t>(t_begin) * DK, DK, L0, tid);
+        load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR>(vr, Vg + static_cast<size_t>(t_begin) * a.dv, a.dv, L0, tid);
+        if (!STATE_ONLY) load_q(t_begin, L0);
+    }
+
     // ---- initial state
     f32x4 sacc[G::MT][G::NT];
     const float* s_src = nullptr;
@@ -175,24 +194,6 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     for (int r = 0; r < 4; ++r) dlane[r] = fast_exp2(static_cast<float>(l16 - 4 * grp - r) * lg2f);
     const float zeta = fast_exp2(static_cast<float>(16 * rb + l16 + 1) * lg2f);
     const float gC = gamma_pow(lg2, C);
-
-    // ---- prefetch the first chunk
-    BlockRows<G::BWK> kr[G::KPT];
-    BlockRows<G::BWV> vr[G::VPT];
-    uint4 qf[G::KSQ];
-    auto load_q = [&](int t, int Lq) {
-        const int row = rb * 16 + l16;
-        const u16* p = Qg + static_cast<size_t>(t + row) * DK + grp * 8;
-#pragma unroll
-        for (int s = 0; s < G::KSQ; ++s)
-            qf[s] = row < Lq ? *reinterpret_cast<const uint4*>(p + s * 32) : make_uint4(0, 0, 0, 0);
-    };
-    {
-        const int L0 = min(C, t_end - t_begin);
-        load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR>(kr, Kg + static_cast<size_t>(t_begin) * DK, DK, L0, tid);
-        load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR>(vr, Vg + static_cast<size_t>(t_begin) * a.dv, a.dv, L0, tid);
-        if (!STATE_ONLY) load_q(t_begin, L0);
-    }
 
     for (int ch = 0; ch < nch; ++ch) {
         // Per-iteration copies the compiler cannot prove loop-invariant: the

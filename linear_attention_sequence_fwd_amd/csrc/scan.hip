@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* ws, const floa
     // Loads are issued in batches ahead of the dependent updates so several
     // segments are in flight per thread (the slots are disjoint from the
     // ones being written, but the compiler cannot prove it).
-    constexpr int kBatch = 8;
+    constexpr int kBatch = 32;
     for (int s0 = 1; s0 < nseg; s0 += kBatch) {
         float4 t[kBatch];
 #pragma unroll
