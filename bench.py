@@ -184,7 +184,7 @@ def run_only(name, steps, warmup, dev):
         out = torch.empty_like(v)
         ws_bytes = R.retention_chunkwise_workspace_size(w["B"], w["H"], w["N"], w["dk"], w["dv"], q.dtype,
                                                         w["chunk"])
-        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
         def fn():
             R.retention_chunkwise_fwd(q, k, v, chunk=w["chunk"], theta=theta, out=out, workspace=ws)
@@ -226,7 +226,7 @@ def main():
     kw = dict(chunk=w["chunk"], theta=R.HostFloats(theta))
     out = torch.empty_like(v)
     ws_bytes = R.retention_chunkwise_workspace_size(w["B"], w["H"], w["N"], w["dk"], w["dv"], q.dtype, w["chunk"])
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     kw.update(out=out, workspace=ws)
     step = lambda: R.retention_chunkwise_fwd(q, k, v, **kw)  # noqa: E731
     ms_eager = time_events(step, args.steps, args.warmup)

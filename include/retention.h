@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define RETENTION_ABI_VERSION 1
+#define RETENTION_ABI_VERSION 2
 #define RETENTION_MAX_HEADS 128 /* H limit (per-head constants travel in kernel arguments) */
 #define RETENTION_MAX_DK 256
 
@@ -96,13 +96,23 @@ ret_status_t retention_parallel_fwd(const void* q, const void* k, const void* v,
  * state_out: device float32 [B, H, dk, dv] receiving the state after the last
  *            token, or NULL. May alias state_in.
  * segments:  0 lets the library choose; s >= 1 asks for s sequence segments
- *            (clamped to the number of chunks). With more than one segment the
- *            library first builds every segment's end state, then scans them
- *            with factor gamma^(segment length), then runs all segments in
- *            parallel; this uses the workspace.
+ *            (clamped to the number of chunks and to 4096; ignored when
+ *            B*H*(value tiles) exceeds 8192). With more than one segment
+ *            the sequence of every head is cut into segments that run in
+ *            parallel, and the state entering each segment is assembled from
+ *            the end states of the segments before it, with factor
+ *            gamma^(segment length) per segment. bf16 does this in one launch
+ *            (workgroups publish segment states and look back at their
+ *            predecessors' through the workspace); float32 runs three
+ *            kernels (segment end states, their scan, the segments).
  * workspace: device buffer of at least retention_chunkwise_workspace_size(...)
- *            bytes (may be NULL when that size is 0). Contents on entry are
- *            ignored; contents on return are unspecified.
+ *            bytes (may be NULL when that size is 0). It must be zero-filled
+ *            before its first use (one hipMemset after allocation); every
+ *            call leaves it ready for the next, so it can be reused without
+ *            clearing, by calls of any sizes and from a captured graph.
+ *            Calls that share a
+ *            workspace must be ordered on one stream (they must not overlap).
+ *            The caller owns it; the library keeps no pointer to it.
  * Implemented set: chunk in {64, 128}; bf16 with dk in {64, 128, 256} and dv a
  * multiple of 64; f32 with chunk*dk <= 8192, dk a multiple of 4, dv a multiple
  * of 16.
@@ -120,7 +130,8 @@ ret_status_t retention_chunkwise_fwd(const void* q, const void* k, const void* v
  * each phase in order: segment pre-pass, segment scan, main chunk kernel. Each
  * pair brackets that kernel's execution on `stream` (recorded by the launch
  * itself, so host submission gaps are not included); a phase that does not
- * run records its pair back to back. Same result and status codes as
+ * run records its pair back to back (bf16 runs every form as the one main
+ * kernel, so its first two pairs are always empty). Same result and status codes as
  * retention_chunkwise_fwd (RET_ERR_NULL if an event is missing).
  */
 ret_status_t retention_chunkwise_fwd_timed(const void* q, const void* k, const void* v, void* o,

@@ -179,6 +179,24 @@ def retention_parallel_fwd(q, k, v, gamma=None, theta=None, pos0=0, out=None, st
     return out
 
 
+_WORKSPACES = {}
+
+
+def _cached_workspace(nbytes, device, stream):
+    """Zero-filled workspace of at least nbytes for calls on `stream` (the
+    current stream when None). Growing it allocates and zero-fills a new
+    buffer, ordered on that stream before the call that uses it."""
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    key = (device.index if device.index is not None else torch.cuda.current_device(), s.cuda_stream)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < nbytes:
+        with torch.cuda.stream(s):
+            ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
 def retention_chunkwise_workspace_size(B, H, N, dk, dv, dtype, chunk, segments=0):
     torch = _torch()
     code = RET_BF16 if dtype == torch.bfloat16 else RET_F32
@@ -191,8 +209,10 @@ def retention_chunkwise_fwd(q, k, v, chunk=64, gamma=None, theta=None, pos0=0, s
     """Chunkwise retention forward. Returns o, or (o, state) with return_state.
 
     state_in / state_out are float32 [B,H,dk,dv] device tensors (state_out may
-    be state_in). The workspace is allocated here from torch's caching
-    allocator when not given. With `events` (six torch.cuda.Event created
+    be state_in). Without `workspace` the call uses a zero-filled workspace
+    this module keeps per (device, stream) and grows as needed; a caller's own
+    workspace must be zero-filled before its first use (the library leaves it
+    ready for the next call). With `events` (six torch.cuda.Event created
     with enable_timing=True: start/stop of the segment pre-pass, the segment
     scan and the main kernel) the call goes through
     retention_chunkwise_fwd_timed.
@@ -208,7 +228,7 @@ def retention_chunkwise_fwd(q, k, v, chunk=64, gamma=None, theta=None, pos0=0, s
     _check_dev(out)
     ws_bytes = retention_chunkwise_workspace_size(B, H, N, dk, dv, q.dtype, chunk, segments)
     if ws_bytes and workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=v.device)
+        workspace = _cached_workspace(ws_bytes, v.device, stream)
     _g, g = _host_floats(gamma, H, "gamma")
     _t, th = _host_floats(theta, dk // 2, "theta")
     args = [

@@ -20,6 +20,11 @@ using ret::HeadParams;
 constexpr size_t kMaxLdsBytes = 160 * 1024;
 constexpr int kTargetBlocks = 256;  // one workgroup per compute unit
 constexpr int kMaxSegments = 4096;
+// The segmented form keeps one ticket counter per (batch, head, value tile)
+// chain in a fixed region at the start of the workspace, so counters stay
+// counters whatever sizes share the workspace.
+constexpr size_t kCtlBytes = 65536;
+constexpr long long kMaxSegmentedChains = kCtlBytes / sizeof(unsigned long long);
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -83,7 +88,10 @@ int f32_parallel_dvt(int dk, int dv) {
 struct ChunkPlan {
     int dvt, nvt, nseg, seg_len, nseg_max;
     size_t ws_bytes;
+    size_t flags_off, agg_off, inc_off;  // byte offsets of the workspace regions
 };
+
+constexpr size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 
 // Segment count: enough (batch, head, value tile, segment) workgroups to keep
 // every compute unit busy, bounded independently of N so the workspace size
@@ -96,7 +104,9 @@ ret_status_t plan_chunk(int B, int H, int N, int dk, int dv, ret_dtype_t dtype, 
     if (p.dvt == 0) return RET_ERR_UNSUPPORTED;
     p.nvt = dv / p.dvt;
     const long long base = static_cast<long long>(B) * H * p.nvt;
-    if (segments > 0)
+    if (base > kMaxSegmentedChains)
+        p.nseg_max = 1;  // the grid is full without splitting sequences
+    else if (segments > 0)
         p.nseg_max = segments;
     else
         p.nseg_max = base >= 256 ? 1 : static_cast<int>((kTargetBlocks + base - 1) / base);
@@ -106,7 +116,13 @@ ret_status_t plan_chunk(int B, int H, int N, int dk, int dv, ret_dtype_t dtype, 
     const int per_seg = (nchunks + want - 1) / want;
     p.seg_len = per_seg * chunk;
     p.nseg = (N + p.seg_len - 1) / p.seg_len;
-    p.ws_bytes = p.nseg_max > 1 ? static_cast<size_t>(B) * H * p.nseg_max * dk * dv * sizeof(float) : 0;
+    // workspace: [ticket counter per chain | flags per (chain, segment) | segment states | inclusive states],
+    // chain = (batch, head, value tile)
+    const size_t states = static_cast<size_t>(B) * H * p.nseg_max * dk * dv * sizeof(float);
+    p.flags_off = kCtlBytes;
+    p.agg_off = p.flags_off + round256(static_cast<size_t>(base) * p.nseg_max * sizeof(unsigned long long));
+    p.inc_off = p.agg_off + states;
+    p.ws_bytes = p.nseg_max > 1 ? p.inc_off + states : 0;
     if (base * p.nseg > 2147483647LL) return RET_ERR_UNSUPPORTED;
     return RET_OK;
 }
@@ -167,7 +183,12 @@ static ret_status_t chunkwise_impl(const void* q, const void* k, const void* v, 
     a.o = static_cast<ret::u16*>(o);
     a.state_in = state_in;
     a.state_out = state_out;
-    a.ws = static_cast<float*>(workspace);
+    char* ws = static_cast<char*>(workspace);
+    const bool seg_ws = p.ws_bytes > 0;
+    a.ctl = seg_ws ? reinterpret_cast<unsigned long long*>(ws) : nullptr;
+    a.flags = seg_ws ? reinterpret_cast<unsigned long long*>(ws + p.flags_off) : nullptr;
+    a.agg = seg_ws ? reinterpret_cast<float*>(ws + p.agg_off) : nullptr;
+    a.inc = seg_ws ? reinterpret_cast<float*>(ws + p.inc_off) : nullptr;
     a.B = B;
     a.H = H;
     a.N = N;

@@ -40,6 +40,8 @@
 #include "kernels.hpp"
 #include "tiles.hpp"
 
+#include <type_traits>
+
 namespace ret {
 
 // Split of the (DK/16) x (DVT/16) state tiles over the waves: NG column
@@ -90,14 +92,76 @@ __device__ __forceinline__ int wave_row_block(int w) {
     return w < NW / 2 ? w : (3 * NW / 2 - 1) - w;
 }
 
-template <int DK, int DVT, int C, bool STATE_ONLY>
+// Segmented form: the workgroups of one (batch, head, value tile) chain split
+// its sequence into segments and pass states along the chain with a decoupled
+// look-back, all inside one launch:
+//   1. Workgroups take tickets from a counter in the workspace; ticket order is
+//      segment-major, so every segment a workgroup waits for belongs to a
+//      workgroup that took its ticket earlier and is already running.
+//   2. Each segment but the last runs the state recurrence over its own chunks
+//      from a zero state (segment 0: from the initial state) and publishes the
+//      result: T_s, the segment's own contribution ("aggregate"), or for
+//      segment 0 directly its end state ("inclusive").
+//   3. Segment s looks back over s-1, s-2, ... until it meets an inclusive
+//      state P_j; its start state is
+//          S_in(s) = sum_{j<i<s} g^(s-1-i) T_i + g^(s-1-j) P_j,   g = gamma^seg_len,
+//      and it publishes its own inclusive state P_s = g S_in(s) + T_s.
+//   4. It then runs the full chunk loop (outputs and state) from S_in(s).
+// Waits only ever target aggregates of earlier tickets, which are published
+// without waiting on anything, so every wait ends; a spin bound backs this up
+// (a look-back that exceeds it poisons the start state with NaN instead of
+// hanging). Each chain has its own ticket counter; a flag carries the chain's
+// launch generation (the high half of its counter, advanced by the workgroup
+// that draws the chain's last ticket) and the chain index, so no flag left by
+// an earlier call, of any size, reads as ready, and the workspace needs
+// zero-filling only once, before its first use.
+//
+// Published states and flags move through device-coherent (agent-scope)
+// loads and stores, which bypass the per-XCD L2 caches; a publisher waits
+// for its state stores to complete before a barrier and the flag store. This
+// avoids device-scope fences, which on this chip write back or invalidate
+// a whole L2 and cost tens of microseconds under load.
+constexpr unsigned kMaxLookbackSpins = 1u << 20;
+
+__device__ __forceinline__ void store_coherent(f32x4* p, const f32x4& v) {
+    unsigned long long* q = reinterpret_cast<unsigned long long*>(p);
+    const f32x2 lo = {v[0], v[1]}, hi = {v[2], v[3]};
+    __hip_atomic_store(q, __builtin_bit_cast(unsigned long long, lo), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, __builtin_bit_cast(unsigned long long, hi), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ f32x4 load_coherent(const f32x4* p) {
+    unsigned long long* q = reinterpret_cast<unsigned long long*>(const_cast<f32x4*>(p));
+    const f32x2 lo =
+        __builtin_bit_cast(f32x2, __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    const f32x2 hi =
+        __builtin_bit_cast(f32x2, __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    return f32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// Wait until this thread's global stores have completed.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Kernel forms: one pass per (batch, head, value tile) chain; segmented with a
+// state-only first pass; segmented with outputs held back (segments of at
+// most kKeepChunks chunks).
+enum ChunkMode { kSinglePass = 0, kTwoPass = 1, kLocalPass = 2 };
+constexpr int kKeepChunks = 2;
+
+template <int DK, int DVT, int C, int MODE>
 __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, HeadParams hp) {
+    constexpr bool SEGMENTED = MODE != kSinglePass;
     using G = ChunkGeo<DK, DVT, C>;
     constexpr int UK = DK / 8;  // 16-byte units in a row of K (row-major) and of S^T
     constexpr int UC = C / 8;   // 16-byte units in a row of K^T and V^T
     __shared__ __attribute__((aligned(16))) u16 kbuf[C * DK];
     __shared__ __attribute__((aligned(16))) u16 vbuf[DVT * C];
-    __shared__ __attribute__((aligned(16))) u16 sbuf[STATE_ONLY ? 8 : DVT * DK];
+    __shared__ __attribute__((aligned(16))) u16 sbuf[DVT * DK];
+    // Broadcast slots of the segmented form, overlaid on sbuf: both are read
+    // before the first write of the state copy (a barrier lies in between).
+    unsigned long long* s_ticket = reinterpret_cast<unsigned long long*>(sbuf);
+    int* s_lookback = reinterpret_cast<int*>(sbuf + 4);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -105,12 +169,26 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     const int l16 = lane & 15;
     const int grp = lane >> 4;
 
-    // ---- which (batch*head, segment, value tile) this workgroup owns
-    const int nseg_grid = STATE_ONLY ? a.nseg - 1 : a.nseg;
-    const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
-    const int vt = lb % a.nvt;
-    const int seg = (lb / a.nvt) % nseg_grid;
-    const int bh = lb / (a.nvt * nseg_grid);
+    // ---- which (batch*head, value tile) chain and segment this workgroup owns
+    int chain, seg = 0;
+    unsigned gen = 0;
+    if constexpr (SEGMENTED) {
+        const int nchains = a.B * a.H * a.nvt;
+        chain = blockIdx.x % nchains;
+        unsigned long long* ctl = a.ctl + chain;
+        if (tid == 0) *s_ticket = __hip_atomic_fetch_add(ctl, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const unsigned long long tk = *s_ticket;
+        const unsigned nseg = static_cast<unsigned>(a.nseg);
+        seg = static_cast<int>(static_cast<unsigned>(tk) % nseg);
+        gen = static_cast<unsigned>(tk >> 32);
+        if (tid == 0 && static_cast<unsigned>(tk) == nseg - 1)  // chain's last ticket: reset count, next generation
+            __hip_atomic_fetch_add(ctl, (1ull << 32) - nseg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        chain = xcd_logical_block(blockIdx.x, gridDim.x);
+    }
+    const int vt = chain % a.nvt;
+    const int bh = chain / a.nvt;
     const int h = bh % a.H;
 
     const float gam = hp.gamma[h];
@@ -131,60 +209,56 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     const int d_base = (wave % G::MG) * G::MT * 16;  // this wave's S rows ...
     const int c_base = (wave / G::MG) * G::NT * 16;  // ... and S columns (within the value tile)
 
-    // ---- prefetch the first chunk (issued before the initial-state loads so the
-    //      two HBM round trips overlap)
     BlockRows<G::BWK> kr[G::KPT];
     BlockRows<G::BWV> vr[G::VPT];
     uint4 qf[G::KSQ];
-    auto load_q = [&](int t, int Lq) {
+    f32x4 sacc[G::MT][G::NT];
+
+    auto load_q = [&](int t, int Lq) __attribute__((always_inline)) {
         const int row = rb * 16 + l16;
         const u16* p = Qg + static_cast<size_t>(t + row) * DK + grp * 8;
 #pragma unroll
         for (int s = 0; s < G::KSQ; ++s)
             qf[s] = row < Lq ? *reinterpret_cast<const uint4*>(p + s * 32) : make_uint4(0, 0, 0, 0);
     };
-    {
+    // first chunk of the segment (issued before state loads so the HBM round trips overlap)
+    auto prefetch_first = [&](bool with_q) __attribute__((always_inline)) {
         const int L0 = min(C, t_end - t_begin);
         load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR>(kr, Kg + static_cast<size_t>(t_begin) * DK, DK, L0, tid);
-        load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR>(vr, Vg + static_cast<size_t>(t_begin) * a.dv, a.dv, L0, tid);
-        if (!STATE_ONLY) load_q(t_begin, L0);
-    }
-
-    // ---- initial state
-    f32x4 sacc[G::MT][G::NT];
-    const float* s_src = nullptr;
-    if (!STATE_ONLY) {
-        if (a.nseg > 1)
-            s_src = a.ws + (static_cast<size_t>(bh) * a.nseg + seg) * DK * a.dv;
-        else if (a.state_in)
-            s_src = a.state_in + static_cast<size_t>(bh) * DK * a.dv;
-    }
+        load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR>(vr, Vg + static_cast<size_t>(t_begin) * a.dv, a.dv, L0,
+                                                          tid);
+        if (with_q) load_q(t_begin, L0);
+    };
+    // this head's state from a caller's [B*H][dk][dv] float32 array, or zeros
+    auto load_state = [&](const float* states) __attribute__((always_inline)) {
+        const float* src = states ? states + static_cast<size_t>(bh) * DK * a.dv : nullptr;
 #pragma unroll
-    for (int mt = 0; mt < G::MT; ++mt)
+        for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < G::NT; ++nt)
+            for (int nt = 0; nt < G::NT; ++nt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int d = d_base + mt * 16 + grp * 4 + r;
-                const int c = vt * DVT + c_base + nt * 16 + l16;
-                sacc[mt][nt][r] = s_src ? s_src[static_cast<size_t>(d) * a.dv + c] : 0.0f;
-            }
-    bool have_state = (s_src != nullptr);
-
+                for (int r = 0; r < 4; ++r) {
+                    const int d = d_base + mt * 16 + grp * 4 + r;
+                    const int c = vt * DVT + c_base + nt * 16 + l16;
+                    sacc[mt][nt][r] = src ? src[static_cast<size_t>(d) * a.dv + c] : 0.0f;
+                }
+    };
     // bf16 copy of this wave's state tiles into S^T (row = value column, 4 consecutive dk)
-    auto write_state_copy = [&](int l16_, int grp_) {
+    auto write_state_copy_of = [&](const f32x4 (&st)[G::MT][G::NT], int l16_, int grp_) __attribute__((always_inline)) {
 #pragma unroll
         for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
             for (int nt = 0; nt < G::NT; ++nt) {
                 const int d = d_base + mt * 16 + grp_ * 4;
                 const int c = c_base + nt * 16 + l16_;
-                const uint2 w = make_uint2(pack2_bf16(sacc[mt][nt][0], sacc[mt][nt][1]),
-                                           pack2_bf16(sacc[mt][nt][2], sacc[mt][nt][3]));
+                const uint2 w = make_uint2(pack2_bf16(st[mt][nt][0], st[mt][nt][1]),
+                                           pack2_bf16(st[mt][nt][2], st[mt][nt][3]));
                 *reinterpret_cast<uint2*>(&sbuf[swz<UK>(c, d >> 3) + (d & 7)]) = w;
             }
     };
-    if (!STATE_ONLY && have_state) write_state_copy(l16, grp);
+    auto write_state_copy = [&](int l16_, int grp_) __attribute__((always_inline)) {
+        write_state_copy_of(sacc, l16_, grp_);
+    };
 
     // ---- per-lane decay constants
     // D[i][j] = gamma^(i-j) with i = 16 rb + l16, j = 16 jt + 4 grp + r:
@@ -194,25 +268,23 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     for (int r = 0; r < 4; ++r) dlane[r] = fast_exp2(static_cast<float>(l16 - 4 * grp - r) * lg2f);
     const float zeta = fast_exp2(static_cast<float>(16 * rb + l16 + 1) * lg2f);
     const float gC = gamma_pow(lg2, C);
+    bool have_state = false;
 
-    for (int ch = 0; ch < nch; ++ch) {
-        // Per-iteration copies the compiler cannot prove loop-invariant: the
-        // block-write addresses and the decay factors are recomputed each
-        // chunk (a few VALU ops under the MFMAs) instead of being hoisted out
-        // of the loop and held in registers for its whole length.
-        int tid_it = tid;
-        float lg2_it = lg2f;
-        asm volatile("" : "+v"(tid_it), "+v"(lg2_it));
-        const float lg2c = lg2_it;
-        const int l16c = tid_it & 15;
-        const int grpc = (tid_it & 63) >> 4;
-        const int t0 = t_begin + ch * C;
-        const int L = min(C, t_end - t0);
-        const bool has_next = (ch + 1) < nch;
-        const int t1 = t0 + C;
-        const int L1 = has_next ? min(C, t_end - t1) : 0;
-
-        // ---- 1. rotate keys; K^T (scaled by xi) and V^T into LDS; rotate queries
+    // ---- pieces of the chunk loop
+    // Step 7: this wave's 16 output rows of the chunk at token t0 (L valid), as bf16.
+    auto store_o = [&](const f32x4 (&o)[G::NTV], int t0, int L) __attribute__((always_inline)) {
+        const int row = rb * 16 + l16;
+        if (row < L) {
+            u16* orow = Og + static_cast<size_t>(t0 + row) * a.dv + grp * 4;
+#pragma unroll
+            for (int nt = 0; nt < G::NTV; ++nt) {
+                const uint2 w = make_uint2(pack2_bf16(o[nt][0], o[nt][1]), pack2_bf16(o[nt][2], o[nt][3]));
+                *reinterpret_cast<uint2*>(orow + nt * 16) = w;
+            }
+        }
+    };
+    // Step 1: rotate the chunk's keys; K^T (scaled by xi) and V^T into LDS.
+    auto stage_kv = [&](auto& krb, auto& vrb, int t0, int L, int tid_it, float lg2c) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < G::KPT; ++u) {
             const int idx = tid_it + u * G::NTHR;
@@ -223,7 +295,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
 #pragma unroll
                     for (int q = 0; q < 8; ++q)
                         if (staged_token(tb, q) < L)
-                            rotate_row<G::BWK>(kr[u].w[q], hp, cb * (G::BWK / 2),
+                            rotate_row<G::BWK>(krb[u].w[q], hp, cb * (G::BWK / 2),
                                                static_cast<double>(a.pos0 + t0 + staged_token(tb, q)));
                 }
                 float xi[8];
@@ -234,8 +306,8 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
                     uint32_t w[4];
 #pragma unroll
                     for (int p = 0; p < 4; ++p) {
-                        const float lo = bf16_to_f32(static_cast<u16>(elem16(kr[u].w[2 * p], c))) * xi[2 * p];
-                        const float hi = bf16_to_f32(static_cast<u16>(elem16(kr[u].w[2 * p + 1], c))) * xi[2 * p + 1];
+                        const float lo = bf16_to_f32(static_cast<u16>(elem16(krb[u].w[2 * p], c))) * xi[2 * p];
+                        const float hi = bf16_to_f32(static_cast<u16>(elem16(krb[u].w[2 * p + 1], c))) * xi[2 * p + 1];
                         w[p] = pack2_bf16(lo, hi);
                     }
                     *reinterpret_cast<uint4*>(&kbuf[swz<UC>(cb * G::BWK + c, tb)]) = make_uint4(w[0], w[1], w[2], w[3]);
@@ -250,22 +322,107 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
                 block_coords<DVT, G::BWV>(idx, tb, cb);
 #pragma unroll
                 for (int c = 0; c < G::BWV; ++c)
-                    *reinterpret_cast<uint4*>(&vbuf[swz<UC>(cb * G::BWV + c, tb)]) = block_column(vr[u], c);
+                    *reinterpret_cast<uint4*>(&vbuf[swz<UC>(cb * G::BWV + c, tb)]) = block_column(vrb[u], c);
             }
         }
-        if (!STATE_ONLY && hp.has_theta) {
-            const int row = rb * 16 + l16;
-            if (row < L) {
+    };
+    // K and V of the chunk starting at token t (L valid tokens) into staging registers.
+    auto load_kv = [&](auto& krb, auto& vrb, int t, int L) __attribute__((always_inline)) {
+        load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR>(krb, Kg + static_cast<size_t>(t) * DK, DK, L, tid);
+        load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR>(vrb, Vg + static_cast<size_t>(t) * a.dv, a.dv, L, tid);
+    };
+    // Step 3 (G4): S = gamma^L S + Kx^T V on this wave's tiles.
+    auto g4 = [&](int L, int l16c, int grpc) __attribute__((always_inline)) {
+        const float gL = (L == C) ? gC : gamma_pow(lg2, L);
+        const FragAddr<UC> fa_kt(d_base + l16c, grpc);  // K^T rows d_base + 16 mt + l16, tokens 32 t + 8 grp
+        const FragAddr<UC> fa_vt(c_base + l16c, grpc);  // V^T rows c_base + 16 nt + l16, tokens 32 t + 8 grp
 #pragma unroll
-                for (int s = 0; s < G::KSQ; ++s)
-                    qf[s] = rotate8_bf16(qf[s], hp, s * 16 + grp * 4, static_cast<double>(a.pos0 + t0 + row));
+        for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < G::NT; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sacc[mt][nt][r] *= gL;
+#pragma unroll
+        for (int t = 0; t < G::KST; ++t) {
+            if (t * 32 < L) {
+                uint4 af[G::MT];
+#pragma unroll
+                for (int mt = 0; mt < G::MT; ++mt) af[mt] = *reinterpret_cast<const uint4*>(&kbuf[fa_kt.at(mt, t)]);
+#pragma unroll
+                for (int nt = 0; nt < G::NT; ++nt) {
+                    const uint4 bfr = *reinterpret_cast<const uint4*>(&vbuf[fa_vt.at(nt, t)]);
+#pragma unroll
+                    for (int mt = 0; mt < G::MT; ++mt) sacc[mt][nt] = mfma16x16x32(af[mt], bfr, sacc[mt][nt]);
+                }
             }
         }
-        __syncthreads();  // A: K^T, V^T written
+    };
 
-        // ---- 2. G3: O^T = S^T Q^T with the previous chunk's state, times zeta
-        f32x4 oacc[G::NTV];
-        if (!STATE_ONLY) {
+    // The state recurrence alone over this segment (keys and values only), with
+    // two chunks of loads in flight: chunk ch + 2 is fetched into the registers
+    // chunk ch has just been staged from, under G4 of chunk ch.
+    BlockRows<G::BWK> kr2[G::KPT];
+    BlockRows<G::BWV> vr2[G::VPT];
+    auto run_state_only = [&]() __attribute__((always_inline)) {
+        if (nch > 1) load_kv(kr2, vr2, t_begin + C, min(C, t_end - t_begin - C));
+        auto step = [&](auto& krb, auto& vrb, int ch) __attribute__((always_inline)) {
+            // per-iteration opaque copies: see run_chunks
+            int tid_it = tid;
+            float lg2_it = lg2f;
+            asm volatile("" : "+v"(tid_it), "+v"(lg2_it));
+            const int t0 = t_begin + ch * C;
+            const int L = min(C, t_end - t0);
+            stage_kv(krb, vrb, t0, L, tid_it, lg2_it);
+            if (ch + 2 < nch) load_kv(krb, vrb, t0 + 2 * C, min(C, t_end - t0 - 2 * C));
+            __syncthreads();  // K^T, V^T written
+            g4(L, tid_it & 15, (tid_it & 63) >> 4);
+            __syncthreads();  // K^T, V^T read
+        };
+        for (int ch = 0; ch < nch; ch += 2) {
+            step(kr, vr, ch);
+            if (ch + 1 < nch) step(kr2, vr2, ch + 1);
+        }
+    };
+
+    // The full chunk loop over this segment: outputs and state. With KEEP the
+    // outputs stay in registers (with the rotated queries) instead of going to
+    // HBM: the segment was started from a zero state and is corrected once its
+    // start state is known.
+    f32x4 oacc_keep[kKeepChunks][G::NTV];
+    uint4 qf_keep[kKeepChunks][G::KSQ];
+    auto run_chunks = [&](auto keep_tag) __attribute__((always_inline)) {
+        constexpr bool KEEP = decltype(keep_tag)::value;
+        auto body = [&](int ch) __attribute__((always_inline)) {
+            // Per-iteration copies the compiler cannot prove loop-invariant: the
+            // block-write addresses and the decay factors are recomputed each
+            // chunk (a few VALU ops under the MFMAs) instead of being hoisted out
+            // of the loop and held in registers for its whole length.
+            int tid_it = tid;
+            float lg2_it = lg2f;
+            asm volatile("" : "+v"(tid_it), "+v"(lg2_it));
+            const float lg2c = lg2_it;
+            const int l16c = tid_it & 15;
+            const int grpc = (tid_it & 63) >> 4;
+            const int t0 = t_begin + ch * C;
+            const int L = min(C, t_end - t0);
+            const bool has_next = (ch + 1) < nch;
+            const int t1 = t0 + C;
+            const int L1 = has_next ? min(C, t_end - t1) : 0;
+
+            // ---- 1. K^T (scaled by xi) and V^T into LDS; rotate queries
+            stage_kv(kr, vr, t0, L, tid_it, lg2c);
+            if (hp.has_theta) {
+                const int row = rb * 16 + l16;
+                if (row < L) {
+#pragma unroll
+                    for (int s = 0; s < G::KSQ; ++s)
+                        qf[s] = rotate8_bf16(qf[s], hp, s * 16 + grp * 4, static_cast<double>(a.pos0 + t0 + row));
+                }
+            }
+            __syncthreads();  // A: K^T, V^T written
+
+            // ---- 2. G3: O^T = S^T Q^T with the previous chunk's state, times zeta
+            f32x4 oacc[G::NTV];
 #pragma unroll
             for (int nt = 0; nt < G::NTV; ++nt) oacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (have_state) {
@@ -283,155 +440,120 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
 #pragma unroll
                     for (int r = 0; r < 4; ++r) oacc[nt][r] *= zeta;
             }
-        }
 
-        // ---- 3. G4: S = gamma^L S + Kx^T V on this wave's tiles
-        {
-            const float gL = (L == C) ? gC : gamma_pow(lg2, L);
-            const FragAddr<UC> fa_kt(d_base + l16c, grpc);  // K^T rows d_base + 16 mt + l16, tokens 32 t + 8 grp
-            const FragAddr<UC> fa_vt(c_base + l16c, grpc);  // V^T rows c_base + 16 nt + l16, tokens 32 t + 8 grp
+            // ---- 3. G4: S = gamma^L S + Kx^T V on this wave's tiles
+            g4(L, l16c, grpc);
+            __syncthreads();  // B: S^T and K^T reads done
+
+            // ---- 4. new bf16 state copy, K row-major into LDS, prefetch next keys/values
+            write_state_copy(l16c, grpc);
+            have_state = true;
 #pragma unroll
-            for (int mt = 0; mt < G::MT; ++mt)
+            for (int u = 0; u < G::KPT; ++u) {
+                const int idx = tid_it + u * G::NTHR;
+                if (idx < G::KB) {
+                    int tb, cb;
+                    block_coords<DK, G::BWK>(idx, tb, cb);
 #pragma unroll
-                for (int nt = 0; nt < G::NT; ++nt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) sacc[mt][nt][r] *= gL;
-#pragma unroll
-            for (int t = 0; t < G::KST; ++t) {
-                if (t * 32 < L) {
-                    uint4 af[G::MT];
-#pragma unroll
-                    for (int mt = 0; mt < G::MT; ++mt) af[mt] = *reinterpret_cast<const uint4*>(&kbuf[fa_kt.at(mt, t)]);
-#pragma unroll
-                    for (int nt = 0; nt < G::NT; ++nt) {
-                        const uint4 bfr = *reinterpret_cast<const uint4*>(&vbuf[fa_vt.at(nt, t)]);
-#pragma unroll
-                        for (int mt = 0; mt < G::MT; ++mt) sacc[mt][nt] = mfma16x16x32(af[mt], bfr, sacc[mt][nt]);
+                    for (int q = 0; q < 8; ++q) {
+                        const int row = staged_token(tb, q);
+                        if constexpr (G::BWK == 8) {
+                            *reinterpret_cast<uint4*>(&kbuf[swz<UK>(row, cb)]) =
+                                make_uint4(kr[u].w[q][0], kr[u].w[q][1], kr[u].w[q][2], kr[u].w[q][3]);
+                        } else {
+                            *reinterpret_cast<uint2*>(&kbuf[swz<UK>(row, cb >> 1) + 4 * (cb & 1)]) =
+                                make_uint2(kr[u].w[q][0], kr[u].w[q][1]);
+                        }
                     }
                 }
             }
-        }
+            if (has_next) load_kv(kr, vr, t1, L1);
+            __syncthreads();  // C: K row-major written
 
-        if (STATE_ONLY) {
-            __syncthreads();  // everyone done reading kbuf / vbuf
-            if (has_next) {
-                load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR>(kr, Kg + static_cast<size_t>(t1) * DK, DK, L1, tid);
-                load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR>(vr, Vg + static_cast<size_t>(t1) * a.dv, a.dv, L1, tid);
-            }
-            continue;
-        }
-
-        __syncthreads();  // B: S^T and K^T reads done
-
-        // ---- 4. new bf16 state copy, K row-major into LDS, prefetch next keys/values
-        write_state_copy(l16c, grpc);
-        have_state = true;
+            // ---- 5. G1: P^T = K Q^T for this wave's rows, decay mask in registers,
+            //         one 32-token step at a time, packed into bf16 B operands for G2.
+            //         Steps entirely above the diagonal are skipped (one uniform
+            //         branch per step); inside a step both 16-key halves run and
+            //         the mask zeroes what lies above the diagonal.
+            uint4 pf[G::KST];
+            {
+                const FragAddr<UK> fa_k(l16c, grpc);  // K rows 16 jt + l16, dk 32 s + 8 grp
 #pragma unroll
-        for (int u = 0; u < G::KPT; ++u) {
-            const int idx = tid_it + u * G::NTHR;
-            if (idx < G::KB) {
-                int tb, cb;
-                block_coords<DK, G::BWK>(idx, tb, cb);
+                for (int t = 0; t < G::KST; ++t) {
+                    pf[t] = make_uint4(0, 0, 0, 0);
+                    if (2 * t <= rb) {
+                        f32x4 pa[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const int row = staged_token(tb, q);
-                    if constexpr (G::BWK == 8) {
-                        *reinterpret_cast<uint4*>(&kbuf[swz<UK>(row, cb)]) =
-                            make_uint4(kr[u].w[q][0], kr[u].w[q][1], kr[u].w[q][2], kr[u].w[q][3]);
-                    } else {
-                        *reinterpret_cast<uint2*>(&kbuf[swz<UK>(row, cb >> 1) + 4 * (cb & 1)]) =
-                            make_uint2(kr[u].w[q][0], kr[u].w[q][1]);
-                    }
-                }
-            }
-        }
-        if (has_next) {
-            load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR>(kr, Kg + static_cast<size_t>(t1) * DK, DK, L1, tid);
-            load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR>(vr, Vg + static_cast<size_t>(t1) * a.dv, a.dv, L1, tid);
-        }
-        __syncthreads();  // C: K row-major written
-
-        // ---- 5. G1: P^T = K Q^T for this wave's rows, decay mask in registers,
-        //         one 32-token step at a time, packed into bf16 B operands for G2.
-        //         Steps entirely above the diagonal are skipped (one uniform
-        //         branch per step); inside a step both 16-key halves run and
-        //         the mask zeroes what lies above the diagonal.
-        uint4 pf[G::KST];
-        {
-            const FragAddr<UK> fa_k(l16c, grpc);  // K rows 16 jt + l16, dk 32 s + 8 grp
+                        for (int s = 0; s < G::KSQ; ++s) {
 #pragma unroll
-            for (int t = 0; t < G::KST; ++t) {
-                pf[t] = make_uint4(0, 0, 0, 0);
-                if (2 * t <= rb) {
-                    f32x4 pa[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-                    for (int s = 0; s < G::KSQ; ++s) {
+                            for (int hh = 0; hh < 2; ++hh) {
+                                const uint4 af = *reinterpret_cast<const uint4*>(&kbuf[fa_k.at(2 * t + hh, s)]);
+                                pa[hh] = mfma16x16x32(af, qf[s], pa[hh]);
+                            }
+                        }
 #pragma unroll
                         for (int hh = 0; hh < 2; ++hh) {
-                            const uint4 af = *reinterpret_cast<const uint4*>(&kbuf[fa_k.at(2 * t + hh, s)]);
-                            pa[hh] = mfma16x16x32(af, qf[s], pa[hh]);
+                            const int delta = rb - (2 * t + hh);
+                            const float blk = fast_exp2(static_cast<float>(16 * delta) * lg2c);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                float val = 0.0f;
+                                if (delta > 0 || (delta == 0 && l16 >= 4 * grp + r)) val = pa[hh][r] * (dlane[r] * blk);
+                                pa[hh][r] = val;
+                            }
+                        }
+                        pf[t] = make_uint4(pack2_bf16(pa[0][0], pa[0][1]), pack2_bf16(pa[0][2], pa[0][3]),
+                                           pack2_bf16(pa[1][0], pa[1][1]), pack2_bf16(pa[1][2], pa[1][3]));
+                    }
+                }
+            }
+
+            // ---- prefetch next chunk's queries (qf is dead for this chunk now)
+            if constexpr (KEEP) {
+#pragma unroll
+                for (int s = 0; s < G::KSQ; ++s) qf_keep[ch][s] = qf[s];
+            }
+            if (has_next) load_q(t1, L1);
+
+            // ---- 6. G2: O^T += V^T P^T
+            {
+                // V^T rows 16 nt + l16, staged unit 4 t + grp: tokens 32 t + 4 grp + {0..3, 16..19},
+                // the order in which pf holds this lane group's scores
+                const FragAddr<UC> fa_v(l16c, grpc);
+#pragma unroll
+                for (int t = 0; t < G::KST; ++t) {
+                    if (2 * t <= rb) {
+#pragma unroll
+                        for (int nt = 0; nt < G::NTV; ++nt) {
+                            const uint4 af = *reinterpret_cast<const uint4*>(&vbuf[fa_v.at(nt, t)]);
+                            oacc[nt] = mfma16x16x32(af, pf[t], oacc[nt]);
                         }
                     }
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const int delta = rb - (2 * t + hh);
-                        const float blk = fast_exp2(static_cast<float>(16 * delta) * lg2c);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            float val = 0.0f;
-                            if (delta > 0 || (delta == 0 && l16 >= 4 * grp + r)) val = pa[hh][r] * (dlane[r] * blk);
-                            pa[hh][r] = val;
-                        }
-                    }
-                    pf[t] = make_uint4(pack2_bf16(pa[0][0], pa[0][1]), pack2_bf16(pa[0][2], pa[0][3]),
-                                       pack2_bf16(pa[1][0], pa[1][1]), pack2_bf16(pa[1][2], pa[1][3]));
                 }
             }
-        }
 
-        // ---- prefetch next chunk's queries (qf is dead for this chunk now)
-        if (has_next) load_q(t1, L1);
-
-        // ---- 6. G2: O^T += V^T P^T
-        {
-            // V^T rows 16 nt + l16, staged unit 4 t + grp: tokens 32 t + 4 grp + {0..3, 16..19},
-            // the order in which pf holds this lane group's scores
-            const FragAddr<UC> fa_v(l16c, grpc);
+            // ---- 7. store O (bf16)
+            if constexpr (KEEP) {
 #pragma unroll
-            for (int t = 0; t < G::KST; ++t) {
-                if (2 * t <= rb) {
-#pragma unroll
-                    for (int nt = 0; nt < G::NTV; ++nt) {
-                        const uint4 af = *reinterpret_cast<const uint4*>(&vbuf[fa_v.at(nt, t)]);
-                        oacc[nt] = mfma16x16x32(af, pf[t], oacc[nt]);
-                    }
-                }
+                for (int nt = 0; nt < G::NTV; ++nt) oacc_keep[ch][nt] = oacc[nt];
+            } else {
+                store_o(oacc, t0, L);
             }
-        }
-
-        // ---- 7. store O (bf16)
-        {
-            const int row = rb * 16 + l16;
-            if (row < L) {
-                u16* orow = Og + static_cast<size_t>(t0 + row) * a.dv + grp * 4;
+            __syncthreads();  // D: reads of kbuf and vbuf done before the next chunk's writes
+        };
+        if constexpr (KEEP) {
 #pragma unroll
-                for (int nt = 0; nt < G::NTV; ++nt) {
-                    const uint2 w = make_uint2(pack2_bf16(oacc[nt][0], oacc[nt][1]),
-                                               pack2_bf16(oacc[nt][2], oacc[nt][3]));
-                    *reinterpret_cast<uint2*>(orow + nt * 16) = w;
-                }
-            }
+            for (int ch = 0; ch < kKeepChunks; ++ch)
+                if (ch < nch) body(ch);
+        } else {
+            for (int ch = 0; ch < nch; ++ch) body(ch);
         }
-        __syncthreads();  // D: reads of kbuf and vbuf done before the next chunk's writes
-    }
+    };
 
-    // ---- final state
-    float* s_dst = nullptr;
-    if (STATE_ONLY)
-        s_dst = a.ws + (static_cast<size_t>(bh) * a.nseg + seg + 1) * DK * a.dv;
-    else if (seg == a.nseg - 1 && a.state_out)
-        s_dst = a.state_out + static_cast<size_t>(bh) * DK * a.dv;
-    if (s_dst) {
+    // ---- final state of the last segment
+    auto write_final_state = [&](const f32x4 (&st)[G::MT][G::NT]) __attribute__((always_inline)) {
+        if (seg != a.nseg - 1 || !a.state_out) return;
+        float* s_dst = a.state_out + static_cast<size_t>(bh) * DK * a.dv;
 #pragma unroll
         for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
@@ -440,26 +562,253 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
                 for (int r = 0; r < 4; ++r) {
                     const int d = d_base + mt * 16 + grp * 4 + r;
                     const int c = vt * DVT + c_base + nt * 16 + l16;
-                    s_dst[static_cast<size_t>(d) * a.dv + c] = sacc[mt][nt][r];
+                    s_dst[static_cast<size_t>(d) * a.dv + c] = st[mt][nt][r];
                 }
+    };
+
+    if constexpr (!SEGMENTED) {
+        prefetch_first(true);
+        load_state(a.state_in);
+        have_state = a.state_in != nullptr;
+        if (have_state) write_state_copy(l16, grp);
+        run_chunks(std::false_type{});
+        write_final_state(sacc);
+        return;
+    }
+
+    // Published states are stored in accumulator order: thread (wave, lane)
+    // keeps its (mt, nt) tile as one float4, so every access is a coalesced
+    // 16-byte load or store by the thread that uses it.
+    constexpr int kSlot = DK * DVT;
+    auto slot = [&](float* region, int j) __attribute__((always_inline)) {
+        return reinterpret_cast<f32x4*>(region + (static_cast<size_t>(chain) * a.nseg + j) * kSlot) +
+               wave * (G::MT * G::NT * 64) + lane;
+    };
+    unsigned long long* flags = a.flags + static_cast<size_t>(chain) * a.nseg;
+    const unsigned long long f_agg =
+        (static_cast<unsigned long long>(gen + 1) << 32) | (static_cast<unsigned long long>(chain) << 1);
+    const unsigned long long f_inc = f_agg | 1ull;
+    auto publish = [&](const f32x4 (&st)[G::MT][G::NT], float* region, unsigned long long flag)
+                       __attribute__((always_inline)) {
+        f32x4* dst = slot(region, seg);
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < G::NT; ++nt) store_coherent(dst + (mt * G::NT + nt) * 64, st[mt][nt]);
+        wait_stores();
+        __syncthreads();
+        if (tid == 0) __hip_atomic_store(flags + seg, flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    const float gseg = static_cast<float>(gamma_pow(lg2, a.seg_len));
+    // S_in of this segment (seg >= 1) into sin, from its predecessors' published states.
+    auto look_back = [&](f32x4 (&sin)[G::MT][G::NT]) __attribute__((always_inline)) {
+        if (wave == 0) {
+            // lane i watches predecessor j0 - i
+            int j0 = seg - 1, n_agg = 0, failed = 0;
+            unsigned spins = 0;
+            for (;;) {
+                const int j = j0 - lane;
+                unsigned long long f = 0;
+                if (j >= 0) f = __hip_atomic_load(flags + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const unsigned long long m_inc = __ballot(j >= 0 && f == f_inc);
+                const unsigned long long m_rdy = __ballot(j >= 0 && (f == f_agg || f == f_inc));
+                if (m_inc != 0) {
+                    const int p = __builtin_ctzll(m_inc);  // nearest inclusive predecessor
+                    const unsigned long long below = (1ull << p) - 1;
+                    if ((m_rdy & below) == below) {
+                        n_agg += p;
+                        break;
+                    }
+                } else if (m_rdy == ~0ull) {  // 64 aggregates and no inclusive state: next window
+                    n_agg += 64;
+                    j0 -= 64;
+                    continue;
+                }
+                if (++spins > kMaxLookbackSpins) {
+                    failed = 1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+            if (lane == 0) {
+                s_lookback[0] = n_agg;
+                s_lookback[1] = failed;
+            }
+        }
+        __syncthreads();
+        const int n_agg = s_lookback[0];
+        const int failed = s_lookback[1];
+        __syncthreads();  // slots read before sbuf receives a state copy
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < G::NT; ++nt) sin[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // predecessors' states are fetched in batches so several are in flight at once
+        constexpr int kBatch = (G::MT * G::NT) >= 16 ? 1 : 16 / (G::MT * G::NT);
+        float fac = 1.0f;
+        int i = 0;
+        for (; i + kBatch <= n_agg; i += kBatch) {
+            f32x4 t[kBatch][G::MT][G::NT];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const f32x4* src = slot(a.agg, seg - 1 - i - u);
+#pragma unroll
+                for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < G::NT; ++nt) t[u][mt][nt] = load_coherent(src + (mt * G::NT + nt) * 64);
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+#pragma unroll
+                for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < G::NT; ++nt) sin[mt][nt] += fac * t[u][mt][nt];
+                fac *= gseg;
+            }
+        }
+        for (; i < n_agg; ++i) {
+            const f32x4* src = slot(a.agg, seg - 1 - i);
+#pragma unroll
+            for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < G::NT; ++nt) sin[mt][nt] += fac * load_coherent(src + (mt * G::NT + nt) * 64);
+            fac *= gseg;
+        }
+        {
+            const f32x4* src = slot(a.inc, seg - 1 - n_agg);
+#pragma unroll
+            for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < G::NT; ++nt) sin[mt][nt] += fac * load_coherent(src + (mt * G::NT + nt) * 64);
+        }
+        if (failed) {
+#pragma unroll
+            for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < G::NT; ++nt) sin[mt][nt] = f32x4{NAN, NAN, NAN, NAN};
+        }
+    };
+
+    if constexpr (MODE == kTwoPass) {
+        // ---- pass 1: this segment's own state (all segments but the last)
+        if (seg < a.nseg - 1) {
+            prefetch_first(false);
+            load_state(seg == 0 ? a.state_in : nullptr);
+            run_state_only();
+            publish(sacc, seg == 0 ? a.inc : a.agg, seg == 0 ? f_inc : f_agg);
+        }
+        // ---- the start state
+        prefetch_first(true);
+        if (seg == 0) {
+            load_state(a.state_in);
+        } else {
+            if (seg < a.nseg - 1) {  // P_s = g S_in + T_s, T_s still in sacc
+                f32x4 sin[G::MT][G::NT];
+                look_back(sin);
+                f32x4* dst = slot(a.inc, seg);
+#pragma unroll
+                for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < G::NT; ++nt) {
+                        store_coherent(dst + (mt * G::NT + nt) * 64, gseg * sin[mt][nt] + sacc[mt][nt]);
+                        sacc[mt][nt] = sin[mt][nt];
+                    }
+                wait_stores();
+                __syncthreads();
+                if (tid == 0) __hip_atomic_store(flags + seg, f_inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                look_back(sacc);
+            }
+        }
+        // ---- pass 2: outputs and state from the start state
+        have_state = seg > 0 || a.state_in != nullptr;
+        if (have_state) write_state_copy(l16, grp);
+        run_chunks(std::false_type{});
+        write_final_state(sacc);
+    } else if constexpr (MODE == kLocalPass) {
+        prefetch_first(true);
+        if (seg == 0) {
+            // the start state is known: the ordinary pass, then publish the end state
+            load_state(a.state_in);
+            have_state = a.state_in != nullptr;
+            if (have_state) write_state_copy(l16, grp);
+            run_chunks(std::false_type{});
+            publish(sacc, a.inc, f_inc);
+            return;
+        }
+        // ---- the segment from a zero state, outputs held back
+        load_state(nullptr);
+        run_chunks(std::true_type{});  // sacc = T_s
+        if (seg < a.nseg - 1) publish(sacc, a.agg, f_agg);
+        f32x4 sin[G::MT][G::NT];
+        look_back(sin);
+        if (seg < a.nseg - 1) {  // P_s = g S_in + T_s
+            f32x4* dst = slot(a.inc, seg);
+#pragma unroll
+            for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < G::NT; ++nt)
+                    store_coherent(dst + (mt * G::NT + nt) * 64, gseg * sin[mt][nt] + sacc[mt][nt]);
+            wait_stores();
+        }
+        // ---- correction: o_n += gamma^(n+1) q_n S_in (n counted from the segment start)
+        write_state_copy_of(sin, l16, grp);
+        __syncthreads();  // S_in^T copy written; P_s stores complete in every wave
+        if (seg < a.nseg - 1 && tid == 0)
+            __hip_atomic_store(flags + seg, f_inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        {
+            const FragAddr<UK> fa_s(l16, grp);  // S^T rows 16 nt + l16, dk 32 s + 8 grp
+#pragma unroll
+            for (int c = 0; c < kKeepChunks; ++c) {
+                if (c < nch) {
+                    const int t0 = t_begin + c * C;
+                    const float zc = zeta * fast_exp2(static_cast<float>(c * C) * lg2f);
+                    f32x4 corr[G::NTV];
+#pragma unroll
+                    for (int nt = 0; nt < G::NTV; ++nt) {
+                        corr[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int s = 0; s < G::KSQ; ++s) {
+                            const uint4 af = *reinterpret_cast<const uint4*>(&sbuf[fa_s.at(nt, s)]);
+                            corr[nt] = mfma16x16x32(af, qf_keep[c][s], corr[nt]);
+                        }
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) oacc_keep[c][nt][r] += zc * corr[nt][r];
+                    }
+                    store_o(oacc_keep[c], t0, min(C, t_end - t0));
+                }
+            }
+        }
+        if (seg == a.nseg - 1) {  // end state = gamma^len S_in + T_s
+            const float glen = static_cast<float>(gamma_pow(lg2, t_end - t_begin));
+#pragma unroll
+            for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < G::NT; ++nt) sacc[mt][nt] += glen * sin[mt][nt];
+            write_final_state(sacc);
+        }
     }
 }
 
 template <int DK, int DVT, int C>
 static hipError_t run_chunk_bf16(const ChunkArgs& a, const HeadParams& hp, hipStream_t st, hipEvent_t* ev) {
     using G = ChunkGeo<DK, DVT, C>;
-    const int bhv = a.B * a.H * a.nvt;
-    if (a.nseg > 1) {
-        launch_timed(chunk_bf16_kernel<DK, DVT, C, true>, dim3(bhv * (a.nseg - 1)), dim3(G::NTHR), 0, st, ev, a,
+    const int chains = a.B * a.H * a.nvt;
+    // the segmented form is a single launch: the pre-pass and scan phases are empty
+    record_empty_phase(st, ev);
+    record_empty_phase(st, ev ? ev + 2 : nullptr);
+    // Holding two chunks of outputs and queries in registers fits with 64-token
+    // chunks (one wave per SIMD) and with small 128-token tiles.
+    constexpr bool kLocalFits = C == 64 || DK + DVT <= 192;
+    hipEvent_t* e = ev ? ev + 4 : nullptr;
+    if (a.nseg == 1)
+        launch_timed(chunk_bf16_kernel<DK, DVT, C, kSinglePass>, dim3(chains), dim3(G::NTHR), 0, st, e, a, hp);
+    else if (kLocalFits && a.seg_len <= kKeepChunks * C)
+        launch_timed(chunk_bf16_kernel<DK, DVT, C, kLocalFits ? kLocalPass : kTwoPass>, dim3(chains * a.nseg),
+                     dim3(G::NTHR), 0, st, e, a, hp);
+    else
+        launch_timed(chunk_bf16_kernel<DK, DVT, C, kTwoPass>, dim3(chains * a.nseg), dim3(G::NTHR), 0, st, e, a,
                      hp);
-        const hipError_t e = launch_segment_scan(a, hp, st, ev ? ev + 2 : nullptr);
-        if (e != hipSuccess) return e;
-    } else {
-        record_empty_phase(st, ev);
-        record_empty_phase(st, ev ? ev + 2 : nullptr);
-    }
-    launch_timed(chunk_bf16_kernel<DK, DVT, C, false>, dim3(bhv * a.nseg), dim3(G::NTHR), 0, st,
-                 ev ? ev + 4 : nullptr, a, hp);
     return hipGetLastError();
 }
 

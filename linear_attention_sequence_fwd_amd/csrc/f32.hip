@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kF32Threads) void chunk_f32_kernel(ChunkArgs a, Hea
     const float* s_src = nullptr;
     if (!STATE_ONLY) {
         if (a.nseg > 1)
-            s_src = a.ws + (static_cast<size_t>(bh) * a.nseg + seg) * DK * a.dv;
+            s_src = a.agg + (static_cast<size_t>(bh) * a.nseg + seg) * DK * a.dv;
         else if (a.state_in)
             s_src = a.state_in + static_cast<size_t>(bh) * DK * a.dv;
     }
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kF32Threads) void chunk_f32_kernel(ChunkArgs a, Hea
 
     float* s_dst = nullptr;
     if (STATE_ONLY)
-        s_dst = a.ws + (static_cast<size_t>(bh) * a.nseg + seg + 1) * DK * a.dv;
+        s_dst = a.agg + (static_cast<size_t>(bh) * a.nseg + seg + 1) * DK * a.dv;
     else if (seg == a.nseg - 1 && a.state_out)
         s_dst = a.state_out + static_cast<size_t>(bh) * DK * a.dv;
     if (s_dst) {

@@ -18,7 +18,11 @@ struct ChunkArgs {
     u16* o;
     const float* state_in;  // [B,H,dk,dv] or nullptr
     float* state_out;       // [B,H,dk,dv] or nullptr
-    float* ws;              // [B*H][nseg][dk][dv] when nseg > 1
+    // Workspace regions when nseg > 1 (carved out of the caller's workspace):
+    unsigned long long* ctl;    // per chain: ticket counter (low 32 bits) and generation (high 32 bits)
+    unsigned long long* flags;  // [B*H*nvt][nseg] publication flags of the bf16 look-back
+    float* agg;                 // per-segment states built from zero ([B*H][nseg][dk][dv] for float32)
+    float* inc;                 // per-segment inclusive states of the bf16 look-back
     int B, H, N, dk, dv;
     int chunk;
     int nvt;      // value tiles per head

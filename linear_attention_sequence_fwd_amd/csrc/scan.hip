@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* ws, const floa
 hipError_t launch_segment_scan(const ChunkArgs& a, const HeadParams& hp, hipStream_t st, hipEvent_t* ev) {
     const int per_bh = a.dk * a.dv;
     dim3 grid((per_bh / 4 + 255) / 256, a.B * a.H);
-    launch_timed(segment_scan_kernel, grid, dim3(256), 0, st, ev, a.ws, a.state_in, a.H, a.nseg, per_bh,
+    launch_timed(segment_scan_kernel, grid, dim3(256), 0, st, ev, a.agg, a.state_in, a.H, a.nseg, per_bh,
                  a.seg_len, hp);
     return hipGetLastError();
 }

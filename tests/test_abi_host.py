@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.retention_abi_version() == 1
+    assert lib.retention_abi_version() == 2
     for s in range(9):
         assert len(lib.retention_status_string(s)) > 0
     assert lib.retention_status_string(123) == b"unknown status"

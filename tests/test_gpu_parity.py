@@ -335,6 +335,28 @@ def test_segment_count_invariance_full_msr():
         assert_close(to64(o), base, 5e-3, "segments vs single pass")
 
 
+def test_workspace_shared_across_sizes():
+    """One zero-filled workspace reused by calls of different sizes (different
+    chain counts, segment counts and layouts inside the workspace) gives the
+    same bits as a fresh workspace per call: nothing an earlier call left in
+    it may be taken for a published segment state."""
+    cases = [BF16_CHUNK_CASES[i] for i in (0, 1, 3, 4, 5, 0, 4, 1)]
+    shared = torch.zeros(48 << 20, dtype=torch.uint8, device=DEV)
+    for B, H, N, dk, dv, C, rot, st, seg in cases:
+        q, k, v = _inputs(B, H, N, dk, dv, torch.bfloat16, seed=N + dk + dv)
+        q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
+        theta = W.rotary_theta(dk) if rot else None
+        s0 = (torch.randn((B, H, dk, dv), generator=torch.Generator().manual_seed(7)) * 0.1).to(DEV) if st else None
+        nbytes = R.retention_chunkwise_workspace_size(B, H, N, dk, dv, torch.bfloat16, C, seg)
+        assert 0 < nbytes <= shared.numel()
+        fresh = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+        kw = dict(chunk=C, theta=theta, pos0=17 if rot else 0, state_in=s0, return_state=True, segments=seg)
+        o1, s1 = R.retention_chunkwise_fwd(q, k, v, workspace=fresh, **kw)
+        o2, s2 = R.retention_chunkwise_fwd(q, k, v, workspace=shared, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(s1, s2), (B, H, N, dk, dv, C, seg)
+
+
 def test_graph_replay_matches_eager():
     """The benchmark replays the step from a HIP graph: every replay, with
     eager work in between, must reproduce the eager result bit for bit."""
@@ -342,8 +364,8 @@ def test_graph_replay_matches_eager():
     q, k, v, theta = W.make_workload("msr_bf16_rotary", device=DEV)
     th = R.HostFloats(theta)
     nbytes = R.retention_chunkwise_workspace_size(w["B"], w["H"], w["N"], w["dk"], w["dv"], q.dtype, w["chunk"])
-    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=DEV)
-    ws2 = torch.empty_like(ws)
+    ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=DEV)
+    ws2 = torch.zeros_like(ws)
     eager = R.retention_chunkwise_fwd(q, k, v, chunk=w["chunk"], theta=th, workspace=ws)
     out = torch.empty_like(eager)
     side = torch.cuda.Stream()
