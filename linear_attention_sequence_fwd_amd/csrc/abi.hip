@@ -20,6 +20,7 @@ using ret::HeadParams;
 constexpr size_t kMaxLdsBytes = 160 * 1024;
 constexpr int kTargetBlocks = 256;  // one workgroup per compute unit
 constexpr int kMaxSegments = 4096;
+constexpr int kMaxAutoSegmentsBf16 = 64;
 // The segmented form keeps one ticket counter per (batch, head, value tile)
 // chain in a fixed region at the start of the workspace, so counters stay
 // counters whatever sizes share the workspace.
@@ -88,7 +89,7 @@ int f32_parallel_dvt(int dk, int dv) {
 struct ChunkPlan {
     int dvt, nvt, nseg, seg_len, nseg_max;
     size_t ws_bytes;
-    size_t flags_off, agg_off, inc_off;  // byte offsets of the workspace regions
+    size_t flags_off, agg_off;  // byte offsets of the workspace regions
 };
 
 constexpr size_t round256(size_t n) { return (n + 255) / 256 * 256; }
@@ -108,21 +109,23 @@ ret_status_t plan_chunk(int B, int H, int N, int dk, int dv, ret_dtype_t dtype, 
         p.nseg_max = 1;  // the grid is full without splitting sequences
     else if (segments > 0)
         p.nseg_max = segments;
-    else
-        p.nseg_max = base >= 256 ? 1 : static_cast<int>((kTargetBlocks + base - 1) / base);
+    else if (base >= 256)
+        p.nseg_max = 1;
+    else  // each bf16 segment reads every predecessor's state: keep the chains short
+        p.nseg_max = static_cast<int>((kTargetBlocks + base - 1) / base);
+    if (segments == 0 && dtype == RET_BF16 && p.nseg_max > kMaxAutoSegmentsBf16) p.nseg_max = kMaxAutoSegmentsBf16;
     if (p.nseg_max > kMaxSegments) p.nseg_max = kMaxSegments;
     const int nchunks = (N + chunk - 1) / chunk;
     const int want = p.nseg_max < nchunks ? p.nseg_max : nchunks;
     const int per_seg = (nchunks + want - 1) / want;
     p.seg_len = per_seg * chunk;
     p.nseg = (N + p.seg_len - 1) / p.seg_len;
-    // workspace: [ticket counter per chain | flags per (chain, segment) | segment states | inclusive states],
+    // workspace: [ticket counter per chain | flags per (chain, segment) | segment states],
     // chain = (batch, head, value tile)
     const size_t states = static_cast<size_t>(B) * H * p.nseg_max * dk * dv * sizeof(float);
     p.flags_off = kCtlBytes;
     p.agg_off = p.flags_off + round256(static_cast<size_t>(base) * p.nseg_max * sizeof(unsigned long long));
-    p.inc_off = p.agg_off + states;
-    p.ws_bytes = p.nseg_max > 1 ? p.inc_off + states : 0;
+    p.ws_bytes = p.nseg_max > 1 ? p.agg_off + states : 0;
     if (base * p.nseg > 2147483647LL) return RET_ERR_UNSUPPORTED;
     return RET_OK;
 }
@@ -188,7 +191,6 @@ static ret_status_t chunkwise_impl(const void* q, const void* k, const void* v, 
     a.ctl = seg_ws ? reinterpret_cast<unsigned long long*>(ws) : nullptr;
     a.flags = seg_ws ? reinterpret_cast<unsigned long long*>(ws + p.flags_off) : nullptr;
     a.agg = seg_ws ? reinterpret_cast<float*>(ws + p.agg_off) : nullptr;
-    a.inc = seg_ws ? reinterpret_cast<float*>(ws + p.inc_off) : nullptr;
     a.B = B;
     a.H = H;
     a.N = N;

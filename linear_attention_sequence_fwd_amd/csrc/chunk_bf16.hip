@@ -93,28 +93,26 @@ __device__ __forceinline__ int wave_row_block(int w) {
 }
 
 // Segmented form: the workgroups of one (batch, head, value tile) chain split
-// its sequence into segments and pass states along the chain with a decoupled
-// look-back, all inside one launch:
-//   1. Workgroups take tickets from a counter in the workspace; ticket order is
-//      segment-major, so every segment a workgroup waits for belongs to a
-//      workgroup that took its ticket earlier and is already running.
-//   2. Each segment but the last runs the state recurrence over its own chunks
-//      from a zero state (segment 0: from the initial state) and publishes the
-//      result: T_s, the segment's own contribution ("aggregate"), or for
-//      segment 0 directly its end state ("inclusive").
-//   3. Segment s looks back over s-1, s-2, ... until it meets an inclusive
-//      state P_j; its start state is
-//          S_in(s) = sum_{j<i<s} g^(s-1-i) T_i + g^(s-1-j) P_j,   g = gamma^seg_len,
-//      and it publishes its own inclusive state P_s = g S_in(s) + T_s.
-//   4. It then runs the full chunk loop (outputs and state) from S_in(s).
-// Waits only ever target aggregates of earlier tickets, which are published
-// without waiting on anything, so every wait ends; a spin bound backs this up
-// (a look-back that exceeds it poisons the start state with NaN instead of
-// hanging). Each chain has its own ticket counter; a flag carries the chain's
-// launch generation (the high half of its counter, advanced by the workgroup
-// that draws the chain's last ticket) and the chain index, so no flag left by
-// an earlier call, of any size, reads as ready, and the workspace needs
-// zero-filling only once, before its first use.
+// its sequence into segments and pass states along the chain with a look-back,
+// all inside one launch:
+//   1. Workgroups take tickets from their chain's counter in the workspace;
+//      ticket order is segment order, so every segment a workgroup waits for
+//      belongs to a workgroup that took its ticket earlier and is running.
+//   2. Segment 0 publishes its end state P_0 (from the initial state); every
+//      other segment but the last publishes T_s, its end state from a zero
+//      start. Publishing never waits on anything.
+//   3. Segment s >= 1 waits until all its predecessors have published and forms
+//          S_in(s) = sum_{0<j<s} g^(s-1-j) T_j + g^(s-1) P_0,   g = gamma^seg_len,
+//      always in the same order, so results are bitwise reproducible.
+//   4. It runs its chunks from S_in(s) (or runs them from zero first and
+//      corrects the held outputs by gamma^(n+1) q_n S_in(s), see kLocalPass).
+// Every wait targets a workgroup that is running and publishes without
+// waiting, so every wait ends; a spin bound backs this up (a look-back that
+// exceeds it poisons the start state with NaN instead of hanging). A flag
+// carries the chain's launch generation (the high half of its counter,
+// advanced by the workgroup that draws the chain's last ticket) and the chain
+// index, so no flag left by an earlier call, of any size, reads as published,
+// and the workspace needs zero-filling only once, before its first use.
 //
 // Published states and flags move through device-coherent (agent-scope)
 // loads and stores, which bypass the per-XCD L2 caches; a publisher waits
@@ -122,6 +120,8 @@ __device__ __forceinline__ int wave_row_block(int w) {
 // avoids device-scope fences, which on this chip write back or invalidate
 // a whole L2 and cost tens of microseconds under load.
 constexpr unsigned kMaxLookbackSpins = 1u << 20;
+
+constexpr int imax(int x, int y) { return x > y ? x : y; }
 
 __device__ __forceinline__ void store_coherent(f32x4* p, const f32x4& v) {
     unsigned long long* q = reinterpret_cast<unsigned long long*>(p);
@@ -158,8 +158,9 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     __shared__ __attribute__((aligned(16))) u16 kbuf[C * DK];
     __shared__ __attribute__((aligned(16))) u16 vbuf[DVT * C];
     __shared__ __attribute__((aligned(16))) u16 sbuf[DVT * DK];
-    // Broadcast slots of the segmented form, overlaid on sbuf: both are read
-    // before the first write of the state copy (a barrier lies in between).
+    // Broadcast slots of the segmented form (ticket, look-back status), overlaid
+    // on sbuf: both are read before the first write of the state copy (a
+    // barrier lies in between).
     unsigned long long* s_ticket = reinterpret_cast<unsigned long long*>(sbuf);
     int* s_lookback = reinterpret_cast<int*>(sbuf + 4);
 
@@ -214,12 +215,12 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     uint4 qf[G::KSQ];
     f32x4 sacc[G::MT][G::NT];
 
-    auto load_q = [&](int t, int Lq) __attribute__((always_inline)) {
+    auto load_q = [&](uint4 (&qd)[G::KSQ], int t, int Lq) __attribute__((always_inline)) {
         const int row = rb * 16 + l16;
         const u16* p = Qg + static_cast<size_t>(t + row) * DK + grp * 8;
 #pragma unroll
         for (int s = 0; s < G::KSQ; ++s)
-            qf[s] = row < Lq ? *reinterpret_cast<const uint4*>(p + s * 32) : make_uint4(0, 0, 0, 0);
+            qd[s] = row < Lq ? *reinterpret_cast<const uint4*>(p + s * 32) : make_uint4(0, 0, 0, 0);
     };
     // first chunk of the segment (issued before state loads so the HBM round trips overlap)
     auto prefetch_first = [&](bool with_q) __attribute__((always_inline)) {
@@ -227,7 +228,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
         load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR>(kr, Kg + static_cast<size_t>(t_begin) * DK, DK, L0, tid);
         load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR>(vr, Vg + static_cast<size_t>(t_begin) * a.dv, a.dv, L0,
                                                           tid);
-        if (with_q) load_q(t_begin, L0);
+        if (with_q) load_q(qf, t_begin, L0);
     };
     // this head's state from a caller's [B*H][dk][dv] float32 array, or zeros
     auto load_state = [&](const float* states) __attribute__((always_inline)) {
@@ -392,7 +393,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     uint4 qf_keep[kKeepChunks][G::KSQ];
     auto run_chunks = [&](auto keep_tag) __attribute__((always_inline)) {
         constexpr bool KEEP = decltype(keep_tag)::value;
-        auto body = [&](int ch) __attribute__((always_inline)) {
+        auto body = [&](int ch, uint4 (&qfb)[G::KSQ], uint4 (&qnext)[G::KSQ]) __attribute__((always_inline)) {
             // Per-iteration copies the compiler cannot prove loop-invariant: the
             // block-write addresses and the decay factors are recomputed each
             // chunk (a few VALU ops under the MFMAs) instead of being hoisted out
@@ -416,7 +417,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
                 if (row < L) {
 #pragma unroll
                     for (int s = 0; s < G::KSQ; ++s)
-                        qf[s] = rotate8_bf16(qf[s], hp, s * 16 + grp * 4, static_cast<double>(a.pos0 + t0 + row));
+                        qfb[s] = rotate8_bf16(qfb[s], hp, s * 16 + grp * 4, static_cast<double>(a.pos0 + t0 + row));
                 }
             }
             __syncthreads();  // A: K^T, V^T written
@@ -432,7 +433,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
 #pragma unroll
                     for (int s = 0; s < G::KSQ; ++s) {
                         const uint4 af = *reinterpret_cast<const uint4*>(&sbuf[fa_s.at(nt, s)]);
-                        oacc[nt] = mfma16x16x32(af, qf[s], oacc[nt]);
+                        oacc[nt] = mfma16x16x32(af, qfb[s], oacc[nt]);
                     }
                 }
 #pragma unroll
@@ -488,7 +489,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
 #pragma unroll
                             for (int hh = 0; hh < 2; ++hh) {
                                 const uint4 af = *reinterpret_cast<const uint4*>(&kbuf[fa_k.at(2 * t + hh, s)]);
-                                pa[hh] = mfma16x16x32(af, qf[s], pa[hh]);
+                                pa[hh] = mfma16x16x32(af, qfb[s], pa[hh]);
                             }
                         }
 #pragma unroll
@@ -509,11 +510,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
             }
 
             // ---- prefetch next chunk's queries (qf is dead for this chunk now)
-            if constexpr (KEEP) {
-#pragma unroll
-                for (int s = 0; s < G::KSQ; ++s) qf_keep[ch][s] = qf[s];
-            }
-            if (has_next) load_q(t1, L1);
+            if (has_next) load_q(qnext, t1, L1);
 
             // ---- 6. G2: O^T += V^T P^T
             {
@@ -541,12 +538,12 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
             }
             __syncthreads();  // D: reads of kbuf and vbuf done before the next chunk's writes
         };
-        if constexpr (KEEP) {
-#pragma unroll
-            for (int ch = 0; ch < kKeepChunks; ++ch)
-                if (ch < nch) body(ch);
+        if constexpr (KEEP) {  // each chunk's queries stay in their own registers
+            static_assert(kKeepChunks == 2, "held chunks");
+            body(0, qf_keep[0], qf_keep[1]);
+            if (nch > 1) body(1, qf_keep[1], qf_keep[1]);
         } else {
-            for (int ch = 0; ch < nch; ++ch) body(ch);
+            for (int ch = 0; ch < nch; ++ch) body(ch, qf, qf);
         }
     };
 
@@ -580,17 +577,16 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     // keeps its (mt, nt) tile as one float4, so every access is a coalesced
     // 16-byte load or store by the thread that uses it.
     constexpr int kSlot = DK * DVT;
-    auto slot = [&](float* region, int j) __attribute__((always_inline)) {
-        return reinterpret_cast<f32x4*>(region + (static_cast<size_t>(chain) * a.nseg + j) * kSlot) +
+    auto slot = [&](int j) __attribute__((always_inline)) {
+        return reinterpret_cast<f32x4*>(a.agg + (static_cast<size_t>(chain) * a.nseg + j) * kSlot) +
                wave * (G::MT * G::NT * 64) + lane;
     };
     unsigned long long* flags = a.flags + static_cast<size_t>(chain) * a.nseg;
     const unsigned long long f_agg =
         (static_cast<unsigned long long>(gen + 1) << 32) | (static_cast<unsigned long long>(chain) << 1);
     const unsigned long long f_inc = f_agg | 1ull;
-    auto publish = [&](const f32x4 (&st)[G::MT][G::NT], float* region, unsigned long long flag)
-                       __attribute__((always_inline)) {
-        f32x4* dst = slot(region, seg);
+    auto publish = [&](const f32x4 (&st)[G::MT][G::NT], unsigned long long flag) __attribute__((always_inline)) {
+        f32x4* dst = slot(seg);
 #pragma unroll
         for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
@@ -600,27 +596,20 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
         if (tid == 0) __hip_atomic_store(flags + seg, flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
     const float gseg = static_cast<float>(gamma_pow(lg2, a.seg_len));
-    // S_in of this segment (seg >= 1) into sin, from its predecessors' published states.
+    // S_in of this segment (seg >= 1) into sin: every predecessor's published
+    // state, nearest first, in a fixed order, so the result does not depend on
+    // which predecessors happened to finish first.
     auto look_back = [&](f32x4 (&sin)[G::MT][G::NT]) __attribute__((always_inline)) {
         if (wave == 0) {
-            // lane i watches predecessor j0 - i
-            int j0 = seg - 1, n_agg = 0, failed = 0;
+            // lane i watches predecessor j0 - i, a window of 64 at a time
+            int failed = 0;
             unsigned spins = 0;
-            for (;;) {
+            for (int j0 = seg - 1; j0 >= 0;) {
                 const int j = j0 - lane;
-                unsigned long long f = 0;
-                if (j >= 0) f = __hip_atomic_load(flags + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const unsigned long long m_inc = __ballot(j >= 0 && f == f_inc);
-                const unsigned long long m_rdy = __ballot(j >= 0 && (f == f_agg || f == f_inc));
-                if (m_inc != 0) {
-                    const int p = __builtin_ctzll(m_inc);  // nearest inclusive predecessor
-                    const unsigned long long below = (1ull << p) - 1;
-                    if ((m_rdy & below) == below) {
-                        n_agg += p;
-                        break;
-                    }
-                } else if (m_rdy == ~0ull) {  // 64 aggregates and no inclusive state: next window
-                    n_agg += 64;
+                const unsigned long long want = j == 0 ? f_inc : f_agg;
+                const unsigned long long f =
+                    j >= 0 ? __hip_atomic_load(flags + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : want;
+                if (__ballot(f != want) == 0) {
                     j0 -= 64;
                     continue;
                 }
@@ -630,56 +619,43 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
                 }
                 __builtin_amdgcn_s_sleep(2);
             }
-            if (lane == 0) {
-                s_lookback[0] = n_agg;
-                s_lookback[1] = failed;
-            }
+            if (lane == 0) s_lookback[0] = failed;
         }
         __syncthreads();
-        const int n_agg = s_lookback[0];
-        const int failed = s_lookback[1];
-        __syncthreads();  // slots read before sbuf receives a state copy
+        const int failed = s_lookback[0];
+        __syncthreads();  // slot read before sbuf receives a state copy
 #pragma unroll
         for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
             for (int nt = 0; nt < G::NT; ++nt) sin[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // predecessors' states are fetched in batches so several are in flight at once
-        constexpr int kBatch = (G::MT * G::NT) >= 16 ? 1 : 16 / (G::MT * G::NT);
+        // Predecessors' states are fetched in predicated batches so a whole batch
+        // is in flight at once. Entry i (i = 0 .. seg-1) is segment seg-1-i with
+        // weight g^i; entry seg-1 is segment 0's end state.
+        constexpr int kBatch = imax(1, (C == 64 ? 32 : 16) / (G::MT * G::NT));
         float fac = 1.0f;
-        int i = 0;
-        for (; i + kBatch <= n_agg; i += kBatch) {
+        for (int i0 = 0; i0 < seg; i0 += kBatch) {
             f32x4 t[kBatch][G::MT][G::NT];
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
-                const f32x4* src = slot(a.agg, seg - 1 - i - u);
+                if (i0 + u < seg) {
+                    const f32x4* src = slot(seg - 1 - i0 - u);
 #pragma unroll
-                for (int mt = 0; mt < G::MT; ++mt)
+                    for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
-                    for (int nt = 0; nt < G::NT; ++nt) t[u][mt][nt] = load_coherent(src + (mt * G::NT + nt) * 64);
+                        for (int nt = 0; nt < G::NT; ++nt)
+                            t[u][mt][nt] = load_coherent(src + (mt * G::NT + nt) * 64);
+                }
             }
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
+                if (i0 + u < seg) {
 #pragma unroll
-                for (int mt = 0; mt < G::MT; ++mt)
+                    for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
-                    for (int nt = 0; nt < G::NT; ++nt) sin[mt][nt] += fac * t[u][mt][nt];
-                fac *= gseg;
+                        for (int nt = 0; nt < G::NT; ++nt) sin[mt][nt] += fac * t[u][mt][nt];
+                    fac *= gseg;
+                }
             }
-        }
-        for (; i < n_agg; ++i) {
-            const f32x4* src = slot(a.agg, seg - 1 - i);
-#pragma unroll
-            for (int mt = 0; mt < G::MT; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < G::NT; ++nt) sin[mt][nt] += fac * load_coherent(src + (mt * G::NT + nt) * 64);
-            fac *= gseg;
-        }
-        {
-            const f32x4* src = slot(a.inc, seg - 1 - n_agg);
-#pragma unroll
-            for (int mt = 0; mt < G::MT; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < G::NT; ++nt) sin[mt][nt] += fac * load_coherent(src + (mt * G::NT + nt) * 64);
         }
         if (failed) {
 #pragma unroll
@@ -695,67 +671,44 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
             prefetch_first(false);
             load_state(seg == 0 ? a.state_in : nullptr);
             run_state_only();
-            publish(sacc, seg == 0 ? a.inc : a.agg, seg == 0 ? f_inc : f_agg);
+            publish(sacc, seg == 0 ? f_inc : f_agg);
         }
         // ---- the start state
         prefetch_first(true);
-        if (seg == 0) {
+        if (seg == 0)
             load_state(a.state_in);
-        } else {
-            if (seg < a.nseg - 1) {  // P_s = g S_in + T_s, T_s still in sacc
-                f32x4 sin[G::MT][G::NT];
-                look_back(sin);
-                f32x4* dst = slot(a.inc, seg);
-#pragma unroll
-                for (int mt = 0; mt < G::MT; ++mt)
-#pragma unroll
-                    for (int nt = 0; nt < G::NT; ++nt) {
-                        store_coherent(dst + (mt * G::NT + nt) * 64, gseg * sin[mt][nt] + sacc[mt][nt]);
-                        sacc[mt][nt] = sin[mt][nt];
-                    }
-                wait_stores();
-                __syncthreads();
-                if (tid == 0) __hip_atomic_store(flags + seg, f_inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            } else {
-                look_back(sacc);
-            }
-        }
+        else
+            look_back(sacc);
         // ---- pass 2: outputs and state from the start state
         have_state = seg > 0 || a.state_in != nullptr;
         if (have_state) write_state_copy(l16, grp);
         run_chunks(std::false_type{});
         write_final_state(sacc);
     } else if constexpr (MODE == kLocalPass) {
-        prefetch_first(true);
         if (seg == 0) {
+            prefetch_first(true);
             // the start state is known: the ordinary pass, then publish the end state
             load_state(a.state_in);
             have_state = a.state_in != nullptr;
             if (have_state) write_state_copy(l16, grp);
             run_chunks(std::false_type{});
-            publish(sacc, a.inc, f_inc);
+            publish(sacc, f_inc);
             return;
         }
         // ---- the segment from a zero state, outputs held back
+        {
+            const int L0 = min(C, t_end - t_begin);
+            load_kv(kr, vr, t_begin, L0);
+            load_q(qf_keep[0], t_begin, L0);
+        }
         load_state(nullptr);
         run_chunks(std::true_type{});  // sacc = T_s
-        if (seg < a.nseg - 1) publish(sacc, a.agg, f_agg);
+        if (seg < a.nseg - 1) publish(sacc, f_agg);
         f32x4 sin[G::MT][G::NT];
         look_back(sin);
-        if (seg < a.nseg - 1) {  // P_s = g S_in + T_s
-            f32x4* dst = slot(a.inc, seg);
-#pragma unroll
-            for (int mt = 0; mt < G::MT; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < G::NT; ++nt)
-                    store_coherent(dst + (mt * G::NT + nt) * 64, gseg * sin[mt][nt] + sacc[mt][nt]);
-            wait_stores();
-        }
         // ---- correction: o_n += gamma^(n+1) q_n S_in (n counted from the segment start)
         write_state_copy_of(sin, l16, grp);
-        __syncthreads();  // S_in^T copy written; P_s stores complete in every wave
-        if (seg < a.nseg - 1 && tid == 0)
-            __hip_atomic_store(flags + seg, f_inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();  // S_in^T copy written
         {
             const FragAddr<UK> fa_s(l16, grp);  // S^T rows 16 nt + l16, dk 32 s + 8 grp
 #pragma unroll

@@ -21,8 +21,8 @@ struct ChunkArgs {
     // Workspace regions when nseg > 1 (carved out of the caller's workspace):
     unsigned long long* ctl;    // per chain: ticket counter (low 32 bits) and generation (high 32 bits)
     unsigned long long* flags;  // [B*H*nvt][nseg] publication flags of the bf16 look-back
-    float* agg;                 // per-segment states built from zero ([B*H][nseg][dk][dv] for float32)
-    float* inc;                 // per-segment inclusive states of the bf16 look-back
+    float* agg;                 // published per-segment states: bf16 [B*H*nvt][nseg][dk*dvt] in
+                                // accumulator order; float32 [B*H][nseg][dk][dv]
     int B, H, N, dk, dv;
     int chunk;
     int nvt;      // value tiles per head
