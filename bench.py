@@ -48,6 +48,40 @@ def decode_alg_bytes(B, H, dk, dv, elt=2):
     return B * H * (2 * dk * dv * 4 + elt * (2 * dk + dv) + elt * dv)
 
 
+PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+SOURCE_DIRS = ("linear_attention_sequence_fwd_amd/csrc", "include")
+
+
+def source_fingerprint():
+    """sha256 (first 16 hex digits) over the kernel sources, in name order."""
+    import hashlib
+
+    root = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for d in SOURCE_DIRS:
+        for name in sorted(os.listdir(os.path.join(root, d))):
+            if name.endswith((".hip", ".hpp", ".h")):
+                h.update(name.encode())
+                with open(os.path.join(root, d, name), "rb") as f:
+                    h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the workload's dominant kernel from the committed
+    counter summary (profiles/hbm_traffic.json: scaled FETCH_SIZE + WRITE_SIZE),
+    or None when the kernel sources changed since the counters were taken."""
+    path = os.path.join(PROFILES, "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_fingerprint") != source_fingerprint() or workload not in rec.get("workloads", {}):
+        return None
+    w = rec["workloads"][workload]
+    return w["read_bytes"] + w["write_bytes"]
+
+
 def time_events(fn, steps, warmup):
     import torch
 
@@ -263,7 +297,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic("msr_bf16_rotary"),
+            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x copy calibration + WRITE_SIZE)",
             "alg_bytes_per_launch": alg_bytes,
             "kernel_ms": main_ms,
         },
@@ -292,6 +327,7 @@ def main():
             "tokens_per_s": w["B"] * w["N"] / (ms3 * 1e-3), "ms": ms3, "main_kernel_ms": ph3[2],
             "tflops": fl / (ph3[2] * 1e-3) / 1e12, "mfma_frac": fl / (ph3[2] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             "gbs": by / (ph3[2] * 1e-3) / 1e9, "hbm_frac": by / (ph3[2] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "alg_bytes_per_launch": by, "traffic": measured_traffic("layer7b_bf16"),
         })
         del q, k, v, out
         torch.cuda.empty_cache()
@@ -313,6 +349,7 @@ def main():
             "workload": "recurrent decode: 64 sequences x H=16, fp32 state 256x512, bf16 q/k/v, 512 steps",
             "ms_per_step": ms4, "state_updates_per_s": w["B"] * w["H"] / (ms4 * 1e-3),
             "gbs": by4 / (ms4 * 1e-3) / 1e9, "hbm_frac": by4 / (ms4 * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "alg_bytes_per_launch": by4, "traffic": measured_traffic("decode_bf16"),
         })
         del s0, qs, ks, vs, state, o
         torch.cuda.empty_cache()
@@ -337,6 +374,7 @@ def main():
             "workload": "long-context chunkwise: B=1 H=8 N=65536 d_k=d_v=128 bf16, chunk 128",
             "tokens_per_s": w["B"] * w["N"] / (ms5 * 1e-3), "ms": ms5,
             "phase_ms": {"segment_states": ph5[0], "segment_scan": ph5[1], "main": ph5[2]},
+            "alg_bytes_per_launch": by5, "traffic": measured_traffic("longctx_bf16"),
             "step_gbs": by5 / (ms5 * 1e-3) / 1e9, "step_hbm_frac": by5 / (ms5 * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "step_tflops": fl5 / (ms5 * 1e-3) / 1e12,
             "parallel_crossover": cross,

@@ -123,20 +123,21 @@ constexpr unsigned kMaxLookbackSpins = 1u << 20;
 
 constexpr int imax(int x, int y) { return x > y ? x : y; }
 
-__device__ __forceinline__ void store_coherent(f32x4* p, const f32x4& v) {
-    unsigned long long* q = reinterpret_cast<unsigned long long*>(p);
+// A float4 per lane as two 8-byte halves, each half of the wavefront stored
+// contiguously (p[0..63] low halves, p[64..127] high halves), so every
+// instruction writes or reads 512 contiguous bytes.
+__device__ __forceinline__ void store_coherent(unsigned long long* p, const f32x4& v) {
     const f32x2 lo = {v[0], v[1]}, hi = {v[2], v[3]};
-    __hip_atomic_store(q, __builtin_bit_cast(unsigned long long, lo), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(q + 1, __builtin_bit_cast(unsigned long long, hi), __ATOMIC_RELAXED,
+    __hip_atomic_store(p, __builtin_bit_cast(unsigned long long, lo), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p + 64, __builtin_bit_cast(unsigned long long, hi), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ f32x4 load_coherent(const f32x4* p) {
-    unsigned long long* q = reinterpret_cast<unsigned long long*>(const_cast<f32x4*>(p));
+__device__ __forceinline__ f32x4 load_coherent(unsigned long long* p) {
     const f32x2 lo =
-        __builtin_bit_cast(f32x2, __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        __builtin_bit_cast(f32x2, __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     const f32x2 hi =
-        __builtin_bit_cast(f32x2, __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        __builtin_bit_cast(f32x2, __hip_atomic_load(p + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     return f32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
@@ -574,23 +575,24 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     }
 
     // Published states are stored in accumulator order: thread (wave, lane)
-    // keeps its (mt, nt) tile as one float4, so every access is a coalesced
-    // 16-byte load or store by the thread that uses it.
+    // keeps its (mt, nt) tile as one float4, split into two 8-byte halves that
+    // are each contiguous over the wavefront, so every access is a coalesced
+    // load or store by the thread that uses the value.
     constexpr int kSlot = DK * DVT;
     auto slot = [&](int j) __attribute__((always_inline)) {
-        return reinterpret_cast<f32x4*>(a.agg + (static_cast<size_t>(chain) * a.nseg + j) * kSlot) +
-               wave * (G::MT * G::NT * 64) + lane;
+        return reinterpret_cast<unsigned long long*>(a.agg + (static_cast<size_t>(chain) * a.nseg + j) * kSlot) +
+               wave * (G::MT * G::NT * 128) + lane;
     };
     unsigned long long* flags = a.flags + static_cast<size_t>(chain) * a.nseg;
     const unsigned long long f_agg =
         (static_cast<unsigned long long>(gen + 1) << 32) | (static_cast<unsigned long long>(chain) << 1);
     const unsigned long long f_inc = f_agg | 1ull;
     auto publish = [&](const f32x4 (&st)[G::MT][G::NT], unsigned long long flag) __attribute__((always_inline)) {
-        f32x4* dst = slot(seg);
+        unsigned long long* dst = slot(seg);
 #pragma unroll
         for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < G::NT; ++nt) store_coherent(dst + (mt * G::NT + nt) * 64, st[mt][nt]);
+            for (int nt = 0; nt < G::NT; ++nt) store_coherent(dst + (mt * G::NT + nt) * 128, st[mt][nt]);
         wait_stores();
         __syncthreads();
         if (tid == 0) __hip_atomic_store(flags + seg, flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -638,12 +640,12 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
                 if (i0 + u < seg) {
-                    const f32x4* src = slot(seg - 1 - i0 - u);
+                    unsigned long long* src = slot(seg - 1 - i0 - u);
 #pragma unroll
                     for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
                         for (int nt = 0; nt < G::NT; ++nt)
-                            t[u][mt][nt] = load_coherent(src + (mt * G::NT + nt) * 64);
+                            t[u][mt][nt] = load_coherent(src + (mt * G::NT + nt) * 128);
                 }
             }
 #pragma unroll

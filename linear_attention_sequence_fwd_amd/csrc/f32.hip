@@ -28,18 +28,20 @@ __device__ __forceinline__ void rotate_row_f32(float* row, int dk, const HeadPar
 }
 
 // Stage rows [t0, t0 + L) of a [*, ld] float matrix (columns c0 .. c0 + w) into
-// LDS as [C][w], zero-filling rows >= L; optionally rotate each row.
-__device__ __forceinline__ void stage_rows(float* dst, const float* src, int ld, int c0, int w, int t0, int L, int C,
-                                           bool rotate, const HeadParams& hp, long long pos0) {
+// LDS as [C][pitch], zero-filling rows >= L; optionally rotate each row. Key
+// rows use pitch w + 1 so that lanes reading one column of consecutive rows
+// hit different banks.
+__device__ __forceinline__ void stage_rows(float* dst, const float* src, int ld, int c0, int w, int pitch, int t0,
+                                           int L, int C, bool rotate, const HeadParams& hp, long long pos0) {
     const int tid = threadIdx.x;
     for (int idx = tid; idx < C * w; idx += kF32Threads) {
         const int r = idx / w, c = idx % w;
-        dst[idx] = r < L ? src[static_cast<size_t>(t0 + r) * ld + c0 + c] : 0.0f;
+        dst[r * pitch + c] = r < L ? src[static_cast<size_t>(t0 + r) * ld + c0 + c] : 0.0f;
     }
     if (rotate) {
         __syncthreads();
         for (int r = tid; r < L; r += kF32Threads)
-            rotate_row_f32(dst + r * w, w, hp, static_cast<double>(pos0 + t0 + r));
+            rotate_row_f32(dst + r * pitch, w, hp, static_cast<double>(pos0 + t0 + r));
     }
 }
 
@@ -47,11 +49,13 @@ template <bool STATE_ONLY>
 __global__ __launch_bounds__(kF32Threads) void chunk_f32_kernel(ChunkArgs a, HeadParams hp, int dvt) {
     extern __shared__ __attribute__((aligned(16))) float smem[];
     const int C = a.chunk, DK = a.dk;
+    const int KP = DK + 1;            // padded key row pitch
     float* sq = smem;                 // [C][DK]
-    float* sk = sq + C * DK;          // [C][DK]
-    float* sv = sk + C * DK;          // [C][dvt]
+    float* sk = sq + C * DK;          // [C][KP]
+    float* sv = sk + C * KP;          // [C][dvt]
     float* ss = sv + C * dvt;         // [DK][dvt]
     float* sp = ss + DK * dvt;        // [C][C]
+    float* sx = sp + C * C;           // [C] key decay xi_j of the current chunk
 
     const int tid = threadIdx.x;
     const int nseg_grid = STATE_ONLY ? a.nseg - 1 : a.nseg;
@@ -88,9 +92,10 @@ __global__ __launch_bounds__(kF32Threads) void chunk_f32_kernel(ChunkArgs a, Hea
     for (int t0 = t_begin; t0 < t_end; t0 += C) {
         const int L = min(C, t_end - t0);
         __syncthreads();
-        if (!STATE_ONLY) stage_rows(sq, Q, DK, 0, DK, t0, L, C, hp.has_theta, hp, a.pos0);
-        stage_rows(sk, K, DK, 0, DK, t0, L, C, hp.has_theta, hp, a.pos0);
-        stage_rows(sv, V, a.dv, c0, dvt, t0, L, C, false, hp, a.pos0);
+        if (!STATE_ONLY) stage_rows(sq, Q, DK, 0, DK, DK, t0, L, C, hp.has_theta, hp, a.pos0);
+        stage_rows(sk, K, DK, 0, DK, KP, t0, L, C, hp.has_theta, hp, a.pos0);
+        stage_rows(sv, V, a.dv, c0, dvt, dvt, t0, L, C, false, hp, a.pos0);
+        for (int j = tid; j < L; j += kF32Threads) sx[j] = exp2f(static_cast<float>(L - 1 - j) * lg2f);
         __syncthreads();
         if (!STATE_ONLY) {
             // scores with decay mask (select, so a non-finite future key never leaks)
@@ -99,7 +104,7 @@ __global__ __launch_bounds__(kF32Threads) void chunk_f32_kernel(ChunkArgs a, Hea
                 float p = 0.0f;
                 if (j <= i) {
                     float acc = 0.0f;
-                    for (int d = 0; d < DK; ++d) acc = fmaf(sq[i * DK + d], sk[j * DK + d], acc);
+                    for (int d = 0; d < DK; ++d) acc = fmaf(sq[i * DK + d], sk[j * KP + d], acc);
                     p = acc * exp2f(static_cast<float>(i - j) * lg2f);
                 }
                 sp[i * C + j] = p;
@@ -122,8 +127,7 @@ __global__ __launch_bounds__(kF32Threads) void chunk_f32_kernel(ChunkArgs a, Hea
         for (int idx = tid; idx < DK * dvt; idx += kF32Threads) {
             const int d = idx / dvt, c = idx % dvt;
             float acc = 0.0f;
-            for (int j = 0; j < L; ++j)
-                acc = fmaf(sk[j * DK + d] * exp2f(static_cast<float>(L - 1 - j) * lg2f), sv[j * dvt + c], acc);
+            for (int j = 0; j < L; ++j) acc = fmaf(sk[j * KP + d] * sx[j], sv[j * dvt + c], acc);
             ss[idx] = gL * ss[idx] + acc;
         }
         have_state = true;
@@ -144,8 +148,9 @@ __global__ __launch_bounds__(kF32Threads) void chunk_f32_kernel(ChunkArgs a, Hea
 }
 
 size_t chunk_f32_lds_bytes(int C, int dk, int dvt) {
-    return sizeof(float) * (2 * static_cast<size_t>(C) * dk + static_cast<size_t>(C) * dvt +
-                            static_cast<size_t>(dk) * dvt + static_cast<size_t>(C) * C);
+    return sizeof(float) * (static_cast<size_t>(C) * dk + static_cast<size_t>(C) * (dk + 1) +
+                            static_cast<size_t>(C) * dvt + static_cast<size_t>(dk) * dvt +
+                            static_cast<size_t>(C) * C + C);
 }
 
 hipError_t launch_chunk_f32(const ChunkArgs& a, const HeadParams& hp, int dvt, hipStream_t st, hipEvent_t* ev) {
@@ -177,9 +182,10 @@ constexpr int kParF32Block = 64;
 __global__ __launch_bounds__(kF32Threads) void parallel_f32_kernel(ParallelArgs a, HeadParams hp, int dvt) {
     extern __shared__ __attribute__((aligned(16))) float smem[];
     const int BQ = kParF32Block, DK = a.dk;
+    const int KP = DK + 1;       // padded key row pitch
     float* sq = smem;            // [BQ][DK]
-    float* sk = sq + BQ * DK;    // [BQ][DK]
-    float* sv = sk + BQ * DK;    // [BQ][dvt]
+    float* sk = sq + BQ * DK;    // [BQ][KP]
+    float* sv = sk + BQ * KP;    // [BQ][dvt]
     float* sp = sv + BQ * dvt;   // [BQ][BQ]
 
     const int tid = threadIdx.x;
@@ -207,15 +213,15 @@ __global__ __launch_bounds__(kF32Threads) void parallel_f32_kernel(ParallelArgs 
 #pragma unroll
     for (int u = 0; u < kMaxOut; ++u) out[u] = 0.0f;
 
-    stage_rows(sq, Q, DK, 0, DK, q0, Lq, BQ, hp.has_theta, hp, a.pos0);
+    stage_rows(sq, Q, DK, 0, DK, DK, q0, Lq, BQ, hp.has_theta, hp, a.pos0);
     for (int kb = qb; kb >= 0; --kb) {
         const int k0 = kb * BQ;
         const int Lk = min(BQ, a.N - k0);
         // every D entry of this block (and all earlier ones) below float32 underflow
         if (lg2 < 0.0 && (static_cast<double>(q0 - k0) - (BQ - 1)) * (-lg2) > 160.0) break;
         __syncthreads();
-        stage_rows(sk, K, DK, 0, DK, k0, Lk, BQ, hp.has_theta, hp, a.pos0);
-        stage_rows(sv, V, a.dv, c0, dvt, k0, Lk, BQ, false, hp, a.pos0);
+        stage_rows(sk, K, DK, 0, DK, KP, k0, Lk, BQ, hp.has_theta, hp, a.pos0);
+        stage_rows(sv, V, a.dv, c0, dvt, dvt, k0, Lk, BQ, false, hp, a.pos0);
         __syncthreads();
         const float blk = gamma_pow(lg2, static_cast<double>(q0 - k0));
         for (int idx = tid; idx < BQ * BQ; idx += kF32Threads) {
@@ -223,7 +229,7 @@ __global__ __launch_bounds__(kF32Threads) void parallel_f32_kernel(ParallelArgs 
             float p = 0.0f;
             if (i < Lq && j < Lk && (kb < qb || j <= i)) {
                 float acc = 0.0f;
-                for (int d = 0; d < DK; ++d) acc = fmaf(sq[i * DK + d], sk[j * DK + d], acc);
+                for (int d = 0; d < DK; ++d) acc = fmaf(sq[i * DK + d], sk[j * KP + d], acc);
                 p = acc * (exp2f(static_cast<float>(i - j) * lg2f) * blk);
             }
             sp[idx] = p;
@@ -252,7 +258,7 @@ __global__ __launch_bounds__(kF32Threads) void parallel_f32_kernel(ParallelArgs 
 
 size_t parallel_f32_lds_bytes(int dk, int dvt) {
     const size_t BQ = kParF32Block;
-    return sizeof(float) * (2 * BQ * dk + BQ * dvt + BQ * BQ);
+    return sizeof(float) * (BQ * dk + BQ * (dk + 1) + BQ * dvt + BQ * BQ);
 }
 
 hipError_t launch_parallel_f32(const ParallelArgs& a, const HeadParams& hp, int dvt, hipStream_t st) {
