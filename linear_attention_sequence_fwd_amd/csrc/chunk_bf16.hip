@@ -40,6 +40,7 @@
 #include "kernels.hpp"
 #include "tiles.hpp"
 
+#include <cmath>
 #include <type_traits>
 
 namespace ret {
@@ -150,7 +151,7 @@ __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)
 enum ChunkMode { kSinglePass = 0, kTwoPass = 1, kLocalPass = 2 };
 constexpr int kKeepChunks = 2;
 
-template <int DK, int DVT, int C, int MODE>
+template <int DK, int DVT, int C, int MODE, bool FAST>
 __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, HeadParams hp) {
     constexpr bool SEGMENTED = MODE != kSinglePass;
     using G = ChunkGeo<DK, DVT, C>;
@@ -263,11 +264,18 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     };
 
     // ---- per-lane decay constants
-    // D[i][j] = gamma^(i-j) with i = 16 rb + l16, j = 16 jt + 4 grp + r:
-    //        = gamma^(l16 - 4 grp - r) * gamma^(16 (rb - jt)).
-    float dlane[4];
+    // D[i][j] = gamma^(i-j) with i = 16 rb + l16, j = 16 jt + 4 grp + r, with no
+    // factor at a negative exponent (small gammas would overflow it):
+    //   diagonal tile (jt = rb): dlane[r] = gamma^(l16 - 4 grp - r), negative
+    //     exponents only in masked entries, which are selected away;
+    //   jt < rb: dlane15[r] * gamma^(16 (rb - jt) - 15), dlane15[r] =
+    //     gamma^(l16 - 4 grp - r + 15).
+    float dlane[4], dlane15[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dlane[r] = fast_exp2(static_cast<float>(l16 - 4 * grp - r) * lg2f);
+    for (int r = 0; r < 4; ++r) {
+        dlane[r] = fast_exp2(static_cast<float>(l16 - 4 * grp - r) * lg2f);
+        dlane15[r] = FAST ? 0.0f : fast_exp2(static_cast<float>(l16 - 4 * grp - r + 15) * lg2f);
+    }
     const float zeta = fast_exp2(static_cast<float>(16 * rb + l16 + 1) * lg2f);
     const float gC = gamma_pow(lg2, C);
     bool have_state = false;
@@ -360,6 +368,99 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
         }
     };
 
+    // ---- the FAST form's pieces (see the kernel comment): keys row-major only,
+    //      values scaled by gamma^-(j+1) on their way into V''^T.
+    auto stage_fast = [&](auto& krb, auto& vrb, int t0, int L, int tid_it, float lg2c) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < G::KPT; ++u) {
+            const int idx = tid_it + u * G::NTHR;
+            if (idx < G::KB) {
+                int tb, cb;
+                block_coords<DK, G::BWK>(idx, tb, cb);
+                if (hp.has_theta) {
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+                        if (staged_token(tb, q) < L)
+                            rotate_row<G::BWK>(krb[u].w[q], hp, cb * (G::BWK / 2),
+                                               static_cast<double>(a.pos0 + t0 + staged_token(tb, q)));
+                }
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int row = staged_token(tb, q);
+                    if constexpr (G::BWK == 8) {
+                        *reinterpret_cast<uint4*>(&kbuf[swz<UK>(row, cb)]) =
+                            make_uint4(krb[u].w[q][0], krb[u].w[q][1], krb[u].w[q][2], krb[u].w[q][3]);
+                    } else {
+                        *reinterpret_cast<uint2*>(&kbuf[swz<UK>(row, cb >> 1) + 4 * (cb & 1)]) =
+                            make_uint2(krb[u].w[q][0], krb[u].w[q][1]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < G::VPT; ++u) {
+            const int idx = tid_it + u * G::NTHR;
+            if (idx < G::VB) {
+                int tb, cb;
+                block_coords<DVT, G::BWV>(idx, tb, cb);
+                float f[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) f[q] = fast_exp2(-static_cast<float>(staged_token(tb, q) + 1) * lg2c);
+#pragma unroll
+                for (int c = 0; c < G::BWV; ++c) {
+                    uint32_t w[4];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const float lo = bf16_to_f32(static_cast<u16>(elem16(vrb[u].w[2 * p], c))) * f[2 * p];
+                        const float hi = bf16_to_f32(static_cast<u16>(elem16(vrb[u].w[2 * p + 1], c))) * f[2 * p + 1];
+                        w[p] = pack2_bf16(lo, hi);
+                    }
+                    *reinterpret_cast<uint4*>(&vbuf[swz<UC>(cb * G::BWV + c, tb)]) = make_uint4(w[0], w[1], w[2], w[3]);
+                }
+            }
+        }
+    };
+    // G4 of the FAST form: S = gamma^L (S + K^T V''). The K^T operand comes from
+    // the row-major keys by transposing reads: lane (grp, r) points at token
+    // 32 t + 4 grp + r/4 (+16), dk columns 4 (r%4) .. +3 of its tile, and
+    // receives dk row l16 at tokens 32 t + 4 grp + {0..3} (+16): the token
+    // order of the V''^T units.
+    auto g4_fast = [&](int L, int l16c, int grpc) __attribute__((always_inline)) {
+        const float gL = (L == C) ? gC : gamma_pow(lg2, L);
+        const int tok = 4 * grpc + (l16c >> 2);
+        int kb[G::MT];
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt) {
+            const int d = d_base + 16 * mt + 4 * (l16c & 3);
+            kb[mt] = swz<UK>(tok, d >> 3) + (d & 7);
+        }
+        const FragAddr<UC> fa_vt(c_base + l16c, grpc);  // V''^T rows c_base + 16 nt + l16, unit 4 t + grp
+#pragma unroll
+        for (int t = 0; t < G::KST; ++t) {
+            if (t * 32 < L) {
+                uint4 af[G::MT];
+#pragma unroll
+                for (int mt = 0; mt < G::MT; ++mt) {
+                    const uint2 lo = lds_read_tr16x4(&kbuf[kb[mt] + (32 * t) * (UK * 8)]);
+                    const uint2 hi = lds_read_tr16x4(&kbuf[kb[mt] + (32 * t + 16) * (UK * 8)]);
+                    af[mt] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                }
+#pragma unroll
+                for (int nt = 0; nt < G::NT; ++nt) {
+                    const uint4 bfr = *reinterpret_cast<const uint4*>(&vbuf[fa_vt.at(nt, t)]);
+#pragma unroll
+                    for (int mt = 0; mt < G::MT; ++mt) sacc[mt][nt] = mfma16x16x32(af[mt], bfr, sacc[mt][nt]);
+                }
+            }
+        }
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < G::NT; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sacc[mt][nt][r] *= gL;
+    };
+
     // The state recurrence alone over this segment (keys and values only), with
     // two chunks of loads in flight: chunk ch + 2 is fetched into the registers
     // chunk ch has just been staged from, under G4 of chunk ch.
@@ -374,11 +475,17 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
             asm volatile("" : "+v"(tid_it), "+v"(lg2_it));
             const int t0 = t_begin + ch * C;
             const int L = min(C, t_end - t0);
-            stage_kv(krb, vrb, t0, L, tid_it, lg2_it);
+            if constexpr (FAST)
+                stage_fast(krb, vrb, t0, L, tid_it, lg2_it);
+            else
+                stage_kv(krb, vrb, t0, L, tid_it, lg2_it);
             if (ch + 2 < nch) load_kv(krb, vrb, t0 + 2 * C, min(C, t_end - t0 - 2 * C));
-            __syncthreads();  // K^T, V^T written
-            g4(L, tid_it & 15, (tid_it & 63) >> 4);
-            __syncthreads();  // K^T, V^T read
+            __syncthreads();  // keys and values written
+            if constexpr (FAST)
+                g4_fast(L, tid_it & 15, (tid_it & 63) >> 4);
+            else
+                g4(L, tid_it & 15, (tid_it & 63) >> 4);
+            __syncthreads();  // keys and values read
         };
         for (int ch = 0; ch < nch; ch += 2) {
             step(kr, vr, ch);
@@ -496,11 +603,12 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
 #pragma unroll
                         for (int hh = 0; hh < 2; ++hh) {
                             const int delta = rb - (2 * t + hh);
-                            const float blk = fast_exp2(static_cast<float>(16 * delta) * lg2c);
+                            const float blk = fast_exp2(static_cast<float>(16 * delta - 15) * lg2c);
 #pragma unroll
                             for (int r = 0; r < 4; ++r) {
                                 float val = 0.0f;
-                                if (delta > 0 || (delta == 0 && l16 >= 4 * grp + r)) val = pa[hh][r] * (dlane[r] * blk);
+                                const float dec = delta == 0 ? dlane[r] : dlane15[r] * blk;
+                                if (delta > 0 || (delta == 0 && l16 >= 4 * grp + r)) val = pa[hh][r] * dec;
                                 pa[hh][r] = val;
                             }
                         }
@@ -539,12 +647,135 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
             }
             __syncthreads();  // D: reads of kbuf and vbuf done before the next chunk's writes
         };
+        // The FAST form of a chunk: two barriers. Staging writes row-major keys
+        // and V''^T and issues the next chunk's loads (its registers are free);
+        // one matrix-core phase (G3, G1, G2 into one accumulator, then G4) reads
+        // LDS only; after the second barrier the new state copy and the outputs
+        // (times gamma^(i+1)) are written.
+        auto body_fast = [&](int ch, uint4 (&qfb)[G::KSQ], uint4 (&qnext)[G::KSQ]) __attribute__((always_inline)) {
+            int tid_it = tid;
+            float lg2_it = lg2f;
+            asm volatile("" : "+v"(tid_it), "+v"(lg2_it));
+            const float lg2c = lg2_it;
+            const int l16c = tid_it & 15;
+            const int grpc = (tid_it & 63) >> 4;
+            const int t0 = t_begin + ch * C;
+            const int L = min(C, t_end - t0);
+            const bool has_next = (ch + 1) < nch;
+            const int t1 = t0 + C;
+            const int L1 = has_next ? min(C, t_end - t1) : 0;
+
+            // ---- 1. keys row-major, V''^T into LDS; rotate queries; fetch the next chunk
+            stage_fast(kr, vr, t0, L, tid_it, lg2c);
+            if (hp.has_theta) {
+                const int row = rb * 16 + l16;
+                if (row < L) {
+#pragma unroll
+                    for (int s = 0; s < G::KSQ; ++s)
+                        qfb[s] = rotate8_bf16(qfb[s], hp, s * 16 + grp * 4, static_cast<double>(a.pos0 + t0 + row));
+                }
+            }
+            if (has_next) load_kv(kr, vr, t1, L1);
+            __syncthreads();  // A: keys and V''^T written
+
+            // ---- 2. G3: O^T = S^T Q^T (the previous chunk's state)
+            f32x4 oacc[G::NTV];
+#pragma unroll
+            for (int nt = 0; nt < G::NTV; ++nt) oacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (have_state) {
+                const FragAddr<UK> fa_s(l16c, grpc);  // S^T rows 16 nt + l16, dk 32 s + 8 grp
+#pragma unroll
+                for (int nt = 0; nt < G::NTV; ++nt) {
+#pragma unroll
+                    for (int s = 0; s < G::KSQ; ++s) {
+                        const uint4 af = *reinterpret_cast<const uint4*>(&sbuf[fa_s.at(nt, s)]);
+                        oacc[nt] = mfma16x16x32(af, qfb[s], oacc[nt]);
+                    }
+                }
+            }
+
+            // ---- 3. G1: P^T = K Q^T, causal mask on the diagonal tile only (the
+            //         decay is carried by V'' and the final gamma^(i+1))
+            uint4 pf[G::KST];
+            {
+                const FragAddr<UK> fa_k(l16c, grpc);  // K rows 16 jt + l16, dk 32 s + 8 grp
+#pragma unroll
+                for (int t = 0; t < G::KST; ++t) {
+                    pf[t] = make_uint4(0, 0, 0, 0);
+                    if (2 * t <= rb) {
+                        f32x4 pa[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+                        for (int s = 0; s < G::KSQ; ++s) {
+#pragma unroll
+                            for (int hh = 0; hh < 2; ++hh) {
+                                const uint4 af = *reinterpret_cast<const uint4*>(&kbuf[fa_k.at(2 * t + hh, s)]);
+                                pa[hh] = mfma16x16x32(af, qfb[s], pa[hh]);
+                            }
+                        }
+#pragma unroll
+                        for (int hh = 0; hh < 2; ++hh) {
+                            const int delta = rb - (2 * t + hh);
+                            if (delta <= 0) {
+#pragma unroll
+                                for (int r = 0; r < 4; ++r)
+                                    pa[hh][r] = (delta == 0 && l16 >= 4 * grp + r) ? pa[hh][r] : 0.0f;
+                            }
+                        }
+                        pf[t] = make_uint4(pack2_bf16(pa[0][0], pa[0][1]), pack2_bf16(pa[0][2], pa[0][3]),
+                                           pack2_bf16(pa[1][0], pa[1][1]), pack2_bf16(pa[1][2], pa[1][3]));
+                    }
+                }
+            }
+            if (has_next) load_q(qnext, t1, L1);  // queries are dead for this chunk now
+
+            // ---- 4. G2: O^T += V''^T P^T
+            {
+                const FragAddr<UC> fa_v(l16c, grpc);
+#pragma unroll
+                for (int t = 0; t < G::KST; ++t) {
+                    if (2 * t <= rb) {
+#pragma unroll
+                        for (int nt = 0; nt < G::NTV; ++nt) {
+                            const uint4 af = *reinterpret_cast<const uint4*>(&vbuf[fa_v.at(nt, t)]);
+                            oacc[nt] = mfma16x16x32(af, pf[t], oacc[nt]);
+                        }
+                    }
+                }
+            }
+
+            // ---- 5. G4: S = gamma^L (S + K^T V'')
+            g4_fast(L, l16c, grpc);
+            __syncthreads();  // B: every read of keys, V''^T and the state copy done
+
+            // ---- 6. new state copy; outputs times gamma^(i+1)
+            write_state_copy(l16c, grpc);
+            have_state = true;
+#pragma unroll
+            for (int nt = 0; nt < G::NTV; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) oacc[nt][r] *= zeta;
+            if constexpr (KEEP) {
+#pragma unroll
+                for (int nt = 0; nt < G::NTV; ++nt) oacc_keep[ch][nt] = oacc[nt];
+            } else {
+                store_o(oacc, t0, L);
+            }
+        };
         if constexpr (KEEP) {  // each chunk's queries stay in their own registers
             static_assert(kKeepChunks == 2, "held chunks");
-            body(0, qf_keep[0], qf_keep[1]);
-            if (nch > 1) body(1, qf_keep[1], qf_keep[1]);
+            if constexpr (FAST) {
+                body_fast(0, qf_keep[0], qf_keep[1]);
+                if (nch > 1) body_fast(1, qf_keep[1], qf_keep[1]);
+            } else {
+                body(0, qf_keep[0], qf_keep[1]);
+                if (nch > 1) body(1, qf_keep[1], qf_keep[1]);
+            }
         } else {
-            for (int ch = 0; ch < nch; ++ch) body(ch, qf, qf);
+            if constexpr (FAST) {
+                for (int ch = 0; ch < nch; ++ch) body_fast(ch, qf, qf);
+            } else {
+                for (int ch = 0; ch < nch; ++ch) body(ch, qf, qf);
+            }
         }
     };
 
@@ -745,25 +976,44 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     }
 }
 
-template <int DK, int DVT, int C>
-static hipError_t run_chunk_bf16(const ChunkArgs& a, const HeadParams& hp, hipStream_t st, hipEvent_t* ev) {
+template <int DK, int DVT, int C, bool FAST>
+static void launch_chunk_form(const ChunkArgs& a, const HeadParams& hp, hipStream_t st, hipEvent_t* e) {
     using G = ChunkGeo<DK, DVT, C>;
     const int chains = a.B * a.H * a.nvt;
-    // the segmented form is a single launch: the pre-pass and scan phases are empty
-    record_empty_phase(st, ev);
-    record_empty_phase(st, ev ? ev + 2 : nullptr);
     // Holding two chunks of outputs and queries in registers fits with 64-token
     // chunks (one wave per SIMD) and with small 128-token tiles.
     constexpr bool kLocalFits = C == 64 || DK + DVT <= 192;
-    hipEvent_t* e = ev ? ev + 4 : nullptr;
     if (a.nseg == 1)
-        launch_timed(chunk_bf16_kernel<DK, DVT, C, kSinglePass>, dim3(chains), dim3(G::NTHR), 0, st, e, a, hp);
+        launch_timed(chunk_bf16_kernel<DK, DVT, C, kSinglePass, FAST>, dim3(chains), dim3(G::NTHR), 0, st, e, a,
+                     hp);
     else if (kLocalFits && a.seg_len <= kKeepChunks * C)
-        launch_timed(chunk_bf16_kernel<DK, DVT, C, kLocalFits ? kLocalPass : kTwoPass>, dim3(chains * a.nseg),
+        launch_timed(chunk_bf16_kernel<DK, DVT, C, kLocalFits ? kLocalPass : kTwoPass, FAST>, dim3(chains * a.nseg),
                      dim3(G::NTHR), 0, st, e, a, hp);
     else
-        launch_timed(chunk_bf16_kernel<DK, DVT, C, kTwoPass>, dim3(chains * a.nseg), dim3(G::NTHR), 0, st, e, a,
-                     hp);
+        launch_timed(chunk_bf16_kernel<DK, DVT, C, kTwoPass, FAST>, dim3(chains * a.nseg), dim3(G::NTHR), 0, st, e,
+                     a, hp);
+}
+
+// The FAST form scales values by gamma^-(j+1) for j < C and outputs by
+// gamma^(i+1): every head's gamma^C must stay far from the float32 range
+// limits, which holds for gamma^C >= 2^-64 (any gamma >= 0.71 at C = 128,
+// >= 0.5 at C = 64, and every default gamma 1 - 2^(-5-h)).
+bool fast_form_ok(const HeadParams& hp, int H, int chunk) {
+    for (int h = 0; h < H; ++h)
+        if (std::log2(static_cast<double>(hp.gamma[h])) * chunk < -64.0) return false;
+    return true;
+}
+
+template <int DK, int DVT, int C>
+static hipError_t run_chunk_bf16(const ChunkArgs& a, const HeadParams& hp, hipStream_t st, hipEvent_t* ev) {
+    // the segmented form is a single launch: the pre-pass and scan phases are empty
+    record_empty_phase(st, ev);
+    record_empty_phase(st, ev ? ev + 2 : nullptr);
+    hipEvent_t* e = ev ? ev + 4 : nullptr;
+    if (fast_form_ok(hp, a.H, C))
+        launch_chunk_form<DK, DVT, C, true>(a, hp, st, e);
+    else
+        launch_chunk_form<DK, DVT, C, false>(a, hp, st, e);
     return hipGetLastError();
 }
 

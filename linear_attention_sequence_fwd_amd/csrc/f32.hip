@@ -223,14 +223,15 @@ __global__ __launch_bounds__(kF32Threads) void parallel_f32_kernel(ParallelArgs 
         stage_rows(sk, K, DK, 0, DK, KP, k0, Lk, BQ, hp.has_theta, hp, a.pos0);
         stage_rows(sv, V, a.dv, c0, dvt, dvt, k0, Lk, BQ, false, hp, a.pos0);
         __syncthreads();
-        const float blk = gamma_pow(lg2, static_cast<double>(q0 - k0));
+        // one exponent per entry, (q0 + i) - (k0 + j) >= 0 for every kept entry,
+        // so no factor overflows for small gamma
         for (int idx = tid; idx < BQ * BQ; idx += kF32Threads) {
             const int i = idx / BQ, j = idx % BQ;
             float p = 0.0f;
             if (i < Lq && j < Lk && (kb < qb || j <= i)) {
                 float acc = 0.0f;
                 for (int d = 0; d < DK; ++d) acc = fmaf(sq[i * DK + d], sk[j * KP + d], acc);
-                p = acc * (exp2f(static_cast<float>(i - j) * lg2f) * blk);
+                p = acc * exp2f(static_cast<float>((q0 - k0) + i - j) * lg2f);
             }
             sp[idx] = p;
         }

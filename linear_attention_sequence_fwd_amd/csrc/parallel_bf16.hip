@@ -74,11 +74,18 @@ __global__ __launch_bounds__((BQ / 16) * 64) void parallel_bf16_kernel(ParallelA
     const int q0 = qb * BQ;
     const int Lq = min(BQ, a.N - q0);
 
-    // D = gamma^((q0 + 16 rb + l16) - (k0 + 16 jt + 4 grp + r))
-    //   = dlane[r] * gamma^(16 (rb - jt)) * gamma^(q0 - k0), the last factor in float64
-    float dlane[4];
+    // D = gamma^((q0 + 16 rb + l16) - (k0 + 16 jt + 4 grp + r)). Every factor is
+    // kept at an exponent >= 0 so that no factor overflows for small gamma:
+    //   diagonal tile (q0 = k0, jt = rb):  dlane[r] = gamma^(l16 - 4 grp - r)
+    //     (negative exponents only in masked entries, which are selected away);
+    //   other tiles: dlane15[r] * gamma^(16 (rb - jt) + (q0 - k0) - 15), with
+    //     dlane15[r] = gamma^(l16 - 4 grp - r + 15) and the tile exponent >= 1.
+    float dlane[4], dlane15[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dlane[r] = fast_exp2(static_cast<float>(l16 - 4 * grp - r) * lg2f);
+    for (int r = 0; r < 4; ++r) {
+        dlane[r] = fast_exp2(static_cast<float>(l16 - 4 * grp - r) * lg2f);
+        dlane15[r] = fast_exp2(static_cast<float>(l16 - 4 * grp - r + 15) * lg2f);
+    }
 
     // queries of this wave's rows, rotated, in MFMA operand registers
     uint4 qf[G::KSQ];
@@ -168,7 +175,6 @@ __global__ __launch_bounds__((BQ / 16) * 64) void parallel_bf16_kernel(ParallelA
             load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR>(vr, Vg + static_cast<size_t>(kn) * a.dv, a.dv, BQ, tid);
         }
 
-        const float blkf = gamma_pow(lg2, static_cast<double>(q0 - k0));
         const FragAddr<UK> fa_k(l16c, grpc);
         const FragAddr<UC> fa_v(l16c, grpc);  // V^T staged unit 4 t + grp (see staged_token)
 #pragma unroll
@@ -187,12 +193,14 @@ __global__ __launch_bounds__((BQ / 16) * 64) void parallel_bf16_kernel(ParallelA
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     const int delta = rb - (2 * t + hh);
-                    const float blk = fast_exp2(static_cast<float>(16 * delta) * lg2c) * blkf;
+                    const bool on_diag = diag && delta == 0;
+                    const float blk = fast_exp2(static_cast<float>(16 * delta + (q0 - k0) - 15) * lg2c);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         float val = 0.0f;
                         const bool keep = !diag || delta > 0 || (delta == 0 && l16 >= 4 * grp + r);
-                        if (keep) val = pa[hh][r] * (dlane[r] * blk);
+                        const float dec = on_diag ? dlane[r] : dlane15[r] * blk;
+                        if (keep) val = pa[hh][r] * dec;
                         pa[hh][r] = val;
                     }
                 }

@@ -130,6 +130,19 @@ __device__ __forceinline__ void rotate_row(uint32_t (&w)[BW / 2], const HeadPara
     }
 }
 
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16). Within each group of 16
+// lanes, lane r supplies the address of 4 consecutive 16-bit elements M[r];
+// lane j receives (M[4k + j/4][j%4], k = 0..3). With lane r pointing at row
+// t0 + r/4, columns c0 + 4(r%4) .. +3 of a row-major matrix X, lane j gets
+// X[t0 + k][c0 + j] for k = 0..3: four consecutive rows of one column, the
+// layout of an MFMA operand whose contraction runs down the rows.
+__device__ __forceinline__ uint2 lds_read_tr16x4(const u16* p) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
+    const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(p));
+    return __builtin_bit_cast(uint2, r);
+}
+
 // Staging block width: 8x8 blocks when there are at least as many as
 // threads, else 8x4 blocks (half the registers per thread).
 constexpr int stage_width(int rows, int cols, int nthr) { return (rows / 8) * (cols / 8) >= nthr ? 8 : 4; }

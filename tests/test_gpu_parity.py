@@ -319,17 +319,35 @@ def test_state_in_out_alias_and_handoff():
     assert_close(to64(state), ref_s, BF16_TOL, "handed-off state")
 
 
-@pytest.mark.parametrize("gammas", [[1.0, 0.99], [0.5, 0.75], [0.9, 0.999999]])
-def test_custom_gammas(gammas):
+@pytest.mark.parametrize("gammas", [[1.0, 0.99], [0.5, 0.75], [0.9, 0.999999], [0.3, 0.97], [0.05, 0.6]])
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_custom_gammas(gammas, chunk):
+    """Gammas far from the defaults, including ones small enough (gamma^chunk <
+    2^-64) that the chunkwise kernel must use its exact per-element decay
+    form instead of the rescaled-values form."""
     B, H, N, dk, dv = 1, 2, 300, 64, 64
     q, k, v = _inputs(B, H, N, dk, dv, torch.bfloat16, seed=44)
     g = np.asarray(gammas, dtype=np.float32).astype(np.float64)
     ref = orc.parallel(to64(q), to64(k), to64(v), g)
-    for o in (R.retention_chunkwise_fwd(q.to(DEV), k.to(DEV), v.to(DEV), chunk=64, gamma=list(g)),
-              R.retention_chunkwise_fwd(q.to(DEV), k.to(DEV), v.to(DEV), chunk=64, gamma=list(g), segments=2),
+    for o in (R.retention_chunkwise_fwd(q.to(DEV), k.to(DEV), v.to(DEV), chunk=chunk, gamma=list(g)),
+              R.retention_chunkwise_fwd(q.to(DEV), k.to(DEV), v.to(DEV), chunk=chunk, gamma=list(g), segments=2),
               R.retention_parallel_fwd(q.to(DEV), k.to(DEV), v.to(DEV), gamma=list(g))):
         torch.cuda.synchronize()
         assert_close(to64(o), ref, BF16_TOL, f"gammas {gammas}")
+
+
+@pytest.mark.parametrize("gammas", [[0.05, 0.6], [0.999, 0.3]])
+def test_custom_gammas_f32(gammas):
+    """float32 inputs with small gammas: the decay of far-apart query/key blocks
+    must not be formed from an overflowing and an underflowing factor."""
+    B, H, N, dk, dv = 1, 2, 300, 64, 64
+    q, k, v = _inputs(B, H, N, dk, dv, torch.float32, seed=45)
+    g = np.asarray(gammas, dtype=np.float32).astype(np.float64)
+    ref = orc.parallel(to64(q), to64(k), to64(v), g)
+    for o in (R.retention_chunkwise_fwd(q.to(DEV), k.to(DEV), v.to(DEV), chunk=64, gamma=list(g)),
+              R.retention_parallel_fwd(q.to(DEV), k.to(DEV), v.to(DEV), gamma=list(g))):
+        torch.cuda.synchronize()
+        assert_close(to64(o), ref, F32_TOL, f"gammas {gammas}")
 
 
 def test_segment_count_invariance_full_msr():
