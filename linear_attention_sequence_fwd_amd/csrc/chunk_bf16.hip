@@ -217,12 +217,20 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     uint4 qf[G::KSQ];
     f32x4 sacc[G::MT][G::NT];
 
+    // queries of this wave's rows (unconditional loads from a clamped row, see load_blocks)
+    // (a wave-uniform base plus a 32-bit per-lane byte offset, like every
+    // global access of the chunk loop: no 64-bit per-lane pointers to keep)
     auto load_q = [&](uint4 (&qd)[G::KSQ], int t, int Lq) __attribute__((always_inline)) {
         const int row = rb * 16 + l16;
-        const u16* p = Qg + static_cast<size_t>(t + row) * DK + grp * 8;
+        const bool ok = row < Lq;
+        const int rc = min(row, Lq > 0 ? Lq - 1 : 0);
+        const char* base = reinterpret_cast<const char*>(Qg + static_cast<size_t>(t) * DK);
+        const uint32_t off = static_cast<uint32_t>((rc * DK + grp * 8) * 2);
 #pragma unroll
-        for (int s = 0; s < G::KSQ; ++s)
-            qd[s] = row < Lq ? *reinterpret_cast<const uint4*>(p + s * 32) : make_uint4(0, 0, 0, 0);
+        for (int s = 0; s < G::KSQ; ++s) {
+            const uint4 x = *reinterpret_cast<const uint4*>(base + off + s * 64);
+            qd[s] = ok ? x : make_uint4(0, 0, 0, 0);
+        }
     };
     // first chunk of the segment (issued before state loads so the HBM round trips overlap)
     auto prefetch_first = [&](bool with_q) __attribute__((always_inline)) {
@@ -285,11 +293,12 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     auto store_o = [&](const f32x4 (&o)[G::NTV], int t0, int L) __attribute__((always_inline)) {
         const int row = rb * 16 + l16;
         if (row < L) {
-            u16* orow = Og + static_cast<size_t>(t0 + row) * a.dv + grp * 4;
+            char* base = reinterpret_cast<char*>(Og + static_cast<size_t>(t0) * a.dv);
+            const uint32_t off = static_cast<uint32_t>((row * a.dv + grp * 4) * 2);
 #pragma unroll
             for (int nt = 0; nt < G::NTV; ++nt) {
                 const uint2 w = make_uint2(pack2_bf16(o[nt][0], o[nt][1]), pack2_bf16(o[nt][2], o[nt][3]));
-                *reinterpret_cast<uint2*>(orow + nt * 16) = w;
+                *reinterpret_cast<uint2*>(base + off + nt * 32) = w;
             }
         }
     };
@@ -467,7 +476,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     BlockRows<G::BWK> kr2[G::KPT];
     BlockRows<G::BWV> vr2[G::VPT];
     auto run_state_only = [&]() __attribute__((always_inline)) {
-        if (nch > 1) load_kv(kr2, vr2, t_begin + C, min(C, t_end - t_begin - C));
+        load_kv(kr2, vr2, nch > 1 ? t_begin + C : t_begin, nch > 1 ? min(C, t_end - t_begin - C) : 0);
         auto step = [&](auto& krb, auto& vrb, int ch) __attribute__((always_inline)) {
             // per-iteration opaque copies: see run_chunks
             int tid_it = tid;
@@ -479,7 +488,8 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
                 stage_fast(krb, vrb, t0, L, tid_it, lg2_it);
             else
                 stage_kv(krb, vrb, t0, L, tid_it, lg2_it);
-            if (ch + 2 < nch) load_kv(krb, vrb, t0 + 2 * C, min(C, t_end - t0 - 2 * C));
+            const bool far = ch + 2 < nch;
+            load_kv(krb, vrb, far ? t0 + 2 * C : t0, far ? min(C, t_end - t0 - 2 * C) : 0);
             __syncthreads();  // keys and values written
             if constexpr (FAST)
                 g4_fast(L, tid_it & 15, (tid_it & 63) >> 4);
@@ -576,7 +586,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
                     }
                 }
             }
-            if (has_next) load_kv(kr, vr, t1, L1);
+            load_kv(kr, vr, has_next ? t1 : t0, L1);  // past the end: a discarded re-read
             __syncthreads();  // C: K row-major written
 
             // ---- 5. G1: P^T = K Q^T for this wave's rows, decay mask in registers,
@@ -619,7 +629,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
             }
 
             // ---- prefetch next chunk's queries (qf is dead for this chunk now)
-            if (has_next) load_q(qnext, t1, L1);
+            load_q(qnext, has_next ? t1 : t0, L1);
 
             // ---- 6. G2: O^T += V^T P^T
             {
@@ -675,7 +685,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
                         qfb[s] = rotate8_bf16(qfb[s], hp, s * 16 + grp * 4, static_cast<double>(a.pos0 + t0 + row));
                 }
             }
-            if (has_next) load_kv(kr, vr, t1, L1);
+            load_kv(kr, vr, has_next ? t1 : t0, L1);  // past the end: a discarded re-read
             __syncthreads();  // A: keys and V''^T written
 
             // ---- 2. G3: O^T = S^T Q^T (the previous chunk's state)
@@ -726,7 +736,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
                     }
                 }
             }
-            if (has_next) load_q(qnext, t1, L1);  // queries are dead for this chunk now
+            load_q(qnext, has_next ? t1 : t0, L1);  // queries are dead for this chunk now
 
             // ---- 4. G2: O^T += V''^T P^T
             {
@@ -763,12 +773,13 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
         };
         if constexpr (KEEP) {  // each chunk's queries stay in their own registers
             static_assert(kKeepChunks == 2, "held chunks");
+            uint4 q_unused[G::KSQ];  // target of the last chunk's discarded query re-read
             if constexpr (FAST) {
                 body_fast(0, qf_keep[0], qf_keep[1]);
-                if (nch > 1) body_fast(1, qf_keep[1], qf_keep[1]);
+                if (nch > 1) body_fast(1, qf_keep[1], q_unused);
             } else {
                 body(0, qf_keep[0], qf_keep[1]);
-                if (nch > 1) body(1, qf_keep[1], qf_keep[1]);
+                if (nch > 1) body(1, qf_keep[1], q_unused);
             }
         } else {
             if constexpr (FAST) {

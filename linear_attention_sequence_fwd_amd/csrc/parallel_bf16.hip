@@ -169,10 +169,13 @@ __global__ __launch_bounds__((BQ / 16) * 64) void parallel_bf16_kernel(ParallelA
         }
         __syncthreads();
 
-        if (m + 1 < nkb) {
-            const int kn = (kb - 1) * BQ;
-            load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR>(kr, Kg + static_cast<size_t>(kn) * DK, DK, BQ, tid);
-            load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR>(vr, Vg + static_cast<size_t>(kn) * a.dv, a.dv, BQ, tid);
+        {  // next key block, issued unconditionally (past the last: a discarded re-read)
+            const bool more = m + 1 < nkb;
+            const int kn = more ? (kb - 1) * BQ : k0;
+            load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR>(kr, Kg + static_cast<size_t>(kn) * DK, DK, more ? BQ : 0,
+                                                             tid);
+            load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR>(vr, Vg + static_cast<size_t>(kn) * a.dv, a.dv,
+                                                              more ? BQ : 0, tid);
         }
 
         const FragAddr<UK> fa_k(l16c, grpc);

@@ -76,33 +76,39 @@ struct BlockRows {
     uint32_t w[8][BW / 2];
 };
 
+// Every load is issued unconditionally (rows past `valid` read a clamped,
+// in-bounds row and are zeroed by a select): with no branch around a load the
+// compiler can count outstanding loads exactly, and a wait for one batch does
+// not also wait for a prefetch issued after it. valid == 0 reads row 0.
 template <int D, int BW, int NBLK, int PT, int NTHR>
 __device__ __forceinline__ void load_blocks(BlockRows<BW> (&r)[PT], const u16* base, int ld, int valid, int tid) {
     // Row pointers are wave-uniform (base + row * ld); the per-lane part is a
     // 32-bit byte offset, so each row load needs one shared offset register
     // and a scalar base instead of its own 64-bit address.
+    const int last = valid > 0 ? valid - 1 : 0;
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
         const int idx = tid + u * NTHR;
+        const bool in_blk = NBLK % NTHR == 0 || idx < NBLK;
         int tb, cb;
-        block_coords<D, BW>(idx < NBLK ? idx : 0, tb, cb);
+        block_coords<D, BW>(in_blk ? idx : 0, tb, cb);
         const int tok0 = staged_token(tb, 0);
-        const uint32_t lane_off = static_cast<uint32_t>((tok0 * ld + cb * BW) * 2);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const int dq = staged_token(0, q);  // token offset of row q inside the block
-            const char* rowq = reinterpret_cast<const char*>(base + static_cast<size_t>(dq) * ld) + lane_off;
-            const bool ok = idx < NBLK && tok0 + dq < valid;
+            const bool ok = in_blk && tok0 + dq < valid;
+            const int row = min(tok0 + dq, last);
+            const char* rowq = reinterpret_cast<const char*>(base) + static_cast<uint32_t>((row * ld + cb * BW) * 2);
             if constexpr (BW == 8) {
-                const uint4 x = ok ? *reinterpret_cast<const uint4*>(rowq) : make_uint4(0, 0, 0, 0);
-                r[u].w[q][0] = x.x;
-                r[u].w[q][1] = x.y;
-                r[u].w[q][2] = x.z;
-                r[u].w[q][3] = x.w;
+                const uint4 x = *reinterpret_cast<const uint4*>(rowq);
+                r[u].w[q][0] = ok ? x.x : 0u;
+                r[u].w[q][1] = ok ? x.y : 0u;
+                r[u].w[q][2] = ok ? x.z : 0u;
+                r[u].w[q][3] = ok ? x.w : 0u;
             } else {
-                const uint2 x = ok ? *reinterpret_cast<const uint2*>(rowq) : make_uint2(0, 0);
-                r[u].w[q][0] = x.x;
-                r[u].w[q][1] = x.y;
+                const uint2 x = *reinterpret_cast<const uint2*>(rowq);
+                r[u].w[q][0] = ok ? x.x : 0u;
+                r[u].w[q][1] = ok ? x.y : 0u;
             }
         }
     }
