@@ -241,7 +241,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
         if (with_q) load_q(qf, t_begin, L0);
     };
     // this head's state from a caller's [B*H][dk][dv] float32 array, or zeros
-    auto load_state = [&](const float* states) __attribute__((always_inline)) {
+    auto load_state_to = [&](f32x4 (&dst)[G::MT][G::NT], const float* states) __attribute__((always_inline)) {
         const float* src = states ? states + static_cast<size_t>(bh) * DK * a.dv : nullptr;
 #pragma unroll
         for (int mt = 0; mt < G::MT; ++mt)
@@ -251,9 +251,10 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
                 for (int r = 0; r < 4; ++r) {
                     const int d = d_base + mt * 16 + grp * 4 + r;
                     const int c = vt * DVT + c_base + nt * 16 + l16;
-                    sacc[mt][nt][r] = src ? src[static_cast<size_t>(d) * a.dv + c] : 0.0f;
+                    dst[mt][nt][r] = src ? src[static_cast<size_t>(d) * a.dv + c] : 0.0f;
                 }
     };
+    auto load_state = [&](const float* states) __attribute__((always_inline)) { load_state_to(sacc, states); };
     // bf16 copy of this wave's state tiles into S^T (row = value column, 4 consecutive dk)
     auto write_state_copy_of = [&](const f32x4 (&st)[G::MT][G::NT], int l16_, int grp_) __attribute__((always_inline)) {
 #pragma unroll
@@ -929,17 +930,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
         run_chunks(std::false_type{});
         write_final_state(sacc);
     } else if constexpr (MODE == kLocalPass) {
-        if (seg == 0) {
-            prefetch_first(true);
-            // the start state is known: the ordinary pass, then publish the end state
-            load_state(a.state_in);
-            have_state = a.state_in != nullptr;
-            if (have_state) write_state_copy(l16, grp);
-            run_chunks(std::false_type{});
-            publish(sacc, f_inc);
-            return;
-        }
-        // ---- the segment from a zero state, outputs held back
+        // ---- every segment runs from a zero state, outputs held back
         {
             const int L0 = min(C, t_end - t_begin);
             load_kv(kr, vr, t_begin, L0);
@@ -947,12 +938,26 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
         }
         load_state(nullptr);
         run_chunks(std::true_type{});  // sacc = T_s
-        if (seg < a.nseg - 1) publish(sacc, f_agg);
         f32x4 sin[G::MT][G::NT];
-        look_back(sin);
+        if (seg == 0) {
+            // the start state is known (the initial state or zero): publish the
+            // end state P_0 = T_0 + g S_0 at once; segment 0 is never the last
+            load_state_to(sin, a.state_in);
+#pragma unroll
+            for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < G::NT; ++nt) sacc[mt][nt] += gseg * sin[mt][nt];
+            publish(sacc, f_inc);
+        } else {
+            if (seg < a.nseg - 1) publish(sacc, f_agg);
+            look_back(sin);
+        }
         // ---- correction: o_n += gamma^(n+1) q_n S_in (n counted from the segment start)
-        write_state_copy_of(sin, l16, grp);
-        __syncthreads();  // S_in^T copy written
+        const bool correct = seg > 0 || a.state_in != nullptr;
+        if (correct) {
+            write_state_copy_of(sin, l16, grp);
+            __syncthreads();  // S_in^T copy written
+        }
         {
             const FragAddr<UK> fa_s(l16, grp);  // S^T rows 16 nt + l16, dk 32 s + 8 grp
 #pragma unroll
@@ -960,17 +965,18 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
                 if (c < nch) {
                     const int t0 = t_begin + c * C;
                     const float zc = zeta * fast_exp2(static_cast<float>(c * C) * lg2f);
-                    f32x4 corr[G::NTV];
+                    if (correct) {
 #pragma unroll
-                    for (int nt = 0; nt < G::NTV; ++nt) {
-                        corr[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        for (int nt = 0; nt < G::NTV; ++nt) {
+                            f32x4 corr = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int s = 0; s < G::KSQ; ++s) {
-                            const uint4 af = *reinterpret_cast<const uint4*>(&sbuf[fa_s.at(nt, s)]);
-                            corr[nt] = mfma16x16x32(af, qf_keep[c][s], corr[nt]);
+                            for (int s = 0; s < G::KSQ; ++s) {
+                                const uint4 af = *reinterpret_cast<const uint4*>(&sbuf[fa_s.at(nt, s)]);
+                                corr = mfma16x16x32(af, qf_keep[c][s], corr);
+                            }
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) oacc_keep[c][nt][r] += zc * corr[r];
                         }
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) oacc_keep[c][nt][r] += zc * corr[nt][r];
                     }
                     store_o(oacc_keep[c], t0, min(C, t_end - t0));
                 }
