@@ -89,7 +89,8 @@ int f32_parallel_dvt(int dk, int dv) {
 struct ChunkPlan {
     int dvt, nvt, nseg, seg_len, nseg_max;
     size_t ws_bytes;
-    size_t flags_off, agg_off;  // byte offsets of the workspace regions
+    int grp;                    // segments per look-back group
+    size_t flags_off, gflags_off, agg_off, gagg_off;  // byte offsets of the workspace regions
 };
 
 constexpr size_t round256(size_t n) { return (n + 255) / 256 * 256; }
@@ -120,12 +121,20 @@ ret_status_t plan_chunk(int B, int H, int N, int dk, int dv, ret_dtype_t dtype, 
     const int per_seg = (nchunks + want - 1) / want;
     p.seg_len = per_seg * chunk;
     p.nseg = (N + p.seg_len - 1) / p.seg_len;
-    // workspace: [ticket counter per chain | flags per (chain, segment) | segment states],
-    // chain = (batch, head, value tile)
-    const size_t states = static_cast<size_t>(B) * H * p.nseg_max * dk * dv * sizeof(float);
+    // Look-back groups of about sqrt(segments) segments (at least 2): a
+    // segment reads its group predecessors' states and one aggregate per
+    // earlier group.
+    p.grp = 2;
+    while ((p.grp + 1) * (p.grp + 1) <= p.nseg) ++p.grp;
+    const int ngroups_max = (p.nseg_max + 1) / 2;
+    // workspace: [ticket counter per chain | flags per (chain, segment) | flags per (chain, group) |
+    //             segment states | group aggregates], chain = (batch, head, value tile)
+    const size_t slot = static_cast<size_t>(B) * H * dk * dv * sizeof(float);  // one state per chain
     p.flags_off = kCtlBytes;
-    p.agg_off = p.flags_off + round256(static_cast<size_t>(base) * p.nseg_max * sizeof(unsigned long long));
-    p.ws_bytes = p.nseg_max > 1 ? p.agg_off + states : 0;
+    p.gflags_off = p.flags_off + round256(static_cast<size_t>(base) * p.nseg_max * sizeof(unsigned long long));
+    p.agg_off = p.gflags_off + round256(static_cast<size_t>(base) * ngroups_max * sizeof(unsigned long long));
+    p.gagg_off = p.agg_off + slot * p.nseg_max;
+    p.ws_bytes = p.nseg_max > 1 ? p.gagg_off + slot * ngroups_max : 0;
     if (base * p.nseg > 2147483647LL) return RET_ERR_UNSUPPORTED;
     return RET_OK;
 }
@@ -191,6 +200,8 @@ static ret_status_t chunkwise_impl(const void* q, const void* k, const void* v, 
     a.ctl = seg_ws ? reinterpret_cast<unsigned long long*>(ws) : nullptr;
     a.flags = seg_ws ? reinterpret_cast<unsigned long long*>(ws + p.flags_off) : nullptr;
     a.agg = seg_ws ? reinterpret_cast<float*>(ws + p.agg_off) : nullptr;
+    a.gflags = seg_ws ? reinterpret_cast<unsigned long long*>(ws + p.gflags_off) : nullptr;
+    a.gagg = seg_ws ? reinterpret_cast<float*>(ws + p.gagg_off) : nullptr;
     a.B = B;
     a.H = H;
     a.N = N;
@@ -200,6 +211,7 @@ static ret_status_t chunkwise_impl(const void* q, const void* k, const void* v, 
     a.nvt = p.nvt;
     a.nseg = p.nseg;
     a.seg_len = p.seg_len;
+    a.grp = p.grp;
     a.pos0 = pos0;
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipEvent_t* ev = events ? reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)) : nullptr;

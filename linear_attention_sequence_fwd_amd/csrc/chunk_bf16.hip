@@ -102,9 +102,10 @@ __device__ __forceinline__ int wave_row_block(int w) {
 //   2. Segment 0 publishes its end state P_0 (from the initial state); every
 //      other segment but the last publishes T_s, its end state from a zero
 //      start. Publishing never waits on anything.
-//   3. Segment s >= 1 waits until all its predecessors have published and forms
-//          S_in(s) = sum_{0<j<s} g^(s-1-j) T_j + g^(s-1) P_0,   g = gamma^seg_len,
-//      always in the same order, so results are bitwise reproducible.
+//   3. Segment s >= 1 forms S_in(s) = sum_{0<j<s} g^(s-1-j) T_j + g^(s-1) P_0,
+//      g = gamma^seg_len, from its group predecessors' states and one published
+//      aggregate per earlier group of segments (see look_back), always in the
+//      same order, so results are bitwise reproducible.
 //   4. It runs its chunks from S_in(s) (or runs them from zero first and
 //      corrects the held outputs by gamma^(n+1) q_n S_in(s), see kLocalPass).
 // Every wait targets a workgroup that is running and publishes without
@@ -841,20 +842,32 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
         if (tid == 0) __hip_atomic_store(flags + seg, flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
     const float gseg = static_cast<float>(gamma_pow(lg2, a.seg_len));
-    // S_in of this segment (seg >= 1) into sin: every predecessor's published
-    // state, nearest first, in a fixed order, so the result does not depend on
-    // which predecessors happened to finish first.
-    auto look_back = [&](f32x4 (&sin)[G::MT][G::NT]) __attribute__((always_inline)) {
+    // Segment groups of a.grp segments: the last member of each group (when it
+    // is not the chain's last segment) publishes the group aggregate
+    //     A_q = sum_{j in group q} g^(last_q - j) T_j     (T_0 read as P_0),
+    // so a segment reads its group predecessors and one aggregate per earlier
+    // group: S_in(s) = sum_{first<=j<s} g^(s-1-j) T_j + sum_{q<group(s)} g^(s-1-last_q) A_q.
+    const int ngroups = (a.nseg + a.grp - 1) / a.grp;
+    unsigned long long* gflags = a.gflags + static_cast<size_t>(chain) * ngroups;
+    auto gslot = [&](int q) __attribute__((always_inline)) {
+        return reinterpret_cast<unsigned long long*>(a.gagg + (static_cast<size_t>(chain) * ngroups + q) * kSlot) +
+               wave * (G::MT * G::NT * 128) + lane;
+    };
+    // Wait (wave 0, then the whole workgroup) until flags fl[lo .. hi] all read as
+    // published (want_lo for index 0 of the chain's segments, else want).
+    // Returns nonzero when the spin bound ran out.
+    auto wait_published = [&](const unsigned long long* fl, int lo, int hi, unsigned long long want,
+                              unsigned long long want0) __attribute__((always_inline)) {
         if (wave == 0) {
-            // lane i watches predecessor j0 - i, a window of 64 at a time
+            // lane i watches index j0 - i, a window of 64 at a time
             int failed = 0;
             unsigned spins = 0;
-            for (int j0 = seg - 1; j0 >= 0;) {
+            for (int j0 = hi; j0 >= lo;) {
                 const int j = j0 - lane;
-                const unsigned long long want = j == 0 ? f_inc : f_agg;
+                const unsigned long long w = j == 0 ? want0 : want;
                 const unsigned long long f =
-                    j >= 0 ? __hip_atomic_load(flags + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : want;
-                if (__ballot(f != want) == 0) {
+                    j >= lo ? __hip_atomic_load(fl + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : w;
+                if (__ballot(f != w) == 0) {
                     j0 -= 64;
                     continue;
                 }
@@ -868,39 +881,69 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
         }
         __syncthreads();
         const int failed = s_lookback[0];
-        __syncthreads();  // slot read before sbuf receives a state copy
-#pragma unroll
-        for (int mt = 0; mt < G::MT; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < G::NT; ++nt) sin[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // Predecessors' states are fetched in predicated batches so a whole batch
-        // is in flight at once. Entry i (i = 0 .. seg-1) is segment seg-1-i with
-        // weight g^i; entry seg-1 is segment 0's end state.
+        __syncthreads();  // slot read before it is written again (or before sbuf receives a state copy)
+        return failed;
+    };
+    // sin += sum_{i < n} fac_i * state(src(i)), fac_0 = fac, fac_(i+1) = fac_i * step, in order of i;
+    // returns the factor after the last entry. Loads go out in predicated batches.
+    auto accumulate = [&](f32x4 (&sin)[G::MT][G::NT], int n, auto src, float fac, float step)
+                          __attribute__((always_inline)) {
         constexpr int kBatch = imax(1, (C == 64 ? 32 : 16) / (G::MT * G::NT));
-        float fac = 1.0f;
-        for (int i0 = 0; i0 < seg; i0 += kBatch) {
+        for (int i0 = 0; i0 < n; i0 += kBatch) {
             f32x4 t[kBatch][G::MT][G::NT];
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
-                if (i0 + u < seg) {
-                    unsigned long long* src = slot(seg - 1 - i0 - u);
+                if (i0 + u < n) {
+                    unsigned long long* sp = src(i0 + u);
 #pragma unroll
                     for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
                         for (int nt = 0; nt < G::NT; ++nt)
-                            t[u][mt][nt] = load_coherent(src + (mt * G::NT + nt) * 128);
+                            t[u][mt][nt] = load_coherent(sp + (mt * G::NT + nt) * 128);
                 }
             }
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
-                if (i0 + u < seg) {
+                if (i0 + u < n) {
 #pragma unroll
                     for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
                         for (int nt = 0; nt < G::NT; ++nt) sin[mt][nt] += fac * t[u][mt][nt];
-                    fac *= gseg;
+                    fac *= step;
                 }
             }
+        }
+        return fac;
+    };
+    // S_in of this segment (seg >= 1) into sin, always in the same order (so the
+    // result does not depend on which segments finished first). When sin is
+    // not sacc, sacc holds T_s (needed if this segment closes a group).
+    auto look_back = [&](f32x4 (&sin)[G::MT][G::NT]) __attribute__((always_inline)) {
+        const int grp_sz = a.grp;
+        const int q = seg / grp_sz, first = q * grp_sz, pos = seg - first;
+        int failed = pos > 0 ? wait_published(flags, first, seg - 1, f_agg, f_inc) : 0;
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < G::NT; ++nt) sin[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // group predecessors: entry i is segment seg-1-i with weight g^i
+        const float fq = accumulate(sin, pos, [&](int i) { return slot(seg - 1 - i); }, 1.0f, gseg);
+        if (pos == grp_sz - 1 && seg < a.nseg - 1) {  // close the group: A_q = T_s + g * (its predecessors)
+            unsigned long long* dst = gslot(q);
+#pragma unroll
+            for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < G::NT; ++nt)
+                    store_coherent(dst + (mt * G::NT + nt) * 128, sacc[mt][nt] + gseg * sin[mt][nt]);
+            wait_stores();
+            __syncthreads();
+            if (tid == 0) __hip_atomic_store(gflags + q, f_agg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // earlier groups: entry k is group q-1-k with weight g^(pos + k grp)
+        if (q > 0) {
+            failed |= wait_published(gflags, 0, q - 1, f_agg, f_agg);
+            const float gstep = static_cast<float>(gamma_pow(lg2, static_cast<double>(grp_sz) * a.seg_len));
+            accumulate(sin, q, [&](int k) { return gslot(q - 1 - k); }, fq, gstep);
         }
         if (failed) {
 #pragma unroll
@@ -920,10 +963,18 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
         }
         // ---- the start state
         prefetch_first(true);
-        if (seg == 0)
+        if (seg == 0) {
             load_state(a.state_in);
-        else
+        } else if (seg < a.nseg - 1) {  // T_s stays in sacc while the look-back may close a group
+            f32x4 sin[G::MT][G::NT];
+            look_back(sin);
+#pragma unroll
+            for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < G::NT; ++nt) sacc[mt][nt] = sin[mt][nt];
+        } else {
             look_back(sacc);
+        }
         // ---- pass 2: outputs and state from the start state
         have_state = seg > 0 || a.state_in != nullptr;
         if (have_state) write_state_copy(l16, grp);

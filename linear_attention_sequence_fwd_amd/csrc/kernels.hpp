@@ -23,11 +23,14 @@ struct ChunkArgs {
     unsigned long long* flags;  // [B*H*nvt][nseg] publication flags of the bf16 look-back
     float* agg;                 // published per-segment states: bf16 [B*H*nvt][nseg][dk*dvt] in
                                 // accumulator order; float32 [B*H][nseg][dk][dv]
+    unsigned long long* gflags;  // [B*H*nvt][ngroups] flags of the bf16 segment-group aggregates
+    float* gagg;                 // [B*H*nvt][ngroups][dk*dvt] segment-group aggregates
     int B, H, N, dk, dv;
     int chunk;
     int nvt;      // value tiles per head
     int nseg;     // sequence segments per head
     int seg_len;  // tokens per segment, a multiple of chunk
+    int grp;      // segments per look-back group (bf16 segmented form)
     long long pos0;
 };
 
