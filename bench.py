@@ -116,10 +116,17 @@ def time_phases(R, q, k, v, kw, steps):
 
 
 def time_graph(fn, steps, warmup, per_graph=20):
-    """Per-step time with the step captured in a HIP graph (per_graph steps per
-    graph) and replayed, so host launch overhead is not in the measurement."""
+    """Per-step time with the step captured in a HIP graph and replayed, so host
+    launch overhead is not in the measurement. Exactly `steps` steps are timed:
+    the graph holds the largest divisor of `steps` that is <= per_graph, and an
+    event between consecutive replays gives the per-step spread.
+    Returns (mean ms per step over all timed steps, {p10, p50, p90} of the
+    per-replay ms per step)."""
+    import numpy as np
     import torch
 
+    per = max(d for d in range(1, min(per_graph, steps) + 1) if steps % d == 0)
+    reps = steps // per
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -129,19 +136,54 @@ def time_graph(fn, steps, warmup, per_graph=20):
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for _ in range(per_graph):
+        for _ in range(per):
             fn()
     g.replay()
     torch.cuda.synchronize()
-    reps = max(1, steps // per_graph)
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(reps):
-        g.replay()
-    stop.record()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     torch.cuda.synchronize()
-    return start.elapsed_time(stop) / (reps * per_graph)
+    ev[0].record()
+    for i in range(reps):
+        g.replay()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = np.array([ev[i].elapsed_time(ev[i + 1]) / per for i in range(reps)])
+    mean = ev[0].elapsed_time(ev[reps]) / steps
+    pct = {f"p{q}": float(np.percentile(per_step, q)) for q in (10, 50, 90)}
+    return mean, pct
+
+
+def measured_peaks():
+    """What this machine delivers on plain library work, beside the spec peaks:
+    a 1 GiB device-to-device copy (HBM read + write) and a bf16 8192^3 matrix
+    product (hipBLASLt through torch)."""
+    import torch
+
+    def timed(f, reps):
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            f()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    ms_copy = timed(lambda: dst.copy_(src), 20)
+    del src, dst
+    n = 8192
+    x = torch.randn((n, n), dtype=torch.bfloat16, device="cuda:0")
+    y = torch.randn((n, n), dtype=torch.bfloat16, device="cuda:0")
+    ms_mm = timed(lambda: torch.mm(x, y), 10)
+    del x, y
+    torch.cuda.empty_cache()
+    return {"copy_gbs": 2 * (1 << 30) / (ms_copy * 1e-3) / 1e9,
+            "bf16_gemm_tflops": 2 * n ** 3 / (ms_mm * 1e-3) / 1e12,
+            "how": "1 GiB device copy; torch.mm bf16 8192x8192x8192 (hipBLASLt)"}
 
 
 def cpu_baseline(q, k, v, theta, H, budget_s):
@@ -264,7 +306,7 @@ def main():
     kw.update(out=out, workspace=ws)
     step = lambda: R.retention_chunkwise_fwd(q, k, v, **kw)  # noqa: E731
     ms_eager = time_events(step, args.steps, args.warmup)
-    ms = time_graph(step, args.steps, args.warmup)
+    ms, spread = time_graph(step, args.steps, args.warmup)
     phases = time_phases(R, q, k, v, kw, max(20, args.steps // 4))
     tokens = w["B"] * w["N"]
     alg_bytes = chunk_alg_bytes(w["B"], w["H"], w["N"], w["dk"], w["dv"])
@@ -292,7 +334,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "chunk_bf16_kernel (main pass)",
+            "kernel": "chunk_bf16_kernel<64, 64, 64, local pass> (the whole step is this one launch)",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -302,12 +344,14 @@ def main():
             "alg_bytes_per_launch": alg_bytes,
             "kernel_ms": main_ms,
         },
-        "phase_ms": {"segment_states": phases[0], "segment_scan": phases[1], "main": phases[2]},
-        "timing": "ms_per_step from HIP-graph replay of the step (20 steps per graph); "
-                  "eager_ms_per_step launches each call from Python",
+        "timing": "ms_per_step from HIP-graph replay of exactly `steps` steps (up to 20 per graph, an event "
+                  "between replays for the spread); eager_ms_per_step launches each call from Python; "
+                  "kernel_ms is the kernel's own duration from events recorded around its execution",
+        "ms_per_step_spread": spread,
         "eager_ms_per_step": ms_eager,
     }
     result["cpu_baseline"] = cpu_baseline(q.cpu(), k.cpu(), v.cpu(), theta, w["H"], args.cpu_seconds)
+    result["measured_peaks"] = measured_peaks()
     del q, k, v, out, ws
     torch.cuda.empty_cache()
 
