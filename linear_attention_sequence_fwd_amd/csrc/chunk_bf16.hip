@@ -661,9 +661,9 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
         };
         // The FAST form of a chunk: two barriers. Staging writes row-major keys
         // and V''^T and issues the next chunk's loads (its registers are free);
-        // one matrix-core phase (G3, G1, G2 into one accumulator, then G4) reads
-        // LDS only; after the second barrier the new state copy and the outputs
-        // (times gamma^(i+1)) are written.
+        // one matrix-core phase reads LDS only: G3, G1, G2 into one accumulator,
+        // the outputs (times gamma^(i+1)) are stored, then G4; after the second
+        // barrier the new state copy is written.
         auto body_fast = [&](int ch, uint4 (&qfb)[G::KSQ], uint4 (&qnext)[G::KSQ]) __attribute__((always_inline)) {
             int tid_it = tid;
             float lg2_it = lg2f;
@@ -755,13 +755,8 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
                 }
             }
 
-            // ---- 5. G4: S = gamma^L (S + K^T V'')
-            g4_fast(L, l16c, grpc);
-            __syncthreads();  // B: every read of keys, V''^T and the state copy done
-
-            // ---- 6. new state copy; outputs times gamma^(i+1)
-            write_state_copy(l16c, grpc);
-            have_state = true;
+            // ---- 5. outputs times gamma^(i+1), stored now (G4 does not touch them): the
+            //         stores of waves with little causal work overlap the others' MFMAs
 #pragma unroll
             for (int nt = 0; nt < G::NTV; ++nt)
 #pragma unroll
@@ -772,6 +767,14 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
             } else {
                 store_o(oacc, t0, L);
             }
+
+            // ---- 6. G4: S = gamma^L (S + K^T V'')
+            g4_fast(L, l16c, grpc);
+            __syncthreads();  // B: every read of keys, V''^T and the state copy done
+
+            // ---- 7. new state copy
+            write_state_copy(l16c, grpc);
+            have_state = true;
         };
         if constexpr (KEEP) {  // each chunk's queries stay in their own registers
             static_assert(kKeepChunks == 2, "held chunks");
