@@ -179,6 +179,80 @@ def test_recurrent_step_small(dtype, rot):
     assert_close(to64(state), S, tol, "final state")
 
 
+# ------------------------------------------------------------ the largest supported shapes
+
+MAX_CHUNK_CASES = [
+    # B, H, N, dk, dv, chunk, rotary, state_in, segments
+    (1, 128, 100, 64, 64, 64, True, True, 0),      # the head limit; chains split in two segments
+    (1, 2, 300, 256, 1024, 128, True, True, 0),    # widest key dim, eight 128-wide value tiles
+    (1, 1, 520, 256, 1024, 64, False, True, 0),    # chunk 64: sixteen 64-wide tiles, nine segments
+    (2, 128, 65, 128, 128, 128, False, False, 0),  # 256 chains: one segment each
+]
+
+
+@pytest.mark.parametrize("case", MAX_CHUNK_CASES, ids=lambda c: "B{}H{}N{}dk{}dv{}C{}rot{}st{}seg{}".format(*c))
+def test_chunkwise_bf16_max_shapes(case):
+    B, H, N, dk, dv, C, rot, st, seg = case
+    q, k, v = _inputs(B, H, N, dk, dv, torch.bfloat16, seed=5 * N + dv)
+    theta = W.rotary_theta(dk) if rot else None
+    s0 = torch.randn((B, H, dk, dv), generator=torch.Generator().manual_seed(21)) * 0.05 if st else None
+    ref, ref_s = orc.recurrent(to64(q), to64(k), to64(v), orc.head_gammas(H),
+                               theta=None if theta is None else to64(theta), pos0=9,
+                               state0=None if s0 is None else to64(s0))
+    o, s = R.retention_chunkwise_fwd(q.to(DEV), k.to(DEV), v.to(DEV), chunk=C, theta=theta, pos0=9,
+                                     state_in=None if s0 is None else s0.to(DEV), return_state=True,
+                                     segments=seg)
+    torch.cuda.synchronize()
+    assert_close(to64(o), ref, BF16_TOL, "O")
+    assert_close(to64(s), ref_s, BF16_TOL, "state")
+
+
+def test_parallel_bf16_max_heads():
+    B, H, N, dk, dv = 1, 128, 70, 128, 256
+    q, k, v = _inputs(B, H, N, dk, dv, torch.bfloat16, seed=71)
+    theta = W.rotary_theta(dk)
+    ref = orc.parallel(to64(q), to64(k), to64(v), orc.head_gammas(H), theta=to64(theta), pos0=2)
+    o = R.retention_parallel_fwd(q.to(DEV), k.to(DEV), v.to(DEV), theta=theta, pos0=2)
+    torch.cuda.synchronize()
+    assert_close(to64(o), ref, BF16_TOL, "O")
+
+
+@pytest.mark.parametrize("dtype,B,H,dk,dv,rot", [
+    (torch.bfloat16, 2, 128, 256, 128, True),   # head limit with rotary at the widest key dim
+    (torch.bfloat16, 1, 1, 4096, 1024, False),  # widest decode state
+    (torch.float32, 1, 2, 4096, 1024, False),
+])
+def test_recurrent_step_max_shapes(dtype, B, H, dk, dv, rot):
+    steps = 3
+    s0, qs, ks, vs = W.make_decode(B, H, dk, dv, dtype, steps, 0.01, seed=13)
+    theta = W.rotary_theta(dk) if rot else None
+    pos = torch.arange(B, dtype=torch.int64) * 1000 + 3
+    g = orc.head_gammas(H)
+    S = to64(s0)
+    state = s0.to(DEV)
+    tol = BF16_TOL if dtype == torch.bfloat16 else F32_TOL
+    for t in range(steps):
+        o_ref, S = orc.decode_step(to64(qs[t]), to64(ks[t]), to64(vs[t]), S, g,
+                                   theta=None if theta is None else to64(theta),
+                                   pos=(pos + t).numpy() if rot else None)
+        o = R.retention_recurrent_step(qs[t].to(DEV), ks[t].to(DEV), vs[t].to(DEV), state, theta=theta,
+                                       pos=(pos + t).to(DEV) if rot else None)
+        torch.cuda.synchronize()
+        assert_close(to64(o), o_ref, tol, f"o step {t}")
+    assert_close(to64(state), S, tol, "final state")
+
+
+def test_oversize_requests_rejected():
+    q, k, v = _inputs(1, 129, 8, 64, 64, torch.bfloat16, seed=1)
+    with pytest.raises(RuntimeError):
+        R.retention_chunkwise_fwd(q.to(DEV), k.to(DEV), v.to(DEV), chunk=64)
+    q, k, v = _inputs(1, 1, 8, 64, 1028, torch.bfloat16, seed=1)
+    s = torch.zeros((1, 1, 64, 1028), dtype=torch.float32, device=DEV)
+    with pytest.raises(RuntimeError):
+        R.retention_recurrent_step(q[:, :, 0].contiguous().to(DEV), k[:, :, 0].contiguous().to(DEV),
+                                   v[:, :, 0].contiguous().to(DEV), s)
+
+
 # ------------------------------------------------------------ the full-size workloads
 
 
