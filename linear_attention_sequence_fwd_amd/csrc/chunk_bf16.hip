@@ -169,7 +169,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15;
     const int grp = lane >> 4;
 
@@ -218,20 +218,18 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     uint4 qf[G::KSQ];
     f32x4 sacc[G::MT][G::NT];
 
-    // queries of this wave's rows (unconditional loads from a clamped row, see load_blocks)
-    // (a wave-uniform base plus a 32-bit per-lane byte offset, like every
-    // global access of the chunk loop: no 64-bit per-lane pointers to keep)
+    // queries of this wave's rows: unconditional loads (a wave-uniform base plus
+    // a 32-bit per-lane byte offset, like every global access of the chunk
+    // loop: no 64-bit per-lane pointers to keep). Rows past the end of the
+    // segment read the last valid row instead; they only feed output rows
+    // that are never stored, so they need no zeroing (a select here would be
+    // turned into branches around the loads).
     auto load_q = [&](uint4 (&qd)[G::KSQ], int t, int Lq) __attribute__((always_inline)) {
-        const int row = rb * 16 + l16;
-        const bool ok = row < Lq;
-        const int rc = min(row, Lq > 0 ? Lq - 1 : 0);
+        const int rc = min(rb * 16 + l16, Lq > 0 ? Lq - 1 : 0);
         const char* base = reinterpret_cast<const char*>(Qg + static_cast<size_t>(t) * DK);
         const uint32_t off = static_cast<uint32_t>((rc * DK + grp * 8) * 2);
 #pragma unroll
-        for (int s = 0; s < G::KSQ; ++s) {
-            const uint4 x = *reinterpret_cast<const uint4*>(base + off + s * 64);
-            qd[s] = ok ? x : make_uint4(0, 0, 0, 0);
-        }
+        for (int s = 0; s < G::KSQ; ++s) qd[s] = *reinterpret_cast<const uint4*>(base + off + s * 64);
     };
     // first chunk of the segment (issued before state loads so the HBM round trips overlap)
     auto prefetch_first = [&](bool with_q) __attribute__((always_inline)) {
@@ -312,12 +310,11 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
             if (idx < G::KB) {
                 int tb, cb;
                 block_coords<DK, G::BWK>(idx, tb, cb);
-                if (hp.has_theta) {
+                if (hp.has_theta) {  // rows past the end are zero: rotating them is harmless
 #pragma unroll
                     for (int q = 0; q < 8; ++q)
-                        if (staged_token(tb, q) < L)
-                            rotate_row<G::BWK>(krb[u].w[q], hp, cb * (G::BWK / 2),
-                                               static_cast<double>(a.pos0 + t0 + staged_token(tb, q)));
+                        rotate_row<G::BWK>(krb[u].w[q], hp, cb * (G::BWK / 2),
+                                           static_cast<double>(a.pos0 + t0 + staged_token(tb, q)));
                 }
                 float xi[8];
 #pragma unroll
@@ -347,14 +344,17 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
             }
         }
     };
-    // K and V of the chunk starting at token t (L valid tokens) into staging registers.
-    auto load_kv = [&](auto& krb, auto& vrb, int t, int L) __attribute__((always_inline)) {
-        load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR>(krb, Kg + static_cast<size_t>(t) * DK, DK, L, tid);
-        load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR>(vrb, Vg + static_cast<size_t>(t) * a.dv, a.dv, L, tid);
+    // K and V of the chunk starting at token t (L valid tokens) into staging
+    // registers (tid_it: the thread index, an opaque per-chunk copy inside the
+    // chunk loops, so the per-row offsets are recomputed instead of being held
+    // in registers across the loop).
+    auto load_kv = [&](auto& krb, auto& vrb, int t, int L, int tid_it) __attribute__((always_inline)) {
+        load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR>(krb, Kg + static_cast<size_t>(t) * DK, DK, L, tid_it);
+        load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR>(vrb, Vg + static_cast<size_t>(t) * a.dv, a.dv, L, tid_it);
     };
     // Step 3 (G4): S = gamma^L S + Kx^T V on this wave's tiles.
     auto g4 = [&](int L, int l16c, int grpc) __attribute__((always_inline)) {
-        const float gL = (L == C) ? gC : gamma_pow(lg2, L);
+        const float gL = (L == C) ? gC : fast_exp2(static_cast<float>(L) * lg2f);  // no float64 in the loop
         const FragAddr<UC> fa_kt(d_base + l16c, grpc);  // K^T rows d_base + 16 mt + l16, tokens 32 t + 8 grp
         const FragAddr<UC> fa_vt(c_base + l16c, grpc);  // V^T rows c_base + 16 nt + l16, tokens 32 t + 8 grp
 #pragma unroll
@@ -388,12 +388,11 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
             if (idx < G::KB) {
                 int tb, cb;
                 block_coords<DK, G::BWK>(idx, tb, cb);
-                if (hp.has_theta) {
+                if (hp.has_theta) {  // rows past the end are zero: rotating them is harmless
 #pragma unroll
                     for (int q = 0; q < 8; ++q)
-                        if (staged_token(tb, q) < L)
-                            rotate_row<G::BWK>(krb[u].w[q], hp, cb * (G::BWK / 2),
-                                               static_cast<double>(a.pos0 + t0 + staged_token(tb, q)));
+                        rotate_row<G::BWK>(krb[u].w[q], hp, cb * (G::BWK / 2),
+                                           static_cast<double>(a.pos0 + t0 + staged_token(tb, q)));
                 }
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
@@ -437,7 +436,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     // receives dk row l16 at tokens 32 t + 4 grp + {0..3} (+16): the token
     // order of the V''^T units.
     auto g4_fast = [&](int L, int l16c, int grpc) __attribute__((always_inline)) {
-        const float gL = (L == C) ? gC : gamma_pow(lg2, L);
+        const float gL = (L == C) ? gC : fast_exp2(static_cast<float>(L) * lg2f);  // no float64 in the loop
         const int tok = 4 * grpc + (l16c >> 2);
         int kb[G::MT];
 #pragma unroll
@@ -478,7 +477,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     BlockRows<G::BWK> kr2[G::KPT];
     BlockRows<G::BWV> vr2[G::VPT];
     auto run_state_only = [&]() __attribute__((always_inline)) {
-        load_kv(kr2, vr2, nch > 1 ? t_begin + C : t_begin, nch > 1 ? min(C, t_end - t_begin - C) : 0);
+        load_kv(kr2, vr2, nch > 1 ? t_begin + C : t_begin, nch > 1 ? min(C, t_end - t_begin - C) : 0, tid);
         auto step = [&](auto& krb, auto& vrb, int ch) __attribute__((always_inline)) {
             // per-iteration opaque copies: see run_chunks
             int tid_it = tid;
@@ -491,7 +490,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
             else
                 stage_kv(krb, vrb, t0, L, tid_it, lg2_it);
             const bool far = ch + 2 < nch;
-            load_kv(krb, vrb, far ? t0 + 2 * C : t0, far ? min(C, t_end - t0 - 2 * C) : 0);
+            load_kv(krb, vrb, far ? t0 + 2 * C : t0, far ? min(C, t_end - t0 - 2 * C) : 0, tid_it);
             __syncthreads();  // keys and values written
             if constexpr (FAST)
                 g4_fast(L, tid_it & 15, (tid_it & 63) >> 4);
@@ -532,13 +531,11 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
 
             // ---- 1. K^T (scaled by xi) and V^T into LDS; rotate queries
             stage_kv(kr, vr, t0, L, tid_it, lg2c);
-            if (hp.has_theta) {
+            if (hp.has_theta) {  // every row: those past the end are never stored
                 const int row = rb * 16 + l16;
-                if (row < L) {
 #pragma unroll
-                    for (int s = 0; s < G::KSQ; ++s)
-                        qfb[s] = rotate8_bf16(qfb[s], hp, s * 16 + grp * 4, static_cast<double>(a.pos0 + t0 + row));
-                }
+                for (int s = 0; s < G::KSQ; ++s)
+                    qfb[s] = rotate8_bf16(qfb[s], hp, s * 16 + grp * 4, static_cast<double>(a.pos0 + t0 + row));
             }
             __syncthreads();  // A: K^T, V^T written
 
@@ -588,7 +585,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
                     }
                 }
             }
-            load_kv(kr, vr, has_next ? t1 : t0, L1);  // past the end: a discarded re-read
+            load_kv(kr, vr, has_next ? t1 : t0, L1, tid_it);  // past the end: a discarded re-read
             __syncthreads();  // C: K row-major written
 
             // ---- 5. G1: P^T = K Q^T for this wave's rows, decay mask in registers,
@@ -679,15 +676,13 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
 
             // ---- 1. keys row-major, V''^T into LDS; rotate queries; fetch the next chunk
             stage_fast(kr, vr, t0, L, tid_it, lg2c);
-            if (hp.has_theta) {
+            if (hp.has_theta) {  // every row: those past the end are never stored
                 const int row = rb * 16 + l16;
-                if (row < L) {
 #pragma unroll
-                    for (int s = 0; s < G::KSQ; ++s)
-                        qfb[s] = rotate8_bf16(qfb[s], hp, s * 16 + grp * 4, static_cast<double>(a.pos0 + t0 + row));
-                }
+                for (int s = 0; s < G::KSQ; ++s)
+                    qfb[s] = rotate8_bf16(qfb[s], hp, s * 16 + grp * 4, static_cast<double>(a.pos0 + t0 + row));
             }
-            load_kv(kr, vr, has_next ? t1 : t0, L1);  // past the end: a discarded re-read
+            load_kv(kr, vr, has_next ? t1 : t0, L1, tid_it);  // past the end: a discarded re-read
             __syncthreads();  // A: keys and V''^T written
 
             // ---- 2. G3: O^T = S^T Q^T (the previous chunk's state)
@@ -987,7 +982,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
         // ---- every segment runs from a zero state, outputs held back
         {
             const int L0 = min(C, t_end - t_begin);
-            load_kv(kr, vr, t_begin, L0);
+            load_kv(kr, vr, t_begin, L0, tid);
             load_q(qf_keep[0], t_begin, L0);
         }
         load_state(nullptr);
