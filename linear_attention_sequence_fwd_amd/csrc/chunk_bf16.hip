@@ -288,6 +288,43 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     const float gC = gamma_pow(lg2, C);
     bool have_state = false;
 
+    // Rotation frequencies this thread applies: its key staging columns and
+    // its query units. 64-token chunk kernels have registers to spare and hold
+    // them for the whole segment (read once, after the first chunk's loads are
+    // on their way); the others read them at each stage (one batch of loads
+    // from the kernel arguments).
+    constexpr bool kThetaRegs = C == 64;
+    float thk[G::KPT][G::BWK / 2];
+    float thq[G::KSQ][4];
+    auto load_theta = [&]() __attribute__((always_inline)) {
+        if (kThetaRegs && hp.has_theta) {
+#pragma unroll
+            for (int u = 0; u < G::KPT; ++u) {
+                const int idx = tid + u * G::NTHR;
+                int tb, cb;
+                block_coords<DK, G::BWK>(idx < G::KB ? idx : 0, tb, cb);
+#pragma unroll
+                for (int p = 0; p < G::BWK / 2; ++p) thk[u][p] = hp.theta[cb * (G::BWK / 2) + p];
+            }
+#pragma unroll
+            for (int s = 0; s < G::KSQ; ++s)
+#pragma unroll
+                for (int p = 0; p < 4; ++p) thq[s][p] = hp.theta[s * 16 + grp * 4 + p];
+        }
+    };
+    auto rotate_key_row = [&](uint32_t (&w)[G::BWK / 2], int u, int cb, int token) __attribute__((always_inline)) {
+        if constexpr (kThetaRegs)
+            rotate_row<G::BWK>(w, thk[u], static_cast<double>(a.pos0 + token));
+        else
+            rotate_row<G::BWK>(w, hp, cb * (G::BWK / 2), static_cast<double>(a.pos0 + token));
+    };
+    auto rotate_query_unit = [&](uint4 x, int s, int token) __attribute__((always_inline)) {
+        if constexpr (kThetaRegs)
+            return rotate8_bf16(x, thq[s], static_cast<double>(a.pos0 + token));
+        else
+            return rotate8_bf16(x, hp, s * 16 + grp * 4, static_cast<double>(a.pos0 + token));
+    };
+
     // ---- pieces of the chunk loop
     // Step 7: this wave's 16 output rows of the chunk at token t0 (L valid), as bf16.
     auto store_o = [&](const f32x4 (&o)[G::NTV], int t0, int L) __attribute__((always_inline)) {
@@ -312,9 +349,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
                 block_coords<DK, G::BWK>(idx, tb, cb);
                 if (hp.has_theta) {  // rows past the end are zero: rotating them is harmless
 #pragma unroll
-                    for (int q = 0; q < 8; ++q)
-                        rotate_row<G::BWK>(krb[u].w[q], hp, cb * (G::BWK / 2),
-                                           static_cast<double>(a.pos0 + t0 + staged_token(tb, q)));
+                    for (int q = 0; q < 8; ++q) rotate_key_row(krb[u].w[q], u, cb, t0 + staged_token(tb, q));
                 }
                 float xi[8];
 #pragma unroll
@@ -390,9 +425,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
                 block_coords<DK, G::BWK>(idx, tb, cb);
                 if (hp.has_theta) {  // rows past the end are zero: rotating them is harmless
 #pragma unroll
-                    for (int q = 0; q < 8; ++q)
-                        rotate_row<G::BWK>(krb[u].w[q], hp, cb * (G::BWK / 2),
-                                           static_cast<double>(a.pos0 + t0 + staged_token(tb, q)));
+                    for (int q = 0; q < 8; ++q) rotate_key_row(krb[u].w[q], u, cb, t0 + staged_token(tb, q));
                 }
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
@@ -534,8 +567,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
             if (hp.has_theta) {  // every row: those past the end are never stored
                 const int row = rb * 16 + l16;
 #pragma unroll
-                for (int s = 0; s < G::KSQ; ++s)
-                    qfb[s] = rotate8_bf16(qfb[s], hp, s * 16 + grp * 4, static_cast<double>(a.pos0 + t0 + row));
+                for (int s = 0; s < G::KSQ; ++s) qfb[s] = rotate_query_unit(qfb[s], s, t0 + row);
             }
             __syncthreads();  // A: K^T, V^T written
 
@@ -679,8 +711,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
             if (hp.has_theta) {  // every row: those past the end are never stored
                 const int row = rb * 16 + l16;
 #pragma unroll
-                for (int s = 0; s < G::KSQ; ++s)
-                    qfb[s] = rotate8_bf16(qfb[s], hp, s * 16 + grp * 4, static_cast<double>(a.pos0 + t0 + row));
+                for (int s = 0; s < G::KSQ; ++s) qfb[s] = rotate_query_unit(qfb[s], s, t0 + row);
             }
             load_kv(kr, vr, has_next ? t1 : t0, L1, tid_it);  // past the end: a discarded re-read
             __syncthreads();  // A: keys and V''^T written
@@ -808,6 +839,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
 
     if constexpr (!SEGMENTED) {
         prefetch_first(true);
+        load_theta();
         load_state(a.state_in);
         have_state = a.state_in != nullptr;
         if (have_state) write_state_copy(l16, grp);
@@ -955,12 +987,14 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
         // ---- pass 1: this segment's own state (all segments but the last)
         if (seg < a.nseg - 1) {
             prefetch_first(false);
+            load_theta();
             load_state(seg == 0 ? a.state_in : nullptr);
             run_state_only();
             publish(sacc, seg == 0 ? f_inc : f_agg);
         }
         // ---- the start state
         prefetch_first(true);
+        if (seg == a.nseg - 1) load_theta();
         if (seg == 0) {
             load_state(a.state_in);
         } else if (seg < a.nseg - 1) {  // T_s stays in sacc while the look-back may close a group
@@ -985,6 +1019,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
             load_kv(kr, vr, t_begin, L0, tid);
             load_q(qf_keep[0], t_begin, L0);
         }
+        load_theta();
         load_state(nullptr);
         run_chunks(std::true_type{});  // sacc = T_s
         f32x4 sin[G::MT][G::NT];

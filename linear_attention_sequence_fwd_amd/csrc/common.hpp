@@ -92,18 +92,23 @@ __device__ __forceinline__ void rot_cs_fast(double position, float theta, float&
     c = __builtin_amdgcn_cosf(r);
 }
 
-// Rotate the four complex pairs held in 8 consecutive bf16 (one uint4) whose
-// first pair has frequency index j0, at absolute position `position`.
-__device__ __forceinline__ uint4 rotate8_bf16(uint4 x, const HeadParams& hp, int j0, double position) {
+// Rotate the four complex pairs held in 8 consecutive bf16 (one uint4) with
+// frequencies th[0..3], at absolute position `position`.
+__device__ __forceinline__ uint4 rotate8_bf16(uint4 x, const float* th, double position) {
     uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         float c, s;
-        rot_cs_fast(position, hp.theta[j0 + p], c, s);
+        rot_cs_fast(position, th[p], c, s);
         float re = lo_bf16(w[p]), im = hi_bf16(w[p]);
         w[p] = pack2_bf16(re * c - im * s, re * s + im * c);
     }
     return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// The same with the frequencies of pairs j0..j0+3 read from the head parameters.
+__device__ __forceinline__ uint4 rotate8_bf16(uint4 x, const HeadParams& hp, int j0, double position) {
+    return rotate8_bf16(x, hp.theta + j0, position);
 }
 
 // ---------------------------------------------------------------- launch grid

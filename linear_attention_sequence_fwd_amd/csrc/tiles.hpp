@@ -123,17 +123,23 @@ __device__ __forceinline__ uint4 block_column(const BlockRows<BW>& b, int c) {
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// Rotate the complex pairs of one staged row in place (BW/2 pairs, first
-// frequency index j0) at absolute position `position`.
+// Rotate the complex pairs of one staged row in place (BW/2 pairs with
+// frequencies th[0..BW/2-1]) at absolute position `position`.
 template <int BW>
-__device__ __forceinline__ void rotate_row(uint32_t (&w)[BW / 2], const HeadParams& hp, int j0, double position) {
+__device__ __forceinline__ void rotate_row(uint32_t (&w)[BW / 2], const float* th, double position) {
 #pragma unroll
     for (int p = 0; p < BW / 2; ++p) {
         float c, s;
-        rot_cs_fast(position, hp.theta[j0 + p], c, s);
+        rot_cs_fast(position, th[p], c, s);
         const float re = lo_bf16(w[p]), im = hi_bf16(w[p]);
         w[p] = pack2_bf16(re * c - im * s, re * s + im * c);
     }
+}
+
+// The same with the frequencies of pairs j0.. read from the head parameters.
+template <int BW>
+__device__ __forceinline__ void rotate_row(uint32_t (&w)[BW / 2], const HeadParams& hp, int j0, double position) {
+    rotate_row<BW>(w, hp.theta + j0, position);
 }
 
 // Transposing LDS read (gfx950 ds_read_b64_tr_b16). Within each group of 16
