@@ -387,6 +387,15 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
         load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR>(krb, Kg + static_cast<size_t>(t) * DK, DK, L, tid_it);
         load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR>(vrb, Vg + static_cast<size_t>(t) * a.dv, a.dv, L, tid_it);
     };
+    // Rows R0 .. R1-1 of every staging block of those loads (one chunk's loads
+    // can be spread over several points of the loop).
+    auto load_kv_rows = [&](auto& krb, auto& vrb, int t, int L, int tid_it, auto r0_tag, auto r1_tag)
+                            __attribute__((always_inline)) {
+        constexpr int R0 = decltype(r0_tag)::value, R1 = decltype(r1_tag)::value;
+        load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR, R0, R1>(krb, Kg + static_cast<size_t>(t) * DK, DK, L, tid_it);
+        load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR, R0, R1>(vrb, Vg + static_cast<size_t>(t) * a.dv, a.dv, L,
+                                                                tid_it);
+    };
     // Step 3 (G4): S = gamma^L S + Kx^T V on this wave's tiles.
     auto g4 = [&](int L, int l16c, int grpc) __attribute__((always_inline)) {
         const float gL = (L == C) ? gC : fast_exp2(static_cast<float>(L) * lg2f);  // no float64 in the loop
@@ -713,7 +722,16 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
 #pragma unroll
                 for (int s = 0; s < G::KSQ; ++s) qfb[s] = rotate_query_unit(qfb[s], s, t0 + row);
             }
-            load_kv(kr, vr, has_next ? t1 : t0, L1, tid_it);  // past the end: a discarded re-read
+            // The next chunk's keys and values are fetched in three parts (half
+            // now, a quarter before G1, a quarter with the queries after G1):
+            // every workgroup reaches this point at about the same time, and
+            // spreading the requests over the chunk keeps them from queueing
+            // behind one another (past the end: discarded re-reads).
+            using I0 = std::integral_constant<int, 0>;
+            using I4 = std::integral_constant<int, 4>;
+            using I6 = std::integral_constant<int, 6>;
+            using I8 = std::integral_constant<int, 8>;
+            load_kv_rows(kr, vr, has_next ? t1 : t0, L1, tid_it, I0{}, I4{});
             __syncthreads();  // A: keys and V''^T written
 
             // ---- 2. G3: O^T = S^T Q^T (the previous chunk's state)
@@ -732,6 +750,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
                 }
             }
 
+            load_kv_rows(kr, vr, has_next ? t1 : t0, L1, tid_it, I4{}, I6{});
             // ---- 3. G1: P^T = K Q^T, causal mask on the diagonal tile only (the
             //         decay is carried by V'' and the final gamma^(i+1))
             uint4 pf[G::KST];
@@ -765,6 +784,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
                 }
             }
             load_q(qnext, has_next ? t1 : t0, L1);  // queries are dead for this chunk now
+            load_kv_rows(kr, vr, has_next ? t1 : t0, L1, tid_it, I6{}, I8{});
 
             // ---- 4. G2: O^T += V''^T P^T
             {

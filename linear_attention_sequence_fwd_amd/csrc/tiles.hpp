@@ -80,7 +80,9 @@ struct BlockRows {
 // in-bounds row and are zeroed by a select): with no branch around a load the
 // compiler can count outstanding loads exactly, and a wait for one batch does
 // not also wait for a prefetch issued after it. valid == 0 reads row 0.
-template <int D, int BW, int NBLK, int PT, int NTHR>
+// Q0..Q1-1: the rows of each block to load (all eight by default), so a caller
+// can spread one chunk's loads over several points of its loop.
+template <int D, int BW, int NBLK, int PT, int NTHR, int Q0 = 0, int Q1 = 8>
 __device__ __forceinline__ void load_blocks(BlockRows<BW> (&r)[PT], const u16* base, int ld, int valid, int tid) {
     // Row pointers are wave-uniform (base + row * ld); the per-lane part is a
     // 32-bit byte offset, so each row load needs one shared offset register
@@ -94,7 +96,7 @@ __device__ __forceinline__ void load_blocks(BlockRows<BW> (&r)[PT], const u16* b
         block_coords<D, BW>(in_blk ? idx : 0, tb, cb);
         const int tok0 = staged_token(tb, 0);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = Q0; q < Q1; ++q) {
             const int dq = staged_token(0, q);  // token offset of row q inside the block
             const bool ok = in_blk && tok0 + dq < valid;
             const int row = min(tok0 + dq, last);
