@@ -173,6 +173,26 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     const int l16 = lane & 15;
     const int grp = lane >> 4;
 
+    // Rotation frequencies this thread applies (kernels with 64-token chunks,
+    // see rotate_key_row): read before anything else, so the round trip to the
+    // kernel arguments hides under the ticket and the first chunk's loads.
+    constexpr bool kThetaRegs = C == 64;
+    float thk[G::KPT][G::BWK / 2], thq[G::KSQ][4];
+    if (kThetaRegs && hp.has_theta) {
+#pragma unroll
+        for (int u = 0; u < G::KPT; ++u) {
+            const int idx = tid + u * G::NTHR;
+            int tb, cb;
+            block_coords<DK, G::BWK>(idx < G::KB ? idx : 0, tb, cb);
+#pragma unroll
+            for (int p = 0; p < G::BWK / 2; ++p) thk[u][p] = hp.theta[cb * (G::BWK / 2) + p];
+        }
+#pragma unroll
+        for (int s = 0; s < G::KSQ; ++s)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) thq[s][p] = hp.theta[s * 16 + grp * 4 + p];
+    }
+
     // ---- which (batch*head, value tile) chain and segment this workgroup owns
     int chain, seg = 0;
     unsigned gen = 0;
@@ -288,41 +308,63 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     const float gC = gamma_pow(lg2, C);
     bool have_state = false;
 
-    // Rotation frequencies this thread applies: its key staging columns and
-    // its query units. 64-token chunk kernels have registers to spare and hold
-    // them for the whole segment (read once, after the first chunk's loads are
-    // on their way); the others read them at each stage (one batch of loads
-    // from the kernel arguments).
-    constexpr bool kThetaRegs = C == 64;
-    float thk[G::KPT][G::BWK / 2];
-    float thq[G::KSQ][4];
-    auto load_theta = [&]() __attribute__((always_inline)) {
-        if (kThetaRegs && hp.has_theta) {
+    // Rotation of this thread's key staging columns and query units. Kernels
+    // with 64-token chunks hold the frequencies in registers (thk, thq, loaded
+    // at the start) and rotate by angle addition: once per chunk, the angle of
+    // the chunk's first position is reduced in float64 (b = frac(t0 w), in
+    // revolutions, w = theta / 2 pi); each row at offset k then turns by
+    // b + k w, formed and reduced in float32 (|k w| < 11 revolutions, error
+    // ~1e-6 rad), so the per-row work has no float64. The other kernels reduce
+    // each row's angle in float64 (their registers are short).
+    float bk[G::KPT][G::BWK / 2], bq[G::KSQ][4];
+    constexpr float kInvTwoPiF = 0.15915494309189533577f;
+    // the chunk's base angles (position pos0 + t0), once per chunk
+    auto theta_bases = [&](int t0) __attribute__((always_inline)) {
+        if constexpr (kThetaRegs) {
+            constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
+            const double p0 = static_cast<double>(a.pos0 + t0);
+            auto frac = [&](float th) __attribute__((always_inline)) {
+                const double x = p0 * (static_cast<double>(th) * kInvTwoPi);
+                return static_cast<float>(x - rint(x));
+            };
 #pragma unroll
-            for (int u = 0; u < G::KPT; ++u) {
-                const int idx = tid + u * G::NTHR;
-                int tb, cb;
-                block_coords<DK, G::BWK>(idx < G::KB ? idx : 0, tb, cb);
+            for (int u = 0; u < G::KPT; ++u)
 #pragma unroll
-                for (int p = 0; p < G::BWK / 2; ++p) thk[u][p] = hp.theta[cb * (G::BWK / 2) + p];
-            }
+                for (int p = 0; p < G::BWK / 2; ++p) bk[u][p] = frac(thk[u][p]);
 #pragma unroll
             for (int s = 0; s < G::KSQ; ++s)
 #pragma unroll
-                for (int p = 0; p < 4; ++p) thq[s][p] = hp.theta[s * 16 + grp * 4 + p];
+                for (int p = 0; p < 4; ++p) bq[s][p] = frac(thq[s][p]);
         }
     };
-    auto rotate_key_row = [&](uint32_t (&w)[G::BWK / 2], int u, int cb, int token) __attribute__((always_inline)) {
-        if constexpr (kThetaRegs)
-            rotate_row<G::BWK>(w, thk[u], static_cast<double>(a.pos0 + token));
-        else
-            rotate_row<G::BWK>(w, hp, cb * (G::BWK / 2), static_cast<double>(a.pos0 + token));
+    // rotate the pairs of x by revolutions base[p] + k step[p]
+    auto rotate_pairs_rev = [&](uint32_t* w, int n, const float* base, const float* th, float k)
+                                __attribute__((always_inline)) {
+#pragma unroll
+        for (int p = 0; p < n; ++p) {
+            float r = fmaf(k, th[p] * kInvTwoPiF, base[p]);
+            r -= rintf(r);
+            const float sn = __builtin_amdgcn_sinf(r), cs = __builtin_amdgcn_cosf(r);
+            const float re = lo_bf16(w[p]), im = hi_bf16(w[p]);
+            w[p] = pack2_bf16(re * cs - im * sn, re * sn + im * cs);
+        }
     };
-    auto rotate_query_unit = [&](uint4 x, int s, int token) __attribute__((always_inline)) {
+    // key row at token t0 + k of staging block u (columns of block column cb)
+    auto rotate_key_row = [&](uint32_t (&w)[G::BWK / 2], int u, int cb, int t0, int k) __attribute__((always_inline)) {
         if constexpr (kThetaRegs)
-            return rotate8_bf16(x, thq[s], static_cast<double>(a.pos0 + token));
+            rotate_pairs_rev(w, G::BWK / 2, bk[u], thk[u], static_cast<float>(k));
         else
-            return rotate8_bf16(x, hp, s * 16 + grp * 4, static_cast<double>(a.pos0 + token));
+            rotate_row<G::BWK>(w, hp, cb * (G::BWK / 2), static_cast<double>(a.pos0 + t0 + k));
+    };
+    // query unit s (8 bf16 = 4 pairs) of the row at token t0 + k
+    auto rotate_query_unit = [&](uint4 x, int s, int t0, int k) __attribute__((always_inline)) {
+        if constexpr (kThetaRegs) {
+            uint32_t w[4] = {x.x, x.y, x.z, x.w};
+            rotate_pairs_rev(w, 4, bq[s], thq[s], static_cast<float>(k));
+            return make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+            return rotate8_bf16(x, hp, s * 16 + grp * 4, static_cast<double>(a.pos0 + t0 + k));
+        }
     };
 
     // ---- pieces of the chunk loop
@@ -341,6 +383,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     };
     // Step 1: rotate the chunk's keys; K^T (scaled by xi) and V^T into LDS.
     auto stage_kv = [&](auto& krb, auto& vrb, int t0, int L, int tid_it, float lg2c) __attribute__((always_inline)) {
+        if (hp.has_theta) theta_bases(t0);  // also used by the queries of this chunk
 #pragma unroll
         for (int u = 0; u < G::KPT; ++u) {
             const int idx = tid_it + u * G::NTHR;
@@ -349,7 +392,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
                 block_coords<DK, G::BWK>(idx, tb, cb);
                 if (hp.has_theta) {  // rows past the end are zero: rotating them is harmless
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) rotate_key_row(krb[u].w[q], u, cb, t0 + staged_token(tb, q));
+                    for (int q = 0; q < 8; ++q) rotate_key_row(krb[u].w[q], u, cb, t0, staged_token(tb, q));
                 }
                 float xi[8];
 #pragma unroll
@@ -426,6 +469,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     // ---- the FAST form's pieces (see the kernel comment): keys row-major only,
     //      values scaled by gamma^-(j+1) on their way into V''^T.
     auto stage_fast = [&](auto& krb, auto& vrb, int t0, int L, int tid_it, float lg2c) __attribute__((always_inline)) {
+        if (hp.has_theta) theta_bases(t0);  // also used by the queries of this chunk
 #pragma unroll
         for (int u = 0; u < G::KPT; ++u) {
             const int idx = tid_it + u * G::NTHR;
@@ -434,7 +478,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
                 block_coords<DK, G::BWK>(idx, tb, cb);
                 if (hp.has_theta) {  // rows past the end are zero: rotating them is harmless
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) rotate_key_row(krb[u].w[q], u, cb, t0 + staged_token(tb, q));
+                    for (int q = 0; q < 8; ++q) rotate_key_row(krb[u].w[q], u, cb, t0, staged_token(tb, q));
                 }
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
@@ -571,14 +615,15 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
             const int t1 = t0 + C;
             const int L1 = has_next ? min(C, t_end - t1) : 0;
 
-            // ---- 1. K^T (scaled by xi) and V^T into LDS; rotate queries
+            // ---- 1. K^T (scaled by xi) and V^T into LDS
             stage_kv(kr, vr, t0, L, tid_it, lg2c);
+            __syncthreads();  // A: K^T, V^T written
+            // rotate the queries (after the barrier: their loads land under the staging)
             if (hp.has_theta) {  // every row: those past the end are never stored
                 const int row = rb * 16 + l16;
 #pragma unroll
-                for (int s = 0; s < G::KSQ; ++s) qfb[s] = rotate_query_unit(qfb[s], s, t0 + row);
+                for (int s = 0; s < G::KSQ; ++s) qfb[s] = rotate_query_unit(qfb[s], s, t0, row);
             }
-            __syncthreads();  // A: K^T, V^T written
 
             // ---- 2. G3: O^T = S^T Q^T with the previous chunk's state, times zeta
             f32x4 oacc[G::NTV];
@@ -715,13 +760,8 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
             const int t1 = t0 + C;
             const int L1 = has_next ? min(C, t_end - t1) : 0;
 
-            // ---- 1. keys row-major, V''^T into LDS; rotate queries; fetch the next chunk
+            // ---- 1. keys row-major, V''^T into LDS; fetch the next chunk
             stage_fast(kr, vr, t0, L, tid_it, lg2c);
-            if (hp.has_theta) {  // every row: those past the end are never stored
-                const int row = rb * 16 + l16;
-#pragma unroll
-                for (int s = 0; s < G::KSQ; ++s) qfb[s] = rotate_query_unit(qfb[s], s, t0 + row);
-            }
             // The next chunk's keys and values are fetched in three parts (half
             // now, a quarter before G1, a quarter with the queries after G1):
             // every workgroup reaches this point at about the same time, and
@@ -733,6 +773,12 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
             using I8 = std::integral_constant<int, 8>;
             load_kv_rows(kr, vr, has_next ? t1 : t0, L1, tid_it, I0{}, I4{});
             __syncthreads();  // A: keys and V''^T written
+            // rotate the queries (after the barrier: their loads land under the staging)
+            if (hp.has_theta) {  // every row: those past the end are never stored
+                const int row = rb * 16 + l16;
+#pragma unroll
+                for (int s = 0; s < G::KSQ; ++s) qfb[s] = rotate_query_unit(qfb[s], s, t0, row);
+            }
 
             // ---- 2. G3: O^T = S^T Q^T (the previous chunk's state)
             f32x4 oacc[G::NTV];
@@ -740,10 +786,11 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
             for (int nt = 0; nt < G::NTV; ++nt) oacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (have_state) {
                 const FragAddr<UK> fa_s(l16c, grpc);  // S^T rows 16 nt + l16, dk 32 s + 8 grp
+                // (s outer: consecutive MFMAs go to different accumulators)
 #pragma unroll
-                for (int nt = 0; nt < G::NTV; ++nt) {
+                for (int s = 0; s < G::KSQ; ++s) {
 #pragma unroll
-                    for (int s = 0; s < G::KSQ; ++s) {
+                    for (int nt = 0; nt < G::NTV; ++nt) {
                         const uint4 af = *reinterpret_cast<const uint4*>(&sbuf[fa_s.at(nt, s)]);
                         oacc[nt] = mfma16x16x32(af, qfb[s], oacc[nt]);
                     }
@@ -859,7 +906,6 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
 
     if constexpr (!SEGMENTED) {
         prefetch_first(true);
-        load_theta();
         load_state(a.state_in);
         have_state = a.state_in != nullptr;
         if (have_state) write_state_copy(l16, grp);
@@ -1007,14 +1053,12 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
         // ---- pass 1: this segment's own state (all segments but the last)
         if (seg < a.nseg - 1) {
             prefetch_first(false);
-            load_theta();
-            load_state(seg == 0 ? a.state_in : nullptr);
+                load_state(seg == 0 ? a.state_in : nullptr);
             run_state_only();
             publish(sacc, seg == 0 ? f_inc : f_agg);
         }
         // ---- the start state
         prefetch_first(true);
-        if (seg == a.nseg - 1) load_theta();
         if (seg == 0) {
             load_state(a.state_in);
         } else if (seg < a.nseg - 1) {  // T_s stays in sacc while the look-back may close a group
@@ -1039,7 +1083,6 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
             load_kv(kr, vr, t_begin, L0, tid);
             load_q(qf_keep[0], t_begin, L0);
         }
-        load_theta();
         load_state(nullptr);
         run_chunks(std::true_type{});  // sacc = T_s
         f32x4 sin[G::MT][G::NT];
