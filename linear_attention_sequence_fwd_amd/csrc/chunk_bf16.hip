@@ -80,10 +80,21 @@ struct ChunkGeo {
     static constexpr int VB = (C / 8) * (DVT / BWV);  // value staging blocks per chunk
     static constexpr int KPT = (KB + NTHR - 1) / NTHR;
     static constexpr int VPT = (VB + NTHR - 1) / NTHR;
+    // When the key and value blocks together need no more than one block per
+    // thread, the value blocks go to the threads the key blocks leave free
+    // (threads VOFF..), so staging work is spread over every wave.
+    static constexpr int VOFF = (KB + VB <= NTHR) ? KB : 0;
     static_assert(C == 64 || C == 128, "chunk");
     static_assert(DK % 64 == 0 && DVT % 64 == 0, "tile sizes");
     static_assert(MG * MT == TM && NG * NT == NTV, "state split");
 };
+
+// Index of thread t among the value-staging threads (see ChunkGeo::VOFF);
+// threads without a value block get an index >= VB.
+template <typename G>
+__device__ __forceinline__ int value_thread(int t) {
+    return t >= G::VOFF ? t - G::VOFF : t + G::NTHR - G::VOFF;
+}
 
 // Row block owned by wave w: waves w and w + NW/2 (which the dispatcher puts
 // on the same SIMD) get blocks b and NW-1-b, so the causal work per SIMD is
@@ -256,7 +267,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
         const int L0 = min(C, t_end - t_begin);
         load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR>(kr, Kg + static_cast<size_t>(t_begin) * DK, DK, L0, tid);
         load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR>(vr, Vg + static_cast<size_t>(t_begin) * a.dv, a.dv, L0,
-                                                          tid);
+                                                          value_thread<G>(tid));
         if (with_q) load_q(qf, t_begin, L0);
     };
     // this head's state from a caller's [B*H][dk][dv] float32 array, or zeros
@@ -412,7 +423,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
         }
 #pragma unroll
         for (int u = 0; u < G::VPT; ++u) {
-            const int idx = tid_it + u * G::NTHR;
+            const int idx = value_thread<G>(tid_it) + u * G::NTHR;
             if (idx < G::VB) {
                 int tb, cb;
                 block_coords<DVT, G::BWV>(idx, tb, cb);
@@ -428,7 +439,8 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     // in registers across the loop).
     auto load_kv = [&](auto& krb, auto& vrb, int t, int L, int tid_it) __attribute__((always_inline)) {
         load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR>(krb, Kg + static_cast<size_t>(t) * DK, DK, L, tid_it);
-        load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR>(vrb, Vg + static_cast<size_t>(t) * a.dv, a.dv, L, tid_it);
+        load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR>(vrb, Vg + static_cast<size_t>(t) * a.dv, a.dv, L,
+                                                          value_thread<G>(tid_it));
     };
     // Rows R0 .. R1-1 of every staging block of those loads (one chunk's loads
     // can be spread over several points of the loop).
@@ -437,7 +449,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
         constexpr int R0 = decltype(r0_tag)::value, R1 = decltype(r1_tag)::value;
         load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR, R0, R1>(krb, Kg + static_cast<size_t>(t) * DK, DK, L, tid_it);
         load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR, R0, R1>(vrb, Vg + static_cast<size_t>(t) * a.dv, a.dv, L,
-                                                                tid_it);
+                                                                value_thread<G>(tid_it));
     };
     // Step 3 (G4): S = gamma^L S + Kx^T V on this wave's tiles.
     auto g4 = [&](int L, int l16c, int grpc) __attribute__((always_inline)) {
@@ -495,7 +507,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
         }
 #pragma unroll
         for (int u = 0; u < G::VPT; ++u) {
-            const int idx = tid_it + u * G::NTHR;
+            const int idx = value_thread<G>(tid_it) + u * G::NTHR;
             if (idx < G::VB) {
                 int tb, cb;
                 block_coords<DVT, G::BWV>(idx, tb, cb);
