@@ -242,6 +242,51 @@ def test_recurrent_step_max_shapes(dtype, B, H, dk, dv, rot):
     assert_close(to64(state), S, tol, "final state")
 
 
+@pytest.mark.parametrize("pos0", [1_000_000_007, 3 * 2**31 + 5])
+@pytest.mark.parametrize("B,H,N,dk,dv,C,seg", [
+    (2, 2, 200, 64, 64, 64, 0),     # 64-token chunks: angle addition, segments of two chunks
+    (1, 1, 130, 64, 64, 64, 1),     # 64-token chunks, one segment
+    (1, 2, 300, 128, 128, 128, 0),  # 128-token chunks: per-row float64 reduction
+])
+def test_rotation_far_positions(pos0, B, H, N, dk, dv, C, seg):
+    """Absolute positions far from zero: the rotation angles must still match the
+    oracle's float64 angles (the bf16 kernels reduce the chunk's base angle in
+    float64 and add in-chunk offsets in float32)."""
+    q, k, v = _inputs(B, H, N, dk, dv, torch.bfloat16, seed=N + 7)
+    theta = W.rotary_theta(dk)
+    ref, ref_s = orc.recurrent(to64(q), to64(k), to64(v), orc.head_gammas(H), theta=to64(theta), pos0=pos0)
+    o, st = R.retention_chunkwise_fwd(q.to(DEV), k.to(DEV), v.to(DEV), chunk=C, theta=theta, pos0=pos0,
+                                      return_state=True, segments=seg)
+    ref_p = orc.parallel(to64(q), to64(k), to64(v), orc.head_gammas(H), theta=to64(theta), pos0=pos0)
+    o_par = R.retention_parallel_fwd(q.to(DEV), k.to(DEV), v.to(DEV), theta=theta, pos0=pos0)
+    torch.cuda.synchronize()
+    assert_close(to64(o), ref, BF16_TOL, "chunkwise O")
+    assert_close(to64(st), ref_s, BF16_TOL, "chunkwise state")
+    assert_close(to64(o_par), ref_p, BF16_TOL, "parallel O")
+
+
+def test_rotation_far_positions_decode_and_f32():
+    pos0 = 1_000_000_007
+    B, H, dk, dv = 2, 2, 64, 64
+    s0, qs, ks, vs = W.make_decode(B, H, dk, dv, torch.float32, 2, 0.01, seed=3)
+    theta = W.rotary_theta(dk)
+    pos = torch.tensor([pos0, 3 * 2**31 + 5], dtype=torch.int64)
+    S = to64(s0)
+    state = s0.to(DEV)
+    for t in range(2):
+        o_ref, S = orc.decode_step(to64(qs[t]), to64(ks[t]), to64(vs[t]), S, orc.head_gammas(H),
+                                   theta=to64(theta), pos=(pos + t).numpy())
+        o = R.retention_recurrent_step(qs[t].to(DEV), ks[t].to(DEV), vs[t].to(DEV), state, theta=theta,
+                                       pos=(pos + t).to(DEV))
+        torch.cuda.synchronize()
+        assert_close(to64(o), o_ref, F32_TOL, f"decode o step {t}")
+    q, k, v = _inputs(1, 2, 150, 64, 64, torch.float32, seed=5)
+    ref, _ = orc.recurrent(to64(q), to64(k), to64(v), orc.head_gammas(2), theta=to64(theta), pos0=pos0)
+    o = R.retention_chunkwise_fwd(q.to(DEV), k.to(DEV), v.to(DEV), chunk=64, theta=theta, pos0=pos0)
+    torch.cuda.synchronize()
+    assert_close(to64(o), ref, F32_TOL, "f32 chunkwise O")
+
+
 def test_oversize_requests_rejected():
     q, k, v = _inputs(1, 129, 8, 64, 64, torch.bfloat16, seed=1)
     with pytest.raises(RuntimeError):
