@@ -1065,7 +1065,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
         // ---- pass 1: this segment's own state (all segments but the last)
         if (seg < a.nseg - 1) {
             prefetch_first(false);
-                load_state(seg == 0 ? a.state_in : nullptr);
+            load_state(seg == 0 ? a.state_in : nullptr);
             run_state_only();
             publish(sacc, seg == 0 ? f_inc : f_agg);
         }
