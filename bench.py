@@ -268,6 +268,35 @@ def run_only(name, steps, warmup, dev):
     print(json.dumps({"workload": key, "ms_per_call": ms, "steps": steps}))
 
 
+def sweep_decode_batch(dev):
+    """Decode step latency against the number of sequences (H=16, 256x512 fp32
+    state per head, bf16 q/k/v): one JSON line per batch size."""
+    import torch
+
+    import linear_attention_sequence_fwd_amd as R
+    from linear_attention_sequence_fwd_amd import workloads as W
+
+    H, dk, dv = 16, 256, 512
+    for B in (1, 2, 4, 8, 16, 32, 64, 128, 256):
+        s0, qs, ks, vs = W.make_decode(B, H, dk, dv, torch.bfloat16, 8, 0.01, seed=B, device=dev)
+        o = torch.empty((B, H, dv), dtype=torch.bfloat16, device=dev)
+        it = [0]
+
+        def fn():
+            t = it[0] % 8
+            it[0] += 1
+            R.retention_recurrent_step(qs[t], ks[t], vs[t], s0, out=o)
+
+        ms, spread = time_graph(fn, 100, 10)
+        by = decode_alg_bytes(B, H, dk, dv)
+        print(json.dumps({"sweep": "decode_batch", "B": B, "H": H, "dk": dk, "dv": dv, "ms_per_step": ms,
+                          "ms_per_step_spread": spread, "state_updates_per_s": B * H / (ms * 1e-3),
+                          "gbs": by / (ms * 1e-3) / 1e9, "hbm_frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}),
+              flush=True)
+        del s0, qs, ks, vs, o
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -277,6 +306,7 @@ def main():
     ap.add_argument("--only", choices=["msr", "layer7b", "decode", "longctx", "single", "copy"],
                     help="time one workload only (no CPU baseline); for profilers")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--sweep", choices=["decode-batch"], help="print one JSON line per point of a sweep")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
@@ -293,6 +323,9 @@ def main():
     dev = "cuda:0"
     if args.only:
         run_only(args.only, args.steps, args.warmup, dev)
+        return
+    if args.sweep == "decode-batch":
+        sweep_decode_batch(dev)
         return
 
     # ---------------- main workload

@@ -300,6 +300,7 @@ ret_status_t retention_recurrent_step(const void* q, const void* k, const void* 
     a.dk = dk;
     a.dv = dv;
     a.bf16 = dtype == RET_BF16;
+    a.ntile = ret::recurrent_step_tiles(B, H, dv);
     const hipError_t e = ret::launch_recurrent_step(a, hp, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? RET_OK : RET_ERR_HIP;
 }

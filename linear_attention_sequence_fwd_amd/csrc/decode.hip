@@ -7,9 +7,13 @@
 // is bound by HBM: each state element is read once and written once with
 // 16-byte non-temporal accesses (the state of a large batch does not fit in
 // the caches, and keeping it out of them leaves room for q, k, v). One
-// workgroup owns one (sequence, head); a row of the state is covered by
-// d_v/4 consecutive threads, so a wavefront streams 1 KiB contiguous per
-// access, and each thread keeps 16 rows of loads in flight. The output row o = q S' is accumulated per thread over its rows and
+// workgroup owns one (sequence, head) and a tile of the state's columns: the
+// whole row width when there are enough (sequence, head) pairs to fill the
+// chip, else d_v is split into tiles of at least 64 columns so that small
+// batches still spread over the compute units (the columns of S' and o are
+// independent, so tiles need no combining). A row of the tile is covered by
+// tile/4 consecutive threads and each thread keeps UNROLL rows of loads in
+// flight. The output o = q S' is accumulated per thread over its rows and
 // reduced across row groups in LDS.
 
 #include "common.hpp"
@@ -38,7 +42,8 @@ __global__ __launch_bounds__(kStepThreads) void recurrent_step_kernel(StepArgs a
     __shared__ float ks[kStepMaxDk];
     __shared__ f32v4 red[kStepThreads];
 
-    const int bh = blockIdx.x;
+    const int bh = blockIdx.x / a.ntile;
+    const int c0 = (blockIdx.x % a.ntile) * (a.dv / a.ntile);  // first column of this tile
     const int b = bh / a.H;
     const int h = bh % a.H;
     const int tid = threadIdx.x;
@@ -66,18 +71,18 @@ __global__ __launch_bounds__(kStepThreads) void recurrent_step_kernel(StepArgs a
     }
     __syncthreads();
 
-    // ---- stream the state: thread (rg, c4) owns columns 4*c4..4*c4+3 of rows rg, rg+RG, ...
-    const int tpr = a.dv / 4;
+    // ---- stream the tile: thread (rg, c4) owns columns c0+4*c4..+3 of rows rg, rg+RG, ...
+    const int tpr = a.dv / a.ntile / 4;
     const int rgs = kStepThreads / tpr;
     const int rg = tid / tpr;
     const int c4 = tid % tpr;
     f32v4 acc = {0.f, 0.f, 0.f, 0.f};
     if (rg < rgs) {
-        const size_t v0 = static_cast<size_t>(bh) * a.dv + 4 * c4;
+        const size_t v0 = static_cast<size_t>(bh) * a.dv + c0 + 4 * c4;
         const f32v4 vv = {load_elem<BF16>(a.v, v0), load_elem<BF16>(a.v, v0 + 1), load_elem<BF16>(a.v, v0 + 2),
                           load_elem<BF16>(a.v, v0 + 3)};
-        f32v4* S = reinterpret_cast<f32v4*>(a.state + static_cast<size_t>(bh) * a.dk * a.dv) + c4;
-        const size_t row_stride = static_cast<size_t>(tpr);
+        f32v4* S = reinterpret_cast<f32v4*>(a.state + static_cast<size_t>(bh) * a.dk * a.dv + c0) + c4;
+        const size_t row_stride = static_cast<size_t>(a.dv / 4);
         int i = rg;
         for (; i + (UNROLL - 1) * rgs < a.dk; i += UNROLL * rgs) {
             f32v4 s[UNROLL];
@@ -106,7 +111,7 @@ __global__ __launch_bounds__(kStepThreads) void recurrent_step_kernel(StepArgs a
     if (tid < tpr) {
         f32v4 o = red[tid];
         for (int g = 1; g < rgs; ++g) o += red[g * tpr + tid];
-        const size_t o0 = static_cast<size_t>(bh) * a.dv + 4 * tid;
+        const size_t o0 = static_cast<size_t>(bh) * a.dv + c0 + 4 * tid;
         if (BF16) {
             u16* op = static_cast<u16*>(a.o) + o0;
             *reinterpret_cast<uint2*>(op) = make_uint2(pack2_bf16(o[0], o[1]), pack2_bf16(o[2], o[3]));
@@ -116,13 +121,32 @@ __global__ __launch_bounds__(kStepThreads) void recurrent_step_kernel(StepArgs a
     }
 }
 
+// Column tiles per (sequence, head): halve the tile while there are fewer
+// than 512 workgroups and the halves keep at least 64 columns.
+int recurrent_step_tiles(int B, int H, int dv) {
+    int nt = 1;
+    while (static_cast<long long>(B) * H * nt < 512 && (dv / nt) % 128 == 0) nt *= 2;
+    return nt;
+}
+
 hipError_t launch_recurrent_step(const StepArgs& a, const HeadParams& hp, hipStream_t st) {
-    if (a.dk > kStepMaxDk || a.dv % 4 != 0 || a.dv / 4 > kStepThreads) return hipErrorInvalidValue;
-    dim3 grid(a.B * a.H), block(kStepThreads);
-    if (a.bf16)
-        recurrent_step_kernel<true, kStepUnroll><<<grid, block, 0, st>>>(a, hp);
-    else
-        recurrent_step_kernel<false, kStepUnroll><<<grid, block, 0, st>>>(a, hp);
+    if (a.dk > kStepMaxDk || a.dv % 4 != 0 || a.ntile < 1 || a.dv % (4 * a.ntile) != 0 ||
+        a.dv / a.ntile / 4 > kStepThreads)
+        return hipErrorInvalidValue;
+    dim3 grid(a.B * a.H * a.ntile), block(kStepThreads);
+    // narrow tiles have more row groups per workgroup and so fewer rows per thread
+    const bool narrow = a.ntile > 1;
+    if (a.bf16) {
+        if (narrow)
+            recurrent_step_kernel<true, kStepUnroll / 2><<<grid, block, 0, st>>>(a, hp);
+        else
+            recurrent_step_kernel<true, kStepUnroll><<<grid, block, 0, st>>>(a, hp);
+    } else {
+        if (narrow)
+            recurrent_step_kernel<false, kStepUnroll / 2><<<grid, block, 0, st>>>(a, hp);
+        else
+            recurrent_step_kernel<false, kStepUnroll><<<grid, block, 0, st>>>(a, hp);
+    }
     return hipGetLastError();
 }
 

@@ -53,6 +53,7 @@ struct StepArgs {
     const int64_t* pos;
     int B, H, dk, dv;
     int bf16;
+    int ntile;  // column tiles per (sequence, head), see recurrent_step_tiles
 };
 
 // Optional timing hook: when ev is not null it holds six events, a start/stop
@@ -65,6 +66,7 @@ hipError_t launch_chunk_f32(const ChunkArgs& a, const HeadParams& hp, int dvt, h
 hipError_t launch_parallel_bf16(const ParallelArgs& a, const HeadParams& hp, int dvt, hipStream_t st);
 hipError_t launch_parallel_f32(const ParallelArgs& a, const HeadParams& hp, int dvt, hipStream_t st);
 hipError_t launch_recurrent_step(const StepArgs& a, const HeadParams& hp, hipStream_t st);
+int recurrent_step_tiles(int B, int H, int dv);
 hipError_t launch_segment_scan(const ChunkArgs& a, const HeadParams& hp, hipStream_t st, hipEvent_t* ev);
 
 // Launch `kernel` with the given configuration; with events, bracket its

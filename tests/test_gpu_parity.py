@@ -242,6 +242,32 @@ def test_recurrent_step_max_shapes(dtype, B, H, dk, dv, rot):
     assert_close(to64(state), S, tol, "final state")
 
 
+@pytest.mark.parametrize("dtype,B,H,dk,dv,rot", [
+    (torch.bfloat16, 1, 2, 128, 512, True),    # 2 (sequence, head) pairs: 8 column tiles of 64
+    (torch.bfloat16, 3, 5, 256, 256, False),   # 15 pairs: 4 tiles of 64
+    (torch.float32, 2, 1, 64, 384, True),      # 384 = 3 x 128: 2 tiles of 192 columns
+])
+def test_recurrent_step_column_tiles(dtype, B, H, dk, dv, rot):
+    """Small batches split each state's columns over several workgroups."""
+    steps = 4
+    s0, qs, ks, vs = W.make_decode(B, H, dk, dv, dtype, steps, 0.01, seed=dv + B)
+    theta = W.rotary_theta(dk) if rot else None
+    pos = torch.arange(B, dtype=torch.int64) * 97 + 11
+    g = orc.head_gammas(H)
+    S = to64(s0)
+    state = s0.to(DEV)
+    tol = BF16_TOL if dtype == torch.bfloat16 else F32_TOL
+    for t in range(steps):
+        o_ref, S = orc.decode_step(to64(qs[t]), to64(ks[t]), to64(vs[t]), S, g,
+                                   theta=None if theta is None else to64(theta),
+                                   pos=(pos + t).numpy() if rot else None)
+        o = R.retention_recurrent_step(qs[t].to(DEV), ks[t].to(DEV), vs[t].to(DEV), state, theta=theta,
+                                       pos=(pos + t).to(DEV) if rot else None)
+        torch.cuda.synchronize()
+        assert_close(to64(o), o_ref, tol, f"o step {t}")
+    assert_close(to64(state), S, tol, "final state")
+
+
 @pytest.mark.parametrize("pos0", [1_000_000_007, 3 * 2**31 + 5])
 @pytest.mark.parametrize("B,H,N,dk,dv,C,seg", [
     (2, 2, 200, 64, 64, 64, 0),     # 64-token chunks: angle addition, segments of two chunks
