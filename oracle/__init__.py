@@ -3,6 +3,7 @@ imported by the tests, the smoke check and the benchmark's CPU-baseline leg,
 never by the product path."""
 
 from .retention import (  # noqa: F401
+    backward,
     chunkwise,
     decay_matrix,
     decode_step,

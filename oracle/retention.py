@@ -40,7 +40,9 @@ Readings taken where the pages are silent, ambiguous or defective:
 
 Parity status: every public function here is pinned by tests that do not
 restate it (hand-worked values, the decay widget's printed gamma and
-half-life, cross-form agreement, textbook special cases, invariants). The
+half-life, cross-form agreement, textbook special cases, invariants; the
+backward by hand-worked values, finite differences, which are exact here
+because the loss is affine in each single input entry, and homogeneity). The
 adjacent-pair rotation convention is a documented choice, not something a
 printed value decides.
 """
@@ -57,6 +59,7 @@ __all__ = [
     "chunkwise",
     "segmented",
     "decode_step",
+    "backward",
 ]
 
 
@@ -266,3 +269,60 @@ def decode_step(q, k, v, state, gammas, theta=None, pos=None):
     S = g * _as64(state) + k[:, :, :, None] * v[:, :, None, :]
     o = np.einsum("bhi,bhij->bhj", q, S)
     return o, S
+
+
+def backward(q, k, v, d_o, gammas, theta=None, pos0=0, state0=None, d_state=None):
+    """Gradients of one retention call with respect to all of its inputs.
+
+    The call is the one `recurrent` computes: O [B, H, N, dv] and the final
+    state S_N [B, H, dk, dv] from q, k [B, H, N, dk], v [B, H, N, dv] and the
+    initial state state0 (None = zeros). Given the gradients d_o of O and
+    d_state of S_N (None = zeros), returns (dq, dk, dv, d_state0).
+
+    Training evaluates the whole sequence at once in the parallel form ("RetNet
+    Guide" section "1. The Parallel Representation for High-Throughput
+    Pretraining"; "Retentive Networks (RetNet)" (krlt), "At a glance": training
+    parallel over the sequence), so its backward is that of the parallel form.
+    Per head, with Q', K' the rotated rows, D the decay matrix,
+    Z_n = gamma^(n+1) and Xi_m = gamma^(N-1-m) (0-based n, m):
+        O   = ((Q' K'^T) * D) V + Z * (Q' S0)
+        S_N = gamma^N S0 + K'^T (Xi * V)
+    and differentiating each term:
+        dV  = ((Q' K'^T) * D)^T dO + Xi * (K' dS)
+        dQ' = ((dO V^T) * D) K' + Z * (dO S0^T)
+        dK' = ((dO V^T) * D)^T Q' + Xi * (V dS^T)
+        dS0 = Q'^T (Z * dO) + gamma^N dS
+    The rotation multiplies each pair by a unit complex number, so its adjoint
+    is the rotation by the opposite angle: dQ = rotate(dQ', -theta), and the
+    same for dK.
+    """
+    q, k, v, d_o = _as64(q), _as64(k), _as64(v), _as64(d_o)
+    qr, kr = _maybe_rotate(q, k, theta, pos0)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    S0 = np.zeros((B, H, dk, dv)) if state0 is None else _as64(state0)
+    dS = np.zeros((B, H, dk, dv)) if d_state is None else _as64(d_state)
+    n = np.arange(N, dtype=np.float64)
+    dq_r = np.empty_like(qr)
+    dk_r = np.empty_like(kr)
+    dv_out = np.empty_like(v)
+    dS0 = np.empty_like(S0)
+    for h in range(H):
+        g = float(gammas[h])
+        D = decay_matrix(g, N)
+        Z = np.power(g, n + 1.0)[:, None]
+        Xi = np.power(g, N - 1.0 - n)[:, None]
+        for b in range(B):
+            Qh, Kh, Vh, dOh = qr[b, h], kr[b, h], v[b, h], d_o[b, h]
+            P = (Qh @ Kh.T) * D
+            dP = (dOh @ Vh.T) * D
+            dv_out[b, h] = P.T @ dOh + Xi * (Kh @ dS[b, h])
+            dq_r[b, h] = dP @ Kh + Z * (dOh @ S0[b, h].T)
+            dk_r[b, h] = dP.T @ Qh + Xi * (Vh @ dS[b, h].T)
+            dS0[b, h] = Qh.T @ (Z * dOh) + (g ** N) * dS[b, h]
+    if theta is not None:
+        positions = pos0 + n
+        minus = -np.asarray(theta, dtype=np.float64)
+        dq_r = rotate_pairs(dq_r, positions, minus)
+        dk_r = rotate_pairs(dk_r, positions, minus)
+    return dq_r, dk_r, dv_out, dS0

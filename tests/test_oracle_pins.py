@@ -330,3 +330,99 @@ def test_brute_force_scalar_loops():
         got = orc.chunkwise(q[None, None], k[None, None], v[None, None], np.array([gam]), 2,
                             theta=th, pos0=pos0)[0][0, 0]
         assert np.allclose(got, expect, atol=1e-12)
+
+
+# ---------------------------------------------------------------- backward
+
+
+def test_backward_hand_worked():
+    # One head, d_k = d_v = 1, two tokens, gamma = 1/2, worked by hand from
+    #   o_0 = g q0 s + q0 k0 v0,  o_1 = g^2 q1 s + q1 (g k0 v0 + k1 v1),
+    #   S_2 = g^2 s + g k0 v0 + k1 v1,
+    # with q = (1, 2), k = (3, -1), v = (1/2, 2), s = 4, dO = (1, -2), dS = 3:
+    #   dq = (dO0 (k0 v0 + g s), dO1 (g k0 v0 + k1 v1 + g^2 s))     = (3.5, 0.5)
+    #   dk = (dO0 q0 v0 + dO1 g q1 v0 + g dS v0, dO1 q1 v1 + dS v1) = (0.25, -2)
+    #   dv = (dO0 q0 k0 + dO1 g q1 k0 + g k0 dS, dO1 q1 k1 + k1 dS) = (1.5, 1)
+    #   ds = g q0 dO0 + g^2 q1 dO1 + g^2 dS                         = 0.25
+    q, k, v = _single([1.0, 2.0]), _single([3.0, -1.0]), _single([0.5, 2.0])
+    d_o = _single([1.0, -2.0])
+    s0 = np.full((1, 1, 1, 1), 4.0)
+    ds = np.full((1, 1, 1, 1), 3.0)
+    dq, dk, dv, dS0 = orc.backward(q, k, v, d_o, [0.5], state0=s0, d_state=ds)
+    assert np.allclose(dq.ravel(), [3.5, 0.5], atol=1e-15)
+    assert np.allclose(dk.ravel(), [0.25, -2.0], atol=1e-15)
+    assert np.allclose(dv.ravel(), [1.5, 1.0], atol=1e-15)
+    assert np.allclose(dS0.ravel(), [0.25], atol=1e-15)
+    # without the state terms only the products inside the sequence remain
+    dq, dk, dv, dS0 = orc.backward(q, k, v, d_o, [0.5])
+    assert np.allclose(dq.ravel(), [1.5, 2.5], atol=1e-15)
+    assert np.allclose(dk.ravel(), [-0.5, -8.0], atol=1e-15)
+    assert np.allclose(dv.ravel(), [-3.0, 4.0], atol=1e-15)
+    assert np.allclose(dS0.ravel(), [-0.5], atol=1e-15)
+
+
+def _loss(q, k, v, s0, d_o, ds, g, th, pos0):
+    o, sn = orc.recurrent(q, k, v, g, theta=th, pos0=pos0, state0=s0)
+    return float(np.sum(d_o * o) + np.sum(ds * sn))
+
+
+@pytest.mark.parametrize("rot", [False, True])
+def test_backward_matches_finite_differences(rot):
+    # <dO, O> + <dS, S_N> is affine in every single input entry, so a central
+    # difference is exact up to rounding for any step: no truncation error.
+    B, H, N, dk, dv = 1, 2, 5, 4, 3
+    q, k = _rand((B, H, N, dk), 41), _rand((B, H, N, dk), 42)
+    v = _rand((B, H, N, dv), 43)
+    s0 = _rand((B, H, dk, dv), 44)
+    d_o, ds = _rand((B, H, N, dv), 45), _rand((B, H, dk, dv), 46)
+    g = [0.8, 0.55]
+    th = _rand((dk // 2,), 47) if rot else None
+    pos0 = 7 if rot else 0
+    got = orc.backward(q, k, v, d_o, g, theta=th, pos0=pos0, state0=s0, d_state=ds)
+    args = [q, k, v, s0]
+    for which, grad in enumerate(got):
+        x = args[which]
+        fd = np.empty_like(x)
+        for idx in np.ndindex(*x.shape):
+            hi = [a.copy() for a in args]
+            lo = [a.copy() for a in args]
+            hi[which][idx] += 0.5
+            lo[which][idx] -= 0.5
+            fd[idx] = _loss(*hi, d_o, ds, g, th, pos0) - _loss(*lo, d_o, ds, g, th, pos0)
+        assert np.allclose(grad, fd, rtol=1e-9, atol=1e-10), which
+
+
+def test_backward_euler_identities():
+    # The loss <dO, O> + <dS, S_N> is homogeneous of degree one in q, in k, in
+    # v and in the initial state taken one at a time (except that the state
+    # also reaches S_N): sum(x * dx) splits the loss into its terms.
+    B, H, N, dk, dv = 2, 2, 23, 6, 5
+    q, k = _rand((B, H, N, dk), 51), _rand((B, H, N, dk), 52)
+    v, s0 = _rand((B, H, N, dv), 53), _rand((B, H, dk, dv), 54)
+    d_o, ds = _rand((B, H, N, dv), 55), _rand((B, H, dk, dv), 56)
+    g, th = orc.head_gammas(H), _rand((dk // 2,), 57)
+    o, sn = orc.recurrent(q, k, v, g, theta=th, pos0=3, state0=s0)
+    o_seq, sn_seq = orc.recurrent(q, k, v, g, theta=th, pos0=3)  # terms without the initial state
+    dq, dk_, dv_, dS0 = orc.backward(q, k, v, d_o, g, theta=th, pos0=3, state0=s0, d_state=ds)
+    loss = np.sum(d_o * o) + np.sum(ds * sn)
+    seq_part = np.sum(d_o * o_seq) + np.sum(ds * sn_seq)
+    assert np.isclose(np.sum(q * dq), np.sum(d_o * o), rtol=1e-11)
+    assert np.isclose(np.sum(k * dk_), seq_part, rtol=1e-11)
+    assert np.isclose(np.sum(v * dv_), seq_part, rtol=1e-11)
+    assert np.isclose(np.sum(s0 * dS0), loss - seq_part, rtol=1e-11)
+
+
+def test_backward_gamma_one_is_cumulative_sums():
+    # gamma = 1, no rotation, no state: dV_m = K_m (sum_{n >= m} Q_n^T dO_n) and
+    # dQ_n = dO_n (sum_{m <= n} V_m^T K_m), suffix and prefix sums of outer
+    # products (the gradient of cumulative linear attention).
+    q, k = _rand((1, 1, 9, 3), 61), _rand((1, 1, 9, 3), 62)
+    v, d_o = _rand((1, 1, 9, 2), 63), _rand((1, 1, 9, 2), 64)
+    dq, dk, dv, _ = orc.backward(q, k, v, d_o, [1.0])
+    Q, K, V, G = q[0, 0], k[0, 0], v[0, 0], d_o[0, 0]
+    for n in range(9):
+        pre = sum(np.outer(V[m], K[m]) for m in range(n + 1))
+        suf_qg = sum(np.outer(Q[t], G[t]) for t in range(n, 9))
+        assert np.allclose(dq[0, 0, n], G[n] @ pre, atol=1e-12)
+        assert np.allclose(dv[0, 0, n], K[n] @ suf_qg, atol=1e-12)
+        assert np.allclose(dk[0, 0, n], suf_qg @ V[n], atol=1e-12)
