@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define RETENTION_ABI_VERSION 2
+#define RETENTION_ABI_VERSION 3
 #define RETENTION_MAX_HEADS 128 /* H limit (per-head constants travel in kernel arguments) */
 #define RETENTION_MAX_DK 256
 
@@ -149,6 +149,50 @@ ret_status_t retention_chunkwise_fwd_timed(const void* q, const void* k, const v
  */
 size_t retention_chunkwise_workspace_size(int B, int H, int N, int dk, int dv, ret_dtype_t dtype,
                                           int chunk, int segments);
+
+/*
+ * Backward of retention_chunkwise_fwd (whose result is that of the parallel
+ * form, which is how training evaluates retention: "RetNet Guide" section "1.
+ * The Parallel Representation for High-Throughput Pretraining"; "Retentive
+ * Networks (RetNet)", "At a glance": training stays parallel over the
+ * sequence). For the forward O, S_N of the same q, k, v, gamma, theta, pos0 and
+ * state_in, and the gradients d_o = dL/dO and d_state_out = dL/dS_N, it writes
+ *     d_q, d_k [B, H, N, dk] and d_v [B, H, N, dv] (dtype): dL/dq, dL/dk, dL/dv
+ *     d_state_in [B, H, dk, dv] float32 (when not NULL): dL/d(state_in)
+ * Per head, with Q', K' the rotated rows, Z_n = gamma^(n+1), Xi_m = gamma^(N-1-m):
+ *     dV  = ((Q' K'^T) (.) D)^T dO + Xi (.) (K' dS)
+ *     dQ' = ((dO V^T) (.) D) K' + Z (.) (dO S0^T),   dq = rotation of dQ' by -theta
+ *     dK' = ((dO V^T) (.) D)^T Q' + Xi (.) (V dS^T), dk likewise
+ *     dS0 = Q'^T (Z (.) dO) + gamma^N dS
+ * Each of dQ', dK', dV is computed as one chunkwise forward pass (the last two
+ * over the reversed sequence, where the transposed decay matrix is causal).
+ *
+ * d_o:         device [B, H, N, dv] in dtype.
+ * state_in:    the forward's initial state, or NULL for zeros.
+ * d_state_out: device float32 [B, H, dk, dv], or NULL for zeros.
+ * d_state_in:  device float32 [B, H, dk, dv] to receive dL/d(state_in), or
+ *              NULL. May alias d_state_out or state_in; d_q, d_k, d_v must not
+ *              overlap any input or each other.
+ * workspace:   device buffer of retention_chunkwise_bwd_workspace_size(...)
+ *              bytes (it grows with N: it holds reversed and rotated copies of
+ *              q, k, v and d_o), zero-filled before its first use, left ready
+ *              for the next call; calls sharing it must be ordered on one
+ *              stream. The caller owns it.
+ * Implemented set: chunk in {64, 128}; dk and dv multiples of 8, and each of
+ * (dk, dv) and (dv, dk) inside retention_chunkwise_fwd's set (bf16: dk and dv
+ * both in {64, 128, 256}; f32: chunk*dk and chunk*dv <= 8192, both multiples
+ * of 16); with d_state_out, every gamma >= 2^-20.
+ */
+ret_status_t retention_chunkwise_bwd(const void* q, const void* k, const void* v, const void* d_o,
+                                     void* d_q, void* d_k, void* d_v, int B, int H, int N, int dk, int dv,
+                                     ret_dtype_t dtype, int chunk, const float* gamma, const float* theta,
+                                     int64_t pos0, const float* state_in, const float* d_state_out,
+                                     float* d_state_in, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
+/* Bytes of workspace retention_chunkwise_bwd needs; 0 for sizes it would reject. */
+size_t retention_chunkwise_bwd_workspace_size(int B, int H, int N, int dk, int dv, ret_dtype_t dtype,
+                                              int chunk);
 
 /*
  * One recurrent decode step for one token per sequence ("RetNet Guide" section

@@ -19,6 +19,8 @@ __all__ = [
     "retention_chunkwise_fwd_timed",
     "retention_chunkwise_workspace_size",
     "retention_recurrent_step",
+    "retention_chunkwise_bwd",
+    "retention_chunkwise_bwd_workspace_size",
     "retention_status_string",
     "retention_abi_version",
     "LIB_PATH",
@@ -74,6 +76,11 @@ def load_library(path=None):
     lib.retention_chunkwise_workspace_size.restype = sz
     lib.retention_recurrent_step.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, fp, fp, vp, vp]
     lib.retention_recurrent_step.restype = i32
+    lib.retention_chunkwise_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, fp,
+                                            fp, i64, vp, vp, vp, vp, sz, vp]
+    lib.retention_chunkwise_bwd.restype = i32
+    lib.retention_chunkwise_bwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.retention_chunkwise_bwd_workspace_size.restype = sz
     lib.retention_status_string.argtypes = [i32]
     lib.retention_status_string.restype = ctypes.c_char_p
     lib.retention_abi_version.argtypes = []
@@ -254,6 +261,47 @@ def retention_chunkwise_fwd(q, k, v, chunk=64, gamma=None, theta=None, pos0=0, s
 def retention_chunkwise_fwd_timed(q, k, v, events, **kw):
     """retention_chunkwise_fwd recording the six phase events (see the C header)."""
     return retention_chunkwise_fwd(q, k, v, events=events, **kw)
+
+
+def retention_chunkwise_bwd_workspace_size(B, H, N, dk, dv, dtype, chunk):
+    torch = _torch()
+    code = RET_BF16 if dtype == torch.bfloat16 else RET_F32
+    return int(load_library().retention_chunkwise_bwd_workspace_size(B, H, N, dk, dv, code, chunk))
+
+
+def retention_chunkwise_bwd(q, k, v, d_o, chunk=64, gamma=None, theta=None, pos0=0, state_in=None,
+                            d_state_out=None, need_d_state_in=False, d_state_in=None, out=None,
+                            workspace=None, stream=None):
+    """Gradients of retention_chunkwise_fwd: returns (d_q, d_k, d_v, d_state_in).
+
+    d_o has the shape and dtype of the forward's output; d_state_out (float32
+    [B,H,dk,dv] or None) is the gradient of its final state. d_state_in is
+    returned (float32 [B,H,dk,dv]) when need_d_state_in or a d_state_in tensor
+    is given, else None. `out` may supply (d_q, d_k, d_v). Without `workspace`
+    the call uses the module's zero-filled per-stream workspace.
+    """
+    torch = _torch()
+    _check_dev(q, k, v, d_o, state_in, d_state_out, d_state_in)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    d_q, d_k, d_v = out
+    _check_dev(d_q, d_k, d_v)
+    if need_d_state_in and d_state_in is None:
+        d_state_in = torch.empty((B, H, dk, dv), dtype=torch.float32, device=v.device)
+    ws_bytes = retention_chunkwise_bwd_workspace_size(B, H, N, dk, dv, q.dtype, chunk)
+    if workspace is None and ws_bytes:
+        workspace = _cached_workspace(ws_bytes, v.device, stream)
+    _g, g = _host_floats(gamma, H, "gamma")
+    _t, th = _host_floats(theta, dk // 2, "theta")
+    st = load_library().retention_chunkwise_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(d_o), _ptr(d_q), _ptr(d_k), _ptr(d_v), B, H, N, dk, dv, _dtype_code(q),
+        int(chunk), g, th, int(pos0), _ptr(state_in), _ptr(d_state_out), _ptr(d_state_in), _ptr(workspace),
+        workspace.numel() if workspace is not None else 0, _stream(stream),
+    )
+    _raise(st, "retention_chunkwise_bwd")
+    return d_q, d_k, d_v, d_state_in
 
 
 def retention_recurrent_step(q, k, v, state, gamma=None, theta=None, pos=None, out=None, stream=None):

@@ -139,6 +139,41 @@ ret_status_t plan_chunk(int B, int H, int N, int dk, int dv, ret_dtype_t dtype, 
     return RET_OK;
 }
 
+// Workspace of the backward: the forward passes' region first (it keeps the
+// zero-filled contract of the forward workspace), then scratch tensors.
+struct BwdPlan {
+    size_t fwd_bytes;                 // region shared by the three forward passes
+    size_t kr, qf, kf, vf, dof;       // [B,H,N,d] rows (kr also receives dK' reversed, vf dV reversed)
+    size_t x1, x2, x3;                // float32 [B,H,dk,dv] states
+    size_t total;
+};
+
+constexpr float kMinBwdGamma = 9.5367431640625e-07f;  // 2^-20: dS / gamma stays far from float32 overflow
+
+ret_status_t plan_bwd(int B, int H, int N, int dk, int dv, ret_dtype_t dtype, int chunk, BwdPlan& b) {
+    if (dk % 8 != 0 || dv % 8 != 0) return RET_ERR_UNSUPPORTED;
+    ChunkPlan p1, p3;  // passes 1 and 2 have key width dv and value width dk; pass 3 the reverse
+    ret_status_t s = plan_chunk(B, H, N, dv, dk, dtype, chunk, 0, p1);
+    if (s != RET_OK) return s;
+    s = plan_chunk(B, H, N, dk, dv, dtype, chunk, 0, p3);
+    if (s != RET_OK) return s;
+    const size_t es = dtype == RET_BF16 ? 2 : 4;
+    const size_t rows = static_cast<size_t>(B) * H * N;
+    const size_t nk = round256(rows * dk * es), nv = round256(rows * dv * es);
+    const size_t ns = round256(static_cast<size_t>(B) * H * dk * dv * sizeof(float));
+    b.fwd_bytes = round256(p1.ws_bytes > p3.ws_bytes ? p1.ws_bytes : p3.ws_bytes);
+    b.kr = b.fwd_bytes;
+    b.qf = b.kr + nk;
+    b.kf = b.qf + nk;
+    b.vf = b.kf + nk;
+    b.dof = b.vf + nv;
+    b.x1 = b.dof + nv;
+    b.x2 = b.x1 + ns;
+    b.x3 = b.x2 + ns;
+    b.total = b.x3 + ns;
+    return RET_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -238,6 +273,99 @@ ret_status_t retention_chunkwise_fwd_timed(const void* q, const void* k, const v
         if (!events[i]) return RET_ERR_NULL;
     return chunkwise_impl(q, k, v, o, B, H, N, dk, dv, dtype, chunk, gamma, theta, pos0, state_in, state_out,
                           segments, workspace, workspace_bytes, stream, events);
+}
+
+size_t retention_chunkwise_bwd_workspace_size(int B, int H, int N, int dk, int dv, ret_dtype_t dtype,
+                                              int chunk) {
+    if (check_common(B, H, N, dk, dv, dtype, nullptr) != RET_OK) return 0;
+    if (check_common(B, H, N, dv, dk, dtype, nullptr) != RET_OK) return 0;
+    BwdPlan b;
+    if (plan_bwd(B, H, N, dk, dv, dtype, chunk, b) != RET_OK) return 0;
+    return b.total;
+}
+
+ret_status_t retention_chunkwise_bwd(const void* q, const void* k, const void* v, const void* d_o, void* d_q,
+                                     void* d_k, void* d_v, int B, int H, int N, int dk, int dv,
+                                     ret_dtype_t dtype, int chunk, const float* gamma, const float* theta,
+                                     int64_t pos0, const float* state_in, const float* d_state_out,
+                                     float* d_state_in, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !d_o || !d_q || !d_k || !d_v) return RET_ERR_NULL;
+    ret_status_t s = check_common(B, H, N, dk, dv, dtype, theta);
+    if (s != RET_OK) return s;
+    s = check_common(B, H, N, dv, dk, dtype, nullptr);  // dv serves as a key width
+    if (s != RET_OK) return s;
+    HeadParams hp;
+    s = fill_head_params(hp, H, dk, gamma, theta);
+    if (s != RET_OK) return s;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(d_o) || !aligned16(d_q) ||
+        !aligned16(d_k) || !aligned16(d_v) || !aligned16(state_in) || !aligned16(d_state_out) ||
+        !aligned16(d_state_in) || !aligned16(workspace))
+        return RET_ERR_ALIGN;
+    BwdPlan b;
+    s = plan_bwd(B, H, N, dk, dv, dtype, chunk, b);
+    if (s != RET_OK) return s;
+    if (d_state_out)
+        for (int h = 0; h < H; ++h)
+            if (hp.gamma[h] < kMinBwdGamma) return RET_ERR_UNSUPPORTED;
+    if (workspace == nullptr || workspace_bytes < b.total) return RET_ERR_WORKSPACE;
+
+    char* ws = static_cast<char*>(workspace);
+    void* kr = ws + b.kr;
+    void* qf = ws + b.qf;
+    void* kf = ws + b.kf;
+    void* vf = ws + b.vf;
+    void* dof = ws + b.dof;
+    float* x1 = reinterpret_cast<float*>(ws + b.x1);
+    float* x2 = reinterpret_cast<float*>(ws + b.x2);
+    float* x3 = reinterpret_cast<float*>(ws + b.x3);
+    const bool rot = theta != nullptr;
+    const bool bf16 = dtype == RET_BF16;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+
+    // rotated and reversed copies of the inputs
+    ret::RowJobs rj;
+    memset(&rj, 0, sizeof(rj));
+    rj.B = B;
+    rj.H = H;
+    rj.N = N;
+    rj.pos0 = pos0;
+    rj.n = 4;
+    rj.j[0] = {q, qf, nullptr, dk, 1, rot ? 1 : 0, 0};
+    rj.j[1] = {k, kf, rot ? kr : nullptr, dk, 1, rot ? 1 : 0, 0};
+    rj.j[2] = {v, vf, nullptr, dv, 1, 0, 0};
+    rj.j[3] = {d_o, dof, nullptr, dv, 1, 0, 0};
+    if (ret::launch_rows(rj, hp, bf16, st) != hipSuccess) return RET_ERR_HIP;
+    if (state_in || d_state_out) {
+        ret::StateJobs sj = {state_in, d_state_out, x1, x2, x3, nullptr, B, H, dk, dv, 0};
+        if (ret::launch_states(sj, hp, st) != hipSuccess) return RET_ERR_HIP;
+    }
+
+    // dQ' = F(dO, V, K'; S0^T) straight into d_q
+    s = chunkwise_impl(d_o, v, rot ? kr : k, d_q, B, H, N, dv, dk, dtype, chunk, gamma, nullptr, 0,
+                       state_in ? x1 : nullptr, nullptr, 0, ws, b.fwd_bytes, stream, nullptr);
+    if (s != RET_OK) return s;
+    // reversed dK' = F(rev V, rev dO, rev Q'; dS^T / gamma) into the K' region
+    s = chunkwise_impl(vf, dof, qf, kr, B, H, N, dv, dk, dtype, chunk, gamma, nullptr, 0,
+                       d_state_out ? x2 : nullptr, nullptr, 0, ws, b.fwd_bytes, stream, nullptr);
+    if (s != RET_OK) return s;
+    // reversed dV = F(rev K', rev Q', rev dO; dS / gamma) into the rev V region; its final state is dS0 / gamma
+    s = chunkwise_impl(kf, qf, dof, vf, B, H, N, dk, dv, dtype, chunk, gamma, nullptr, 0,
+                       d_state_out ? x3 : nullptr, d_state_in, 0, ws, b.fwd_bytes, stream, nullptr);
+    if (s != RET_OK) return s;
+
+    // back to token order and unrotated coordinates
+    memset(&rj.j, 0, sizeof(rj.j));
+    int n = 0;
+    if (rot) rj.j[n++] = {d_q, d_q, nullptr, dk, 0, -1, 0};
+    rj.j[n++] = {kr, d_k, nullptr, dk, 1, rot ? -1 : 0, 1};
+    rj.j[n++] = {vf, d_v, nullptr, dv, 1, 0, 1};
+    rj.n = n;
+    if (ret::launch_rows(rj, hp, bf16, st) != hipSuccess) return RET_ERR_HIP;
+    if (d_state_in) {
+        ret::StateJobs sj = {nullptr, nullptr, nullptr, nullptr, nullptr, d_state_in, B, H, dk, dv, 1};
+        if (ret::launch_states(sj, hp, st) != hipSuccess) return RET_ERR_HIP;
+    }
+    return RET_OK;
 }
 
 ret_status_t retention_parallel_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N,

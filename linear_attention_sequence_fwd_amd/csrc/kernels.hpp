@@ -56,6 +56,40 @@ struct StepArgs {
     int ntile;  // column tiles per (sequence, head), see recurrent_step_tiles
 };
 
+// Row transforms of the backward (backward.hip): one job per tensor.
+struct RowJob {
+    const void* src;  // [B,H,N,d] rows
+    void* dst0;       // [B,H,N,d]; row t lands at N-1-t when flip0
+    void* dst1;       // optional second copy, rows in order (nullptr: none)
+    int d;            // row width in elements, a multiple of 8
+    int flip0;
+    int rot;          // 0: none, +1: rotate by +theta, -1: by -theta
+    int src_rev;      // src rows are in reverse token order: row t holds token N-1-t (its rotation position)
+};
+
+struct RowJobs {
+    RowJob j[4];
+    int n;  // jobs in use
+    int B, H, N;
+    long long pos0;
+};
+
+// State transforms of the backward: mode 0 writes x1 = s0^T, x2 = ds^T / gamma,
+// x3 = ds / gamma (per head, [dk, dv] sources); mode 1 scales dsi by gamma.
+struct StateJobs {
+    const float* s0;
+    const float* ds;
+    float* x1;
+    float* x2;
+    float* x3;
+    float* dsi;
+    int B, H, dk, dv;
+    int mode;
+};
+
+hipError_t launch_rows(const RowJobs& jobs, const HeadParams& hp, bool bf16, hipStream_t st);
+hipError_t launch_states(const StateJobs& sj, const HeadParams& hp, hipStream_t st);
+
 // Optional timing hook: when ev is not null it holds six events, a start/stop
 // pair per phase (segment pre-pass, segment scan, main chunk kernel), each pair
 // recorded by the launch itself around that kernel's execution

@@ -77,3 +77,14 @@ def make_decode_workload(name="decode_bf16", device="cpu", steps=None):
     w = WORKLOADS[name]
     return make_decode(w["B"], w["H"], w["dk"], w["dv"], w["dtype"], steps or w["steps"], w["state_std"],
                        w["seed"], device)
+
+
+def make_upstream_grads(B, H, N, dk, dv, dtype, seed, device="cpu"):
+    """Gradients arriving at a retention call from the layers after it, for
+    the backward: dO [B,H,N,dv] ~ N(0,1) in dtype and dS [B,H,dk,dv] ~ N(0,1)
+    float32 (the gradient of the final state, as when the next piece of a
+    sequence continued from it)."""
+    g = _gen(device, seed)
+    d_o = torch.randn((B, H, N, dv), generator=g, device=device, dtype=torch.float32).to(dtype)
+    d_s = torch.randn((B, H, dk, dv), generator=g, device=device, dtype=torch.float32)
+    return d_o, d_s

@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.retention_abi_version() == 2
+    assert lib.retention_abi_version() == 3
     for s in range(9):
         assert len(lib.retention_status_string(s)) > 0
     assert lib.retention_status_string(123) == b"unknown status"
@@ -171,3 +171,42 @@ def test_product_path_never_touches_the_oracle():
                 assert not imp.search(open(path).read()), path
             elif f.endswith((".hip", ".hpp", ".cpp", ".h")):
                 assert not inc.search(open(path).read()), path
+
+
+def bwd(lib, **kw):
+    a = dict(q=A, k=A, v=A, d_o=A, d_q=A, d_k=A, d_v=A, B=1, H=2, N=100, dk=64, dv=64, dtype=BF16, chunk=64,
+             gamma=None, theta=None, pos0=0, state_in=None, d_state_out=None, d_state_in=None, ws=None,
+             ws_bytes=0)
+    a.update(kw)
+    return lib.retention_chunkwise_bwd(a["q"], a["k"], a["v"], a["d_o"], a["d_q"], a["d_k"], a["d_v"], a["B"],
+                                       a["H"], a["N"], a["dk"], a["dv"], a["dtype"], a["chunk"], a["gamma"],
+                                       a["theta"], a["pos0"], a["state_in"], a["d_state_out"], a["d_state_in"],
+                                       a["ws"], a["ws_bytes"], None)
+
+
+def test_backward_validation(lib):
+    for key in ("q", "k", "v", "d_o", "d_q", "d_k", "d_v"):
+        assert bwd(lib, **{key: None}) == NULL
+    for key in ("B", "H", "N", "dk", "dv"):
+        assert bwd(lib, **{key: 0}) == SHAPE
+    assert bwd(lib, dtype=5) == DTYPE
+    g, _keep = floats(0.9, 1.5)
+    assert bwd(lib, gamma=g) == GAMMA
+    assert bwd(lib, d_state_in=A + 4) == ALIGN
+    assert bwd(lib, d_o=A + 2) == ALIGN
+    # each of dk and dv is the key width of some pass: both must be bf16 key widths
+    assert bwd(lib, dv=512) == UNSUP
+    assert bwd(lib, dk=256, dv=512, chunk=128) == UNSUP
+    assert bwd(lib, chunk=32) == UNSUP
+    assert bwd(lib, dtype=F32, dk=64, dv=200) == UNSUP  # not a multiple of 8 / 16
+    # the state gradient divides by gamma: tiny gammas are outside the set only then
+    tiny, _keep2 = floats(0.9, 1e-7)
+    need = lib.retention_chunkwise_bwd_workspace_size(1, 2, 100, 64, 64, BF16, 64)
+    assert bwd(lib, gamma=tiny, d_state_out=A, ws=A, ws_bytes=need) == UNSUP
+    # the workspace is always needed (reversed copies of the inputs) and grows with N
+    assert need > 0
+    assert bwd(lib) == WS
+    assert bwd(lib, ws=A, ws_bytes=need - 1) == WS
+    assert lib.retention_chunkwise_bwd_workspace_size(1, 2, 200, 64, 64, BF16, 64) > need
+    assert lib.retention_chunkwise_bwd_workspace_size(1, 2, 100, 64, 512, BF16, 64) == 0
+    assert lib.retention_chunkwise_bwd_workspace_size(1, 2, 100, 64, 64, BF16, 48) == 0

@@ -555,3 +555,74 @@ def test_graph_replay_matches_eager():
         other = R.retention_chunkwise_fwd(q, k, v, chunk=w["chunk"], theta=th, workspace=ws2, segments=3)
         torch.cuda.synchronize()
         assert torch.isfinite(other).all()
+
+
+# ------------------------------------------------------------ backward
+
+BWD_CASES = [
+    # B, H, N, dk, dv, chunk, dtype, rotary, state_in, d_state_out
+    (2, 3, 300, 64, 64, 64, torch.bfloat16, False, False, False),
+    (1, 2, 333, 128, 128, 128, torch.bfloat16, True, True, True),
+    (1, 2, 200, 64, 128, 64, torch.bfloat16, True, False, True),
+    (2, 2, 257, 256, 128, 128, torch.bfloat16, False, True, True),
+    (1, 2, 1, 64, 64, 64, torch.bfloat16, True, True, True),
+    (1, 1, 4100, 64, 64, 64, torch.bfloat16, True, True, True),
+    (1, 2, 130, 64, 64, 64, torch.float32, True, True, True),
+    (2, 1, 200, 32, 64, 64, torch.float32, False, True, True),
+]
+
+
+def _bwd_check(B, H, N, dk, dv, chunk, dtype, rot, st, ds, seed, gamma=None):
+    tol = BF16_TOL if dtype == torch.bfloat16 else F32_TOL
+    q, k, v = _inputs(B, H, N, dk, dv, dtype, seed)
+    d_o, d_s = W.make_upstream_grads(B, H, N, dk, dv, dtype, seed + 1000)
+    s0 = W.make_decode(B, H, dk, dv, dtype, 1, 0.1, seed + 2000)[0] if st else None
+    theta = W.rotary_theta(dk) if rot else None
+    g = _gammas_for(H, gamma)
+    ref = orc.backward(to64(q), to64(k), to64(v), to64(d_o), g, theta=None if theta is None else to64(theta),
+                       pos0=11 if rot else 0, state0=None if s0 is None else to64(s0),
+                       d_state=to64(d_s) if ds else None)
+    got = R.retention_chunkwise_bwd(
+        q.to(DEV), k.to(DEV), v.to(DEV), d_o.to(DEV), chunk=chunk, gamma=gamma, theta=theta, pos0=11 if rot else 0,
+        state_in=None if s0 is None else s0.to(DEV), d_state_out=d_s.to(DEV) if ds else None, need_d_state_in=True)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv", "d_state_in"), got, ref):
+        assert_close(to64(a), b, tol, name)
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "B{}H{}N{}dk{}dv{}C{}{}rot{}st{}ds{}".format(
+    *c[:6], str(c[6])[6:], *c[7:]))
+def test_chunkwise_backward_small(case):
+    _bwd_check(*case, seed=71)
+
+
+@pytest.mark.parametrize("gammas", [[1.0, 0.99], [0.05, 0.6], [0.9, 0.999999]])
+def test_chunkwise_backward_custom_gammas(gammas):
+    _bwd_check(1, 2, 700, 64, 64, 64, torch.bfloat16, True, True, True, seed=72, gamma=gammas)
+
+
+def test_chunkwise_backward_msr_full():
+    """The multi-scale bf16 workload with rotation, every element of every gradient."""
+    w = W.WORKLOADS["msr_bf16_rotary"]
+    _bwd_check(w["B"], w["H"], w["N"], w["dk"], w["dv"], w["chunk"], w["dtype"], True, False, False, seed=w["seed"])
+
+
+def test_chunkwise_backward_long_d128():
+    _bwd_check(1, 2, 4096, 128, 128, 128, torch.bfloat16, False, True, True, seed=73)
+
+
+def test_chunkwise_backward_leaves_inputs_and_aliases_state():
+    B, H, N, dk, dv = 1, 2, 300, 64, 64
+    q, k, v = (t.to(DEV) for t in _inputs(B, H, N, dk, dv, torch.bfloat16, 74))
+    d_o, d_s = (t.to(DEV) for t in W.make_upstream_grads(B, H, N, dk, dv, torch.bfloat16, 75))
+    theta = W.rotary_theta(dk)
+    keep = [t.clone() for t in (q, k, v, d_o, d_s)]
+    a = R.retention_chunkwise_bwd(q, k, v, d_o, theta=theta, d_state_out=d_s, need_d_state_in=True)
+    ds_alias = d_s.clone()
+    b = R.retention_chunkwise_bwd(q, k, v, d_o, theta=theta, d_state_out=ds_alias, d_state_in=ds_alias)
+    torch.cuda.synchronize()
+    for x, y in zip(keep, (q, k, v, d_o, d_s)):
+        assert torch.equal(x, y)
+    for x, y in zip(a[:3], b[:3]):
+        assert torch.equal(x, y)
+    assert torch.equal(a[3], ds_alias)
