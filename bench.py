@@ -44,6 +44,11 @@ def parallel_alg_flops(B, H, N, dk, dv):
     return B * H * N * (N + 1) * (dk + dv)
 
 
+def bwd_alg_bytes(B, H, N, dk, dv, elt=2):
+    """Algorithmic HBM bytes of one backward: read q, k, v, dO; write dq, dk, dv."""
+    return B * H * N * elt * (2 * dk + 2 * dv + 2 * dk + dv)
+
+
 def decode_alg_bytes(B, H, dk, dv, elt=2):
     return B * H * (2 * dk * dv * 4 + elt * (2 * dk + dv) + elt * dv)
 
@@ -245,9 +250,12 @@ def run_only(name, steps, warmup, dev):
                           "bytes_written": dst.numel() * 4}))
         return
     key = {"msr": "msr_bf16_rotary", "layer7b": "layer7b_bf16", "decode": "decode_bf16",
-           "longctx": "longctx_bf16", "single": "single_head_f32"}[name]
+           "longctx": "longctx_bf16", "single": "single_head_f32", "bwd": "msr_bf16_rotary"}[name]
     w = W.WORKLOADS[key]
-    if name == "decode":
+    if name == "bwd":
+        fn = backward_step(R, W, key, dev)
+        key = "msr_bf16_rotary backward"
+    elif name == "decode":
         s0, qs, ks, vs = W.make_decode_workload(device=dev, steps=steps + warmup)
         o = torch.empty((w["B"], w["H"], w["dv"]), dtype=w["dtype"], device=dev)
         it = iter(range(steps + warmup))
@@ -266,6 +274,26 @@ def run_only(name, steps, warmup, dev):
             R.retention_chunkwise_fwd(q, k, v, chunk=w["chunk"], theta=theta, out=out, workspace=ws)
     ms = time_events(fn, steps, warmup)
     print(json.dumps({"workload": key, "ms_per_call": ms, "steps": steps}))
+
+
+def backward_step(R, W, name, dev):
+    """One retention_chunkwise_bwd call over a named workload (dO drawn once)."""
+    import torch
+
+    w = W.WORKLOADS[name]
+    q, k, v, theta = W.make_workload(name, device=dev)
+    d_o, _ = W.make_upstream_grads(w["B"], w["H"], w["N"], w["dk"], w["dv"], w["dtype"], w["seed"] + 1000,
+                                   device=dev)
+    outs = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    nbytes = R.retention_chunkwise_bwd_workspace_size(w["B"], w["H"], w["N"], w["dk"], w["dv"], q.dtype,
+                                                      w["chunk"])
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    th = R.HostFloats(theta) if theta is not None else None
+
+    def fn():
+        R.retention_chunkwise_bwd(q, k, v, d_o, chunk=w["chunk"], theta=th, out=outs, workspace=ws)
+
+    return fn
 
 
 def sweep_decode_batch(dev):
@@ -303,7 +331,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--quick", action="store_true", help="main workload only")
-    ap.add_argument("--only", choices=["msr", "layer7b", "decode", "longctx", "single", "copy"],
+    ap.add_argument("--only", choices=["msr", "layer7b", "decode", "longctx", "single", "copy", "bwd"],
                     help="time one workload only (no CPU baseline); for profilers")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sweep", choices=["decode-batch"], help="print one JSON line per point of a sweep")
@@ -457,6 +485,22 @@ def main():
             "parallel_crossover": cross,
         })
         del q, k, v
+        torch.cuda.empty_cache()
+
+        # ---------------- backward of the main workload
+        w = W.WORKLOADS["msr_bf16_rotary"]
+        bstep = backward_step(R, W, "msr_bf16_rotary", dev)
+        msb, spb = time_graph(bstep, 100, 10)
+        flb = 3 * chunk_alg_flops(w["B"], w["H"], w["N"], w["dk"], w["dv"], w["chunk"])
+        byb = bwd_alg_bytes(w["B"], w["H"], w["N"], w["dk"], w["dv"])
+        also.append({
+            "workload": "backward of the multi-scale workload (dq, dk, dv; rotation; B=2 H=8 N=2048 d=64 "
+                        "bf16, chunk 64): the three chunkwise passes in one launch between two row kernels",
+            "ms": msb, "ms_spread": spb, "tokens_per_s": w["B"] * w["N"] / (msb * 1e-3),
+            "tflops": flb / (msb * 1e-3) / 1e12, "mfma_frac": flb / (msb * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "gbs": byb / (msb * 1e-3) / 1e9, "alg_bytes": byb, "alg_flops": flb,
+            "forward_graph_ms": ms,
+        })
         torch.cuda.empty_cache()
 
         # ---------------- single-head fp32

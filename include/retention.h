@@ -165,7 +165,8 @@ size_t retention_chunkwise_workspace_size(int B, int H, int N, int dk, int dv, r
  *     dK' = ((dO V^T) (.) D)^T Q' + Xi (.) (V dS^T), dk likewise
  *     dS0 = Q'^T (Z (.) dO) + gamma^N dS
  * Each of dQ', dK', dV is computed as one chunkwise forward pass (the last two
- * over the reversed sequence, where the transposed decay matrix is causal).
+ * over the reversed sequence, where the transposed decay matrix is causal);
+ * for bf16 with dk == dv the three passes share one launch.
  *
  * d_o:         device [B, H, N, dv] in dtype.
  * state_in:    the forward's initial state, or NULL for zeros.
@@ -175,9 +176,12 @@ size_t retention_chunkwise_workspace_size(int B, int H, int N, int dk, int dv, r
  *              overlap any input or each other.
  * workspace:   device buffer of retention_chunkwise_bwd_workspace_size(...)
  *              bytes (it grows with N: it holds reversed and rotated copies of
- *              q, k, v and d_o), zero-filled before its first use, left ready
- *              for the next call; calls sharing it must be ordered on one
- *              stream. The caller owns it.
+ *              q, k, v and d_o). It needs no initialisation: every call clears
+ *              the counters its passes use, in a kernel (so the call can be
+ *              captured in a graph). Backward calls of any sizes may share it
+ *              when ordered on one stream; a forward workspace must not be the
+ *              same memory (the backward's scratch would overwrite the
+ *              counters a forward call expects to find). The caller owns it.
  * Implemented set: chunk in {64, 128}; dk and dv multiples of 8, and each of
  * (dk, dv) and (dv, dk) inside retention_chunkwise_fwd's set (bf16: dk and dv
  * both in {64, 128, 256}; f32: chunk*dk and chunk*dv <= 8192, both multiples

@@ -189,13 +189,15 @@ def retention_parallel_fwd(q, k, v, gamma=None, theta=None, pos0=0, out=None, st
 _WORKSPACES = {}
 
 
-def _cached_workspace(nbytes, device, stream):
+def _cached_workspace(nbytes, device, stream, kind="fwd"):
     """Zero-filled workspace of at least nbytes for calls on `stream` (the
     current stream when None). Growing it allocates and zero-fills a new
-    buffer, ordered on that stream before the call that uses it."""
+    buffer, ordered on that stream before the call that uses it. Forward and
+    backward calls keep separate buffers (`kind`): the backward's scratch must
+    not land on a forward call's counters."""
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream(device)
-    key = (device.index if device.index is not None else torch.cuda.current_device(), s.cuda_stream)
+    key = (kind, device.index if device.index is not None else torch.cuda.current_device(), s.cuda_stream)
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < nbytes:
         with torch.cuda.stream(s):
@@ -278,7 +280,7 @@ def retention_chunkwise_bwd(q, k, v, d_o, chunk=64, gamma=None, theta=None, pos0
     [B,H,dk,dv] or None) is the gradient of its final state. d_state_in is
     returned (float32 [B,H,dk,dv]) when need_d_state_in or a d_state_in tensor
     is given, else None. `out` may supply (d_q, d_k, d_v). Without `workspace`
-    the call uses the module's zero-filled per-stream workspace.
+    the call uses a per-stream workspace this module keeps for backward calls.
     """
     torch = _torch()
     _check_dev(q, k, v, d_o, state_in, d_state_out, d_state_in)
@@ -292,7 +294,7 @@ def retention_chunkwise_bwd(q, k, v, d_o, chunk=64, gamma=None, theta=None, pos0
         d_state_in = torch.empty((B, H, dk, dv), dtype=torch.float32, device=v.device)
     ws_bytes = retention_chunkwise_bwd_workspace_size(B, H, N, dk, dv, q.dtype, chunk)
     if workspace is None and ws_bytes:
-        workspace = _cached_workspace(ws_bytes, v.device, stream)
+        workspace = _cached_workspace(ws_bytes, v.device, stream, kind="bwd")
     _g, g = _host_floats(gamma, H, "gamma")
     _t, th = _host_floats(theta, dk // 2, "theta")
     st = load_library().retention_chunkwise_bwd(

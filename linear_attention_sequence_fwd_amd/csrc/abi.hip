@@ -139,12 +139,45 @@ ret_status_t plan_chunk(int B, int H, int N, int dk, int dv, ret_dtype_t dtype, 
     return RET_OK;
 }
 
-// Workspace of the backward: the forward passes' region first (it keeps the
-// zero-filled contract of the forward workspace), then scratch tensors.
+void fill_chunk_args(ret::ChunkArgs& a, const void* q, const void* k, const void* v, void* o, int B, int H, int N,
+                     int dk, int dv, int chunk, int64_t pos0, const float* state_in, float* state_out,
+                     const ChunkPlan& p, void* workspace) {
+    a.q = static_cast<const ret::u16*>(q);
+    a.k = static_cast<const ret::u16*>(k);
+    a.v = static_cast<const ret::u16*>(v);
+    a.o = static_cast<ret::u16*>(o);
+    a.state_in = state_in;
+    a.state_out = state_out;
+    char* ws = static_cast<char*>(workspace);
+    const bool seg_ws = p.ws_bytes > 0;
+    a.ctl = seg_ws ? reinterpret_cast<unsigned long long*>(ws) : nullptr;
+    a.flags = seg_ws ? reinterpret_cast<unsigned long long*>(ws + p.flags_off) : nullptr;
+    a.agg = seg_ws ? reinterpret_cast<float*>(ws + p.agg_off) : nullptr;
+    a.gflags = seg_ws ? reinterpret_cast<unsigned long long*>(ws + p.gflags_off) : nullptr;
+    a.gagg = seg_ws ? reinterpret_cast<float*>(ws + p.gagg_off) : nullptr;
+    a.B = B;
+    a.H = H;
+    a.N = N;
+    a.dk = dk;
+    a.dv = dv;
+    a.chunk = chunk;
+    a.nvt = p.nvt;
+    a.nseg = p.nseg;
+    a.seg_len = p.seg_len;
+    a.grp = p.grp;
+    a.pos0 = pos0;
+}
+
+// Workspace of the backward: one forward-workspace region per pass first (each
+// keeps the zero-filled contract of the forward workspace), then scratch
+// tensors. Every pass reads and writes its own buffers, so the passes may run
+// concurrently.
 struct BwdPlan {
-    size_t fwd_bytes;                 // region shared by the three forward passes
-    size_t kr, qf, kf, vf, dof;       // [B,H,N,d] rows (kr also receives dK' reversed, vf dV reversed)
-    size_t x1, x2, x3;                // float32 [B,H,dk,dv] states
+    size_t fwd_bytes;                  // one pass's region; three follow each other from offset 0
+    size_t ctl_bytes;                  // leading bytes of each region (counters and flags) cleared per call
+    size_t kr, qf, kf, vf, dof;        // [B,H,N,d] rotated / reversed inputs
+    size_t dkf, dvf;                   // [B,H,N,d] reversed dK' and dV
+    size_t x1, x2, x3;                 // float32 [B,H,dk,dv] states
     size_t total;
 };
 
@@ -162,12 +195,17 @@ ret_status_t plan_bwd(int B, int H, int N, int dk, int dv, ret_dtype_t dtype, in
     const size_t nk = round256(rows * dk * es), nv = round256(rows * dv * es);
     const size_t ns = round256(static_cast<size_t>(B) * H * dk * dv * sizeof(float));
     b.fwd_bytes = round256(p1.ws_bytes > p3.ws_bytes ? p1.ws_bytes : p3.ws_bytes);
-    b.kr = b.fwd_bytes;
+    // counters and flags precede the published states in a forward workspace
+    const size_t c1 = p1.ws_bytes > 0 ? p1.agg_off : 0, c3 = p3.ws_bytes > 0 ? p3.agg_off : 0;
+    b.ctl_bytes = c1 > c3 ? c1 : c3;
+    b.kr = 3 * b.fwd_bytes;
     b.qf = b.kr + nk;
     b.kf = b.qf + nk;
     b.vf = b.kf + nk;
     b.dof = b.vf + nv;
-    b.x1 = b.dof + nv;
+    b.dkf = b.dof + nv;
+    b.dvf = b.dkf + nk;
+    b.x1 = b.dvf + nv;
     b.x2 = b.x1 + ns;
     b.x3 = b.x2 + ns;
     b.total = b.x3 + ns;
@@ -224,30 +262,7 @@ static ret_status_t chunkwise_impl(const void* q, const void* k, const void* v, 
     if (p.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < p.ws_bytes)) return RET_ERR_WORKSPACE;
 
     ret::ChunkArgs a;
-    a.q = static_cast<const ret::u16*>(q);
-    a.k = static_cast<const ret::u16*>(k);
-    a.v = static_cast<const ret::u16*>(v);
-    a.o = static_cast<ret::u16*>(o);
-    a.state_in = state_in;
-    a.state_out = state_out;
-    char* ws = static_cast<char*>(workspace);
-    const bool seg_ws = p.ws_bytes > 0;
-    a.ctl = seg_ws ? reinterpret_cast<unsigned long long*>(ws) : nullptr;
-    a.flags = seg_ws ? reinterpret_cast<unsigned long long*>(ws + p.flags_off) : nullptr;
-    a.agg = seg_ws ? reinterpret_cast<float*>(ws + p.agg_off) : nullptr;
-    a.gflags = seg_ws ? reinterpret_cast<unsigned long long*>(ws + p.gflags_off) : nullptr;
-    a.gagg = seg_ws ? reinterpret_cast<float*>(ws + p.gagg_off) : nullptr;
-    a.B = B;
-    a.H = H;
-    a.N = N;
-    a.dk = dk;
-    a.dv = dv;
-    a.chunk = chunk;
-    a.nvt = p.nvt;
-    a.nseg = p.nseg;
-    a.seg_len = p.seg_len;
-    a.grp = p.grp;
-    a.pos0 = pos0;
+    fill_chunk_args(a, q, k, v, o, B, H, N, dk, dv, chunk, pos0, state_in, state_out, p, workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipEvent_t* ev = events ? reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)) : nullptr;
     const hipError_t e = (dtype == RET_BF16) ? ret::launch_chunk_bf16(a, hp, p.dvt, st, ev)
@@ -315,6 +330,8 @@ ret_status_t retention_chunkwise_bwd(const void* q, const void* k, const void* v
     void* kf = ws + b.kf;
     void* vf = ws + b.vf;
     void* dof = ws + b.dof;
+    void* dkf = ws + b.dkf;
+    void* dvf = ws + b.dvf;
     float* x1 = reinterpret_cast<float*>(ws + b.x1);
     float* x2 = reinterpret_cast<float*>(ws + b.x2);
     float* x3 = reinterpret_cast<float*>(ws + b.x3);
@@ -334,31 +351,59 @@ ret_status_t retention_chunkwise_bwd(const void* q, const void* k, const void* v
     rj.j[1] = {k, kf, rot ? kr : nullptr, dk, 1, rot ? 1 : 0, 0};
     rj.j[2] = {v, vf, nullptr, dv, 1, 0, 0};
     rj.j[3] = {d_o, dof, nullptr, dv, 1, 0, 0};
+    // the passes' counters and flags start from zero on every call (the
+    // scratch tensors of earlier calls of other sizes may have covered them)
+    if (b.ctl_bytes > 0) {
+        for (int r = 0; r < 3; ++r) rj.zero[r] = reinterpret_cast<uint4*>(ws + r * b.fwd_bytes);
+        rj.nzero = static_cast<long long>(b.ctl_bytes / 16);
+    }
     if (ret::launch_rows(rj, hp, bf16, st) != hipSuccess) return RET_ERR_HIP;
     if (state_in || d_state_out) {
         ret::StateJobs sj = {state_in, d_state_out, x1, x2, x3, nullptr, B, H, dk, dv, 0};
         if (ret::launch_states(sj, hp, st) != hipSuccess) return RET_ERR_HIP;
     }
 
-    // dQ' = F(dO, V, K'; S0^T) straight into d_q
-    s = chunkwise_impl(d_o, v, rot ? kr : k, d_q, B, H, N, dv, dk, dtype, chunk, gamma, nullptr, 0,
-                       state_in ? x1 : nullptr, nullptr, 0, ws, b.fwd_bytes, stream, nullptr);
-    if (s != RET_OK) return s;
-    // reversed dK' = F(rev V, rev dO, rev Q'; dS^T / gamma) into the K' region
-    s = chunkwise_impl(vf, dof, qf, kr, B, H, N, dv, dk, dtype, chunk, gamma, nullptr, 0,
-                       d_state_out ? x2 : nullptr, nullptr, 0, ws, b.fwd_bytes, stream, nullptr);
-    if (s != RET_OK) return s;
-    // reversed dV = F(rev K', rev Q', rev dO; dS / gamma) into the rev V region; its final state is dS0 / gamma
-    s = chunkwise_impl(kf, qf, dof, vf, B, H, N, dk, dv, dtype, chunk, gamma, nullptr, 0,
-                       d_state_out ? x3 : nullptr, d_state_in, 0, ws, b.fwd_bytes, stream, nullptr);
-    if (s != RET_OK) return s;
+    // The three passes:
+    //   dQ' = F(dO, V, K'; S0^T) straight into d_q
+    //   reversed dK' = F(rev V, rev dO, rev Q'; dS^T / gamma)
+    //   reversed dV = F(rev K', rev Q', rev dO; dS / gamma), whose final state is dS0 / gamma
+    const void* pk = rot ? kr : k;
+    const float* sx1 = state_in ? x1 : nullptr;
+    const float* sx2 = d_state_out ? x2 : nullptr;
+    const float* sx3 = d_state_out ? x3 : nullptr;
+    if (bf16 && dk == dv) {
+        // one shape for all three: a single launch runs them side by side
+        ChunkPlan p;
+        s = plan_chunk(B, H, N, dk, dv, dtype, chunk, 0, p);
+        if (s != RET_OK) return s;
+        ret::ChunkCalls cs;
+        cs.n = 3;
+        fill_chunk_args(cs.a[0], d_o, v, pk, d_q, B, H, N, dv, dk, chunk, 0, sx1, nullptr, p, ws);
+        fill_chunk_args(cs.a[1], vf, dof, qf, dkf, B, H, N, dv, dk, chunk, 0, sx2, nullptr, p, ws + b.fwd_bytes);
+        fill_chunk_args(cs.a[2], kf, qf, dof, dvf, B, H, N, dk, dv, chunk, 0, sx3, d_state_in, p,
+                        ws + 2 * b.fwd_bytes);
+        HeadParams hp_passes = hp;
+        hp_passes.has_theta = 0;
+        if (ret::launch_chunk_bf16_multi(cs, hp_passes, p.dvt, st) != hipSuccess) return RET_ERR_HIP;
+    } else {
+        s = chunkwise_impl(d_o, v, pk, d_q, B, H, N, dv, dk, dtype, chunk, gamma, nullptr, 0, sx1, nullptr, 0, ws,
+                           b.fwd_bytes, stream, nullptr);
+        if (s != RET_OK) return s;
+        s = chunkwise_impl(vf, dof, qf, dkf, B, H, N, dv, dk, dtype, chunk, gamma, nullptr, 0, sx2, nullptr, 0,
+                           ws + b.fwd_bytes, b.fwd_bytes, stream, nullptr);
+        if (s != RET_OK) return s;
+        s = chunkwise_impl(kf, qf, dof, dvf, B, H, N, dk, dv, dtype, chunk, gamma, nullptr, 0, sx3, d_state_in, 0,
+                           ws + 2 * b.fwd_bytes, b.fwd_bytes, stream, nullptr);
+        if (s != RET_OK) return s;
+    }
 
     // back to token order and unrotated coordinates
     memset(&rj.j, 0, sizeof(rj.j));
+    rj.nzero = 0;
     int n = 0;
     if (rot) rj.j[n++] = {d_q, d_q, nullptr, dk, 0, -1, 0};
-    rj.j[n++] = {kr, d_k, nullptr, dk, 1, rot ? -1 : 0, 1};
-    rj.j[n++] = {vf, d_v, nullptr, dv, 1, 0, 1};
+    rj.j[n++] = {dkf, d_k, nullptr, dk, 1, rot ? -1 : 0, 1};
+    rj.j[n++] = {dvf, d_v, nullptr, dv, 1, 0, 1};
     rj.n = n;
     if (ret::launch_rows(rj, hp, bf16, st) != hipSuccess) return RET_ERR_HIP;
     if (d_state_in) {

@@ -19,7 +19,8 @@
 //
 // The kernels here are the HBM-bound glue around those passes: rows_kernel
 // rotates and/or reverses rows (up to four tensors per launch, one per
-// grid row), state_kernel transposes and scales the [dk, dv] states.
+// grid row; one more row can zero-fill the control words of the passes'
+// workspace regions), state_kernel transposes and scales the [dk, dv] states.
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -83,6 +84,16 @@ __device__ __forceinline__ void store8(void* base, size_t i, const float* x) {
 // and writes only its own 8 elements.
 template <bool BF16>
 __global__ __launch_bounds__(kRowThreads) void rows_kernel(RowJobs jobs, HeadParams hp) {
+    if (static_cast<int>(blockIdx.y) == jobs.n) {  // the zero-fill row
+        const long long stride = static_cast<long long>(gridDim.x) * kRowThreads;
+        for (int r = 0; r < 3; ++r) {
+            if (!jobs.zero[r]) continue;
+            for (long long e = static_cast<long long>(blockIdx.x) * kRowThreads + threadIdx.x; e < jobs.nzero;
+                 e += stride)
+                jobs.zero[r][e] = make_uint4(0u, 0u, 0u, 0u);
+        }
+        return;
+    }
     const RowJob& jb = jobs.j[blockIdx.y];
     const int d = jb.d;
     const long long total8 = static_cast<long long>(jobs.B) * jobs.H * jobs.N * d / 8;
@@ -152,7 +163,7 @@ hipError_t launch_rows(const RowJobs& jobs, const HeadParams& hp, bool bf16, hip
     int dmax = 0;
     for (int i = 0; i < jobs.n; ++i) dmax = jobs.j[i].d > dmax ? jobs.j[i].d : dmax;
     const long long items = static_cast<long long>(jobs.B) * jobs.H * jobs.N * dmax / 8;
-    const dim3 grid(grid_for(items, kRowThreads), jobs.n);
+    const dim3 grid(grid_for(items, kRowThreads), jobs.n + (jobs.nzero > 0 ? 1 : 0));
     if (bf16)
         hipLaunchKernelGGL(rows_kernel<true>, grid, dim3(kRowThreads), 0, st, jobs, hp);
     else

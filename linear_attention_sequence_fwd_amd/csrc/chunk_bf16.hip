@@ -163,8 +163,10 @@ __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)
 enum ChunkMode { kSinglePass = 0, kTwoPass = 1, kLocalPass = 2 };
 constexpr int kKeepChunks = 2;
 
+// The body of one workgroup: `bid` is its index among the `nblk` workgroups of
+// its call (the launch may carry several calls of the same shape).
 template <int DK, int DVT, int C, int MODE, bool FAST>
-__global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, HeadParams hp) {
+__device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams& hp, unsigned bid, unsigned nblk) {
     constexpr bool SEGMENTED = MODE != kSinglePass;
     using G = ChunkGeo<DK, DVT, C>;
     constexpr int UK = DK / 8;  // 16-byte units in a row of K (row-major) and of S^T
@@ -209,7 +211,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     unsigned gen = 0;
     if constexpr (SEGMENTED) {
         const int nchains = a.B * a.H * a.nvt;
-        chain = blockIdx.x % nchains;
+        chain = bid % static_cast<unsigned>(nchains);
         unsigned long long* ctl = a.ctl + chain;
         if (tid == 0) *s_ticket = __hip_atomic_fetch_add(ctl, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
@@ -220,7 +222,7 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
         if (tid == 0 && static_cast<unsigned>(tk) == nseg - 1)  // chain's last ticket: reset count, next generation
             __hip_atomic_fetch_add(ctl, (1ull << 32) - nseg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
-        chain = xcd_logical_block(blockIdx.x, gridDim.x);
+        chain = xcd_logical_block(bid, nblk);
     }
     const int vt = chain % a.nvt;
     const int bh = chain / a.nvt;
@@ -1152,22 +1154,76 @@ __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, 
     }
 }
 
+template <int DK, int DVT, int C, int MODE, bool FAST>
+__global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, HeadParams hp) {
+    chunk_body<DK, DVT, C, MODE, FAST>(a, hp, blockIdx.x, gridDim.x);
+}
+
+// Several calls of one shape in one launch, their workgroups interleaved so
+// that all of them progress together: workgroup b serves call b % n. With
+// 64-token chunks of 64 x 64 tiles the body fits the registers of two waves
+// per SIMD, so two workgroups share a compute unit.
+template <int DK, int DVT, int C>
+constexpr int kMultiWaves = (C == 64 && DK == 64 && DVT == 64) ? 2 : 1;
+
+template <int DK, int DVT, int C, int MODE, bool FAST>
+__global__ __launch_bounds__((C / 16) * 64, (kMultiWaves<DK, DVT, C>)) void chunk_bf16_multi_kernel(ChunkCalls cs,
+                                                                                                  HeadParams hp) {
+    const int n = cs.n;
+    const int b = blockIdx.x;
+    chunk_body<DK, DVT, C, MODE, FAST>(cs.a[b % n], hp, b / n, gridDim.x / n);
+}
+
+// Holding two chunks of outputs and queries in registers fits with 64-token
+// chunks (one wave per SIMD) and with small 128-token tiles.
+template <int DK, int DVT, int C>
+constexpr bool kLocalFits = C == 64 || DK + DVT <= 192;
+
+template <int DK, int DVT, int C>
+int chunk_mode(const ChunkArgs& a) {
+    if (a.nseg == 1) return kSinglePass;
+    if (kLocalFits<DK, DVT, C> && a.seg_len <= kKeepChunks * C) return kLocalPass;
+    return kTwoPass;
+}
+
 template <int DK, int DVT, int C, bool FAST>
 static void launch_chunk_form(const ChunkArgs& a, const HeadParams& hp, hipStream_t st, hipEvent_t* e) {
     using G = ChunkGeo<DK, DVT, C>;
-    const int chains = a.B * a.H * a.nvt;
-    // Holding two chunks of outputs and queries in registers fits with 64-token
-    // chunks (one wave per SIMD) and with small 128-token tiles.
-    constexpr bool kLocalFits = C == 64 || DK + DVT <= 192;
-    if (a.nseg == 1)
-        launch_timed(chunk_bf16_kernel<DK, DVT, C, kSinglePass, FAST>, dim3(chains), dim3(G::NTHR), 0, st, e, a,
-                     hp);
-    else if (kLocalFits && a.seg_len <= kKeepChunks * C)
-        launch_timed(chunk_bf16_kernel<DK, DVT, C, kLocalFits ? kLocalPass : kTwoPass, FAST>, dim3(chains * a.nseg),
-                     dim3(G::NTHR), 0, st, e, a, hp);
-    else
-        launch_timed(chunk_bf16_kernel<DK, DVT, C, kTwoPass, FAST>, dim3(chains * a.nseg), dim3(G::NTHR), 0, st, e,
-                     a, hp);
+    constexpr int kLocal = kLocalFits<DK, DVT, C> ? kLocalPass : kTwoPass;
+    const int blocks = a.B * a.H * a.nvt * a.nseg;
+    switch (chunk_mode<DK, DVT, C>(a)) {
+        case kSinglePass:
+            launch_timed(chunk_bf16_kernel<DK, DVT, C, kSinglePass, FAST>, dim3(blocks), dim3(G::NTHR), 0, st, e,
+                         a, hp);
+            break;
+        case kLocalPass:
+            launch_timed(chunk_bf16_kernel<DK, DVT, C, kLocal, FAST>, dim3(blocks), dim3(G::NTHR), 0, st, e, a, hp);
+            break;
+        default:
+            launch_timed(chunk_bf16_kernel<DK, DVT, C, kTwoPass, FAST>, dim3(blocks), dim3(G::NTHR), 0, st, e, a,
+                         hp);
+    }
+}
+
+template <int DK, int DVT, int C, bool FAST>
+static void launch_chunk_multi_form(const ChunkCalls& cs, const HeadParams& hp, hipStream_t st) {
+    using G = ChunkGeo<DK, DVT, C>;
+    constexpr int kLocal = kLocalFits<DK, DVT, C> ? kLocalPass : kTwoPass;
+    const ChunkArgs& a = cs.a[0];
+    const dim3 grid(a.B * a.H * a.nvt * a.nseg * cs.n);
+    switch (chunk_mode<DK, DVT, C>(a)) {
+        case kSinglePass:
+            hipLaunchKernelGGL((chunk_bf16_multi_kernel<DK, DVT, C, kSinglePass, FAST>), grid, dim3(G::NTHR), 0, st,
+                               cs, hp);
+            break;
+        case kLocalPass:
+            hipLaunchKernelGGL((chunk_bf16_multi_kernel<DK, DVT, C, kLocal, FAST>), grid, dim3(G::NTHR), 0, st, cs,
+                               hp);
+            break;
+        default:
+            hipLaunchKernelGGL((chunk_bf16_multi_kernel<DK, DVT, C, kTwoPass, FAST>), grid, dim3(G::NTHR), 0, st,
+                               cs, hp);
+    }
 }
 
 // The FAST form scales values by gamma^-(j+1) for j < C and outputs by
@@ -1193,22 +1249,52 @@ static hipError_t run_chunk_bf16(const ChunkArgs& a, const HeadParams& hp, hipSt
     return hipGetLastError();
 }
 
-hipError_t launch_chunk_bf16(const ChunkArgs& a, const HeadParams& hp, int dvt, hipStream_t st, hipEvent_t* ev) {
-#define RET_CASE(DK_, DVT_, C_) \
-    if (a.dk == DK_ && dvt == DVT_ && a.chunk == C_) return run_chunk_bf16<DK_, DVT_, C_>(a, hp, st, ev);
-    RET_CASE(64, 64, 64)
-    RET_CASE(64, 128, 64)
-    RET_CASE(128, 64, 64)
-    RET_CASE(128, 128, 64)
-    RET_CASE(256, 64, 64)
-    RET_CASE(64, 64, 128)
-    RET_CASE(64, 128, 128)
-    RET_CASE(128, 64, 128)
-    RET_CASE(128, 128, 128)
-    RET_CASE(256, 64, 128)
+template <int DK, int DVT, int C>
+static hipError_t run_chunk_bf16_multi(const ChunkCalls& cs, const HeadParams& hp, hipStream_t st) {
+    if (fast_form_ok(hp, cs.a[0].H, C))
+        launch_chunk_multi_form<DK, DVT, C, true>(cs, hp, st);
+    else
+        launch_chunk_multi_form<DK, DVT, C, false>(cs, hp, st);
+    return hipGetLastError();
+}
+
+#define RET_CHUNK_SHAPES \
+    RET_CASE(64, 64, 64)   \
+    RET_CASE(64, 128, 64)  \
+    RET_CASE(128, 64, 64)  \
+    RET_CASE(128, 128, 64) \
+    RET_CASE(256, 64, 64)  \
+    RET_CASE(64, 64, 128)  \
+    RET_CASE(64, 128, 128) \
+    RET_CASE(128, 64, 128) \
+    RET_CASE(128, 128, 128) \
+    RET_CASE(256, 64, 128) \
     RET_CASE(256, 128, 128)
+
+hipError_t launch_chunk_bf16_multi(const ChunkCalls& cs, const HeadParams& hp, int dvt, hipStream_t st) {
+    if (cs.n < 1 || cs.n > kMaxChunkCalls) return hipErrorInvalidValue;
+    const ChunkArgs& a = cs.a[0];
+    for (int i = 1; i < cs.n; ++i) {  // one shape and one plan for every call
+        const ChunkArgs& b = cs.a[i];
+        if (b.B != a.B || b.H != a.H || b.N != a.N || b.dk != a.dk || b.dv != a.dv || b.chunk != a.chunk ||
+            b.nvt != a.nvt || b.nseg != a.nseg || b.seg_len != a.seg_len || b.grp != a.grp)
+            return hipErrorInvalidValue;
+    }
+#define RET_CASE(DK_, DVT_, C_) \
+    if (a.dk == DK_ && dvt == DVT_ && a.chunk == C_) return run_chunk_bf16_multi<DK_, DVT_, C_>(cs, hp, st);
+    RET_CHUNK_SHAPES
 #undef RET_CASE
     return hipErrorInvalidValue;
 }
+
+hipError_t launch_chunk_bf16(const ChunkArgs& a, const HeadParams& hp, int dvt, hipStream_t st, hipEvent_t* ev) {
+#define RET_CASE(DK_, DVT_, C_) \
+    if (a.dk == DK_ && dvt == DVT_ && a.chunk == C_) return run_chunk_bf16<DK_, DVT_, C_>(a, hp, st, ev);
+    RET_CHUNK_SHAPES
+#undef RET_CASE
+    return hipErrorInvalidValue;
+}
+
+#undef RET_CHUNK_SHAPES
 
 }  // namespace ret

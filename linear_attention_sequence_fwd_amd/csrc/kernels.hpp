@@ -34,6 +34,14 @@ struct ChunkArgs {
     long long pos0;
 };
 
+// Several chunkwise calls of one shape and plan (different tensors, states and
+// workspace regions) run by one launch.
+constexpr int kMaxChunkCalls = 3;
+struct ChunkCalls {
+    ChunkArgs a[kMaxChunkCalls];
+    int n;
+};
+
 struct ParallelArgs {
     const u16* q;
     const u16* k;
@@ -72,6 +80,10 @@ struct RowJobs {
     int n;  // jobs in use
     int B, H, N;
     long long pos0;
+    // Optional extra grid row that zero-fills nzero 16-byte units at each
+    // non-null zero[i] (nzero = 0: none).
+    uint4* zero[3];
+    long long nzero;
 };
 
 // State transforms of the backward: mode 0 writes x1 = s0^T, x2 = ds^T / gamma,
@@ -96,6 +108,7 @@ hipError_t launch_states(const StateJobs& sj, const HeadParams& hp, hipStream_t 
 // (hipExtLaunchKernelGGL); a phase that does not run records its pair back to
 // back.
 hipError_t launch_chunk_bf16(const ChunkArgs& a, const HeadParams& hp, int dvt, hipStream_t st, hipEvent_t* ev);
+hipError_t launch_chunk_bf16_multi(const ChunkCalls& cs, const HeadParams& hp, int dvt, hipStream_t st);
 hipError_t launch_chunk_f32(const ChunkArgs& a, const HeadParams& hp, int dvt, hipStream_t st, hipEvent_t* ev);
 hipError_t launch_parallel_bf16(const ParallelArgs& a, const HeadParams& hp, int dvt, hipStream_t st);
 hipError_t launch_parallel_f32(const ParallelArgs& a, const HeadParams& hp, int dvt, hipStream_t st);

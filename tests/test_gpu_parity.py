@@ -626,3 +626,22 @@ def test_chunkwise_backward_leaves_inputs_and_aliases_state():
     for x, y in zip(a[:3], b[:3]):
         assert torch.equal(x, y)
     assert torch.equal(a[3], ds_alias)
+
+
+def test_chunkwise_backward_workspace_needs_no_clearing():
+    """One workspace, filled with garbage, serves backward calls of several
+    sizes in a row (each clears the counters its passes use)."""
+    shapes = [(1, 2, 700, 64, 64, 64), (1, 1, 4100, 64, 64, 64), (2, 2, 300, 128, 128, 128), (1, 2, 700, 64, 64, 64)]
+    need = max(R.retention_chunkwise_bwd_workspace_size(B, H, N, dk, dv, torch.bfloat16, C)
+               for B, H, N, dk, dv, C in shapes)
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=DEV)
+    for i, (B, H, N, dk, dv, C) in enumerate(shapes):
+        q, k, v = _inputs(B, H, N, dk, dv, torch.bfloat16, 80 + i)
+        d_o, d_s = W.make_upstream_grads(B, H, N, dk, dv, torch.bfloat16, 90 + i)
+        g = orc.head_gammas(H)
+        ref = orc.backward(to64(q), to64(k), to64(v), to64(d_o), g, d_state=to64(d_s))
+        got = R.retention_chunkwise_bwd(q.to(DEV), k.to(DEV), v.to(DEV), d_o.to(DEV), chunk=C,
+                                        d_state_out=d_s.to(DEV), need_d_state_in=True, workspace=ws)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dq", "dk", "dv", "d_state_in"), got, ref):
+            assert_close(to64(a), b, BF16_TOL, f"call {i} {name}")
