@@ -9,6 +9,7 @@ from .retention import (  # noqa: F401
     decode_step,
     half_life,
     head_gammas,
+    msr_epilogue,
     parallel,
     recurrent,
     rotate_pairs,

@@ -42,7 +42,9 @@ Parity status: every public function here is pinned by tests that do not
 restate it (hand-worked values, the decay widget's printed gamma and
 half-life, cross-form agreement, textbook special cases, invariants; the
 backward by hand-worked values, finite differences, which are exact here
-because the loss is affine in each single input entry, and homogeneity). The
+because the loss is affine in each single input entry, and homogeneity; the
+output stage by a hand-worked value, torch's GroupNorm and linear layer, and
+the per-group mean and variance). The
 adjacent-pair rotation convention is a documented choice, not something a
 printed value decides.
 """
@@ -60,6 +62,7 @@ __all__ = [
     "segmented",
     "decode_step",
     "backward",
+    "msr_epilogue",
 ]
 
 
@@ -326,3 +329,34 @@ def backward(q, k, v, d_o, gammas, theta=None, pos0=0, state0=None, d_state=None
         dq_r = rotate_pairs(dq_r, positions, minus)
         dk_r = rotate_pairs(dk_r, positions, minus)
     return dq_r, dk_r, dv_out, dS0
+
+
+def msr_epilogue(o, w_o, gn_weight=None, gn_bias=None, gate=None, eps=1e-6):
+    """Multi-scale retention's output stage: GroupNorm of the concatenated heads,
+    an optional gate, and the output projection.
+
+    "RetNet Guide" section "1. The Parallel Representation for High-Throughput
+    Pretraining" writes MSR(X) = GroupNorm(Concat(R_1, ..., R_H)) W_O; its
+    listing normalises with one group per head (eps 1e-6, per-channel weight
+    and bias) and projects with a bias-free linear layer whose weight is
+    [d_out, H*dv]. "How RetNet Combines ..." names a gating step applied with
+    the GroupNorm but gives no formula: here the gate is an optional tensor the
+    caller supplies, multiplied element by element after the GroupNorm.
+
+    o: [B, H, N, dv] retention outputs; w_o: [d_out, H*dv]; gn_weight, gn_bias:
+    [H*dv] (None: ones / zeros); gate: [B, N, H*dv] or None.
+    Returns y [B, N, d_out] = (GroupNorm(concat) * gate) w_o^T.
+    """
+    o = _as64(o)
+    B, H, N, dv = o.shape
+    x = np.transpose(o, (0, 2, 1, 3))  # [B, N, H, dv]: the heads of one token side by side
+    mean = x.mean(axis=-1, keepdims=True)
+    var = ((x - mean) ** 2).mean(axis=-1, keepdims=True)  # biased, over the head's dv channels
+    z = ((x - mean) / np.sqrt(var + eps)).reshape(B, N, H * dv)
+    if gn_weight is not None:
+        z = z * _as64(gn_weight)
+    if gn_bias is not None:
+        z = z + _as64(gn_bias)
+    if gate is not None:
+        z = z * _as64(gate)
+    return z @ _as64(w_o).T

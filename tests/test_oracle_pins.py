@@ -426,3 +426,48 @@ def test_backward_gamma_one_is_cumulative_sums():
         assert np.allclose(dq[0, 0, n], G[n] @ pre, atol=1e-12)
         assert np.allclose(dv[0, 0, n], K[n] @ suf_qg, atol=1e-12)
         assert np.allclose(dk[0, 0, n], suf_qg @ V[n], atol=1e-12)
+
+
+# ---------------------------------------------------------------- MSR epilogue
+
+
+def test_epilogue_hand_worked():
+    # one head, dv = 2, one token (1, 3): mean 2, biased variance 1, so with
+    # eps = 0 the normalised row is (-1, 1); weight (2, 3), bias (1, 0) give
+    # (-1, 3); gate (1, 0.5) gives (-1, 1.5); w_o = [[1, 1], [2, -1]] gives
+    # (0.5, -3.5).
+    o = np.array([1.0, 3.0]).reshape(1, 1, 1, 2)
+    y = orc.msr_epilogue(o, [[1.0, 1.0], [2.0, -1.0]], gn_weight=[2.0, 3.0], gn_bias=[1.0, 0.0],
+                         gate=np.array([1.0, 0.5]).reshape(1, 1, 2), eps=0.0)
+    assert np.allclose(y.ravel(), [0.5, -3.5], atol=1e-15)
+
+
+def test_epilogue_matches_torch_group_norm_and_linear():
+    # torch's GroupNorm over [tokens, channels] with one group per head is the
+    # listing's normalisation; the oracle computes it by hand
+    torch = pytest.importorskip("torch")
+    B, H, N, dv, d_out = 2, 3, 7, 8, 5
+    o = _rand((B, H, N, dv), 101)
+    w_o, wt, bs = _rand((d_out, H * dv), 102), _rand((H * dv,), 103), _rand((H * dv,), 104)
+    gate = _rand((B, N, H * dv), 105)
+    got = orc.msr_epilogue(o, w_o, gn_weight=wt, gn_bias=bs, gate=gate)
+    x = torch.from_numpy(np.transpose(o, (0, 2, 1, 3)).reshape(B * N, H * dv))
+    gn = torch.nn.functional.group_norm(x, H, torch.from_numpy(wt), torch.from_numpy(bs), eps=1e-6)
+    ref = torch.nn.functional.linear(gn * torch.from_numpy(gate.reshape(B * N, H * dv)), torch.from_numpy(w_o))
+    assert np.allclose(got.reshape(B * N, d_out), ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_epilogue_normalises_each_head_of_each_token():
+    # identity projection, no affine, no gate: every (token, head) group has
+    # mean 0 and variance var / (var + eps); with eps = 0 the result does not
+    # change when a head's outputs are scaled or shifted
+    B, H, N, dv = 1, 4, 6, 16
+    o = _rand((B, H, N, dv), 106) * np.arange(1, H + 1)[None, :, None, None]
+    eye = np.eye(H * dv)
+    y = orc.msr_epilogue(o, eye, eps=1e-6).reshape(B, N, H, dv)
+    x = np.transpose(o, (0, 2, 1, 3))
+    var = x.var(axis=-1)
+    assert np.allclose(y.mean(axis=-1), 0.0, atol=1e-12)
+    assert np.allclose(y.var(axis=-1), var / (var + 1e-6), rtol=1e-12)
+    o2 = o * 3.5 + 2.0
+    assert np.allclose(orc.msr_epilogue(o2, eye, eps=0.0), orc.msr_epilogue(o, eye, eps=0.0), atol=1e-12)
