@@ -250,11 +250,15 @@ def run_only(name, steps, warmup, dev):
                           "bytes_written": dst.numel() * 4}))
         return
     key = {"msr": "msr_bf16_rotary", "layer7b": "layer7b_bf16", "decode": "decode_bf16",
-           "longctx": "longctx_bf16", "single": "single_head_f32", "bwd": "msr_bf16_rotary"}[name]
+           "longctx": "longctx_bf16", "single": "single_head_f32", "bwd": "msr_bf16_rotary",
+           "epi": "layer7b_bf16"}[name]
     w = W.WORKLOADS[key]
     if name == "bwd":
         fn = backward_step(R, W, key, dev)
         key = "msr_bf16_rotary backward"
+    elif name == "epi":
+        fn = epilogue_step(R, W, dev)
+        key = "layer7b output stage"
     elif name == "decode":
         s0, qs, ks, vs = W.make_decode_workload(device=dev, steps=steps + warmup)
         o = torch.empty((w["B"], w["H"], w["dv"]), dtype=w["dtype"], device=dev)
@@ -296,6 +300,25 @@ def backward_step(R, W, name, dev):
     return fn
 
 
+EPI_SHAPE = dict(B=4, H=16, N=8192, dv=512, d_out=4096)  # the 7B-shaped layer's heads into d_model 4096
+
+
+def epilogue_step(R, W, dev):
+    """One retention_msr_epilogue call on the 7B-shaped layer's outputs."""
+    import torch
+
+    e = EPI_SHAPE
+    o, w_o, gw, gb, gt = W.make_epilogue(e["B"], e["H"], e["N"], e["dv"], e["d_out"], 7, device=dev)
+    y = torch.empty((e["B"], e["N"], e["d_out"]), dtype=torch.bfloat16, device=dev)
+    nbytes = R.retention_msr_epilogue_workspace_size(e["B"], e["H"], e["N"], e["dv"], e["d_out"], torch.bfloat16)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+    def fn():
+        R.retention_msr_epilogue(o, w_o, gn_weight=gw, gn_bias=gb, gate=gt, out=y, workspace=ws)
+
+    return fn
+
+
 def sweep_decode_batch(dev):
     """Decode step latency against the number of sequences (H=16, 256x512 fp32
     state per head, bf16 q/k/v): one JSON line per batch size."""
@@ -331,7 +354,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--quick", action="store_true", help="main workload only")
-    ap.add_argument("--only", choices=["msr", "layer7b", "decode", "longctx", "single", "copy", "bwd"],
+    ap.add_argument("--only", choices=["msr", "layer7b", "decode", "longctx", "single", "copy", "bwd", "epi"],
                     help="time one workload only (no CPU baseline); for profilers")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sweep", choices=["decode-batch"], help="print one JSON line per point of a sweep")
@@ -501,6 +524,20 @@ def main():
             "gbs": byb / (msb * 1e-3) / 1e9, "alg_bytes": byb, "alg_flops": flb,
             "forward_graph_ms": ms,
         })
+        torch.cuda.empty_cache()
+
+        # ---------------- output stage of the 7B-shaped layer
+        e = EPI_SHAPE
+        estep = epilogue_step(R, W, dev)
+        mse = time_events(estep, 10, 3)
+        fle = 2.0 * e["B"] * e["N"] * e["H"] * e["dv"] * e["d_out"]
+        also.append({
+            "workload": "output stage of the 7B-shaped layer: GroupNorm (16 heads of 512) + gate + W_O "
+                        "(8192 -> 4096) over 32768 tokens, bf16",
+            "ms": mse, "tokens_per_s": e["B"] * e["N"] / (mse * 1e-3), "tflops": fle / (mse * 1e-3) / 1e12,
+            "mfma_frac": fle / (mse * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, "alg_flops": fle,
+        })
+        del estep
         torch.cuda.empty_cache()
 
         # ---------------- single-head fp32

@@ -212,6 +212,37 @@ ret_status_t retention_recurrent_step(const void* q, const void* k, const void* 
                                       ret_dtype_t dtype, const float* gamma, const float* theta,
                                       const int64_t* pos, void* stream);
 
+/*
+ * Output stage of multi-scale retention ("RetNet Guide" section "1. The
+ * Parallel Representation for High-Throughput Pretraining": MSR(X) =
+ * GroupNorm(Concat(R_1, ..., R_H)) W_O; its listing uses one GroupNorm group
+ * per head with eps 1e-6 and a bias-free projection; "How RetNet Combines
+ * Parallel Training and Constant Inference" adds a gate, with no formula):
+ *     Z[b, n, h*dv + j] = ((o[b,h,n,j] - mean) / sqrt(var + eps) * w[h*dv+j]
+ *                          + beta[h*dv+j]) * gate[b, n, h*dv+j]
+ *     y[b, n, :] = Z[b, n, :] W_O^T
+ * with mean and (biased) var over the dv channels of head h of token n.
+ *
+ * o:         device bf16 [B, H, N, dv], a retention call's output.
+ * gate:      device bf16 [B, N, H*dv] or NULL (no gate); the caller applies
+ *            whatever activation its gate uses.
+ * gn_weight, gn_bias: device float32 [H*dv] or NULL (ones / zeros).
+ * eps:       >= 0 and finite (else RET_ERR_GAMMA).
+ * w_o:       device bf16 [d_out, H*dv] (the layout of a linear layer's weight).
+ * y:         device bf16 [B, N, d_out], written.
+ * workspace: retention_msr_epilogue_workspace_size(...) bytes (holds Z); no
+ *            initialisation needed.
+ * Implemented set: dtype RET_BF16, dv in {64, 128, 256, 512}, d_out a
+ * multiple of 128, H*dv a multiple of 64.
+ */
+ret_status_t retention_msr_epilogue(const void* o, const void* gate, const float* gn_weight,
+                                    const float* gn_bias, float eps, const void* w_o, void* y, int B,
+                                    int H, int N, int dv, int d_out, ret_dtype_t dtype, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace retention_msr_epilogue needs; 0 for sizes it would reject. */
+size_t retention_msr_epilogue_workspace_size(int B, int H, int N, int dv, int d_out, ret_dtype_t dtype);
+
 /* Static, NUL-terminated description of a status code. */
 const char* retention_status_string(ret_status_t status);
 

@@ -21,6 +21,8 @@ __all__ = [
     "retention_recurrent_step",
     "retention_chunkwise_bwd",
     "retention_chunkwise_bwd_workspace_size",
+    "retention_msr_epilogue",
+    "retention_msr_epilogue_workspace_size",
     "retention_status_string",
     "retention_abi_version",
     "LIB_PATH",
@@ -81,6 +83,11 @@ def load_library(path=None):
     lib.retention_chunkwise_bwd.restype = i32
     lib.retention_chunkwise_bwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.retention_chunkwise_bwd_workspace_size.restype = sz
+    f32 = ctypes.c_float
+    lib.retention_msr_epilogue.argtypes = [vp, vp, vp, vp, f32, vp, vp, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+    lib.retention_msr_epilogue.restype = i32
+    lib.retention_msr_epilogue_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.retention_msr_epilogue_workspace_size.restype = sz
     lib.retention_status_string.argtypes = [i32]
     lib.retention_status_string.restype = ctypes.c_char_p
     lib.retention_abi_version.argtypes = []
@@ -304,6 +311,35 @@ def retention_chunkwise_bwd(q, k, v, d_o, chunk=64, gamma=None, theta=None, pos0
     )
     _raise(st, "retention_chunkwise_bwd")
     return d_q, d_k, d_v, d_state_in
+
+
+def retention_msr_epilogue_workspace_size(B, H, N, dv, d_out, dtype):
+    torch = _torch()
+    code = RET_BF16 if dtype == torch.bfloat16 else RET_F32
+    return int(load_library().retention_msr_epilogue_workspace_size(B, H, N, dv, d_out, code))
+
+
+def retention_msr_epilogue(o, w_o, gn_weight=None, gn_bias=None, gate=None, eps=1e-6, out=None, workspace=None,
+                           stream=None):
+    """y = (GroupNorm(concat heads of o) * gate) w_o^T for o [B,H,N,dv] bf16 and
+    w_o [d_out, H*dv] bf16; returns y [B,N,d_out] bf16 (see the C header)."""
+    torch = _torch()
+    _check_dev(o, w_o, gn_weight, gn_bias, gate)
+    B, H, N, dv = o.shape
+    d_out = w_o.shape[0]
+    if out is None:
+        out = torch.empty((B, N, d_out), dtype=o.dtype, device=o.device)
+    _check_dev(out)
+    if workspace is None:
+        nbytes = retention_msr_epilogue_workspace_size(B, H, N, dv, d_out, o.dtype)
+        if nbytes:
+            workspace = _cached_workspace(nbytes, o.device, stream, kind="epilogue")
+    st = load_library().retention_msr_epilogue(
+        _ptr(o), _ptr(gate), _ptr(gn_weight), _ptr(gn_bias), float(eps), _ptr(w_o), _ptr(out), B, H, N, dv, d_out,
+        _dtype_code(o), _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream(stream),
+    )
+    _raise(st, "retention_msr_epilogue")
+    return out
 
 
 def retention_recurrent_step(q, k, v, state, gamma=None, theta=None, pos=None, out=None, stream=None):

@@ -413,6 +413,52 @@ ret_status_t retention_chunkwise_bwd(const void* q, const void* k, const void* v
     return RET_OK;
 }
 
+size_t retention_msr_epilogue_workspace_size(int B, int H, int N, int dv, int d_out, ret_dtype_t dtype) {
+    if (B < 1 || H < 1 || N < 1 || dv < 1 || d_out < 1 || dtype != RET_BF16) return 0;
+    if (dv != 64 && dv != 128 && dv != 256 && dv != 512) return 0;
+    if (d_out % 128 != 0 || (static_cast<long long>(H) * dv) % 64 != 0) return 0;
+    const double rows = static_cast<double>(B) * N;
+    if (rows > 2147483647.0 || rows * H * dv > 9.0e15) return 0;
+    return round256(static_cast<size_t>(B) * N * H * dv * sizeof(uint16_t));
+}
+
+ret_status_t retention_msr_epilogue(const void* o, const void* gate, const float* gn_weight, const float* gn_bias,
+                                    float eps, const void* w_o, void* y, int B, int H, int N, int dv, int d_out,
+                                    ret_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!o || !w_o || !y) return RET_ERR_NULL;
+    if (B < 1 || H < 1 || N < 1 || dv < 1 || d_out < 1) return RET_ERR_SHAPE;
+    if (dtype != RET_F32 && dtype != RET_BF16) return RET_ERR_DTYPE;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return RET_ERR_GAMMA;
+    if (!aligned16(o) || !aligned16(gate) || !aligned16(gn_weight) || !aligned16(gn_bias) || !aligned16(w_o) ||
+        !aligned16(y) || !aligned16(workspace))
+        return RET_ERR_ALIGN;
+    const size_t need = retention_msr_epilogue_workspace_size(B, H, N, dv, d_out, dtype);
+    if (need == 0) return RET_ERR_UNSUPPORTED;
+    if (workspace == nullptr || workspace_bytes < need) return RET_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    ret::EpilogueArgs a;
+    a.o = static_cast<const ret::u16*>(o);
+    a.gate = static_cast<const ret::u16*>(gate);
+    a.gn_weight = gn_weight;
+    a.gn_bias = gn_bias;
+    a.z = static_cast<ret::u16*>(workspace);
+    a.B = B;
+    a.H = H;
+    a.N = N;
+    a.dv = dv;
+    a.eps = eps;
+    if (ret::launch_groupnorm_gate(a, st) != hipSuccess) return RET_ERR_HIP;
+    ret::GemmArgs g;
+    g.a = a.z;
+    g.b = static_cast<const ret::u16*>(w_o);
+    g.c = static_cast<ret::u16*>(y);
+    g.M = B * N;
+    g.N = d_out;
+    g.K = H * dv;
+    if (ret::launch_gemm_bt(g, st) != hipSuccess) return RET_ERR_HIP;
+    return RET_OK;
+}
+
 ret_status_t retention_parallel_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N,
                                     int dk, int dv, ret_dtype_t dtype, const float* gamma, const float* theta,
                                     int64_t pos0, void* stream) {

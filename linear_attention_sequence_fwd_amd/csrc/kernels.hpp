@@ -99,6 +99,27 @@ struct StateJobs {
     int mode;
 };
 
+// Output stage (epilogue.hip).
+struct EpilogueArgs {
+    const u16* o;          // [B,H,N,dv] bf16
+    const u16* gate;       // [B*N, H*dv] bf16 or nullptr
+    const float* gn_weight;  // [H*dv] or nullptr (ones)
+    const float* gn_bias;    // [H*dv] or nullptr (zeros)
+    u16* z;                // [B*N, H*dv] bf16 out
+    int B, H, N, dv;
+    float eps;
+};
+
+struct GemmArgs {  // c[M, N] = a[M, K] b[N, K]^T, all bf16 row-major
+    const u16* a;
+    const u16* b;
+    u16* c;
+    int M, N, K;
+};
+
+hipError_t launch_groupnorm_gate(const EpilogueArgs& a, hipStream_t st);
+hipError_t launch_gemm_bt(const GemmArgs& g, hipStream_t st);
+
 hipError_t launch_rows(const RowJobs& jobs, const HeadParams& hp, bool bf16, hipStream_t st);
 hipError_t launch_states(const StateJobs& sj, const HeadParams& hp, hipStream_t st);
 

@@ -88,3 +88,18 @@ def make_upstream_grads(B, H, N, dk, dv, dtype, seed, device="cpu"):
     d_o = torch.randn((B, H, N, dv), generator=g, device=device, dtype=torch.float32).to(dtype)
     d_s = torch.randn((B, H, dk, dv), generator=g, device=device, dtype=torch.float32)
     return d_o, d_s
+
+
+def make_epilogue(B, H, N, dv, d_out, seed, device="cpu", dtype=torch.bfloat16):
+    """Inputs of the output stage: retention outputs o [B,H,N,dv] ~ N(0,1),
+    projection weight [d_out, H*dv] ~ N(0,1)/sqrt(H*dv) (random init, no
+    trained weights exist here), GroupNorm weight ~ 1 + 0.1 N(0,1) and bias
+    ~ 0.1 N(0,1) (float32 [H*dv]), and a gate ~ U(0,1) [B,N,H*dv]."""
+    g = _gen(device, seed)
+    K = H * dv
+    o = torch.randn((B, H, N, dv), generator=g, device=device, dtype=torch.float32).to(dtype)
+    w_o = torch.randn((d_out, K), generator=g, device=device, dtype=torch.float32).mul_(1.0 / math.sqrt(K)).to(dtype)
+    gn_w = torch.randn((K,), generator=g, device=device, dtype=torch.float32).mul_(0.1).add_(1.0)
+    gn_b = torch.randn((K,), generator=g, device=device, dtype=torch.float32).mul_(0.1)
+    gate = torch.rand((B, N, K), generator=g, device=device, dtype=torch.float32).to(dtype)
+    return o, w_o, gn_w, gn_b, gate

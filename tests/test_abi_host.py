@@ -210,3 +210,30 @@ def test_backward_validation(lib):
     assert lib.retention_chunkwise_bwd_workspace_size(1, 2, 200, 64, 64, BF16, 64) > need
     assert lib.retention_chunkwise_bwd_workspace_size(1, 2, 100, 64, 512, BF16, 64) == 0
     assert lib.retention_chunkwise_bwd_workspace_size(1, 2, 100, 64, 64, BF16, 48) == 0
+
+
+def epi(lib, **kw):
+    a = dict(o=A, gate=None, w=None, b=None, eps=1e-6, w_o=A, y=A, B=1, H=2, N=100, dv=64, d_out=128, dtype=BF16,
+             ws=None, ws_bytes=0)
+    a.update(kw)
+    return lib.retention_msr_epilogue(a["o"], a["gate"], a["w"], a["b"], a["eps"], a["w_o"], a["y"], a["B"], a["H"],
+                                      a["N"], a["dv"], a["d_out"], a["dtype"], a["ws"], a["ws_bytes"], None)
+
+
+def test_epilogue_validation(lib):
+    for key in ("o", "w_o", "y"):
+        assert epi(lib, **{key: None}) == NULL
+    for key in ("B", "H", "N", "dv", "d_out"):
+        assert epi(lib, **{key: 0}) == SHAPE
+    assert epi(lib, dtype=9) == DTYPE
+    assert epi(lib, eps=-1.0) == GAMMA
+    assert epi(lib, eps=float("nan")) == GAMMA
+    assert epi(lib, gate=A + 2) == ALIGN
+    assert epi(lib, dtype=F32) == UNSUP
+    assert epi(lib, dv=96) == UNSUP
+    assert epi(lib, d_out=100) == UNSUP
+    need = lib.retention_msr_epilogue_workspace_size(1, 2, 100, 64, 128, BF16)
+    assert need >= 100 * 128 * 2
+    assert epi(lib) == WS
+    assert epi(lib, ws=A, ws_bytes=need - 1) == WS
+    assert lib.retention_msr_epilogue_workspace_size(1, 2, 100, 64, 100, BF16) == 0

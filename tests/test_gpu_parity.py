@@ -645,3 +645,50 @@ def test_chunkwise_backward_workspace_needs_no_clearing():
         torch.cuda.synchronize()
         for name, a, b in zip(("dq", "dk", "dv", "d_state_in"), got, ref):
             assert_close(to64(a), b, BF16_TOL, f"call {i} {name}")
+
+
+# ------------------------------------------------------------ output stage
+
+EPI_CASES = [
+    # B, H, N, dv, d_out, gate, affine
+    (2, 3, 50, 64, 128, False, False),
+    (2, 3, 50, 64, 128, True, True),
+    (1, 2, 300, 128, 256, True, False),
+    (1, 1, 130, 256, 128, False, True),
+    (1, 2, 77, 512, 384, True, True),
+    (3, 4, 129, 64, 640, True, True),
+]
+
+
+def _epi_check(B, H, N, dv, d_out, gate, affine, seed):
+    o, w_o, gw, gb, gt = W.make_epilogue(B, H, N, dv, d_out, seed)
+    ref = orc.msr_epilogue(to64(o), to64(w_o), gn_weight=to64(gw) if affine else None,
+                           gn_bias=to64(gb) if affine else None, gate=to64(gt) if gate else None)
+    got = R.retention_msr_epilogue(o.to(DEV), w_o.to(DEV), gn_weight=gw.to(DEV) if affine else None,
+                                   gn_bias=gb.to(DEV) if affine else None, gate=gt.to(DEV) if gate else None)
+    torch.cuda.synchronize()
+    assert_close(to64(got), ref, BF16_TOL, "y", per_head_axes=1)
+
+
+@pytest.mark.parametrize("case", EPI_CASES, ids=lambda c: "B{}H{}N{}dv{}out{}gate{}aff{}".format(*c))
+def test_msr_epilogue_small(case):
+    _epi_check(*case, seed=111)
+
+
+def test_msr_epilogue_msr_full():
+    _epi_check(2, 8, 2048, 64, 512, True, True, seed=112)
+
+
+def test_msr_epilogue_layer7b_sampled_rows():
+    """The 7B-shaped layer's output stage (32768 tokens, 16 heads of 512, d_out
+    4096) as the benchmark runs it; 96 sampled tokens recomputed by the oracle."""
+    B, H, N, dv, d_out = 4, 16, 8192, 512, 4096
+    o, w_o, gw, gb, gt = W.make_epilogue(B, H, N, dv, d_out, 113, device=DEV)
+    y = R.retention_msr_epilogue(o, w_o, gn_weight=gw, gn_bias=gb, gate=gt)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    bs, ns = rng.integers(0, B, 96), rng.integers(0, N, 96)
+    ns[:4] = [0, N - 1, 1, N - 2]
+    o_s = to64(o[bs, :, ns, :])[:, :, None, :]   # [96, H, 1, dv]: each sampled token as its own batch entry
+    ref = orc.msr_epilogue(o_s, to64(w_o), gn_weight=to64(gw), gn_bias=to64(gb), gate=to64(gt[bs, ns])[:, None, :])
+    assert_close(to64(y[bs, ns])[:, None, :], ref, BF16_TOL, "sampled rows", per_head_axes=1)
