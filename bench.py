@@ -540,6 +540,39 @@ def main():
         del estep
         torch.cuda.empty_cache()
 
+        # ---------------- decode step + output stage (one token per sequence through the layer's W_O)
+        w = W.WORKLOADS["decode_bf16"]
+        s0, qs, ks, vs = W.make_decode_workload(device=dev, steps=8)
+        _, w_o, gw, gb, gt = W.make_epilogue(w["B"], w["H"], 1, w["dv"], 4096, 8, device=dev)
+        gt = gt[:, 0, :].contiguous()
+        yd = torch.empty((w["B"], 4096), dtype=torch.bfloat16, device=dev)
+        od = torch.empty((w["B"], w["H"], w["dv"]), dtype=torch.bfloat16, device=dev)
+        itd = [0]
+
+        def dstep():
+            t = itd[0] % 8
+            itd[0] += 1
+            R.retention_recurrent_step_msr(qs[t], ks[t], vs[t], s0, w_o, gate=gt, gn_weight=gw, gn_bias=gb, o=od,
+                                           out=yd)
+
+        msd, spd = time_graph(dstep, 100, 10)
+        itd[0] = 0
+
+        def ostep():
+            R.retention_msr_epilogue(od.view(w["B"], w["H"], 1, w["dv"]), w_o, gn_weight=gw, gn_bias=gb,
+                                     gate=gt.view(w["B"], 1, -1), out=yd.view(w["B"], 1, 4096))
+
+        mso, _ = time_graph(ostep, 100, 10)
+        wbytes = 4096 * w["H"] * w["dv"] * 2
+        also.append({
+            "workload": "decode step + output stage: 64 sequences x H=16 (state 256x512) -> GroupNorm, gate, "
+                        "W_O 8192 -> 4096, bf16",
+            "ms_per_token_step": msd, "spread": spd, "output_stage_ms": mso,
+            "output_stage_w_o_gbs": wbytes / (mso * 1e-3) / 1e9,
+        })
+        del s0, qs, ks, vs, w_o, gw, gb, gt, yd, od
+        torch.cuda.empty_cache()
+
         # ---------------- single-head fp32
         q, k, v, _ = W.make_workload("single_head_f32", device=dev)
         ms1 = time_events(lambda: R.retention_chunkwise_fwd(q, k, v, chunk=64), 50, 5)

@@ -243,6 +243,26 @@ ret_status_t retention_msr_epilogue(const void* o, const void* gate, const float
 /* Bytes of workspace retention_msr_epilogue needs; 0 for sizes it would reject. */
 size_t retention_msr_epilogue_workspace_size(int B, int H, int N, int dv, int d_out, ret_dtype_t dtype);
 
+/*
+ * One decode step of a multi-scale retention layer: retention_recurrent_step
+ * (state updated in place, o = q' S written to `o`, device [B, H, dv]) followed
+ * by retention_msr_epilogue on that token (o read as [B, H, 1, dv]; gate
+ * [B, H*dv] or NULL): y [B, d_out] = (GroupNorm(o) * gate) W_O^T ("RetNet
+ * Guide" section "2. The Recurrent Representation for Constant-Memory O(1)
+ * Decoding": the listing's recurrent step normalises and projects each
+ * token's output). With few tokens the projection splits its contraction over
+ * workgroups so the whole of W_O streams from HBM in parallel.
+ * Arguments as in the two calls; workspace:
+ * retention_msr_epilogue_workspace_size(B, H, 1, dv, d_out, RET_BF16) bytes.
+ * Implemented set: bf16, and each call's own set.
+ */
+ret_status_t retention_recurrent_step_msr(const void* q, const void* k, const void* v, float* state,
+                                          int B, int H, int dk, int dv, ret_dtype_t dtype,
+                                          const float* gamma, const float* theta, const int64_t* pos,
+                                          const void* gate, const float* gn_weight, const float* gn_bias,
+                                          float eps, const void* w_o, int d_out, void* o, void* y,
+                                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* retention_status_string(ret_status_t status);
 

@@ -23,6 +23,7 @@ __all__ = [
     "retention_chunkwise_bwd_workspace_size",
     "retention_msr_epilogue",
     "retention_msr_epilogue_workspace_size",
+    "retention_recurrent_step_msr",
     "retention_status_string",
     "retention_abi_version",
     "LIB_PATH",
@@ -88,6 +89,9 @@ def load_library(path=None):
     lib.retention_msr_epilogue.restype = i32
     lib.retention_msr_epilogue_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.retention_msr_epilogue_workspace_size.restype = sz
+    lib.retention_recurrent_step_msr.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, fp, fp, vp, vp, vp, vp,
+                                                 f32, vp, i32, vp, vp, vp, sz, vp]
+    lib.retention_recurrent_step_msr.restype = i32
     lib.retention_status_string.argtypes = [i32]
     lib.retention_status_string.restype = ctypes.c_char_p
     lib.retention_abi_version.argtypes = []
@@ -340,6 +344,36 @@ def retention_msr_epilogue(o, w_o, gn_weight=None, gn_bias=None, gate=None, eps=
     )
     _raise(st, "retention_msr_epilogue")
     return out
+
+
+def retention_recurrent_step_msr(q, k, v, state, w_o, gamma=None, theta=None, pos=None, gate=None, gn_weight=None,
+                                 gn_bias=None, eps=1e-6, o=None, out=None, workspace=None, stream=None):
+    """One decode step and the layer's output stage: returns (y [B,d_out], o [B,H,dv]); the state is updated in place."""
+    torch = _torch()
+    _check_dev(q, k, v, state, w_o, pos, gate, gn_weight, gn_bias)
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    d_out = w_o.shape[0]
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=v.dtype, device=v.device)
+    if out is None:
+        out = torch.empty((B, d_out), dtype=v.dtype, device=v.device)
+    _check_dev(o, out)
+    if pos is not None and pos.dtype != torch.int64:
+        raise TypeError("pos must be int64")
+    if workspace is None:
+        nbytes = retention_msr_epilogue_workspace_size(B, H, 1, dv, d_out, v.dtype)
+        if nbytes:
+            workspace = _cached_workspace(nbytes, v.device, stream, kind="epilogue")
+    _g, g = _host_floats(gamma, H, "gamma")
+    _t, th = _host_floats(theta, dk // 2, "theta")
+    st = load_library().retention_recurrent_step_msr(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(state), B, H, dk, dv, _dtype_code(q), g, th, _ptr(pos), _ptr(gate),
+        _ptr(gn_weight), _ptr(gn_bias), float(eps), _ptr(w_o), d_out, _ptr(o), _ptr(out), _ptr(workspace),
+        workspace.numel() if workspace is not None else 0, _stream(stream),
+    )
+    _raise(st, "retention_recurrent_step_msr")
+    return out, o
 
 
 def retention_recurrent_step(q, k, v, state, gamma=None, theta=None, pos=None, out=None, stream=None):

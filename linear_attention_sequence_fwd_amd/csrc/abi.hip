@@ -419,7 +419,9 @@ size_t retention_msr_epilogue_workspace_size(int B, int H, int N, int dv, int d_
     if (d_out % 128 != 0 || (static_cast<long long>(H) * dv) % 64 != 0) return 0;
     const double rows = static_cast<double>(B) * N;
     if (rows > 2147483647.0 || rows * H * dv > 9.0e15) return 0;
-    return round256(static_cast<size_t>(B) * N * H * dv * sizeof(uint16_t));
+    const int splits = ret::gemm_splits(B * N, d_out, H * dv);
+    const size_t part = splits > 1 ? static_cast<size_t>(splits) * B * N * d_out * sizeof(float) : 0;
+    return round256(static_cast<size_t>(B) * N * H * dv * sizeof(uint16_t)) + part;
 }
 
 ret_status_t retention_msr_epilogue(const void* o, const void* gate, const float* gn_weight, const float* gn_bias,
@@ -455,8 +457,40 @@ ret_status_t retention_msr_epilogue(const void* o, const void* gate, const float
     g.M = B * N;
     g.N = d_out;
     g.K = H * dv;
+    g.splits = ret::gemm_splits(g.M, g.N, g.K);
+    g.part = g.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                     round256(static_cast<size_t>(B) * N * H * dv * sizeof(uint16_t)))
+                          : nullptr;
     if (ret::launch_gemm_bt(g, st) != hipSuccess) return RET_ERR_HIP;
     return RET_OK;
+}
+
+ret_status_t retention_recurrent_step_msr(const void* q, const void* k, const void* v, float* state, int B, int H,
+                                          int dk, int dv, ret_dtype_t dtype, const float* gamma, const float* theta,
+                                          const int64_t* pos, const void* gate, const float* gn_weight,
+                                          const float* gn_bias, float eps, const void* w_o, int d_out, void* o,
+                                          void* y, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !o || !state || !w_o || !y) return RET_ERR_NULL;
+    if (theta && !pos) return RET_ERR_NULL;
+    ret_status_t s = check_common(B, H, 1, dk, dv, dtype, theta);
+    if (s != RET_OK) return s;
+    if (d_out < 1) return RET_ERR_SHAPE;
+    HeadParams hp;
+    s = fill_head_params(hp, H, dk, gamma, theta);
+    if (s != RET_OK) return s;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return RET_ERR_GAMMA;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(state) || !aligned16(pos) ||
+        !aligned16(gate) || !aligned16(gn_weight) || !aligned16(gn_bias) || !aligned16(w_o) || !aligned16(y) ||
+        !aligned16(workspace))
+        return RET_ERR_ALIGN;
+    if (dtype != RET_BF16 || dv % 4 != 0 || dv > 1024 || dk > 4096) return RET_ERR_UNSUPPORTED;
+    const size_t need = retention_msr_epilogue_workspace_size(B, H, 1, dv, d_out, dtype);
+    if (need == 0) return RET_ERR_UNSUPPORTED;
+    if (workspace == nullptr || workspace_bytes < need) return RET_ERR_WORKSPACE;
+    s = retention_recurrent_step(q, k, v, o, state, B, H, dk, dv, dtype, gamma, theta, pos, stream);
+    if (s != RET_OK) return s;
+    return retention_msr_epilogue(o, gate, gn_weight, gn_bias, eps, w_o, y, B, H, 1, dv, d_out, dtype, workspace,
+                                  workspace_bytes, stream);
 }
 
 ret_status_t retention_parallel_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N,

@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kNormThreads) void groupnorm_gate_kernel(EpilogueAr
 // read touches land in different banks. A global-to-LDS load writes 1 KiB per
 // wave at consecutive addresses (16 bytes per lane), so lane l of load i fills
 // row R = 8 i + l / 8, position l % 8, and fetches the chunk that belongs there.
-constexpr int GM = 256, GK = 64;
+constexpr int GK = 64;
 constexpr int kGroupM = 8;   // row tiles per group of the tile order
 // Eight waves in 2 x 4: 128 x 64 output blocks (128 accumulator registers a
 // lane, held in ordinary VGPRs), two waves per SIMD. Four waves with 128 x 128
@@ -174,14 +174,14 @@ __device__ __forceinline__ uint4 panel_read(const u16* lds, int r, int c) {
 // next step fill (an, bn) when `more`; then wait for those loads and
 // synchronise. The two stages are distinct LDS objects, so the compiler can
 // see that reading one does not wait for the loads into the other.
-template <int BN, int WM, int WN, int NW>
+template <int BM, int BN, int WM, int WN, int NW>
 __device__ __forceinline__ void gemm_step(f32x4 (&acc)[WM / 16][WN / 16], const u16* as, const u16* bs, u16* an,
                                           u16* bn, bool more, const GemmArgs& g, int m0, int n0, int knext, int wm,
                                           int wn, int wave, int lane) {
     constexpr int TI = WM / 16, TJ = WN / 16;
     const int l16 = lane & 15, grp = lane >> 4;
     if (more) {
-        panel_fill<GM, NW>(an, g.a, m0, g.M, g.K, knext, wave, lane);
+        panel_fill<BM, NW>(an, g.a, m0, g.M, g.K, knext, wave, lane);
         panel_fill<BN, NW>(bn, g.b, n0, g.N, g.K, knext, wave, lane);
     }
 #pragma unroll
@@ -201,9 +201,12 @@ __device__ __forceinline__ void gemm_step(f32x4 (&acc)[WM / 16][WN / 16], const 
     __syncthreads();
 }
 
-// NWM x NWN waves; wave tile (GM / NWM) x (BN / NWN).
-template <int BN, int NWM, int NWN>
+// NWM x NWN waves; wave tile (BM / NWM) x (BN / NWN). With SPLIT, workgroup
+// b multiplies K range (b / tiles) of g.splits equal ranges for tile b % tiles
+// and writes float32 partial sums (reduced by reduce_splits_kernel).
+template <int BM, int BN, int NWM, int NWN, bool SPLIT>
 __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bt_kernel(GemmArgs g) {
+    constexpr int GM = BM;
     constexpr int NW = NWM * NWN;
     constexpr int WM = GM / NWM, WN = BN / NWN;  // wave tile
     constexpr int TI = WM / 16, TJ = WN / 16;    // 16 x 16 accumulator tiles per wave
@@ -220,7 +223,8 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bt_kernel(GemmArgs g) {
     // tile order: consecutive ids on one XCD, grouped by kGroupM row tiles so
     // that the workgroups running together share row and column panels in L2
     const int tiles_m = (g.M + GM - 1) / GM, tiles_n = g.N / BN;
-    const int id = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int split = SPLIT ? static_cast<int>(blockIdx.x) / (tiles_m * tiles_n) : 0;
+    const int id = SPLIT ? static_cast<int>(blockIdx.x) % (tiles_m * tiles_n) : xcd_logical_block(blockIdx.x, gridDim.x);
     const int per_group = kGroupM * tiles_n;
     const int first_m = (id / per_group) * kGroupM;
     const int gsize = min(tiles_m - first_m, kGroupM);
@@ -234,24 +238,39 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bt_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int KT = g.K / GK;
-    panel_fill<GM, NW>(a0, g.a, m0, g.M, g.K, 0, wave, lane);
-    panel_fill<BN, NW>(b0, g.b, n0, g.N, g.K, 0, wave, lane);
+    const int KT = g.K / GK / (SPLIT ? g.splits : 1);  // K steps of this workgroup
+    const int kb = split * KT * GK;                     // first K index
+    panel_fill<GM, NW>(a0, g.a, m0, g.M, g.K, kb, wave, lane);
+    panel_fill<BN, NW>(b0, g.b, n0, g.N, g.K, kb, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int kt = 0; kt < KT; kt += 2) {
-        gemm_step<BN, WM, WN, NW>(acc, a0, b0, a1, b1, kt + 1 < KT, g, m0, n0, (kt + 1) * GK, wm, wn, wave, lane);
-        if (kt + 1 < KT)
-            gemm_step<BN, WM, WN, NW>(acc, a1, b1, a0, b0, kt + 2 < KT, g, m0, n0, (kt + 2) * GK, wm, wn, wave,
+        gemm_step<BM, BN, WM, WN, NW>(acc, a0, b0, a1, b1, kt + 1 < KT, g, m0, n0, kb + (kt + 1) * GK, wm, wn, wave,
                                       lane);
+        if (kt + 1 < KT)
+            gemm_step<BM, BN, WM, WN, NW>(acc, a1, b1, a0, b0, kt + 2 < KT, g, m0, n0, kb + (kt + 2) * GK, wm, wn,
+                                          wave, lane);
+    }
+    if constexpr (SPLIT) {  // four consecutive float32 columns of one row per lane
+        float* part = g.part + static_cast<size_t>(split) * g.M * g.N;
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+            const int row = m0 + wm * WM + i * 16 + l16;
+            if (row < g.M)
+#pragma unroll
+                for (int j = 0; j < TJ; ++j)
+                    *reinterpret_cast<f32x4*>(part + static_cast<size_t>(row) * g.N + n0 + wn * WN + j * 16 +
+                                              4 * grp) = acc[i][j];
+        }
+        return;
     }
 
     // acc[i][j][r]: output row m0 + wm*WM + i*16 + l16, column n0 + wn*WN + j*16 + 4*grp + r:
     // four consecutive columns of one row per lane. Stage SLICE-row slices
     // through LDS and store rows with 16-byte writes.
     constexpr int LDC = BN + 8;
-    constexpr int SLICE = 32;
-    static_assert(SLICE * LDC <= GM * GK, "slice fits one A stage");
+    constexpr int SLICE = GM < 32 ? GM : 32;
+    static_assert(SPLIT || SLICE * LDC <= GM * GK, "slice fits one A stage");
     u16* cs = a0;
 #pragma unroll
     for (int sl = 0; sl < GM / SLICE; ++sl) {
@@ -282,6 +301,20 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bt_kernel(GemmArgs g) {
     }
 }
 
+// c[m][n] = bf16(sum over splits of part[split][m][n]), 8 outputs per thread.
+__global__ __launch_bounds__(256) void reduce_splits_kernel(GemmArgs g) {
+    const long long e = (static_cast<long long>(blockIdx.x) * 256 + threadIdx.x) * 8;
+    if (e >= static_cast<long long>(g.M) * g.N) return;
+    f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < g.splits; ++s) {
+        const f32x4* p = reinterpret_cast<const f32x4*>(g.part + static_cast<size_t>(s) * g.M * g.N + e);
+        lo += p[0];
+        hi += p[1];
+    }
+    *reinterpret_cast<uint4*>(g.c + e) =
+        make_uint4(pack2_bf16(lo[0], lo[1]), pack2_bf16(lo[2], lo[3]), pack2_bf16(hi[0], hi[1]), pack2_bf16(hi[2], hi[3]));
+}
+
 }  // namespace
 
 hipError_t launch_groupnorm_gate(const EpilogueArgs& a, hipStream_t st) {
@@ -303,14 +336,36 @@ hipError_t launch_groupnorm_gate(const EpilogueArgs& a, hipStream_t st) {
 
 hipError_t launch_gemm_bt(const GemmArgs& g, hipStream_t st) {
     if (g.M < 1 || g.N % 128 != 0 || g.K % GK != 0 || g.K < GK) return hipErrorInvalidValue;
-    const long long tiles_m = (g.M + GM - 1) / GM;
+    const int splits = gemm_splits(g.M, g.N, g.K);
+    if (splits > 1) {  // few rows (a decode step's tokens): split K, then sum the partials
+        if (!g.part || g.splits != splits) return hipErrorInvalidValue;
+        const unsigned tiles = static_cast<unsigned>((g.M + 63) / 64) * (g.N / 128);
+        hipLaunchKernelGGL((gemm_bt_kernel<64, 128, kWavesM, kWavesN, true>), dim3(tiles * splits),
+                           dim3(kWavesM * kWavesN * 64), 0, st, g);
+        const long long n8 = static_cast<long long>(g.M) * g.N / 8;
+        hipLaunchKernelGGL(reduce_splits_kernel, dim3(static_cast<unsigned>((n8 + 255) / 256)), dim3(256), 0, st, g);
+        return hipGetLastError();
+    }
+    const long long tiles_m = (g.M + 255) / 256;
     if (g.N % 256 == 0)
-        hipLaunchKernelGGL((gemm_bt_kernel<256, kWavesM, kWavesN>),
+        hipLaunchKernelGGL((gemm_bt_kernel<256, 256, kWavesM, kWavesN, false>),
                            dim3(static_cast<unsigned>(tiles_m * (g.N / 256))), dim3(kWavesM * kWavesN * 64), 0, st, g);
     else
-        hipLaunchKernelGGL((gemm_bt_kernel<128, kWavesM, kWavesN>),
+        hipLaunchKernelGGL((gemm_bt_kernel<256, 128, kWavesM, kWavesN, false>),
                            dim3(static_cast<unsigned>(tiles_m * (g.N / 128))), dim3(kWavesM * kWavesN * 64), 0, st, g);
     return hipGetLastError();
+}
+
+// K splits for c = a b^T: 1 unless there are at most 64 rows, then enough
+// splits (a divisor of K/64, at most 16) that the 64 x 128 tiles times the
+// splits give about 256 workgroups, one per compute unit.
+int gemm_splits(int M, int N, int K) {
+    if (M > 64) return 1;
+    const int tiles = N / 128, steps = K / GK;
+    int s = 1;
+    for (int c = 2; c <= 16; ++c)
+        if (steps % c == 0 && static_cast<long long>(tiles) * c <= 256) s = c;
+    return s;
 }
 
 }  // namespace ret

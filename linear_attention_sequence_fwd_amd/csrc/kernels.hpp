@@ -114,8 +114,12 @@ struct GemmArgs {  // c[M, N] = a[M, K] b[N, K]^T, all bf16 row-major
     const u16* a;
     const u16* b;
     u16* c;
+    float* part;  // [splits][M][N] float32 partial sums when gemm_splits(M, N, K) > 1
     int M, N, K;
+    int splits;
 };
+
+int gemm_splits(int M, int N, int K);
 
 hipError_t launch_groupnorm_gate(const EpilogueArgs& a, hipStream_t st);
 hipError_t launch_gemm_bt(const GemmArgs& g, hipStream_t st);

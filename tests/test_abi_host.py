@@ -237,3 +237,24 @@ def test_epilogue_validation(lib):
     assert epi(lib) == WS
     assert epi(lib, ws=A, ws_bytes=need - 1) == WS
     assert lib.retention_msr_epilogue_workspace_size(1, 2, 100, 64, 100, BF16) == 0
+
+
+def test_decode_msr_validation(lib):
+    def call(**kw):
+        a = dict(q=A, k=A, v=A, state=A, B=2, H=2, dk=64, dv=64, dtype=BF16, gamma=None, theta=None, pos=None,
+                 gate=None, w=None, b=None, eps=1e-6, w_o=A, d_out=128, o=A, y=A, ws=None, ws_bytes=0)
+        a.update(kw)
+        return lib.retention_recurrent_step_msr(a["q"], a["k"], a["v"], a["state"], a["B"], a["H"], a["dk"], a["dv"],
+                                                a["dtype"], a["gamma"], a["theta"], a["pos"], a["gate"], a["w"], a["b"],
+                                                a["eps"], a["w_o"], a["d_out"], a["o"], a["y"], a["ws"], a["ws_bytes"],
+                                                None)
+    for key in ("q", "k", "v", "state", "w_o", "o", "y"):
+        assert call(**{key: None}) == NULL
+    assert call(B=0) == SHAPE
+    assert call(d_out=0) == SHAPE
+    assert call(dtype=4) == DTYPE
+    assert call(eps=-1.0) == GAMMA
+    assert call(y=A + 2) == ALIGN
+    assert call(dtype=F32) == UNSUP
+    assert call(d_out=100) == UNSUP
+    assert call() == WS

@@ -692,3 +692,35 @@ def test_msr_epilogue_layer7b_sampled_rows():
     o_s = to64(o[bs, :, ns, :])[:, :, None, :]   # [96, H, 1, dv]: each sampled token as its own batch entry
     ref = orc.msr_epilogue(o_s, to64(w_o), gn_weight=to64(gw), gn_bias=to64(gb), gate=to64(gt[bs, ns])[:, None, :])
     assert_close(to64(y[bs, ns])[:, None, :], ref, BF16_TOL, "sampled rows", per_head_axes=1)
+
+
+@pytest.mark.parametrize("B,H,dv,d_out", [(64, 16, 512, 4096), (3, 2, 64, 256), (1, 4, 128, 384), (64, 8, 64, 512)])
+def test_msr_epilogue_few_rows_split_k(B, H, dv, d_out):
+    """At most 64 tokens (a decode step): the projection splits its contraction."""
+    _epi_check(B, H, 1, dv, d_out, True, True, seed=114 + B)
+
+
+@pytest.mark.parametrize("rot", [False, True])
+def test_recurrent_step_msr_matches_oracle(rot):
+    B, H, dk, dv, d_out = 5, 4, 64, 128, 256
+    s0, qs, ks, vs = W.make_decode(B, H, dk, dv, torch.bfloat16, 1, 0.05, seed=120)
+    _, w_o, gw, gb, gt = W.make_epilogue(B, H, 1, dv, d_out, 121)
+    theta = W.rotary_theta(dk) if rot else None
+    pos = torch.tensor([3, 70, 0, 1_000_003, 9], dtype=torch.int64)
+    g = orc.head_gammas(H)
+    o_ref, s_ref = orc.decode_step(to64(qs[0]), to64(ks[0]), to64(vs[0]), to64(s0), g,
+                                   theta=None if theta is None else to64(theta), pos=pos.numpy() if rot else None)
+    y_ref = orc.msr_epilogue(o_ref[:, :, None, :], to64(w_o), gn_weight=to64(gw), gn_bias=to64(gb),
+                             gate=to64(gt))[:, 0, :]
+    state = s0.to(DEV)
+    y, o = R.retention_recurrent_step_msr(qs[0].to(DEV), ks[0].to(DEV), vs[0].to(DEV), state, w_o.to(DEV), theta=theta,
+                                          pos=pos.to(DEV) if rot else None, gate=gt[:, 0, :].contiguous().to(DEV),
+                                          gn_weight=gw.to(DEV), gn_bias=gb.to(DEV))
+    torch.cuda.synchronize()
+    assert_close(to64(o), o_ref, BF16_TOL, "o")
+    assert_close(to64(state), s_ref, BF16_TOL, "state")
+    # the output stage sees the bf16-rounded o the step wrote: compare with the oracle on that o too
+    y_on_o = orc.msr_epilogue(to64(o)[:, :, None, :], to64(w_o), gn_weight=to64(gw), gn_bias=to64(gb),
+                              gate=to64(gt))[:, 0, :]
+    assert_close(to64(y), y_on_o, BF16_TOL, "y (on the step's o)", per_head_axes=0)
+    assert_close(to64(y), y_ref, BF16_TOL, "y", per_head_axes=0)
