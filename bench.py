@@ -251,7 +251,7 @@ def run_only(name, steps, warmup, dev):
         return
     key = {"msr": "msr_bf16_rotary", "layer7b": "layer7b_bf16", "decode": "decode_bf16",
            "longctx": "longctx_bf16", "single": "single_head_f32", "bwd": "msr_bf16_rotary",
-           "epi": "layer7b_bf16"}[name]
+           "epi": "layer7b_bf16", "decmsr": "decode_bf16"}[name]
     w = W.WORKLOADS[key]
     if name == "bwd":
         fn = backward_step(R, W, key, dev)
@@ -259,6 +259,16 @@ def run_only(name, steps, warmup, dev):
     elif name == "epi":
         fn = epilogue_step(R, W, dev)
         key = "layer7b output stage"
+    elif name == "decmsr":
+        s0, qs, ks, vs = W.make_decode_workload(device=dev, steps=8)
+        _, w_o, gw, gb, gt = W.make_epilogue(w["B"], w["H"], 1, w["dv"], 4096, 8, device=dev)
+        gt = gt[:, 0, :].contiguous()
+        it = iter(range(10 ** 9))
+
+        def fn():
+            t = next(it) % 8
+            R.retention_recurrent_step_msr(qs[t], ks[t], vs[t], s0, w_o, gate=gt, gn_weight=gw, gn_bias=gb)
+        key = "decode step + output stage"
     elif name == "decode":
         s0, qs, ks, vs = W.make_decode_workload(device=dev, steps=steps + warmup)
         o = torch.empty((w["B"], w["H"], w["dv"]), dtype=w["dtype"], device=dev)
@@ -354,7 +364,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--quick", action="store_true", help="main workload only")
-    ap.add_argument("--only", choices=["msr", "layer7b", "decode", "longctx", "single", "copy", "bwd", "epi"],
+    ap.add_argument("--only", choices=["msr", "layer7b", "decode", "longctx", "single", "copy", "bwd", "epi",
+                                       "decmsr"],
                     help="time one workload only (no CPU baseline); for profilers")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sweep", choices=["decode-batch"], help="print one JSON line per point of a sweep")
