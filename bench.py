@@ -329,6 +329,38 @@ def epilogue_step(R, W, dev):
     return fn
 
 
+def sweep_chunk(dev):
+    """Chunkwise forward time against the chunk size (64 and 128: the kernel
+    tile; larger: 128-token tiles with the state exchanged between chunks) on
+    the multi-scale and long-context workloads: one JSON line per point."""
+    import torch
+
+    import linear_attention_sequence_fwd_amd as R
+    from linear_attention_sequence_fwd_amd import workloads as W
+
+    for name in ("msr_bf16_rotary", "longctx_bf16"):
+        w = W.WORKLOADS[name]
+        q, k, v, theta = W.make_workload(name, device=dev)
+        th = R.HostFloats(theta) if theta is not None else None
+        out = torch.empty_like(v)
+        for C in (64, 128, 256, 512, 1024, 2048, 4096, 8192):
+            if C >= w["N"]:
+                break
+            nb = R.retention_chunkwise_workspace_size(w["B"], w["H"], w["N"], w["dk"], w["dv"], q.dtype, C)
+            ws = torch.zeros(max(nb, 16), dtype=torch.uint8, device=dev)
+
+            def fn():
+                R.retention_chunkwise_fwd(q, k, v, chunk=C, theta=th, out=out, workspace=ws)
+
+            ms, spread = time_graph(fn, 50 if w["N"] <= 4096 else 10, 5)
+            fl = chunk_alg_flops(w["B"], w["H"], w["N"], w["dk"], w["dv"], C)
+            print(json.dumps({"sweep": "chunk", "workload": name, "chunk": C, "ms": ms, "ms_spread": spread,
+                              "tokens_per_s": w["B"] * w["N"] / (ms * 1e-3),
+                              "chunk_form_tflops": fl / (ms * 1e-3) / 1e12}), flush=True)
+        del q, k, v, out
+        torch.cuda.empty_cache()
+
+
 def sweep_decode_batch(dev):
     """Decode step latency against the number of sequences (H=16, 256x512 fp32
     state per head, bf16 q/k/v): one JSON line per batch size."""
@@ -368,7 +400,7 @@ def main():
                                        "decmsr"],
                     help="time one workload only (no CPU baseline); for profilers")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--sweep", choices=["decode-batch"], help="print one JSON line per point of a sweep")
+    ap.add_argument("--sweep", choices=["decode-batch", "chunk"], help="print one JSON line per point of a sweep")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
@@ -388,6 +420,9 @@ def main():
         return
     if args.sweep == "decode-batch":
         sweep_decode_batch(dev)
+        return
+    if args.sweep == "chunk":
+        sweep_chunk(dev)
         return
 
     # ---------------- main workload

@@ -113,9 +113,16 @@ ret_status_t retention_parallel_fwd(const void* q, const void* k, const void* v,
  *            Calls that share a
  *            workspace must be ordered on one stream (they must not overlap).
  *            The caller owns it; the library keeps no pointer to it.
- * Implemented set: chunk in {64, 128}; bf16 with dk in {64, 128, 256} and dv a
- * multiple of 64; f32 with chunk*dk <= 8192, dk a multiple of 4, dv a multiple
- * of 16.
+ * Large chunks ("RetNet Guide" section "3. The Chunkwise Recurrent
+ * Representation" suggests 512 or 1024 tokens for long prefill): for bf16,
+ * chunk may be any multiple of 128 up to 65536. Inside a chunk the kernel
+ * still works in 128-token tiles (the matrix-core tile that fits the register
+ * file); the state is exchanged between chunks, which run in parallel as
+ * segments (`segments` is then ignored: one segment per chunk, at most 4096).
+ * The workspace then grows with N / chunk (one state per chunk).
+ * Implemented set: chunk in {64, 128} (and the large chunks above for bf16);
+ * bf16 with dk in {64, 128, 256} and dv a multiple of 64; f32 with
+ * chunk*dk <= 8192, dk a multiple of 4, dv a multiple of 16.
  */
 ret_status_t retention_chunkwise_fwd(const void* q, const void* k, const void* v, void* o,
                                      int B, int H, int N, int dk, int dv, ret_dtype_t dtype,
@@ -143,9 +150,9 @@ ret_status_t retention_chunkwise_fwd_timed(const void* q, const void* k, const v
 
 /*
  * Bytes of workspace retention_chunkwise_fwd needs for these sizes and this
- * `segments` request. The value does not depend on N (the segment count is
- * bounded independently of the sequence length). Returns 0 for sizes the
- * call would reject.
+ * `segments` request. For chunk <= 128 the value does not depend on N (the
+ * segment count is bounded independently of the sequence length). Returns 0
+ * for sizes the call would reject.
  */
 size_t retention_chunkwise_workspace_size(int B, int H, int N, int dk, int dv, ret_dtype_t dtype,
                                           int chunk, int segments);

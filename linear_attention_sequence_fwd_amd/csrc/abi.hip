@@ -21,6 +21,7 @@ constexpr size_t kMaxLdsBytes = 160 * 1024;
 constexpr int kTargetBlocks = 256;  // one workgroup per compute unit
 constexpr int kMaxSegments = 4096;
 constexpr int kMaxAutoSegmentsBf16 = 64;
+constexpr int kMaxLargeChunk = 1 << 16;
 // The segmented form keeps one ticket counter per (batch, head, value tile)
 // chain in a fixed region at the start of the workspace, so counters stay
 // counters whatever sizes share the workspace.
@@ -87,6 +88,7 @@ int f32_parallel_dvt(int dk, int dv) {
 }
 
 struct ChunkPlan {
+    int tile;  // tokens per kernel chunk (64 or 128): the MFMA tile of the intra-chunk products
     int dvt, nvt, nseg, seg_len, nseg_max;
     size_t ws_bytes;
     int grp;                    // segments per look-back group
@@ -100,13 +102,23 @@ constexpr size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 // does not depend on the sequence length.
 ret_status_t plan_chunk(int B, int H, int N, int dk, int dv, ret_dtype_t dtype, int chunk, int segments,
                         ChunkPlan& p) {
-    if (chunk != 64 && chunk != 128) return RET_ERR_UNSUPPORTED;
+    // Chunks of 64 or 128 tokens are the kernel's tile. Larger chunks (multiples
+    // of 128, bf16) keep the 128-token tile inside the chunk and exchange the
+    // state between chunks: one segment per chunk.
+    const bool large = chunk > 128;
+    if (large ? (dtype != RET_BF16 || chunk % 128 != 0 || chunk > kMaxLargeChunk) : (chunk != 64 && chunk != 128))
+        return RET_ERR_UNSUPPORTED;
     if (segments < 0) return RET_ERR_SHAPE;
-    p.dvt = (dtype == RET_BF16) ? bf16_dvt(dk, dv, chunk) : f32_chunk_dvt(dk, dv, chunk);
+    p.tile = large ? 128 : chunk;
+    p.dvt = (dtype == RET_BF16) ? bf16_dvt(dk, dv, p.tile) : f32_chunk_dvt(dk, dv, p.tile);
     if (p.dvt == 0) return RET_ERR_UNSUPPORTED;
     p.nvt = dv / p.dvt;
     const long long base = static_cast<long long>(B) * H * p.nvt;
-    if (base > kMaxSegmentedChains)
+    if (large) {
+        const long long nseg = (static_cast<long long>(N) + chunk - 1) / chunk;
+        if (nseg > kMaxSegments) return RET_ERR_UNSUPPORTED;
+        p.nseg_max = base > kMaxSegmentedChains ? 1 : static_cast<int>(nseg);  // too many chains: one pass
+    } else if (base > kMaxSegmentedChains)
         p.nseg_max = 1;  // the grid is full without splitting sequences
     else if (segments > 0)
         p.nseg_max = segments;
@@ -114,13 +126,16 @@ ret_status_t plan_chunk(int B, int H, int N, int dk, int dv, ret_dtype_t dtype, 
         p.nseg_max = 1;
     else  // each bf16 segment reads every predecessor's state: keep the chains short
         p.nseg_max = static_cast<int>((kTargetBlocks + base - 1) / base);
-    if (segments == 0 && dtype == RET_BF16 && p.nseg_max > kMaxAutoSegmentsBf16) p.nseg_max = kMaxAutoSegmentsBf16;
+    if (!large && segments == 0 && dtype == RET_BF16 && p.nseg_max > kMaxAutoSegmentsBf16)
+        p.nseg_max = kMaxAutoSegmentsBf16;
     if (p.nseg_max > kMaxSegments) p.nseg_max = kMaxSegments;
-    const int nchunks = (N + chunk - 1) / chunk;
+    const int nchunks = (N + p.tile - 1) / p.tile;
     const int want = p.nseg_max < nchunks ? p.nseg_max : nchunks;
     const int per_seg = (nchunks + want - 1) / want;
-    p.seg_len = per_seg * chunk;
+    p.seg_len = (large && p.nseg_max > 1) ? chunk : per_seg * p.tile;
     p.nseg = (N + p.seg_len - 1) / p.seg_len;
+    // the workspace below holds nseg_max segments per chain: the kernels index up to nseg
+    if (p.nseg > p.nseg_max) return RET_ERR_UNSUPPORTED;
     // Look-back groups of about sqrt(segments) segments (at least 2): a
     // segment reads its group predecessors' states and one aggregate per
     // earlier group.
@@ -160,7 +175,7 @@ void fill_chunk_args(ret::ChunkArgs& a, const void* q, const void* k, const void
     a.N = N;
     a.dk = dk;
     a.dv = dv;
-    a.chunk = chunk;
+    a.chunk = p.tile;
     a.nvt = p.nvt;
     a.nseg = p.nseg;
     a.seg_len = p.seg_len;

@@ -258,3 +258,26 @@ def test_decode_msr_validation(lib):
     assert call(dtype=F32) == UNSUP
     assert call(d_out=100) == UNSUP
     assert call() == WS
+
+
+def test_large_chunks(lib):
+    assert chunk(lib, chunk=192) == UNSUP              # not a multiple of 128
+    assert chunk(lib, chunk=256, dtype=F32) == UNSUP   # large chunks are bf16 only
+    assert chunk(lib, chunk=1 << 17) == UNSUP
+    # one state per chunk: the workspace grows with N / chunk
+    w1 = lib.retention_chunkwise_workspace_size(1, 2, 4096, 64, 64, BF16, 512, 0)
+    w2 = lib.retention_chunkwise_workspace_size(1, 2, 16384, 64, 64, BF16, 512, 0)
+    assert 0 < w1 < w2
+    assert chunk(lib, N=4096, chunk=512, ws=A, ws_bytes=w1 - 1) == WS
+    # more than 4096 chunks per sequence is outside the set
+    assert lib.retention_chunkwise_workspace_size(1, 1, 4097 * 256, 64, 64, BF16, 256, 0) == 0
+
+
+def test_large_chunk_workspace_holds_every_chunk(lib):
+    # 65536 tokens in chunks of 256 are 256 segments per chain: the workspace
+    # must hold one 128 x 128 float32 state per segment for each of the 8
+    # chains (a plan that capped the count at the automatic limit of 64 sized
+    # it for a quarter of them while the kernel indexed all 256)
+    need = lib.retention_chunkwise_workspace_size(1, 8, 65536, 128, 128, BF16, 256, 0)
+    assert need >= 8 * 256 * 128 * 128 * 4
+    assert need > lib.retention_chunkwise_workspace_size(1, 8, 16384, 128, 128, BF16, 256, 0)

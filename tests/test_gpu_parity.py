@@ -724,3 +724,43 @@ def test_recurrent_step_msr_matches_oracle(rot):
                               gate=to64(gt))[:, 0, :]
     assert_close(to64(y), y_on_o, BF16_TOL, "y (on the step's o)", per_head_axes=0)
     assert_close(to64(y), y_ref, BF16_TOL, "y", per_head_axes=0)
+
+
+# ------------------------------------------------------------ large chunks
+
+LARGE_CHUNK_CASES = [
+    # B, H, N, dk, dv, chunk, rotary, state_in
+    (1, 2, 1000, 64, 64, 256, True, True),
+    (2, 2, 700, 128, 128, 512, False, True),
+    (1, 1, 3000, 64, 128, 1024, True, False),
+    (1, 2, 130, 256, 128, 512, False, True),
+    (2, 3, 2100, 64, 64, 384, True, True),
+]
+
+
+@pytest.mark.parametrize("case", LARGE_CHUNK_CASES, ids=lambda c: "B{}H{}N{}dk{}dv{}C{}rot{}st{}".format(*c))
+def test_chunkwise_large_chunks(case):
+    B, H, N, dk, dv, C, rot, st = case
+    q, k, v = _inputs(B, H, N, dk, dv, torch.bfloat16, 130)
+    theta = W.rotary_theta(dk) if rot else None
+    s0 = W.make_decode(B, H, dk, dv, torch.bfloat16, 1, 0.1, 131)[0] if st else None
+    g = orc.head_gammas(H)
+    ref, ref_s = orc.chunkwise(to64(q), to64(k), to64(v), g, C, theta=None if theta is None else to64(theta), pos0=5,
+                               state0=None if s0 is None else to64(s0))
+    o, s = R.retention_chunkwise_fwd(q.to(DEV), k.to(DEV), v.to(DEV), chunk=C, theta=theta, pos0=5,
+                                     state_in=None if s0 is None else s0.to(DEV), return_state=True)
+    torch.cuda.synchronize()
+    assert_close(to64(o), ref, BF16_TOL, "o")
+    assert_close(to64(s), ref_s, BF16_TOL, "state")
+
+
+def test_chunk_size_does_not_change_the_result_msr():
+    """The multi-scale workload at chunk 64, 128, 256, 512 and 1024: every result
+    within tolerance of the oracle, as all chunk sizes compute the same retention."""
+    w = W.WORKLOADS["msr_bf16_rotary"]
+    q, k, v, theta = W.make_workload("msr_bf16_rotary", device="cpu")
+    ref = orc.parallel(to64(q), to64(k), to64(v), orc.head_gammas(w["H"]), theta=to64(theta))
+    for C in (64, 128, 256, 512, 1024):
+        o = R.retention_chunkwise_fwd(q.to(DEV), k.to(DEV), v.to(DEV), chunk=C, theta=theta)
+        torch.cuda.synchronize()
+        assert_close(to64(o), ref, BF16_TOL, f"chunk {C}")
