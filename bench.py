@@ -353,10 +353,11 @@ def sweep_chunk(dev):
                 R.retention_chunkwise_fwd(q, k, v, chunk=C, theta=th, out=out, workspace=ws)
 
             ms, spread = time_graph(fn, 50 if w["N"] <= 4096 else 10, 5)
-            fl = chunk_alg_flops(w["B"], w["H"], w["N"], w["dk"], w["dv"], C)
+            # FLOPs the kernel does: its tile is min(C, 128) tokens
+            fl = chunk_alg_flops(w["B"], w["H"], w["N"], w["dk"], w["dv"], min(C, 128))
             print(json.dumps({"sweep": "chunk", "workload": name, "chunk": C, "ms": ms, "ms_spread": spread,
                               "tokens_per_s": w["B"] * w["N"] / (ms * 1e-3),
-                              "chunk_form_tflops": fl / (ms * 1e-3) / 1e12}), flush=True)
+                              "tile_tflops": fl / (ms * 1e-3) / 1e12}), flush=True)
         del q, k, v, out
         torch.cuda.empty_cache()
 
