@@ -181,6 +181,7 @@ void fill_chunk_args(ret::ChunkArgs& a, const void* q, const void* k, const void
     a.seg_len = p.seg_len;
     a.grp = p.grp;
     a.pos0 = pos0;
+    a.rev = 0;
 }
 
 // Workspace of the backward: one forward-workspace region per pass first (each
@@ -354,63 +355,111 @@ ret_status_t retention_chunkwise_bwd(const void* q, const void* k, const void* v
     const bool bf16 = dtype == RET_BF16;
     hipStream_t st = static_cast<hipStream_t>(stream);
 
-    // rotated and reversed copies of the inputs
     ret::RowJobs rj;
     memset(&rj, 0, sizeof(rj));
     rj.B = B;
     rj.H = H;
     rj.N = N;
     rj.pos0 = pos0;
-    rj.n = 4;
-    rj.j[0] = {q, qf, nullptr, dk, 1, rot ? 1 : 0, 0};
-    rj.j[1] = {k, kf, rot ? kr : nullptr, dk, 1, rot ? 1 : 0, 0};
-    rj.j[2] = {v, vf, nullptr, dv, 1, 0, 0};
-    rj.j[3] = {d_o, dof, nullptr, dv, 1, 0, 0};
     // the passes' counters and flags start from zero on every call (the
     // scratch tensors of earlier calls of other sizes may have covered them)
     if (b.ctl_bytes > 0) {
         for (int r = 0; r < 3; ++r) rj.zero[r] = reinterpret_cast<uint4*>(ws + r * b.fwd_bytes);
         rj.nzero = static_cast<long long>(b.ctl_bytes / 16);
     }
-    if (ret::launch_rows(rj, hp, bf16, st) != hipSuccess) return RET_ERR_HIP;
-    if (state_in || d_state_out) {
-        ret::StateJobs sj = {state_in, d_state_out, x1, x2, x3, nullptr, B, H, dk, dv, 0};
-        if (ret::launch_states(sj, hp, st) != hipSuccess) return RET_ERR_HIP;
-    }
-
-    // The three passes:
-    //   dQ' = F(dO, V, K'; S0^T) straight into d_q
-    //   reversed dK' = F(rev V, rev dO, rev Q'; dS^T / gamma)
-    //   reversed dV = F(rev K', rev Q', rev dO; dS / gamma), whose final state is dS0 / gamma
-    const void* pk = rot ? kr : k;
     const float* sx1 = state_in ? x1 : nullptr;
     const float* sx2 = d_state_out ? x2 : nullptr;
     const float* sx3 = d_state_out ? x3 : nullptr;
-    if (bf16 && dk == dv) {
-        // one shape for all three: a single launch runs them side by side
-        ChunkPlan p;
-        s = plan_chunk(B, H, N, dk, dv, dtype, chunk, 0, p);
+    auto prep_states = [&]() -> ret_status_t {
+        if (state_in || d_state_out) {
+            ret::StateJobs sj = {state_in, d_state_out, x1, x2, x3, nullptr, B, H, dk, dv, 0};
+            if (ret::launch_states(sj, hp, st) != hipSuccess) return RET_ERR_HIP;
+        }
+        return RET_OK;
+    };
+    auto finish_states = [&]() -> ret_status_t {
+        if (d_state_in) {
+            ret::StateJobs sj = {nullptr, nullptr, nullptr, nullptr, nullptr, d_state_in, B, H, dk, dv, 1};
+            if (ret::launch_states(sj, hp, st) != hipSuccess) return RET_ERR_HIP;
+        }
+        return RET_OK;
+    };
+
+    // The three passes:
+    //   dQ' = F(dO, V, K'; S0^T)
+    //   dK' = rev F(rev V, rev dO, rev Q'; dS^T / gamma)
+    //   dV  = rev F(rev K', rev Q', rev dO; dS / gamma), whose final state is dS0 / gamma
+    if (bf16) {
+        // The matrix-core kernel reads and writes the reversed passes in
+        // reverse token order itself: only the rotation needs copies (K' and
+        // Q' in token order) and, at the end, the rotation of dQ', dK' back.
+        if (rot) {
+            rj.n = 2;
+            rj.j[0] = {q, qf, nullptr, dk, 0, 1, 0};
+            rj.j[1] = {k, kr, nullptr, dk, 0, 1, 0};
+        }
+        if (rj.n > 0 || rj.nzero > 0)
+            if (ret::launch_rows(rj, hp, bf16, st) != hipSuccess) return RET_ERR_HIP;
+        s = prep_states();
+        if (s != RET_OK) return s;
+        const void* kp = rot ? kr : k;  // K'
+        const void* qp = rot ? qf : q;  // Q'
+        ChunkPlan p1, p3;  // key width dv (passes 1, 2) and dk (pass 3)
+        s = plan_chunk(B, H, N, dv, dk, dtype, chunk, 0, p1);
+        if (s != RET_OK) return s;
+        s = plan_chunk(B, H, N, dk, dv, dtype, chunk, 0, p3);
         if (s != RET_OK) return s;
         ret::ChunkCalls cs;
-        cs.n = 3;
-        fill_chunk_args(cs.a[0], d_o, v, pk, d_q, B, H, N, dv, dk, chunk, 0, sx1, nullptr, p, ws);
-        fill_chunk_args(cs.a[1], vf, dof, qf, dkf, B, H, N, dv, dk, chunk, 0, sx2, nullptr, p, ws + b.fwd_bytes);
-        fill_chunk_args(cs.a[2], kf, qf, dof, dvf, B, H, N, dk, dv, chunk, 0, sx3, d_state_in, p,
-                        ws + 2 * b.fwd_bytes);
+        fill_chunk_args(cs.a[0], d_o, v, kp, d_q, B, H, N, dv, dk, chunk, 0, sx1, nullptr, p1, ws);
+        fill_chunk_args(cs.a[1], v, d_o, qp, d_k, B, H, N, dv, dk, chunk, 0, sx2, nullptr, p1, ws + b.fwd_bytes);
+        cs.a[1].rev = 1;
         HeadParams hp_passes = hp;
         hp_passes.has_theta = 0;
-        if (ret::launch_chunk_bf16_multi(cs, hp_passes, p.dvt, st) != hipSuccess) return RET_ERR_HIP;
-    } else {
-        s = chunkwise_impl(d_o, v, pk, d_q, B, H, N, dv, dk, dtype, chunk, gamma, nullptr, 0, sx1, nullptr, 0, ws,
-                           b.fwd_bytes, stream, nullptr);
-        if (s != RET_OK) return s;
-        s = chunkwise_impl(vf, dof, qf, dkf, B, H, N, dv, dk, dtype, chunk, gamma, nullptr, 0, sx2, nullptr, 0,
-                           ws + b.fwd_bytes, b.fwd_bytes, stream, nullptr);
-        if (s != RET_OK) return s;
-        s = chunkwise_impl(kf, qf, dof, dvf, B, H, N, dk, dv, dtype, chunk, gamma, nullptr, 0, sx3, d_state_in, 0,
-                           ws + 2 * b.fwd_bytes, b.fwd_bytes, stream, nullptr);
-        if (s != RET_OK) return s;
+        ret::ChunkArgs a3;
+        fill_chunk_args(a3, kp, qp, d_o, d_v, B, H, N, dk, dv, chunk, 0, sx3, d_state_in, p3, ws + 2 * b.fwd_bytes);
+        a3.rev = 1;
+        if (dk == dv) {  // one shape: a single launch runs the three side by side
+            cs.a[2] = a3;
+            cs.n = 3;
+            if (ret::launch_chunk_bf16_multi(cs, hp_passes, p1.dvt, st) != hipSuccess) return RET_ERR_HIP;
+        } else {
+            cs.n = 2;
+            if (ret::launch_chunk_bf16_multi(cs, hp_passes, p1.dvt, st) != hipSuccess) return RET_ERR_HIP;
+            ret::ChunkCalls c3;
+            c3.a[0] = a3;
+            c3.n = 1;
+            if (ret::launch_chunk_bf16_multi(c3, hp_passes, p3.dvt, st) != hipSuccess) return RET_ERR_HIP;
+        }
+        if (rot) {
+            memset(&rj.j, 0, sizeof(rj.j));
+            rj.nzero = 0;
+            rj.n = 2;
+            rj.j[0] = {d_q, d_q, nullptr, dk, 0, -1, 0};
+            rj.j[1] = {d_k, d_k, nullptr, dk, 0, -1, 0};
+            if (ret::launch_rows(rj, hp, bf16, st) != hipSuccess) return RET_ERR_HIP;
+        }
+        return finish_states();
     }
+
+    // float32: the passes run on reversed and rotated copies
+    rj.n = 4;
+    rj.j[0] = {q, qf, nullptr, dk, 1, rot ? 1 : 0, 0};
+    rj.j[1] = {k, kf, rot ? kr : nullptr, dk, 1, rot ? 1 : 0, 0};
+    rj.j[2] = {v, vf, nullptr, dv, 1, 0, 0};
+    rj.j[3] = {d_o, dof, nullptr, dv, 1, 0, 0};
+    if (ret::launch_rows(rj, hp, bf16, st) != hipSuccess) return RET_ERR_HIP;
+    s = prep_states();
+    if (s != RET_OK) return s;
+    const void* pk = rot ? kr : k;
+    s = chunkwise_impl(d_o, v, pk, d_q, B, H, N, dv, dk, dtype, chunk, gamma, nullptr, 0, sx1, nullptr, 0, ws,
+                       b.fwd_bytes, stream, nullptr);
+    if (s != RET_OK) return s;
+    s = chunkwise_impl(vf, dof, qf, dkf, B, H, N, dv, dk, dtype, chunk, gamma, nullptr, 0, sx2, nullptr, 0,
+                       ws + b.fwd_bytes, b.fwd_bytes, stream, nullptr);
+    if (s != RET_OK) return s;
+    s = chunkwise_impl(kf, qf, dof, dvf, B, H, N, dk, dv, dtype, chunk, gamma, nullptr, 0, sx3, d_state_in, 0,
+                       ws + 2 * b.fwd_bytes, b.fwd_bytes, stream, nullptr);
+    if (s != RET_OK) return s;
 
     // back to token order and unrotated coordinates
     memset(&rj.j, 0, sizeof(rj.j));
@@ -421,11 +470,7 @@ ret_status_t retention_chunkwise_bwd(const void* q, const void* k, const void* v
     rj.j[n++] = {dvf, d_v, nullptr, dv, 1, 0, 1};
     rj.n = n;
     if (ret::launch_rows(rj, hp, bf16, st) != hipSuccess) return RET_ERR_HIP;
-    if (d_state_in) {
-        ret::StateJobs sj = {nullptr, nullptr, nullptr, nullptr, nullptr, d_state_in, B, H, dk, dv, 1};
-        if (ret::launch_states(sj, hp, st) != hipSuccess) return RET_ERR_HIP;
-    }
-    return RET_OK;
+    return finish_states();
 }
 
 size_t retention_msr_epilogue_workspace_size(int B, int H, int N, int dv, int d_out, ret_dtype_t dtype) {

@@ -159,10 +159,11 @@ int grid_for(long long items, int threads) {
 }  // namespace
 
 hipError_t launch_rows(const RowJobs& jobs, const HeadParams& hp, bool bf16, hipStream_t st) {
-    if (jobs.n < 1 || jobs.n > 4) return hipErrorInvalidValue;
+    if (jobs.n < 0 || jobs.n > 4 || (jobs.n == 0 && jobs.nzero <= 0)) return hipErrorInvalidValue;
     int dmax = 0;
     for (int i = 0; i < jobs.n; ++i) dmax = jobs.j[i].d > dmax ? jobs.j[i].d : dmax;
-    const long long items = static_cast<long long>(jobs.B) * jobs.H * jobs.N * dmax / 8;
+    long long items = static_cast<long long>(jobs.B) * jobs.H * jobs.N * dmax / 8;
+    if (jobs.nzero > items) items = jobs.nzero;
     const dim3 grid(grid_for(items, kRowThreads), jobs.n + (jobs.nzero > 0 ? 1 : 0));
     if (bf16)
         hipLaunchKernelGGL(rows_kernel<true>, grid, dim3(kRowThreads), 0, st, jobs, hp);

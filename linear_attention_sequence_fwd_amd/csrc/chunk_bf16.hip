@@ -164,8 +164,10 @@ enum ChunkMode { kSinglePass = 0, kTwoPass = 1, kLocalPass = 2 };
 constexpr int kKeepChunks = 2;
 
 // The body of one workgroup: `bid` is its index among the `nblk` workgroups of
-// its call (the launch may carry several calls of the same shape).
-template <int DK, int DVT, int C, int MODE, bool FAST>
+// its call (the launch may carry several calls of the same shape). With REVM,
+// a call whose `rev` is set reads and writes its rows in reverse token order:
+// kernel token t is memory row N-1-t (rotation is not supported then).
+template <int DK, int DVT, int C, int MODE, bool FAST, int REVM>
 __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams& hp, unsigned bid, unsigned nblk) {
     constexpr bool SEGMENTED = MODE != kSinglePass;
     using G = ChunkGeo<DK, DVT, C>;
@@ -241,6 +243,10 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
     const u16* Qg = a.q + tok0 * DK;
     const u16* Vg = a.v + tok0 * a.dv + vt * DVT;
     u16* Og = a.o + tok0 * a.dv + vt * DVT;
+    const bool rev = REVM != 0 && a.rev != 0;
+    // first memory row of the chunk at kernel token t with L valid rows (at
+    // least one, so a discarded re-read past the end stays inside the sequence)
+    auto mrow0 = [&](int t, int L) __attribute__((always_inline)) { return rev ? a.N - t - max(L, 1) : t; };
 
     const int rb = wave_row_block<G::NW>(wave);      // this wave's 16 chunk rows
     const int d_base = (wave % G::MG) * G::MT * 16;  // this wave's S rows ...
@@ -258,8 +264,9 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
     // that are never stored, so they need no zeroing (a select here would be
     // turned into branches around the loads).
     auto load_q = [&](uint4 (&qd)[G::KSQ], int t, int Lq) __attribute__((always_inline)) {
-        const int rc = min(rb * 16 + l16, Lq > 0 ? Lq - 1 : 0);
-        const char* base = reinterpret_cast<const char*>(Qg + static_cast<size_t>(t) * DK);
+        const int lastq = Lq > 0 ? Lq - 1 : 0;
+        const int rc = rev ? lastq - min(rb * 16 + l16, lastq) : min(rb * 16 + l16, lastq);
+        const char* base = reinterpret_cast<const char*>(Qg + static_cast<size_t>(mrow0(t, Lq)) * DK);
         const uint32_t off = static_cast<uint32_t>((rc * DK + grp * 8) * 2);
 #pragma unroll
         for (int s = 0; s < G::KSQ; ++s) qd[s] = *reinterpret_cast<const uint4*>(base + off + s * 64);
@@ -267,9 +274,10 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
     // first chunk of the segment (issued before state loads so the HBM round trips overlap)
     auto prefetch_first = [&](bool with_q) __attribute__((always_inline)) {
         const int L0 = min(C, t_end - t_begin);
-        load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR>(kr, Kg + static_cast<size_t>(t_begin) * DK, DK, L0, tid);
-        load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR>(vr, Vg + static_cast<size_t>(t_begin) * a.dv, a.dv, L0,
-                                                          value_thread<G>(tid));
+        load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR>(kr, Kg + static_cast<size_t>(mrow0(t_begin, L0)) * DK, DK,
+                                                        L0, tid, rev);
+        load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR>(vr, Vg + static_cast<size_t>(mrow0(t_begin, L0)) * a.dv,
+                                                          a.dv, L0, value_thread<G>(tid), rev);
         if (with_q) load_q(qf, t_begin, L0);
     };
     // this head's state from a caller's [B*H][dk][dv] float32 array, or zeros
@@ -383,9 +391,9 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
     // ---- pieces of the chunk loop
     // Step 7: this wave's 16 output rows of the chunk at token t0 (L valid), as bf16.
     auto store_o = [&](const f32x4 (&o)[G::NTV], int t0, int L) __attribute__((always_inline)) {
-        const int row = rb * 16 + l16;
-        if (row < L) {
-            char* base = reinterpret_cast<char*>(Og + static_cast<size_t>(t0) * a.dv);
+        const int row = rev ? L - 1 - (rb * 16 + l16) : rb * 16 + l16;
+        if (rb * 16 + l16 < L) {
+            char* base = reinterpret_cast<char*>(Og + static_cast<size_t>(mrow0(t0, L)) * a.dv);
             const uint32_t off = static_cast<uint32_t>((row * a.dv + grp * 4) * 2);
 #pragma unroll
             for (int nt = 0; nt < G::NTV; ++nt) {
@@ -440,18 +448,20 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
     // chunk loops, so the per-row offsets are recomputed instead of being held
     // in registers across the loop).
     auto load_kv = [&](auto& krb, auto& vrb, int t, int L, int tid_it) __attribute__((always_inline)) {
-        load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR>(krb, Kg + static_cast<size_t>(t) * DK, DK, L, tid_it);
-        load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR>(vrb, Vg + static_cast<size_t>(t) * a.dv, a.dv, L,
-                                                          value_thread<G>(tid_it));
+        load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR>(krb, Kg + static_cast<size_t>(mrow0(t, L)) * DK, DK, L,
+                                                        tid_it, rev);
+        load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR>(vrb, Vg + static_cast<size_t>(mrow0(t, L)) * a.dv, a.dv, L,
+                                                          value_thread<G>(tid_it), rev);
     };
     // Rows R0 .. R1-1 of every staging block of those loads (one chunk's loads
     // can be spread over several points of the loop).
     auto load_kv_rows = [&](auto& krb, auto& vrb, int t, int L, int tid_it, auto r0_tag, auto r1_tag)
                             __attribute__((always_inline)) {
         constexpr int R0 = decltype(r0_tag)::value, R1 = decltype(r1_tag)::value;
-        load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR, R0, R1>(krb, Kg + static_cast<size_t>(t) * DK, DK, L, tid_it);
-        load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR, R0, R1>(vrb, Vg + static_cast<size_t>(t) * a.dv, a.dv, L,
-                                                                value_thread<G>(tid_it));
+        load_blocks<DK, G::BWK, G::KB, G::KPT, G::NTHR, R0, R1>(krb, Kg + static_cast<size_t>(mrow0(t, L)) * DK, DK,
+                                                                L, tid_it, rev);
+        load_blocks<DVT, G::BWV, G::VB, G::VPT, G::NTHR, R0, R1>(vrb, Vg + static_cast<size_t>(mrow0(t, L)) * a.dv,
+                                                                a.dv, L, value_thread<G>(tid_it), rev);
     };
     // Step 3 (G4): S = gamma^L S + Kx^T V on this wave's tiles.
     auto g4 = [&](int L, int l16c, int grpc) __attribute__((always_inline)) {
@@ -1156,7 +1166,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
 
 template <int DK, int DVT, int C, int MODE, bool FAST>
 __global__ __launch_bounds__((C / 16) * 64) void chunk_bf16_kernel(ChunkArgs a, HeadParams hp) {
-    chunk_body<DK, DVT, C, MODE, FAST>(a, hp, blockIdx.x, gridDim.x);
+    chunk_body<DK, DVT, C, MODE, FAST, 0>(a, hp, blockIdx.x, gridDim.x);
 }
 
 // Several calls of one shape in one launch, their workgroups interleaved so
@@ -1171,7 +1181,7 @@ __global__ __launch_bounds__((C / 16) * 64, (kMultiWaves<DK, DVT, C>)) void chun
                                                                                                   HeadParams hp) {
     const int n = cs.n;
     const int b = blockIdx.x;
-    chunk_body<DK, DVT, C, MODE, FAST>(cs.a[b % n], hp, b / n, gridDim.x / n);
+    chunk_body<DK, DVT, C, MODE, FAST, 1>(cs.a[b % n], hp, b / n, gridDim.x / n);
 }
 
 // Holding two chunks of outputs and queries in registers fits with 64-token

@@ -32,6 +32,7 @@ struct ChunkArgs {
     int seg_len;  // tokens per segment, a multiple of chunk
     int grp;      // segments per look-back group (bf16 segmented form)
     long long pos0;
+    int rev;      // rows in reverse token order (chunk_bf16_multi_kernel only; no rotation then)
 };
 
 // Several chunkwise calls of one shape and plan (different tensors, states and

@@ -82,8 +82,11 @@ struct BlockRows {
 // not also wait for a prefetch issued after it. valid == 0 reads row 0.
 // Q0..Q1-1: the rows of each block to load (all eight by default), so a caller
 // can spread one chunk's loads over several points of its loop.
+// With rev, row i of the chunk is memory row (valid - 1 - i) from base (a
+// chunk read in reverse token order; base then points at its last token).
 template <int D, int BW, int NBLK, int PT, int NTHR, int Q0 = 0, int Q1 = 8>
-__device__ __forceinline__ void load_blocks(BlockRows<BW> (&r)[PT], const u16* base, int ld, int valid, int tid) {
+__device__ __forceinline__ void load_blocks(BlockRows<BW> (&r)[PT], const u16* base, int ld, int valid, int tid,
+                                            bool rev = false) {
     // Row pointers are wave-uniform (base + row * ld); the per-lane part is a
     // 32-bit byte offset, so each row load needs one shared offset register
     // and a scalar base instead of its own 64-bit address.
@@ -99,7 +102,7 @@ __device__ __forceinline__ void load_blocks(BlockRows<BW> (&r)[PT], const u16* b
         for (int q = Q0; q < Q1; ++q) {
             const int dq = staged_token(0, q);  // token offset of row q inside the block
             const bool ok = in_blk && tok0 + dq < valid;
-            const int row = min(tok0 + dq, last);
+            const int row = rev ? last - min(tok0 + dq, last) : min(tok0 + dq, last);
             const char* rowq = reinterpret_cast<const char*>(base) + static_cast<uint32_t>((row * ld + cb * BW) * 2);
             if constexpr (BW == 8) {
                 const uint4 x = *reinterpret_cast<const uint4*>(rowq);
