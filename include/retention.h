@@ -173,7 +173,8 @@ size_t retention_chunkwise_workspace_size(int B, int H, int N, int dk, int dv, r
  *     dS0 = Q'^T (Z (.) dO) + gamma^N dS
  * Each of dQ', dK', dV is computed as one chunkwise forward pass (the last two
  * over the reversed sequence, where the transposed decay matrix is causal);
- * for bf16 with dk == dv the three passes share one launch.
+ * for bf16 the matrix-core kernel reads and writes those two in reverse token
+ * order itself, and with dk == dv the three passes share one launch.
  *
  * d_o:         device [B, H, N, dv] in dtype.
  * state_in:    the forward's initial state, or NULL for zeros.
@@ -182,8 +183,9 @@ size_t retention_chunkwise_workspace_size(int B, int H, int N, int dk, int dv, r
  *              NULL. May alias d_state_out or state_in; d_q, d_k, d_v must not
  *              overlap any input or each other.
  * workspace:   device buffer of retention_chunkwise_bwd_workspace_size(...)
- *              bytes (it grows with N: it holds reversed and rotated copies of
- *              q, k, v and d_o). It needs no initialisation: every call clears
+ *              bytes (it grows with N: it holds the rotated copies of q and k,
+ *              and for float32 reversed copies of q, k, v and d_o). It needs
+ *              no initialisation: every call clears
  *              the counters its passes use, in a kernel (so the call can be
  *              captured in a graph). Backward calls of any sizes may share it
  *              when ordered on one stream; a forward workspace must not be the

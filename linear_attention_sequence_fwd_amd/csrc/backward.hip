@@ -17,10 +17,12 @@
 // state times gamma is dS0. The rotation is orthogonal per pair, so dQ and dK
 // are dQ', dK' rotated by the opposite angle.
 //
-// The kernels here are the HBM-bound glue around those passes: rows_kernel
-// rotates and/or reverses rows (up to four tensors per launch, one per
-// grid row; one more row can zero-fill the control words of the passes'
-// workspace regions), state_kernel transposes and scales the [dk, dv] states.
+// For bf16 the matrix-core kernel runs the reversed passes in reverse token
+// order itself; float32 passes run on reversed copies. The kernels here are
+// the HBM-bound glue around the passes: rows_kernel rotates and/or reverses
+// rows (up to four tensors per launch, one per grid row; one more row can
+// zero-fill the control words of the passes' workspace regions),
+// state_kernel transposes and scales the [dk, dv] states.
 
 #include "common.hpp"
 #include "kernels.hpp"
