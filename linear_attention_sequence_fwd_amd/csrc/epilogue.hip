@@ -16,7 +16,7 @@
 //   gemm_bt_kernel: Y [M, d_out] = Z [M, K] W^T with W [d_out, K], both
 //     K-contiguous; bf16 operands on v_mfma_f32_16x16x32_bf16, float32
 //     accumulation. Tiles of 256 x 256 (256 x 128) per workgroup of eight
-//     waves that each hold a 128 x 64 (128 x 32) output block, so a 16-byte
+//     waves that each hold a 64 x 128 (64 x 64) output block, so a 16-byte
 //     operand read from LDS feeds 4 to 8 matrix instructions; 64-deep K steps
 //     double-buffered in LDS and filled by direct global-to-LDS loads (the
 //     next step's loads are in flight while the current one is multiplied);
@@ -139,12 +139,13 @@ __global__ __launch_bounds__(kNormThreads) void groupnorm_gate_kernel(EpilogueAr
 // wave at consecutive addresses (16 bytes per lane), so lane l of load i fills
 // row R = 8 i + l / 8, position l % 8, and fetches the chunk that belongs there.
 constexpr int GK = 64;
-constexpr int kGroupM = 8;   // row tiles per group of the tile order
-// Eight waves in 2 x 4: 128 x 64 output blocks (128 accumulator registers a
-// lane, held in ordinary VGPRs), two waves per SIMD. Four waves with 128 x 128
-// blocks would read half the operand bytes from LDS but fill the whole
-// accumulator file, and the register allocator then shuffles it.
-constexpr int kWavesM = 2, kWavesN = 4;
+constexpr int kGroupM = 4;   // row tiles per group of the tile order (4 measured best of 1..32)
+// Eight waves in 4 x 2: 64 x 128 output blocks (128 accumulator registers a
+// lane, held in ordinary VGPRs), two waves per SIMD (4 x 2 measured 3% faster
+// than 2 x 4). Four waves with 128 x 128 blocks would read half the operand
+// bytes from LDS but fill the whole accumulator file, and the register
+// allocator then shuffles it.
+constexpr int kWavesM = 4, kWavesN = 2;
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
