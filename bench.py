@@ -573,6 +573,19 @@ def main():
         })
         torch.cuda.empty_cache()
 
+        # ---------------- backward of the long-context workload
+        w = W.WORKLOADS["longctx_bf16"]
+        bstep = backward_step(R, W, "longctx_bf16", dev)
+        msl = time_events(bstep, 5, 2)
+        fll = 3 * chunk_alg_flops(w["B"], w["H"], w["N"], w["dk"], w["dv"], w["chunk"])
+        also.append({
+            "workload": "backward of the long-context workload (B=1 H=8 N=65536 d=128 bf16, chunk 128)",
+            "ms": msl, "tokens_per_s": w["B"] * w["N"] / (msl * 1e-3), "tflops": fll / (msl * 1e-3) / 1e12,
+            "mfma_frac": fll / (msl * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        })
+        del bstep
+        torch.cuda.empty_cache()
+
         # ---------------- output stage of the 7B-shaped layer
         e = EPI_SHAPE
         estep = epilogue_step(R, W, dev)

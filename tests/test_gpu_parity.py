@@ -764,3 +764,56 @@ def test_chunk_size_does_not_change_the_result_msr():
         o = R.retention_chunkwise_fwd(q.to(DEV), k.to(DEV), v.to(DEV), chunk=C, theta=theta)
         torch.cuda.synchronize()
         assert_close(to64(o), ref, BF16_TOL, f"chunk {C}")
+
+
+def test_backward_and_output_stage_graph_replay():
+    """The backward (row kernels that also clear its counters, the multi-pass
+    launch) and the output stage (GroupNorm, GEMM; and the split-K path) are
+    captured in one graph; every replay, with other eager calls in between,
+    reproduces the eager results bit for bit."""
+    w = W.WORKLOADS["msr_bf16_rotary"]
+    q, k, v, theta = W.make_workload("msr_bf16_rotary", device=DEV)
+    th = R.HostFloats(theta)
+    d_o, d_s = W.make_upstream_grads(w["B"], w["H"], w["N"], w["dk"], w["dv"], w["dtype"], 140, device=DEV)
+    o, w_o, gw, gb, gt = W.make_epilogue(w["B"], w["H"], w["N"], w["dv"], 512, 141, device=DEV)
+    o1, w1, gw1, gb1, gt1 = W.make_epilogue(16, 8, 1, 64, 512, 142, device=DEV)  # 16 tokens: split-K path
+    nb = R.retention_chunkwise_bwd_workspace_size(w["B"], w["H"], w["N"], w["dk"], w["dv"], q.dtype, w["chunk"])
+    wsb = torch.full((nb,), 0x5A, dtype=torch.uint8, device=DEV)
+    ne = R.retention_msr_epilogue_workspace_size(w["B"], w["H"], w["N"], w["dv"], 512, q.dtype)
+    ne1 = R.retention_msr_epilogue_workspace_size(16, 8, 1, 64, 512, q.dtype)
+    wse = torch.empty(ne, dtype=torch.uint8, device=DEV)
+    wse1 = torch.empty(ne1, dtype=torch.uint8, device=DEV)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dsi = torch.empty((w["B"], w["H"], w["dk"], w["dv"]), dtype=torch.float32, device=DEV)
+    y = torch.empty((w["B"], w["N"], 512), dtype=torch.bfloat16, device=DEV)
+    y1 = torch.empty((16, 1, 512), dtype=torch.bfloat16, device=DEV)
+
+    def step():
+        R.retention_chunkwise_bwd(q, k, v, d_o, chunk=w["chunk"], theta=th, d_state_out=d_s, d_state_in=dsi,
+                                  out=grads, workspace=wsb)
+        R.retention_msr_epilogue(o, w_o, gn_weight=gw, gn_bias=gb, gate=gt, out=y, workspace=wse)
+        R.retention_msr_epilogue(o1, w1, gn_weight=gw1, gn_bias=gb1, gate=gt1, out=y1, workspace=wse1)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (*grads, dsi, y, y1)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        for t in (*grads, dsi, y, y1):
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((*grads, dsi, y, y1), eager):
+            assert torch.equal(a, b)
+        other = R.retention_chunkwise_bwd(q[:, :, :700].contiguous(), k[:, :, :700].contiguous(),
+                                          v[:, :, :700].contiguous(), d_o[:, :, :700].contiguous(), theta=th)
+        torch.cuda.synchronize()
+        assert all(torch.isfinite(t).all() for t in other[:3])
