@@ -120,9 +120,9 @@ ret_status_t retention_parallel_fwd(const void* q, const void* k, const void* v,
  * file); the state is exchanged between chunks, which run in parallel as
  * segments (`segments` is then ignored: one segment per chunk, at most 4096).
  * The workspace then grows with N / chunk (one state per chunk).
- * Implemented set: chunk in {64, 128} (and the large chunks above for bf16);
- * bf16 with dk in {64, 128, 256} and dv a multiple of 64; f32 with
- * chunk*dk <= 8192, dk a multiple of 4, dv a multiple of 16.
+ * Implemented set: chunk in {64, 128} (and the large chunks above for bf16;
+ * f32 also takes 16 and 32); bf16 with dk in {64, 128, 256} and dv a multiple
+ * of 64; f32 with chunk*dk <= 8192, dk a multiple of 4, dv a multiple of 16.
  */
 ret_status_t retention_chunkwise_fwd(const void* q, const void* k, const void* v, void* o,
                                      int B, int H, int N, int dk, int dv, ret_dtype_t dtype,

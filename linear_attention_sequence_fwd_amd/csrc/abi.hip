@@ -106,7 +106,9 @@ ret_status_t plan_chunk(int B, int H, int N, int dk, int dv, ret_dtype_t dtype, 
     // of 128, bf16) keep the 128-token tile inside the chunk and exchange the
     // state between chunks: one segment per chunk.
     const bool large = chunk > 128;
-    if (large ? (dtype != RET_BF16 || chunk % 128 != 0 || chunk > kMaxLargeChunk) : (chunk != 64 && chunk != 128))
+    const bool small_ok = (chunk == 16 || chunk == 32) && dtype == RET_F32;  // the float32 kernel takes any chunk
+    if (large ? (dtype != RET_BF16 || chunk % 128 != 0 || chunk > kMaxLargeChunk)
+              : (chunk != 64 && chunk != 128 && !small_ok))
         return RET_ERR_UNSUPPORTED;
     if (segments < 0) return RET_ERR_SHAPE;
     p.tile = large ? 128 : chunk;

@@ -118,7 +118,9 @@ def test_gamma_and_theta_validation(lib):
 
 
 def test_unsupported_sets(lib):
+    assert chunk(lib, chunk=16) == UNSUP  # bf16 tiles are 64 or 128 tokens (the float32 kernel takes 16 and 32)
     assert chunk(lib, chunk=32) == UNSUP
+    assert chunk(lib, chunk=48) == UNSUP
     assert chunk(lib, chunk=100) == UNSUP
     assert chunk(lib, dk=96) == UNSUP          # bf16 dk outside {64,128,256}
     assert chunk(lib, dv=96) == UNSUP          # bf16 dv not a multiple of 64
@@ -281,3 +283,11 @@ def test_large_chunk_workspace_holds_every_chunk(lib):
     need = lib.retention_chunkwise_workspace_size(1, 8, 65536, 128, 128, BF16, 256, 0)
     assert need >= 8 * 256 * 128 * 128 * 4
     assert need > lib.retention_chunkwise_workspace_size(1, 8, 16384, 128, 128, BF16, 256, 0)
+
+
+def test_small_chunks(lib):
+    # 16- and 32-token chunks in float32 only
+    assert lib.retention_chunkwise_workspace_size(1, 2, 4096, 64, 64, F32, 16, 0) > 0
+    assert lib.retention_chunkwise_workspace_size(1, 2, 4096, 64, 64, F32, 32, 0) > 0
+    assert lib.retention_chunkwise_workspace_size(1, 2, 4096, 64, 64, BF16, 32, 0) == 0
+    assert lib.retention_chunkwise_workspace_size(1, 2, 4096, 64, 64, BF16, 16, 0) == 0

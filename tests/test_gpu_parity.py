@@ -817,3 +817,33 @@ def test_backward_and_output_stage_graph_replay():
                                           v[:, :, :700].contiguous(), d_o[:, :, :700].contiguous(), theta=th)
         torch.cuda.synchronize()
         assert all(torch.isfinite(t).all() for t in other[:3])
+
+
+# ------------------------------------------------------------ small chunks
+
+SMALL_CHUNK_CASES = [
+    # B, H, N, dk, dv, chunk, dtype, rotary, state_in, segments (float32: its kernel takes any chunk)
+    (1, 2, 150, 64, 64, 16, torch.float32, True, True, 0),
+    (2, 1, 130, 32, 64, 32, torch.float32, False, True, 2),
+    (1, 3, 300, 64, 128, 32, torch.float32, True, False, 0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_CHUNK_CASES, ids=lambda c: "B{}H{}N{}dk{}dv{}C{}{}rot{}st{}seg{}".format(
+    *c[:6], str(c[6])[6:], *c[7:]))
+def test_chunkwise_small_chunks(case):
+    B, H, N, dk, dv, C, dtype, rot, st, seg = case
+    tol = BF16_TOL if dtype == torch.bfloat16 else F32_TOL
+    q, k, v = _inputs(B, H, N, dk, dv, dtype, 150)
+    theta = W.rotary_theta(dk) if rot else None
+    s0 = W.make_decode(B, H, dk, dv, dtype, 1, 0.1, 151)[0] if st else None
+    ref, ref_s = orc.chunkwise(to64(q), to64(k), to64(v), orc.head_gammas(H), C,
+                               theta=None if theta is None else to64(theta), pos0=9,
+                               state0=None if s0 is None else to64(s0))
+    o, s = R.retention_chunkwise_fwd(q.to(DEV), k.to(DEV), v.to(DEV), chunk=C, theta=theta, pos0=9,
+                                     state_in=None if s0 is None else s0.to(DEV), return_state=True, segments=seg)
+    torch.cuda.synchronize()
+    assert_close(to64(o), ref, tol, "o")
+    assert_close(to64(s), ref_s, tol, "state")
+
+
