@@ -569,6 +569,9 @@ BWD_CASES = [
     (1, 1, 4100, 64, 64, 64, torch.bfloat16, True, True, True),
     (1, 2, 130, 64, 64, 64, torch.float32, True, True, True),
     (2, 1, 200, 32, 64, 64, torch.float32, False, True, True),
+    (1, 2, 700, 64, 64, 256, torch.bfloat16, True, True, True),     # large chunks: one segment per chunk
+    (1, 1, 2000, 128, 128, 512, torch.bfloat16, False, True, True),
+    (1, 2, 150, 64, 64, 32, torch.float32, True, True, True),       # float32 small chunks
 ]
 
 
