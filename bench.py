@@ -586,6 +586,21 @@ def main():
         del bstep
         torch.cuda.empty_cache()
 
+        # ---------------- backward of the 7B-shaped layer
+        w = W.WORKLOADS["layer7b_bf16"]
+        bstep = backward_step(R, W, "layer7b_bf16", dev)
+        ms7 = time_events(bstep, 3, 1)
+        fl7 = (4 * chunk_alg_flops(w["B"], w["H"], w["N"], w["dv"] // 2, w["dk"], w["chunk"]) +
+               chunk_alg_flops(w["B"], w["H"], w["N"], w["dk"], w["dv"], w["chunk"]))
+        also.append({
+            "workload": "backward of the 7B-shaped layer (B=4 H=16 N=8192 d_k=256 d_v=512 bf16, chunk 128): "
+                        "passes 1 and 2 over the two halves of d_v, pass 3 at full width",
+            "ms": ms7, "tokens_per_s": w["B"] * w["N"] / (ms7 * 1e-3), "tflops": fl7 / (ms7 * 1e-3) / 1e12,
+            "mfma_frac": fl7 / (ms7 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, "forward_ms": ms3,
+        })
+        del bstep
+        torch.cuda.empty_cache()
+
         # ---------------- output stage of the 7B-shaped layer
         e = EPI_SHAPE
         estep = epilogue_step(R, W, dev)

@@ -191,10 +191,12 @@ size_t retention_chunkwise_workspace_size(int B, int H, int N, int dk, int dv, r
  *              when ordered on one stream; a forward workspace must not be the
  *              same memory (the backward's scratch would overwrite the
  *              counters a forward call expects to find). The caller owns it.
- * Implemented set: chunk in {64, 128}; dk and dv multiples of 8, and each of
- * (dk, dv) and (dv, dk) inside retention_chunkwise_fwd's set (bf16: dk and dv
- * both in {64, 128, 256}; f32: chunk*dk and chunk*dv <= 8192, both multiples
- * of 16); with d_state_out, every gamma >= 2^-20.
+ * Implemented set: retention_chunkwise_fwd's chunks; dk and dv multiples of
+ * 8, and each of (dk, dv) and (dv, dk) inside retention_chunkwise_fwd's set,
+ * except that for bf16 a dv twice a supported key width is taken too (the two
+ * passes keyed by dv then run over its halves): bf16 with dk in {64, 128, 256}
+ * and dv in {64, 128, 256, 512}; f32 with chunk*dk and chunk*dv <= 8192, both
+ * multiples of 16; with d_state_out, every gamma >= 2^-20.
  */
 ret_status_t retention_chunkwise_bwd(const void* q, const void* k, const void* v, const void* d_o,
                                      void* d_q, void* d_k, void* d_v, int B, int H, int N, int dk, int dv,

@@ -191,10 +191,14 @@ void fill_chunk_args(ret::ChunkArgs& a, const void* q, const void* k, const void
 // tensors. Every pass reads and writes its own buffers, so the passes may run
 // concurrently.
 struct BwdPlan {
-    size_t fwd_bytes;                  // one pass's region; three follow each other from offset 0
+    bool split;                        // bf16 with dv above the key widths: passes 1 and 2 over halves of dv
+    int npass;                         // forward passes (3, or 5 when split)
+    size_t fwd_bytes;                  // one pass's region; npass of them follow each other from offset 0
     size_t ctl_bytes;                  // leading bytes of each region (counters and flags) cleared per call
     size_t kr, qf, kf, vf, dof;        // [B,H,N,d] rotated / reversed inputs
     size_t dkf, dvf;                   // [B,H,N,d] reversed dK' and dV
+    size_t doh, vh;                    // split: halves of dO and V, [B,H,N,dv/2] twice each
+    size_t t1, t2;                     // split: second halves' dQ' and dK', [B,H,N,dk]
     size_t x1, x2, x3;                 // float32 [B,H,dk,dv] states
     size_t total;
 };
@@ -204,8 +208,15 @@ constexpr float kMinBwdGamma = 9.5367431640625e-07f;  // 2^-20: dS / gamma stays
 ret_status_t plan_bwd(int B, int H, int N, int dk, int dv, ret_dtype_t dtype, int chunk, BwdPlan& b) {
     if (dk % 8 != 0 || dv % 8 != 0) return RET_ERR_UNSUPPORTED;
     ChunkPlan p1, p3;  // passes 1 and 2 have key width dv and value width dk; pass 3 the reverse
+    b.split = false;
     ret_status_t s = plan_chunk(B, H, N, dv, dk, dtype, chunk, 0, p1);
+    if (s == RET_ERR_UNSUPPORTED && dtype == RET_BF16 && dv % 16 == 0) {
+        // dv wider than the matrix-core kernel's keys: run passes 1 and 2 over the halves of dv
+        s = plan_chunk(B, H, N, dv / 2, dk, dtype, chunk, 0, p1);
+        b.split = s == RET_OK;
+    }
     if (s != RET_OK) return s;
+    b.npass = b.split ? 5 : 3;
     s = plan_chunk(B, H, N, dk, dv, dtype, chunk, 0, p3);
     if (s != RET_OK) return s;
     const size_t es = dtype == RET_BF16 ? 2 : 4;
@@ -216,14 +227,18 @@ ret_status_t plan_bwd(int B, int H, int N, int dk, int dv, ret_dtype_t dtype, in
     // counters and flags precede the published states in a forward workspace
     const size_t c1 = p1.ws_bytes > 0 ? p1.agg_off : 0, c3 = p3.ws_bytes > 0 ? p3.agg_off : 0;
     b.ctl_bytes = c1 > c3 ? c1 : c3;
-    b.kr = 3 * b.fwd_bytes;
+    b.kr = static_cast<size_t>(b.npass) * b.fwd_bytes;
     b.qf = b.kr + nk;
     b.kf = b.qf + nk;
     b.vf = b.kf + nk;
     b.dof = b.vf + nv;
     b.dkf = b.dof + nv;
     b.dvf = b.dkf + nk;
-    b.x1 = b.dvf + nv;
+    b.doh = b.dvf + nv;
+    b.vh = b.doh + (b.split ? nv : 0);
+    b.t1 = b.vh + (b.split ? nv : 0);
+    b.t2 = b.t1 + (b.split ? nk : 0);
+    b.x1 = b.t2 + (b.split ? nk : 0);
     b.x2 = b.x1 + ns;
     b.x3 = b.x2 + ns;
     b.total = b.x3 + ns;
@@ -366,7 +381,7 @@ ret_status_t retention_chunkwise_bwd(const void* q, const void* k, const void* v
     // the passes' counters and flags start from zero on every call (the
     // scratch tensors of earlier calls of other sizes may have covered them)
     if (b.ctl_bytes > 0) {
-        for (int r = 0; r < 3; ++r) rj.zero[r] = reinterpret_cast<uint4*>(ws + r * b.fwd_bytes);
+        for (int r = 0; r < b.npass; ++r) rj.zero[r] = reinterpret_cast<uint4*>(ws + r * b.fwd_bytes);
         rj.nzero = static_cast<long long>(b.ctl_bytes / 16);
     }
     const float* sx1 = state_in ? x1 : nullptr;
@@ -374,14 +389,14 @@ ret_status_t retention_chunkwise_bwd(const void* q, const void* k, const void* v
     const float* sx3 = d_state_out ? x3 : nullptr;
     auto prep_states = [&]() -> ret_status_t {
         if (state_in || d_state_out) {
-            ret::StateJobs sj = {state_in, d_state_out, x1, x2, x3, nullptr, B, H, dk, dv, 0};
+            ret::StateJobs sj = {state_in, d_state_out, x1, x2, x3, nullptr, B, H, dk, dv, 0, b.split ? 1 : 0};
             if (ret::launch_states(sj, hp, st) != hipSuccess) return RET_ERR_HIP;
         }
         return RET_OK;
     };
     auto finish_states = [&]() -> ret_status_t {
         if (d_state_in) {
-            ret::StateJobs sj = {nullptr, nullptr, nullptr, nullptr, nullptr, d_state_in, B, H, dk, dv, 1};
+            ret::StateJobs sj = {nullptr, nullptr, nullptr, nullptr, nullptr, d_state_in, B, H, dk, dv, 1, 0};
             if (ret::launch_states(sj, hp, st) != hipSuccess) return RET_ERR_HIP;
         }
         return RET_OK;
@@ -395,10 +410,21 @@ ret_status_t retention_chunkwise_bwd(const void* q, const void* k, const void* v
         // The matrix-core kernel reads and writes the reversed passes in
         // reverse token order itself: only the rotation needs copies (K' and
         // Q' in token order) and, at the end, the rotation of dQ', dK' back.
+        // With split, the halves of dO and V are copied out as well.
+        const int hv = b.split ? dv / 2 : dv;  // key width of passes 1 and 2
+        char* doa = ws + b.doh;
+        char* dob = doa + static_cast<size_t>(B) * H * N * hv * 2;
+        char* va = ws + b.vh;
+        char* vb = va + static_cast<size_t>(B) * H * N * hv * 2;
         if (rot) {
-            rj.n = 2;
-            rj.j[0] = {q, qf, nullptr, dk, 0, 1, 0};
-            rj.j[1] = {k, kr, nullptr, dk, 0, 1, 0};
+            rj.j[rj.n++] = {q, qf, nullptr, dk, 0, 1, 0, 0, 0, nullptr};
+            rj.j[rj.n++] = {k, kr, nullptr, dk, 0, 1, 0, 0, 0, nullptr};
+        }
+        if (b.split) {
+            rj.j[rj.n++] = {d_o, doa, nullptr, hv, 0, 0, 0, dv, 0, nullptr};
+            rj.j[rj.n++] = {d_o, dob, nullptr, hv, 0, 0, 0, dv, hv, nullptr};
+            rj.j[rj.n++] = {v, va, nullptr, hv, 0, 0, 0, dv, 0, nullptr};
+            rj.j[rj.n++] = {v, vb, nullptr, hv, 0, 0, 0, dv, hv, nullptr};
         }
         if (rj.n > 0 || rj.nzero > 0)
             if (ret::launch_rows(rj, hp, bf16, st) != hipSuccess) return RET_ERR_HIP;
@@ -406,38 +432,57 @@ ret_status_t retention_chunkwise_bwd(const void* q, const void* k, const void* v
         if (s != RET_OK) return s;
         const void* kp = rot ? kr : k;  // K'
         const void* qp = rot ? qf : q;  // Q'
-        ChunkPlan p1, p3;  // key width dv (passes 1, 2) and dk (pass 3)
-        s = plan_chunk(B, H, N, dv, dk, dtype, chunk, 0, p1);
+        ChunkPlan p1, p3;  // key width hv (passes 1, 2) and dk (pass 3)
+        s = plan_chunk(B, H, N, hv, dk, dtype, chunk, 0, p1);
         if (s != RET_OK) return s;
         s = plan_chunk(B, H, N, dk, dv, dtype, chunk, 0, p3);
         if (s != RET_OK) return s;
-        ret::ChunkCalls cs;
-        fill_chunk_args(cs.a[0], d_o, v, kp, d_q, B, H, N, dv, dk, chunk, 0, sx1, nullptr, p1, ws);
-        fill_chunk_args(cs.a[1], v, d_o, qp, d_k, B, H, N, dv, dk, chunk, 0, sx2, nullptr, p1, ws + b.fwd_bytes);
-        cs.a[1].rev = 1;
         HeadParams hp_passes = hp;
         hp_passes.has_theta = 0;
+        ret::ChunkCalls cs;
         ret::ChunkArgs a3;
-        fill_chunk_args(a3, kp, qp, d_o, d_v, B, H, N, dk, dv, chunk, 0, sx3, d_state_in, p3, ws + 2 * b.fwd_bytes);
+        const size_t xh = static_cast<size_t>(B) * H * hv * dk;  // floats in one half of a split state
+        if (b.split) {
+            char* t1 = ws + b.t1;
+            char* t2 = ws + b.t2;
+            fill_chunk_args(cs.a[0], doa, va, kp, d_q, B, H, N, hv, dk, chunk, 0, sx1, nullptr, p1, ws);
+            fill_chunk_args(cs.a[1], dob, vb, kp, t1, B, H, N, hv, dk, chunk, 0, sx1 ? sx1 + xh : nullptr, nullptr,
+                            p1, ws + b.fwd_bytes);
+            fill_chunk_args(cs.a[2], va, doa, qp, d_k, B, H, N, hv, dk, chunk, 0, sx2, nullptr, p1,
+                            ws + 2 * b.fwd_bytes);
+            fill_chunk_args(cs.a[3], vb, dob, qp, t2, B, H, N, hv, dk, chunk, 0, sx2 ? sx2 + xh : nullptr, nullptr,
+                            p1, ws + 3 * b.fwd_bytes);
+            cs.a[2].rev = 1;
+            cs.a[3].rev = 1;
+            cs.n = 4;
+            fill_chunk_args(a3, kp, qp, d_o, d_v, B, H, N, dk, dv, chunk, 0, sx3, d_state_in, p3,
+                            ws + 4 * b.fwd_bytes);
+        } else {
+            fill_chunk_args(cs.a[0], d_o, v, kp, d_q, B, H, N, dv, dk, chunk, 0, sx1, nullptr, p1, ws);
+            fill_chunk_args(cs.a[1], v, d_o, qp, d_k, B, H, N, dv, dk, chunk, 0, sx2, nullptr, p1, ws + b.fwd_bytes);
+            cs.a[1].rev = 1;
+            cs.n = 2;
+            fill_chunk_args(a3, kp, qp, d_o, d_v, B, H, N, dk, dv, chunk, 0, sx3, d_state_in, p3,
+                            ws + 2 * b.fwd_bytes);
+        }
         a3.rev = 1;
-        if (dk == dv) {  // one shape: a single launch runs the three side by side
+        if (!b.split && dk == dv) {  // one shape: a single launch runs the three side by side
             cs.a[2] = a3;
             cs.n = 3;
             if (ret::launch_chunk_bf16_multi(cs, hp_passes, p1.dvt, st) != hipSuccess) return RET_ERR_HIP;
         } else {
-            cs.n = 2;
             if (ret::launch_chunk_bf16_multi(cs, hp_passes, p1.dvt, st) != hipSuccess) return RET_ERR_HIP;
             ret::ChunkCalls c3;
             c3.a[0] = a3;
             c3.n = 1;
             if (ret::launch_chunk_bf16_multi(c3, hp_passes, p3.dvt, st) != hipSuccess) return RET_ERR_HIP;
         }
-        if (rot) {
+        if (rot || b.split) {  // dQ = R^-1 (dQ'_a + dQ'_b), dK likewise (in place)
             memset(&rj.j, 0, sizeof(rj.j));
             rj.nzero = 0;
             rj.n = 2;
-            rj.j[0] = {d_q, d_q, nullptr, dk, 0, -1, 0};
-            rj.j[1] = {d_k, d_k, nullptr, dk, 0, -1, 0};
+            rj.j[0] = {d_q, d_q, nullptr, dk, 0, rot ? -1 : 0, 0, 0, 0, b.split ? ws + b.t1 : nullptr};
+            rj.j[1] = {d_k, d_k, nullptr, dk, 0, rot ? -1 : 0, 0, 0, 0, b.split ? ws + b.t2 : nullptr};
             if (ret::launch_rows(rj, hp, bf16, st) != hipSuccess) return RET_ERR_HIP;
         }
         return finish_states();
@@ -445,10 +490,10 @@ ret_status_t retention_chunkwise_bwd(const void* q, const void* k, const void* v
 
     // float32: the passes run on reversed and rotated copies
     rj.n = 4;
-    rj.j[0] = {q, qf, nullptr, dk, 1, rot ? 1 : 0, 0};
-    rj.j[1] = {k, kf, rot ? kr : nullptr, dk, 1, rot ? 1 : 0, 0};
-    rj.j[2] = {v, vf, nullptr, dv, 1, 0, 0};
-    rj.j[3] = {d_o, dof, nullptr, dv, 1, 0, 0};
+    rj.j[0] = {q, qf, nullptr, dk, 1, rot ? 1 : 0, 0, 0, 0, nullptr};
+    rj.j[1] = {k, kf, rot ? kr : nullptr, dk, 1, rot ? 1 : 0, 0, 0, 0, nullptr};
+    rj.j[2] = {v, vf, nullptr, dv, 1, 0, 0, 0, 0, nullptr};
+    rj.j[3] = {d_o, dof, nullptr, dv, 1, 0, 0, 0, 0, nullptr};
     if (ret::launch_rows(rj, hp, bf16, st) != hipSuccess) return RET_ERR_HIP;
     s = prep_states();
     if (s != RET_OK) return s;
@@ -467,9 +512,9 @@ ret_status_t retention_chunkwise_bwd(const void* q, const void* k, const void* v
     memset(&rj.j, 0, sizeof(rj.j));
     rj.nzero = 0;
     int n = 0;
-    if (rot) rj.j[n++] = {d_q, d_q, nullptr, dk, 0, -1, 0};
-    rj.j[n++] = {dkf, d_k, nullptr, dk, 1, rot ? -1 : 0, 1};
-    rj.j[n++] = {dvf, d_v, nullptr, dv, 1, 0, 1};
+    if (rot) rj.j[n++] = {d_q, d_q, nullptr, dk, 0, -1, 0, 0, 0, nullptr};
+    rj.j[n++] = {dkf, d_k, nullptr, dk, 1, rot ? -1 : 0, 1, 0, 0, nullptr};
+    rj.j[n++] = {dvf, d_v, nullptr, dv, 1, 0, 1, 0, 0, nullptr};
     rj.n = n;
     if (ret::launch_rows(rj, hp, bf16, st) != hipSuccess) return RET_ERR_HIP;
     return finish_states();

@@ -18,11 +18,14 @@
 // are dQ', dK' rotated by the opposite angle.
 //
 // For bf16 the matrix-core kernel runs the reversed passes in reverse token
-// order itself; float32 passes run on reversed copies. The kernels here are
-// the HBM-bound glue around the passes: rows_kernel rotates and/or reverses
-// rows (up to four tensors per launch, one per grid row; one more row can
-// zero-fill the control words of the passes' workspace regions),
-// state_kernel transposes and scales the [dk, dv] states.
+// order itself; float32 passes run on reversed copies. When dv is wider than
+// the kernel's key width (the first two passes use V and dO as keys), those
+// passes run as two passes over the halves of dv, whose outputs add up: the
+// scores q k^T and the carried state q S are sums over key columns. The
+// kernels here are the HBM-bound glue around the passes: rows_kernel rotates,
+// reverses, slices or adds rows (up to six tensors per launch, one per grid
+// row; one more row can zero-fill the control words of the passes' workspace
+// regions), state_kernel transposes, splits and scales the [dk, dv] states.
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -78,7 +81,8 @@ __device__ __forceinline__ void store8(void* base, size_t i, const float* x) {
 }
 
 // One thread moves 8 elements of one row of the tensor selected by blockIdx.y.
-// Row t of every (batch, head) is read from src, rotated by sign * theta at
+// Row t of every (batch, head) is read from src (columns src_col .. of rows of
+// src_ld elements; plus the same row of `add` when given), rotated by sign * theta at
 // the position of the token it holds when the job asks (pos0 + t, or
 // pos0 + N-1-t when src is in reverse order), and written to row t' of dst0
 // (t' = N-1-t when flip0, else t) and to row t of dst1 when dst1 is given. A job
@@ -88,7 +92,7 @@ template <bool BF16>
 __global__ __launch_bounds__(kRowThreads) void rows_kernel(RowJobs jobs, HeadParams hp) {
     if (static_cast<int>(blockIdx.y) == jobs.n) {  // the zero-fill row
         const long long stride = static_cast<long long>(gridDim.x) * kRowThreads;
-        for (int r = 0; r < 3; ++r) {
+        for (int r = 0; r < kMaxZeroRegions; ++r) {
             if (!jobs.zero[r]) continue;
             for (long long e = static_cast<long long>(blockIdx.x) * kRowThreads + threadIdx.x; e < jobs.nzero;
                  e += stride)
@@ -107,7 +111,14 @@ __global__ __launch_bounds__(kRowThreads) void rows_kernel(RowJobs jobs, HeadPar
         const long long bh = row / jobs.N;
         const int t = static_cast<int>(row - bh * jobs.N);
         float x[8];
-        load8<BF16>(jb.src, static_cast<size_t>(elem), x);
+        const int ld = jb.src_ld ? jb.src_ld : d;
+        load8<BF16>(jb.src, static_cast<size_t>(row * ld + jb.src_col + col), x);
+        if (jb.add) {
+            float y[8];
+            load8<BF16>(jb.add, static_cast<size_t>(elem), y);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] += y[i];
+        }
         if (jb.rot != 0) {
             const double position = static_cast<double>(jobs.pos0) + (jb.src_rev ? jobs.N - 1 - t : t);
 #pragma unroll
@@ -138,7 +149,11 @@ __global__ __launch_bounds__(kStateThreads) void state_kernel(StateJobs sj, Head
         const int ij = static_cast<int>(e - bh * per);
         const int i = ij / sj.dv, j = ij - (ij / sj.dv) * sj.dv;
         const float g = hp.gamma[bh % sj.H];
-        const long long tr = bh * per + static_cast<long long>(j) * sj.dk + i;
+        // transposed position: row j of [dv, dk], in the first or second half array when split
+        const int hv = sj.split ? sj.dv / 2 : sj.dv;
+        const int half = j / hv, jj = j - half * hv;
+        const long long tr = static_cast<long long>(half) * sj.B * sj.H * hv * sj.dk + bh * hv * sj.dk +
+                             static_cast<long long>(jj) * sj.dk + i;
         if (sj.mode == 0) {
             if (sj.s0) sj.x1[tr] = sj.s0[e];
             if (sj.ds) {
@@ -161,7 +176,7 @@ int grid_for(long long items, int threads) {
 }  // namespace
 
 hipError_t launch_rows(const RowJobs& jobs, const HeadParams& hp, bool bf16, hipStream_t st) {
-    if (jobs.n < 0 || jobs.n > 4 || (jobs.n == 0 && jobs.nzero <= 0)) return hipErrorInvalidValue;
+    if (jobs.n < 0 || jobs.n > kMaxRowJobs || (jobs.n == 0 && jobs.nzero <= 0)) return hipErrorInvalidValue;
     int dmax = 0;
     for (int i = 0; i < jobs.n; ++i) dmax = jobs.j[i].d > dmax ? jobs.j[i].d : dmax;
     long long items = static_cast<long long>(jobs.B) * jobs.H * jobs.N * dmax / 8;

@@ -37,7 +37,7 @@ struct ChunkArgs {
 
 // Several chunkwise calls of one shape and plan (different tensors, states and
 // workspace regions) run by one launch.
-constexpr int kMaxChunkCalls = 3;
+constexpr int kMaxChunkCalls = 4;
 struct ChunkCalls {
     ChunkArgs a[kMaxChunkCalls];
     int n;
@@ -67,28 +67,35 @@ struct StepArgs {
 
 // Row transforms of the backward (backward.hip): one job per tensor.
 struct RowJob {
-    const void* src;  // [B,H,N,d] rows
+    const void* src;  // [B,H,N,src_ld] rows; the job reads columns src_col .. src_col + d - 1
     void* dst0;       // [B,H,N,d]; row t lands at N-1-t when flip0
     void* dst1;       // optional second copy, rows in order (nullptr: none)
     int d;            // row width in elements, a multiple of 8
     int flip0;
     int rot;          // 0: none, +1: rotate by +theta, -1: by -theta
     int src_rev;      // src rows are in reverse token order: row t holds token N-1-t (its rotation position)
+    int src_ld;       // row stride of src in elements (0: d)
+    int src_col;      // first column read from src
+    const void* add;  // optional [B,H,N,d] rows added to src before the rotation (nullptr: none)
 };
 
+constexpr int kMaxRowJobs = 6;
+constexpr int kMaxZeroRegions = 5;
 struct RowJobs {
-    RowJob j[4];
+    RowJob j[kMaxRowJobs];
     int n;  // jobs in use
     int B, H, N;
     long long pos0;
     // Optional extra grid row that zero-fills nzero 16-byte units at each
     // non-null zero[i] (nzero = 0: none).
-    uint4* zero[3];
+    uint4* zero[kMaxZeroRegions];
     long long nzero;
 };
 
 // State transforms of the backward: mode 0 writes x1 = s0^T, x2 = ds^T / gamma,
 // x3 = ds / gamma (per head, [dk, dv] sources); mode 1 scales dsi by gamma.
+// With split, x1 and x2 ([dv, dk] per head) are written as two arrays of their
+// first and second dv/2 rows, [B,H,dv/2,dk] each, one after the other.
 struct StateJobs {
     const float* s0;
     const float* ds;
@@ -98,6 +105,7 @@ struct StateJobs {
     float* dsi;
     int B, H, dk, dv;
     int mode;
+    int split;
 };
 
 // Output stage (epilogue.hip).

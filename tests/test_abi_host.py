@@ -196,9 +196,12 @@ def test_backward_validation(lib):
     assert bwd(lib, gamma=g) == GAMMA
     assert bwd(lib, d_state_in=A + 4) == ALIGN
     assert bwd(lib, d_o=A + 2) == ALIGN
-    # each of dk and dv is the key width of some pass: both must be bf16 key widths
-    assert bwd(lib, dv=512) == UNSUP
-    assert bwd(lib, dk=256, dv=512, chunk=128) == UNSUP
+    # each of dk and dv is the key width of some pass: dk must be a bf16 key width, and dv one or twice one
+    # (a dv of 512 runs the first two passes over its halves)
+    assert bwd(lib, dv=512) == WS
+    assert bwd(lib, dk=256, dv=512, chunk=128) == WS
+    assert bwd(lib, dv=1024) == UNSUP
+    assert bwd(lib, dk=512, dv=64) == UNSUP
     assert bwd(lib, chunk=32) == UNSUP
     assert bwd(lib, dtype=F32, dk=64, dv=200) == UNSUP  # not a multiple of 8 / 16
     # the state gradient divides by gamma: tiny gammas are outside the set only then
@@ -210,7 +213,8 @@ def test_backward_validation(lib):
     assert bwd(lib) == WS
     assert bwd(lib, ws=A, ws_bytes=need - 1) == WS
     assert lib.retention_chunkwise_bwd_workspace_size(1, 2, 200, 64, 64, BF16, 64) > need
-    assert lib.retention_chunkwise_bwd_workspace_size(1, 2, 100, 64, 512, BF16, 64) == 0
+    assert lib.retention_chunkwise_bwd_workspace_size(1, 2, 100, 64, 512, BF16, 64) > 0
+    assert lib.retention_chunkwise_bwd_workspace_size(1, 2, 100, 64, 1024, BF16, 64) == 0
     assert lib.retention_chunkwise_bwd_workspace_size(1, 2, 100, 64, 64, BF16, 48) == 0
 
 

@@ -572,6 +572,9 @@ BWD_CASES = [
     (1, 2, 700, 64, 64, 256, torch.bfloat16, True, True, True),     # large chunks: one segment per chunk
     (1, 1, 2000, 128, 128, 512, torch.bfloat16, False, True, True),
     (1, 2, 150, 64, 64, 32, torch.float32, True, True, True),       # float32 small chunks
+    (1, 2, 300, 64, 512, 64, torch.bfloat16, True, True, True),     # dv = 512: passes 1, 2 over halves of dv
+    (2, 2, 257, 256, 512, 128, torch.bfloat16, False, True, True),
+    (1, 1, 1100, 128, 256, 128, torch.bfloat16, True, True, True),
 ]
 
 
@@ -850,3 +853,20 @@ def test_chunkwise_small_chunks(case):
     assert_close(to64(s), ref_s, tol, "state")
 
 
+
+
+def test_chunkwise_backward_layer7b_sampled_heads():
+    """The 7B-shaped layer's backward (B=4 H=16 N=8192 d_k=256 d_v=512, chunk 128: the
+    passes keyed by d_v run over its halves) as the benchmark runs it; two sampled
+    (batch, head) pairs recomputed by the oracle."""
+    w = W.WORKLOADS["layer7b_bf16"]
+    q, k, v, _ = W.make_workload("layer7b_bf16", device=DEV)
+    d_o, _ = W.make_upstream_grads(w["B"], w["H"], w["N"], w["dk"], w["dv"], w["dtype"], w["seed"] + 1000, device=DEV)
+    dq, dk_, dv_, _ = R.retention_chunkwise_bwd(q, k, v, d_o, chunk=w["chunk"])
+    torch.cuda.synchronize()
+    g = orc.head_gammas(w["H"])
+    for b, h in ((0, 0), (3, 13)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = orc.backward(to64(q[sl]), to64(k[sl]), to64(v[sl]), to64(d_o[sl]), [g[h]])
+        for name, got, r in zip(("dq", "dk", "dv"), (dq[sl], dk_[sl], dv_[sl]), ref):
+            assert_close(to64(got), r, BF16_TOL, f"{name} (b={b}, h={h})")
