@@ -437,6 +437,20 @@ ret_status_t retention_chunkwise_bwd(const void* q, const void* k, const void* v
         if (s != RET_OK) return s;
         s = plan_chunk(B, H, N, dk, dv, dtype, chunk, 0, p3);
         if (s != RET_OK) return s;
+        // Split passes whose tile matches pass 3's (hv == dk) share its launch
+        // when the five passes together fill the chip without sequence
+        // segments (one kernel form for all of them).
+        bool together = false;
+        if (b.split && hv == dk) {
+            ChunkPlan q1, q3;
+            if (plan_chunk(B, H, N, hv, dk, dtype, chunk, 1, q1) == RET_OK &&
+                plan_chunk(B, H, N, dk, dv, dtype, chunk, 1, q3) == RET_OK && q1.dvt == q3.dvt &&
+                4LL * B * H * q1.nvt + static_cast<long long>(B) * H * q3.nvt >= kTargetBlocks) {
+                p1 = q1;
+                p3 = q3;
+                together = true;
+            }
+        }
         HeadParams hp_passes = hp;
         hp_passes.has_theta = 0;
         ret::ChunkCalls cs;
@@ -466,9 +480,8 @@ ret_status_t retention_chunkwise_bwd(const void* q, const void* k, const void* v
                             ws + 2 * b.fwd_bytes);
         }
         a3.rev = 1;
-        if (!b.split && dk == dv) {  // one shape: a single launch runs the three side by side
-            cs.a[2] = a3;
-            cs.n = 3;
+        if ((!b.split && dk == dv) || together) {  // a single launch runs them all side by side
+            cs.a[cs.n++] = a3;
             if (ret::launch_chunk_bf16_multi(cs, hp_passes, p1.dvt, st) != hipSuccess) return RET_ERR_HIP;
         } else {
             if (ret::launch_chunk_bf16_multi(cs, hp_passes, p1.dvt, st) != hipSuccess) return RET_ERR_HIP;

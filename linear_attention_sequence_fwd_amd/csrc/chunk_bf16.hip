@@ -1177,15 +1177,22 @@ __global__ __launch_bounds__((C / 16) * 64, (kWavesPerSimd<DK, DVT, C>)) void ch
     chunk_body<DK, DVT, C, MODE, FAST, 0>(a, hp, blockIdx.x, gridDim.x);
 }
 
-// Several calls of one shape in one launch, their workgroups interleaved so
-// that all of them progress together: workgroup b serves call b % n.
+// Several calls in one launch. Calls of one shape interleave their workgroups
+// so that all of them progress together (workgroup b serves call b % n);
+// calls of different sizes (same tile and form) take consecutive ranges.
 
 template <int DK, int DVT, int C, int MODE, bool FAST>
 __global__ __launch_bounds__((C / 16) * 64, (kWavesPerSimd<DK, DVT, C>)) void chunk_bf16_multi_kernel(ChunkCalls cs,
                                                                                                   HeadParams hp) {
     const int n = cs.n;
     const int b = blockIdx.x;
-    chunk_body<DK, DVT, C, MODE, FAST, 1>(cs.a[b % n], hp, b / n, gridDim.x / n);
+    if (cs.interleave) {
+        chunk_body<DK, DVT, C, MODE, FAST, 1>(cs.a[b % n], hp, b / n, gridDim.x / n);
+    } else {  // calls of different sizes: call c owns workgroups first[c] .. first[c+1]-1
+        int c = 0;
+        while (c + 1 < n && b >= cs.first[c + 1]) ++c;
+        chunk_body<DK, DVT, C, MODE, FAST, 1>(cs.a[c], hp, b - cs.first[c], cs.first[c + 1] - cs.first[c]);
+    }
 }
 
 // Holding two chunks of outputs and queries in registers fits with 64-token
@@ -1224,7 +1231,7 @@ static void launch_chunk_multi_form(const ChunkCalls& cs, const HeadParams& hp, 
     using G = ChunkGeo<DK, DVT, C>;
     constexpr int kLocal = kLocalFits<DK, DVT, C> ? kLocalPass : kTwoPass;
     const ChunkArgs& a = cs.a[0];
-    const dim3 grid(a.B * a.H * a.nvt * a.nseg * cs.n);
+    const dim3 grid(cs.first[cs.n]);
     switch (chunk_mode<DK, DVT, C>(a)) {
         case kSinglePass:
             hipLaunchKernelGGL((chunk_bf16_multi_kernel<DK, DVT, C, kSinglePass, FAST>), grid, dim3(G::NTHR), 0, st,
@@ -1285,15 +1292,29 @@ static hipError_t run_chunk_bf16_multi(const ChunkCalls& cs, const HeadParams& h
     RET_CASE(256, 64, 128) \
     RET_CASE(256, 128, 128)
 
-hipError_t launch_chunk_bf16_multi(const ChunkCalls& cs, const HeadParams& hp, int dvt, hipStream_t st) {
-    if (cs.n < 1 || cs.n > kMaxChunkCalls) return hipErrorInvalidValue;
+// The kernel form (single pass, local pass, two-pass) a call takes.
+static int call_form(const ChunkArgs& a) {
+    if (a.nseg == 1) return kSinglePass;
+    const bool local_fits = a.chunk == 64 || a.dk + a.dv / a.nvt <= 192;
+    return (local_fits && a.seg_len <= kKeepChunks * a.chunk) ? kLocalPass : kTwoPass;
+}
+
+hipError_t launch_chunk_bf16_multi(const ChunkCalls& in, const HeadParams& hp, int dvt, hipStream_t st) {
+    if (in.n < 1 || in.n > kMaxChunkCalls) return hipErrorInvalidValue;
+    ChunkCalls cs = in;
     const ChunkArgs& a = cs.a[0];
-    for (int i = 1; i < cs.n; ++i) {  // one shape and one plan for every call
+    bool same = true;
+    cs.first[0] = 0;
+    for (int i = 0; i < cs.n; ++i) {  // one tile and one kernel form for every call
         const ChunkArgs& b = cs.a[i];
-        if (b.B != a.B || b.H != a.H || b.N != a.N || b.dk != a.dk || b.dv != a.dv || b.chunk != a.chunk ||
-            b.nvt != a.nvt || b.nseg != a.nseg || b.seg_len != a.seg_len || b.grp != a.grp)
+        if (b.dk != a.dk || b.chunk != a.chunk || b.dv % dvt != 0 || b.dv / dvt != b.nvt ||
+            call_form(b) != call_form(a))
             return hipErrorInvalidValue;
+        same = same && b.B == a.B && b.H == a.H && b.N == a.N && b.dv == a.dv && b.nseg == a.nseg &&
+               b.seg_len == a.seg_len && b.grp == a.grp;
+        cs.first[i + 1] = cs.first[i] + b.B * b.H * b.nvt * b.nseg;
     }
+    cs.interleave = same ? 1 : 0;
 #define RET_CASE(DK_, DVT_, C_) \
     if (a.dk == DK_ && dvt == DVT_ && a.chunk == C_) return run_chunk_bf16_multi<DK_, DVT_, C_>(cs, hp, st);
     RET_CHUNK_SHAPES

@@ -35,12 +35,15 @@ struct ChunkArgs {
     int rev;      // rows in reverse token order (chunk_bf16_multi_kernel only; no rotation then)
 };
 
-// Several chunkwise calls of one shape and plan (different tensors, states and
-// workspace regions) run by one launch.
-constexpr int kMaxChunkCalls = 4;
+// Several chunkwise calls with one tile and kernel form (different tensors,
+// states and workspace regions) run by one launch; `first` and `interleave`
+// are filled by launch_chunk_bf16_multi.
+constexpr int kMaxChunkCalls = 5;
 struct ChunkCalls {
     ChunkArgs a[kMaxChunkCalls];
     int n;
+    int first[kMaxChunkCalls + 1];  // workgroup ranges when the calls differ in size
+    int interleave;                 // calls of one size: workgroup b serves call b % n
 };
 
 struct ParallelArgs {
