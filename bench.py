@@ -404,7 +404,7 @@ def main():
     ap.add_argument("--sweep", choices=["decode-batch", "chunk"], help="print one JSON line per point of a sweep")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(sequence and head sharding across GPUs is a design note, not implemented)", file=sys.stderr)
         sys.exit(2)
 
