@@ -122,10 +122,13 @@ __global__ __launch_bounds__(kStepThreads) void recurrent_step_kernel(StepArgs a
 }
 
 // Column tiles per (sequence, head): halve the tile while there are fewer
-// than 512 workgroups and the halves keep at least 64 columns.
+// than 256 workgroups and the halves keep at least 64 columns. (A sweep of
+// the target over 256..2048 and of 32-column tiles at 16 heads of 256 x 512
+// put it here: 8 sequences, 23.4 us against 27.8 with a target of 512; other
+// batch sizes within 2%.)
 int recurrent_step_tiles(int B, int H, int dv) {
     int nt = 1;
-    while (static_cast<long long>(B) * H * nt < 512 && (dv / nt) % 128 == 0) nt *= 2;
+    while (static_cast<long long>(B) * H * nt < 256 && (dv / nt) % 128 == 0) nt *= 2;
     return nt;
 }
 
