@@ -184,6 +184,7 @@ void fill_chunk_args(ret::ChunkArgs& a, const void* q, const void* k, const void
     a.grp = p.grp;
     a.pos0 = pos0;
     a.rev = 0;
+    a.orot = 0;
 }
 
 // Workspace of the backward: one forward-workspace region per pass first (each
@@ -451,6 +452,9 @@ ret_status_t retention_chunkwise_bwd(const void* q, const void* k, const void* v
                 together = true;
             }
         }
+        // with rotation and no dv split the first two passes rotate their outputs back when the
+        // frequencies fit in LDS beside their tiles; otherwise a row kernel does it afterwards
+        const bool orot = rot && !b.split && ret::chunk_orot_fits(dv, p1.dvt, p1.tile);
         HeadParams hp_passes = hp;
         hp_passes.has_theta = 0;
         ret::ChunkCalls cs;
@@ -475,6 +479,10 @@ ret_status_t retention_chunkwise_bwd(const void* q, const void* k, const void* v
             fill_chunk_args(cs.a[0], d_o, v, kp, d_q, B, H, N, dv, dk, chunk, 0, sx1, nullptr, p1, ws);
             fill_chunk_args(cs.a[1], v, d_o, qp, d_k, B, H, N, dv, dk, chunk, 0, sx2, nullptr, p1, ws + b.fwd_bytes);
             cs.a[1].rev = 1;
+            if (orot) {  // the passes store dQ = R^-1 dQ' and dK = R^-1 dK' themselves
+                cs.a[0].orot = cs.a[1].orot = 1;
+                cs.a[0].pos0 = cs.a[1].pos0 = pos0;  // positions of the output rotation (has_theta is off)
+            }
             cs.n = 2;
             fill_chunk_args(a3, kp, qp, d_o, d_v, B, H, N, dk, dv, chunk, 0, sx3, d_state_in, p3,
                             ws + 2 * b.fwd_bytes);
@@ -490,7 +498,7 @@ ret_status_t retention_chunkwise_bwd(const void* q, const void* k, const void* v
             c3.n = 1;
             if (ret::launch_chunk_bf16_multi(c3, hp_passes, p3.dvt, st) != hipSuccess) return RET_ERR_HIP;
         }
-        if (rot || b.split) {  // dQ = R^-1 (dQ'_a + dQ'_b), dK likewise (in place)
+        if (b.split || (rot && !orot)) {  // dQ = R^-1 (dQ'_a + dQ'_b), dK likewise (in place)
             memset(&rj.j, 0, sizeof(rj.j));
             rj.nzero = 0;
             rj.n = 2;

@@ -173,9 +173,13 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
     using G = ChunkGeo<DK, DVT, C>;
     constexpr int UK = DK / 8;  // 16-byte units in a row of K (row-major) and of S^T
     constexpr int UC = C / 8;   // 16-byte units in a row of K^T and V^T
-    __shared__ __attribute__((aligned(16))) u16 kbuf[C * DK];
+    // the multi-call kernel's output rotation (a.orot, see store_o) keeps this
+    // value tile's DVT/2 frequencies in float32 after the keys
+    constexpr bool kORot = REVM != 0 && chunk_orot_fits(DK, DVT, C);
+    __shared__ __attribute__((aligned(16))) u16 kbuf[C * DK + (kORot ? DVT : 0)];
     __shared__ __attribute__((aligned(16))) u16 vbuf[DVT * C];
     __shared__ __attribute__((aligned(16))) u16 sbuf[DVT * DK];
+    float* s_oth = reinterpret_cast<float*>(kbuf + C * DK);
     // Broadcast slots of the segmented form (ticket, look-back status), overlaid
     // on sbuf: both are read before the first write of the state copy (a
     // barrier lies in between).
@@ -229,6 +233,9 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
     const int vt = chain % a.nvt;
     const int bh = chain / a.nvt;
     const int h = bh % a.H;
+    if constexpr (kORot) {  // the column pairs of this value tile; read after later barriers
+        if (a.orot && tid < DVT / 2) s_oth[tid] = hp.theta[vt * (DVT / 2) + tid];
+    }
 
     const float gam = hp.gamma[h];
     const double lg2 = log2_gamma(gam);
@@ -390,14 +397,36 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
 
     // ---- pieces of the chunk loop
     // Step 7: this wave's 16 output rows of the chunk at token t0 (L valid), as bf16.
+    // With a.orot, each row is first rotated by minus theta at its token's
+    // position: the lane's columns 16 nt + 4 grp .. +3 are pairs 8 nt + 2 grp
+    // and 8 nt + 2 grp + 1 of the tile (frequencies from LDS, so no global load
+    // sits behind the branch).
     auto store_o = [&](const f32x4 (&o)[G::NTV], int t0, int L) __attribute__((always_inline)) {
         const int row = rev ? L - 1 - (rb * 16 + l16) : rb * 16 + l16;
         if (rb * 16 + l16 < L) {
             char* base = reinterpret_cast<char*>(Og + static_cast<size_t>(mrow0(t0, L)) * a.dv);
             const uint32_t off = static_cast<uint32_t>((row * a.dv + grp * 4) * 2);
+            f32x4 x[G::NTV];
+#pragma unroll
+            for (int nt = 0; nt < G::NTV; ++nt) x[nt] = o[nt];
+            if constexpr (kORot) {
+                if (a.orot) {
+                    const double position = static_cast<double>(a.pos0 + mrow0(t0, L) + row);
+#pragma unroll
+                    for (int nt = 0; nt < G::NTV; ++nt)
+#pragma unroll
+                        for (int p = 0; p < 2; ++p) {
+                            float c, sn;
+                            rot_cs_fast(position, -s_oth[nt * 8 + grp * 2 + p], c, sn);
+                            const float re = x[nt][2 * p], im = x[nt][2 * p + 1];
+                            x[nt][2 * p] = re * c - im * sn;
+                            x[nt][2 * p + 1] = re * sn + im * c;
+                        }
+                }
+            }
 #pragma unroll
             for (int nt = 0; nt < G::NTV; ++nt) {
-                const uint2 w = make_uint2(pack2_bf16(o[nt][0], o[nt][1]), pack2_bf16(o[nt][2], o[nt][3]));
+                const uint2 w = make_uint2(pack2_bf16(x[nt][0], x[nt][1]), pack2_bf16(x[nt][2], x[nt][3]));
                 *reinterpret_cast<uint2*>(base + off + nt * 32) = w;
             }
         }
@@ -1308,7 +1337,7 @@ hipError_t launch_chunk_bf16_multi(const ChunkCalls& in, const HeadParams& hp, i
     for (int i = 0; i < cs.n; ++i) {  // one tile and one kernel form for every call
         const ChunkArgs& b = cs.a[i];
         if (b.dk != a.dk || b.chunk != a.chunk || b.dv % dvt != 0 || b.dv / dvt != b.nvt ||
-            call_form(b) != call_form(a))
+            call_form(b) != call_form(a) || (b.orot && !chunk_orot_fits(b.dk, dvt, b.chunk)))
             return hipErrorInvalidValue;
         same = same && b.B == a.B && b.H == a.H && b.N == a.N && b.dv == a.dv && b.nseg == a.nseg &&
                b.seg_len == a.seg_len && b.grp == a.grp;

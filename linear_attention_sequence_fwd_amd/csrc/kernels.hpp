@@ -33,7 +33,15 @@ struct ChunkArgs {
     int grp;      // segments per look-back group (bf16 segmented form)
     long long pos0;
     int rev;      // rows in reverse token order (chunk_bf16_multi_kernel only; no rotation then)
+    int orot;     // rotate each output row by minus theta at its token's position before rounding
+                  // (chunk_bf16_multi_kernel only, where chunk_orot_fits; output columns are the pairs)
 };
+
+// LDS bytes of the bf16 chunk kernel's tiles (keys, values, state copy), and
+// whether the multi-call kernel also holds the output rotation's frequencies
+// next to them within a compute unit's 160 KiB.
+constexpr int chunk_bf16_tile_lds(int dk, int dvt, int c) { return (c * dk + dvt * c + dvt * dk) * 2; }
+constexpr bool chunk_orot_fits(int dk, int dvt, int c) { return chunk_bf16_tile_lds(dk, dvt, c) + dvt * 2 <= 160 * 1024; }
 
 // Several chunkwise calls with one tile and kernel form (different tensors,
 // states and workspace regions) run by one launch; `first` and `interleave`
