@@ -565,7 +565,8 @@ def main():
         byb = bwd_alg_bytes(w["B"], w["H"], w["N"], w["dk"], w["dv"])
         also.append({
             "workload": "backward of the multi-scale workload (dq, dk, dv; rotation; B=2 H=8 N=2048 d=64 "
-                        "bf16, chunk 64): the three chunkwise passes in one launch between two row kernels",
+                        "bf16, chunk 64): a row kernel (rotated K, Q), then the three chunkwise passes in one "
+                        "launch (dq, dk rotated back as they are stored)",
             "ms": msb, "ms_spread": spb, "tokens_per_s": w["B"] * w["N"] / (msb * 1e-3),
             "tflops": flb / (msb * 1e-3) / 1e12, "mfma_frac": flb / (msb * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             "gbs": byb / (msb * 1e-3) / 1e9, "alg_bytes": byb, "alg_flops": flb,
