@@ -578,18 +578,20 @@ BWD_CASES = [
 ]
 
 
-def _bwd_check(B, H, N, dk, dv, chunk, dtype, rot, st, ds, seed, gamma=None):
+def _bwd_check(B, H, N, dk, dv, chunk, dtype, rot, st, ds, seed, gamma=None, pos0=None):
     tol = BF16_TOL if dtype == torch.bfloat16 else F32_TOL
+    if pos0 is None:
+        pos0 = 11 if rot else 0
     q, k, v = _inputs(B, H, N, dk, dv, dtype, seed)
     d_o, d_s = W.make_upstream_grads(B, H, N, dk, dv, dtype, seed + 1000)
     s0 = W.make_decode(B, H, dk, dv, dtype, 1, 0.1, seed + 2000)[0] if st else None
     theta = W.rotary_theta(dk) if rot else None
     g = _gammas_for(H, gamma)
     ref = orc.backward(to64(q), to64(k), to64(v), to64(d_o), g, theta=None if theta is None else to64(theta),
-                       pos0=11 if rot else 0, state0=None if s0 is None else to64(s0),
+                       pos0=pos0, state0=None if s0 is None else to64(s0),
                        d_state=to64(d_s) if ds else None)
     got = R.retention_chunkwise_bwd(
-        q.to(DEV), k.to(DEV), v.to(DEV), d_o.to(DEV), chunk=chunk, gamma=gamma, theta=theta, pos0=11 if rot else 0,
+        q.to(DEV), k.to(DEV), v.to(DEV), d_o.to(DEV), chunk=chunk, gamma=gamma, theta=theta, pos0=pos0,
         state_in=None if s0 is None else s0.to(DEV), d_state_out=d_s.to(DEV) if ds else None, need_d_state_in=True)
     torch.cuda.synchronize()
     for name, a, b in zip(("dq", "dk", "dv", "d_state_in"), got, ref):
@@ -600,6 +602,16 @@ def _bwd_check(B, H, N, dk, dv, chunk, dtype, rot, st, ds, seed, gamma=None):
     *c[:6], str(c[6])[6:], *c[7:]))
 def test_chunkwise_backward_small(case):
     _bwd_check(*case, seed=71)
+
+
+@pytest.mark.parametrize("pos0", [1_000_000_007, 3 * 2**31 + 5])
+@pytest.mark.parametrize("dk,dv,C", [(64, 64, 64), (128, 128, 128), (256, 256, 128)])
+def test_chunkwise_backward_rotation_far_positions(pos0, dk, dv, C):
+    """dq and dk at absolute positions far from zero. The first two passes rotate
+    their output rows back themselves (angle reduced in float64 per row); with
+    256-wide keys, 128-column values and 128-token chunks the tile has no LDS
+    left for the frequencies and a row kernel rotates them afterwards."""
+    _bwd_check(1, 2, 300, dk, dv, C, torch.bfloat16, True, True, True, seed=73, pos0=pos0)
 
 
 @pytest.mark.parametrize("gammas", [[1.0, 0.99], [0.05, 0.6], [0.9, 0.999999]])
