@@ -97,7 +97,7 @@ ret_status_t retention_parallel_fwd(const void* q, const void* k, const void* v,
  *            token, or NULL. May alias state_in.
  * segments:  0 lets the library choose; s >= 1 asks for s sequence segments
  *            (clamped to the number of chunks and to 4096; ignored when
- *            B*H*(value tiles) exceeds 8192). With more than one segment
+ *            B*H*(value tiles) exceeds 512). With more than one segment
  *            the sequence of every head is cut into segments that run in
  *            parallel, and the state entering each segment is assembled from
  *            the end states of the segments before it, with factor

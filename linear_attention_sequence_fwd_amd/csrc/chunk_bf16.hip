@@ -218,7 +218,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
     if constexpr (SEGMENTED) {
         const int nchains = a.B * a.H * a.nvt;
         chain = bid % static_cast<unsigned>(nchains);
-        unsigned long long* ctl = a.ctl + chain;
+        unsigned long long* ctl = a.ctl + static_cast<size_t>(chain) * kCtlStride;
         if (tid == 0) *s_ticket = __hip_atomic_fetch_add(ctl, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
         const unsigned long long tk = *s_ticket;

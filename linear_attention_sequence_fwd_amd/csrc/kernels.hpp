@@ -37,6 +37,10 @@ struct ChunkArgs {
                   // (chunk_bf16_multi_kernel only, where chunk_orot_fits; output columns are the pairs)
 };
 
+// Ticket counters of the segmented bf16 chunk kernel: one per chain, each on a
+// 128-byte line of its own (64-bit words apart).
+constexpr int kCtlStride = 16;
+
 // LDS bytes of the bf16 chunk kernel's tiles (keys, values, state copy), and
 // whether the multi-call kernel also holds the output rotation's frequencies
 // next to them within a compute unit's 160 KiB.
