@@ -151,8 +151,9 @@ ret_status_t plan_chunk(int B, int H, int N, int dk, int dv, ret_dtype_t dtype, 
     //             segment states | group aggregates], chain = (batch, head, value tile)
     const size_t slot = static_cast<size_t>(B) * H * dk * dv * sizeof(float);  // one state per chain
     p.flags_off = kCtlBytes;
-    p.gflags_off = p.flags_off + round256(static_cast<size_t>(base) * p.nseg_max * sizeof(unsigned long long));
-    p.agg_off = p.gflags_off + round256(static_cast<size_t>(base) * ngroups_max * sizeof(unsigned long long));
+    const size_t flag_bytes = ret::kFlagStride * sizeof(unsigned long long);
+    p.gflags_off = p.flags_off + round256(static_cast<size_t>(base) * p.nseg_max * flag_bytes);
+    p.agg_off = p.gflags_off + round256(static_cast<size_t>(base) * ngroups_max * flag_bytes);
     p.gagg_off = p.agg_off + slot * p.nseg_max;
     p.ws_bytes = p.nseg_max > 1 ? p.gagg_off + slot * ngroups_max : 0;
     if (base * p.nseg > 2147483647LL) return RET_ERR_UNSUPPORTED;

@@ -976,7 +976,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
         return reinterpret_cast<unsigned long long*>(a.agg + (static_cast<size_t>(chain) * a.nseg + j) * kSlot) +
                wave * (G::MT * G::NT * 128) + lane;
     };
-    unsigned long long* flags = a.flags + static_cast<size_t>(chain) * a.nseg;
+    unsigned long long* flags = a.flags + static_cast<size_t>(chain) * a.nseg * kFlagStride;
     const unsigned long long f_agg =
         (static_cast<unsigned long long>(gen + 1) << 32) | (static_cast<unsigned long long>(chain) << 1);
     const unsigned long long f_inc = f_agg | 1ull;
@@ -988,7 +988,9 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
             for (int nt = 0; nt < G::NT; ++nt) store_coherent(dst + (mt * G::NT + nt) * 128, st[mt][nt]);
         wait_stores();
         __syncthreads();
-        if (tid == 0) __hip_atomic_store(flags + seg, flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0)
+            __hip_atomic_store(flags + static_cast<size_t>(seg) * kFlagStride, flag, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     };
     const float gseg = static_cast<float>(gamma_pow(lg2, a.seg_len));
     // Segment groups of a.grp segments: the last member of each group (when it
@@ -997,7 +999,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
     // so a segment reads its group predecessors and one aggregate per earlier
     // group: S_in(s) = sum_{first<=j<s} g^(s-1-j) T_j + sum_{q<group(s)} g^(s-1-last_q) A_q.
     const int ngroups = (a.nseg + a.grp - 1) / a.grp;
-    unsigned long long* gflags = a.gflags + static_cast<size_t>(chain) * ngroups;
+    unsigned long long* gflags = a.gflags + static_cast<size_t>(chain) * ngroups * kFlagStride;
     auto gslot = [&](int q) __attribute__((always_inline)) {
         return reinterpret_cast<unsigned long long*>(a.gagg + (static_cast<size_t>(chain) * ngroups + q) * kSlot) +
                wave * (G::MT * G::NT * 128) + lane;
@@ -1015,7 +1017,9 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
                 const int j = j0 - lane;
                 const unsigned long long w = j == 0 ? want0 : want;
                 const unsigned long long f =
-                    j >= lo ? __hip_atomic_load(fl + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : w;
+                    j >= lo ? __hip_atomic_load(fl + static_cast<size_t>(j) * kFlagStride, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT)
+                            : w;
                 if (__ballot(f != w) == 0) {
                     j0 -= 64;
                     continue;
@@ -1086,7 +1090,9 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
                     store_coherent(dst + (mt * G::NT + nt) * 128, sacc[mt][nt] + gseg * sin[mt][nt]);
             wait_stores();
             __syncthreads();
-            if (tid == 0) __hip_atomic_store(gflags + q, f_agg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (tid == 0)
+                __hip_atomic_store(gflags + static_cast<size_t>(q) * kFlagStride, f_agg, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
         // earlier groups: entry k is group q-1-k with weight g^(pos + k grp)
         if (q > 0) {

@@ -40,6 +40,9 @@ struct ChunkArgs {
 // Ticket counters of the segmented bf16 chunk kernel: one per chain, each on a
 // 128-byte line of its own (64-bit words apart).
 constexpr int kCtlStride = 16;
+// Published-state flags (per chain and segment, per chain and segment group)
+// likewise sit one per 128-byte line.
+constexpr int kFlagStride = 16;
 
 // LDS bytes of the bf16 chunk kernel's tiles (keys, values, state copy), and
 // whether the multi-call kernel also holds the output rotation's frequencies
