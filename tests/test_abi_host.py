@@ -151,6 +151,9 @@ def test_workspace_contract(lib):
     assert lib.retention_chunkwise_workspace_size(0, 2, 4096, 64, 64, BF16, 64, 0) == 0
     # many heads: no split, no workspace
     assert lib.retention_chunkwise_workspace_size(4, 16, 8192, 256, 512, BF16, 128, 0) == 0
+    # requested segments are honoured up to 512 (batch x heads x value tiles) chains, ignored beyond
+    assert lib.retention_chunkwise_workspace_size(4, 128, 4096, 64, 64, BF16, 64, 4) > 0
+    assert lib.retention_chunkwise_workspace_size(5, 128, 4096, 64, 64, BF16, 64, 4) == 0
 
 
 @pytest.mark.parametrize("cfg", [(1, 8, 64, 64, BF16, 64), (1, 8, 128, 128, BF16, 128), (2, 8, 64, 64, F32, 64),
