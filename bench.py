@@ -191,47 +191,129 @@ def measured_peaks():
             "how": "1 GiB device copy; torch.mm bf16 8192x8192x8192 (hipBLASLt)"}
 
 
-def cpu_baseline(q, k, v, theta, H, budget_s):
-    """The fp64 oracle's recurrent form on the host, on a bounded sample of the
-    workload: whole sequences of the first batch entry, repeated until the
-    time budget is used."""
-    import numpy as np
+# ---------------------------------------------------------------- CPU baseline (the fp64 oracle)
+#
+# The oracle runs in worker processes started before this process touches the
+# GPU (spawn context), one head per task, single-threaded numpy each, so the
+# host's cores work on independent heads. Each worker draws its inputs with the
+# workloads' recipe on the CPU generator (same shapes, distributions and
+# dtypes as the GPU inputs; the timing does not depend on the values).
 
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
+
+def _oracle_task(kind, shape, seed, reps):
+    """One timed oracle run in a worker: returns (seconds, units of work)."""
+    import time as _t
+
+    import numpy as np
+    import torch
+
+    from linear_attention_sequence_fwd_amd import workloads as W
     from oracle import retention as orc
 
-    q64 = q[:1].float().cpu().numpy().astype(np.float64)
-    k64 = k[:1].float().cpu().numpy().astype(np.float64)
-    v64 = v[:1].float().cpu().numpy().astype(np.float64)
-    th = None if theta is None else theta.double().numpy()
-    g = orc.head_gammas(H)
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    if ctx:
-        ctx.__enter__()
-    try:
-        t0 = time.perf_counter()
-        reps = 0
-        while True:
+    torch.set_num_threads(1)
+    if kind == "recurrent":
+        N, dk, dv, dtype, h, rot = shape
+        q, k, v = W.make_qkv(1, 1, N, dk, dv, getattr(torch, dtype), seed)
+        q64, k64, v64 = (x.float().numpy().astype(np.float64) for x in (q, k, v))
+        g = orc.head_gammas(h + 1)[h:h + 1]
+        th = W.rotary_theta(dk).double().numpy() if rot else None
+        t0 = _t.perf_counter()
+        for _ in range(reps):
             orc.recurrent(q64, k64, v64, g, theta=th)
-            reps += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        dt = time.perf_counter() - t0
+        return _t.perf_counter() - t0, reps * N
+    if kind == "decode":  # reps consecutive steps of one head
+        dk, dv, h = shape
+        s0, qs, ks, vs = W.make_decode(1, 1, dk, dv, torch.bfloat16, reps, 0.01, seed)
+        st = s0.double().numpy()
+        q64, k64, v64 = (x.float().numpy().astype(np.float64) for x in (qs, ks, vs))
+        g = orc.head_gammas(h + 1)[h:h + 1]
+        t0 = _t.perf_counter()
+        for n in range(reps):
+            _, st = orc.decode_step(q64[n], k64[n], v64[n], st, g)
+        return _t.perf_counter() - t0, reps
+    raise ValueError(kind)
+
+
+def host_cores():
+    """Cores this process may use, capped at the 16 host cores a one-GPU machine shares out."""
+    return max(1, min(len(os.sched_getaffinity(0)), 16))
+
+
+def start_oracle_pool():
+    """Worker pool for the CPU baseline, started before any GPU use (workers
+    never touch the GPU; numpy/BLAS single-threaded in each)."""
+    import multiprocessing as mp
+
+    n = host_cores()
+    saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for k in saved:
+        os.environ[k] = "1"
+    try:
+        pool = mp.get_context("spawn").Pool(n)
     finally:
-        if ctx:
-            ctx.__exit__(None, None, None)
-    tokens = reps * q64.shape[2]
-    return {
-        "value": tokens / dt,
-        "unit": "tokens/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": f"fp64 recurrent oracle, batch entry 0 (H={H}, N={q64.shape[2]}), {reps} repetitions in "
-                  f"{dt:.1f} s, numpy single-threaded",
-    }
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    return pool, n
+
+
+def cpu_baselines(pool, cores):
+    """The fp64 oracle on every workload, one head per worker task; per workload
+    a bounded sample of heads (and of decode steps), scaled to the workload's
+    unit. Returns {workload: {...}}."""
+    import numpy as np
+
+    from linear_attention_sequence_fwd_amd import workloads as W
+
+    def run(tasks):
+        t0 = time.perf_counter()
+        res = pool.starmap(_oracle_task, tasks)
+        return time.perf_counter() - t0, res
+
+    out = {}
+    # 7B-shaped layer: `cores` heads (of B*H = 64), full N; the job is B*H heads
+    w = W.WORKLOADS["layer7b_bf16"]
+    nh = min(cores, w["B"] * w["H"])
+    wall, res = run([("recurrent", (w["N"], w["dk"], w["dv"], "bfloat16", i % w["H"], False), 100 + i, 1)
+                     for i in range(nh)])
+    job_s = wall * (w["B"] * w["H"]) / nh
+    out["layer7b_bf16"] = {"value": w["B"] * w["N"] / job_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                           "sample": f"fp64 recurrent oracle on {nh} of the {w['B'] * w['H']} heads (full N="
+                                     f"{w['N']}, d_k={w['dk']}, d_v={w['dv']}), one head per core, {wall:.1f} s "
+                                     f"wall; whole-job time scaled by {w['B'] * w['H']}/{nh}",
+                           "wall_s": wall, "cpu_s": float(sum(r[0] for r in res))}
+    # multi-scale workload: all B*H = 16 heads, with rotation
+    w = W.WORKLOADS["msr_bf16_rotary"]
+    heads = w["B"] * w["H"]
+    wall, res = run([("recurrent", (w["N"], w["dk"], w["dv"], "bfloat16", i % w["H"], True), 200 + i, 4)
+                     for i in range(heads)])
+    out["msr_bf16_rotary"] = {"value": 4 * w["B"] * w["N"] / wall, "unit": "tokens/s", "cores": cores,
+                              "kind": "oracle", "sample": f"fp64 recurrent oracle with rotation, all {heads} heads, "
+                                                          f"4 repetitions, {wall:.1f} s wall", "wall_s": wall}
+    # long context: all 8 heads over the first 16384 tokens (the recurrent form is linear in N)
+    w = W.WORKLOADS["longctx_bf16"]
+    n = 16384
+    wall, res = run([("recurrent", (n, w["dk"], w["dv"], "bfloat16", i, False), 300 + i, 1) for i in range(w["H"])])
+    out["longctx_bf16"] = {"value": w["B"] * n / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                           "sample": f"fp64 recurrent oracle, all {w['H']} heads over the first {n} of "
+                                     f"{w['N']} tokens, {wall:.1f} s wall", "wall_s": wall}
+    # decode: 16 heads per core for 64 steps each (of 64 x 16 heads x 512 steps)
+    w = W.WORKLOADS["decode_bf16"]
+    nh = 16 * cores
+    steps = 64
+    wall, res = run([("decode", (w["dk"], w["dv"], i % w["H"]), 400 + i, steps) for i in range(nh)])
+    out["decode_bf16"] = {"value": nh * steps / wall, "unit": "state updates/s", "cores": cores, "kind": "oracle",
+                          "sample": f"fp64 decode-step oracle, {nh} of the {w['B'] * w['H']} heads for {steps} "
+                                    f"consecutive steps each, {wall:.1f} s wall", "wall_s": wall}
+    # single head fp32: the whole workload, one core (one head)
+    w = W.WORKLOADS["single_head_f32"]
+    wall, res = run([("recurrent", (w["N"], w["dk"], w["dv"], "float32", 0, False), 1, 50)])
+    out["single_head_f32"] = {"value": 50 * w["N"] / wall, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                              "sample": f"fp64 recurrent oracle, the whole workload 50 times, {wall:.2f} s wall",
+                              "wall_s": wall}
+    return out
 
 
 def run_only(name, steps, warmup, dev):
@@ -391,16 +473,53 @@ def sweep_decode_batch(dev):
         torch.cuda.empty_cache()
 
 
+def time_kernel(R, q, k, v, kw, reps, evict=None):
+    """Durations (ms) of the chunkwise call's main kernel from the events the
+    library records around its execution, one call at a time; with `evict`
+    (a callable that writes 1 GiB) the caches are flushed before each call.
+    Returns (median, {p10, p50, p90})."""
+    import numpy as np
+    import torch
+
+    ts = []
+    for i in range(reps + 2):
+        if evict is not None:
+            evict()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        R.retention_chunkwise_fwd(q, k, v, events=evs, **kw)
+        torch.cuda.synchronize()
+        if i >= 2:
+            ts.append(evs[4].elapsed_time(evs[5]))
+    ts = np.array(ts)
+    return float(np.median(ts)), {f"p{p}": float(np.percentile(ts, p)) for p in (10, 50, 90)}
+
+
+def make_evict(dev):
+    """A 1 GiB device write: evicts the XCD L2 caches and the 256 MB MALL."""
+    import torch
+
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+    def evict():
+        scratch.fill_(1.0)
+
+    return evict, scratch
+
+
+LAYER7B_DESC = ("7B-shaped retention layer forward, chunkwise: B=4 H=16 N=8192 d_k=256 d_v=512 bf16, "
+                "gamma_h=1-2^(-5-h), chunk 128")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--quick", action="store_true", help="main workload only")
+    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", choices=["msr", "layer7b", "decode", "longctx", "single", "copy", "bwd", "epi",
                                        "decmsr"],
                     help="time one workload only (no CPU baseline); for profilers")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sweep", choices=["decode-batch", "chunk"], help="print one JSON line per point of a sweep")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -409,6 +528,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    pool = cores = None
+    if not (args.only or args.sweep or args.no_cpu):
+        pool, cores = start_oracle_pool()  # before the first GPU call
 
     import linear_attention_sequence_fwd_amd as R
     from linear_attention_sequence_fwd_amd import workloads as W
@@ -426,26 +549,23 @@ def main():
         sweep_chunk(dev)
         return
 
-    # ---------------- main workload
-    name = "msr_bf16_rotary"
+    # ---------------- headline: the 7B-shaped layer
+    name = "layer7b_bf16"
     w = W.WORKLOADS[name]
-    q, k, v, theta = W.make_workload(name, device=dev)
-    kw = dict(chunk=w["chunk"], theta=R.HostFloats(theta))
+    q, k, v, _ = W.make_workload(name, device=dev)
     out = torch.empty_like(v)
-    ws_bytes = R.retention_chunkwise_workspace_size(w["B"], w["H"], w["N"], w["dk"], w["dv"], q.dtype, w["chunk"])
-    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    kw.update(out=out, workspace=ws)
+    kw = dict(chunk=w["chunk"], out=out)
     step = lambda: R.retention_chunkwise_fwd(q, k, v, **kw)  # noqa: E731
     ms_eager = time_events(step, args.steps, args.warmup)
     ms, spread = time_graph(step, args.steps, args.warmup)
-    phases = time_phases(R, q, k, v, kw, max(20, args.steps // 4))
-    tokens = w["B"] * w["N"]
-    alg_bytes = chunk_alg_bytes(w["B"], w["H"], w["N"], w["dk"], w["dv"])
-    main_ms = phases[2]
-    achieved = alg_bytes / (main_ms * 1e-3) / 1e9
+    kernel_ms, kspread = time_kernel(R, q, k, v, kw, max(20, args.steps // 4))
+    flops = chunk_alg_flops(w["B"], w["H"], w["N"], w["dk"], w["dv"], w["chunk"])
+    nbytes = chunk_alg_bytes(w["B"], w["H"], w["N"], w["dk"], w["dv"])
+    tflops = flops / (kernel_ms * 1e-3) / 1e12
+    gbs = nbytes / (kernel_ms * 1e-3) / 1e9
     result = {
         "metric": METRIC,
-        "value": tokens / (ms * 1e-3),
+        "value": w["B"] * w["N"] / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -456,24 +576,24 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {
-            "workload": "multi-scale retention forward, chunkwise: B=2 H=8 N=2048 d_k=d_v=64 bf16, "
-                        "rotary theta_j=10000^(-2j/64), gamma_h=1-2^(-5-h), chunk 64",
-            "global_batch": w["B"],
-            "seq_len": w["N"],
-            "parallelism": "single GPU",
-        },
+        "config": {"workload": LAYER7B_DESC, "global_batch": w["B"], "seq_len": w["N"],
+                   "parallelism": "single GPU"},
         "roofline": {
-            "bound": "hbm",
-            "kernel": "chunk_bf16_kernel<64, 64, 64, local pass> (the whole step is this one launch)",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured_traffic("msr_bf16_rotary"),
+            "bound": "mfma",
+            "kernel": "chunk_wide_kernel<256> (the whole step is this one launch)",
+            "achieved": tflops,
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": tflops / BF16_PEAK_TFLOPS,
+            "traffic": measured_traffic(name),
             "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x copy calibration + WRITE_SIZE)",
-            "alg_bytes_per_launch": alg_bytes,
-            "kernel_ms": main_ms,
+            "alg_flops_per_launch": flops,
+            "alg_bytes_per_launch": nbytes,
+            "kernel_ms": kernel_ms,
+            "kernel_ms_spread": kspread,
+            "hbm": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS},
+            "binding": "HBM by arithmetic intensity (198.8 FLOP/B against a ridge of 312.5): the MFMA fraction "
+                       "at the HBM roofline is 0.636",
         },
         "timing": "ms_per_step from HIP-graph replay of exactly `steps` steps (up to 20 per graph, an event "
                   "between replays for the spread); eager_ms_per_step launches each call from Python; "
@@ -481,182 +601,222 @@ def main():
         "ms_per_step_spread": spread,
         "eager_ms_per_step": ms_eager,
     }
-    result["cpu_baseline"] = cpu_baseline(q.cpu(), k.cpu(), v.cpu(), theta, w["H"], args.cpu_seconds)
+    del q, k, v, out
+    torch.cuda.empty_cache()
     result["measured_peaks"] = measured_peaks()
+
+    also = []
+    if not args.quick:
+        also = run_also(R, W, torch, dev)
+    if pool is not None:
+        cpu = cpu_baselines(pool, cores)
+        pool.close()
+        pool.join()
+        result["cpu_baseline"] = cpu.pop("layer7b_bf16")
+        for entry in also:
+            key = entry.get("key")
+            if key in cpu:
+                entry["cpu_baseline"] = cpu[key]
+    for entry in also:
+        entry.pop("key", None)
+    if also:
+        result["also"] = also
+    print(json.dumps(result))
+
+
+def run_also(R, W, torch, dev):
+    also = []
+    evict, scratch = make_evict(dev)
+
+    # ---------------- multi-scale workload with rotation (warm and cold caches)
+    name = "msr_bf16_rotary"
+    w = W.WORKLOADS[name]
+    q, k, v, theta = W.make_workload(name, device=dev)
+    out = torch.empty_like(v)
+    ws_bytes = R.retention_chunkwise_workspace_size(w["B"], w["H"], w["N"], w["dk"], w["dv"], q.dtype, w["chunk"])
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    kw = dict(chunk=w["chunk"], theta=R.HostFloats(theta), out=out, workspace=ws)
+    ms2, sp2 = time_graph(lambda: R.retention_chunkwise_fwd(q, k, v, **kw), 200, 20)
+    warm_ms, warm_sp = time_kernel(R, q, k, v, kw, 50)
+    cold_ms, cold_sp = time_kernel(R, q, k, v, kw, 20, evict=evict)
+    by2 = chunk_alg_bytes(w["B"], w["H"], w["N"], w["dk"], w["dv"])
+    also.append({
+        "key": name,
+        "workload": "multi-scale retention forward, chunkwise: B=2 H=8 N=2048 d_k=d_v=64 bf16, rotary "
+                    "theta_j=10000^(-2j/64), gamma_h=1-2^(-5-h), chunk 64",
+        "tokens_per_s": w["B"] * w["N"] / (ms2 * 1e-3), "ms": ms2, "ms_spread": sp2,
+        "kernel_ms_warm": warm_ms, "kernel_ms_warm_spread": warm_sp,
+        "kernel_ms_cold": cold_ms, "kernel_ms_cold_spread": cold_sp,
+        "cold": "a 1 GiB device write before each call evicts the L2 caches and the 256 MB MALL",
+        "roofline": {"bound": "hbm", "kernel": "chunk_bf16_kernel<64, 64, 64, local pass>",
+                     "achieved": by2 / (warm_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": by2 / (warm_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "frac_cold": by2 / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(name), "alg_bytes_per_launch": by2},
+    })
     del q, k, v, out, ws
     torch.cuda.empty_cache()
 
-    if not args.quick:
-        also = []
-        # ---------------- 7B-shaped layer
-        w = W.WORKLOADS["layer7b_bf16"]
-        q, k, v, _ = W.make_workload("layer7b_bf16", device=dev)
-        out = torch.empty_like(v)
-        kw3 = dict(chunk=w["chunk"], out=out)
-        ms3 = time_events(lambda: R.retention_chunkwise_fwd(q, k, v, **kw3), 10, 3)
-        ph3 = time_phases(R, q, k, v, kw3, 5)
-        fl = chunk_alg_flops(w["B"], w["H"], w["N"], w["dk"], w["dv"], w["chunk"])
-        by = chunk_alg_bytes(w["B"], w["H"], w["N"], w["dk"], w["dv"])
-        also.append({
-            "workload": "7B-shaped layer chunkwise: B=4 H=16 N=8192 d_k=256 d_v=512 bf16, chunk 128",
-            "tokens_per_s": w["B"] * w["N"] / (ms3 * 1e-3), "ms": ms3, "main_kernel_ms": ph3[2],
-            "tflops": fl / (ph3[2] * 1e-3) / 1e12, "mfma_frac": fl / (ph3[2] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-            "gbs": by / (ph3[2] * 1e-3) / 1e9, "hbm_frac": by / (ph3[2] * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "alg_bytes_per_launch": by, "traffic": measured_traffic("layer7b_bf16"),
-        })
-        del q, k, v, out
-        torch.cuda.empty_cache()
+    # ---------------- decode
+    name = "decode_bf16"
+    w = W.WORKLOADS[name]
+    s0, qs, ks, vs = W.make_decode_workload(device=dev)
+    state = s0.clone()
+    o = torch.empty((w["B"], w["H"], w["dv"]), dtype=torch.bfloat16, device=dev)
+    steps = w["steps"]
 
-        # ---------------- decode
-        w = W.WORKLOADS["decode_bf16"]
-        s0, qs, ks, vs = W.make_decode_workload(device=dev)
-        state = s0.clone()
-        o = torch.empty((w["B"], w["H"], w["dv"]), dtype=torch.bfloat16, device=dev)
-        steps = w["steps"]
+    def run_decode():
+        for t in range(steps):
+            R.retention_recurrent_step(qs[t], ks[t], vs[t], state, out=o)
 
-        def run_decode():
-            for t in range(steps):
-                R.retention_recurrent_step(qs[t], ks[t], vs[t], state, out=o)
+    ms4 = time_events(run_decode, 2, 1) / steps
+    by4 = decode_alg_bytes(w["B"], w["H"], w["dk"], w["dv"])
+    also.append({
+        "key": name,
+        "workload": "recurrent decode: 64 sequences x H=16, fp32 state 256x512, bf16 q/k/v, 512 steps",
+        "ms_per_step": ms4, "state_updates_per_s": w["B"] * w["H"] / (ms4 * 1e-3),
+        "roofline": {"bound": "hbm", "kernel": "recurrent_step_kernel", "achieved": by4 / (ms4 * 1e-3) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": by4 / (ms4 * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(name), "alg_bytes_per_launch": by4},
+    })
+    del s0, qs, ks, vs, state, o
+    torch.cuda.empty_cache()
 
-        ms4 = time_events(run_decode, 2, 1) / steps
-        by4 = decode_alg_bytes(w["B"], w["H"], w["dk"], w["dv"])
-        also.append({
-            "workload": "recurrent decode: 64 sequences x H=16, fp32 state 256x512, bf16 q/k/v, 512 steps",
-            "ms_per_step": ms4, "state_updates_per_s": w["B"] * w["H"] / (ms4 * 1e-3),
-            "gbs": by4 / (ms4 * 1e-3) / 1e9, "hbm_frac": by4 / (ms4 * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "alg_bytes_per_launch": by4, "traffic": measured_traffic("decode_bf16"),
-        })
-        del s0, qs, ks, vs, state, o
-        torch.cuda.empty_cache()
+    # ---------------- long context + parallel crossover
+    name = "longctx_bf16"
+    w = W.WORKLOADS[name]
+    q, k, v, _ = W.make_workload(name, device=dev)
+    kw5 = dict(chunk=w["chunk"])
+    ms5 = time_events(lambda: R.retention_chunkwise_fwd(q, k, v, **kw5), 10, 3)
+    k5, _ = time_kernel(R, q, k, v, kw5, 5)
+    by5 = chunk_alg_bytes(w["B"], w["H"], w["N"], w["dk"], w["dv"])
+    fl5 = chunk_alg_flops(w["B"], w["H"], w["N"], w["dk"], w["dv"], w["chunk"])
+    cross = []
+    for n in w["parallel_lengths"]:
+        qn, kn, vn = q[:, :, :n].contiguous(), k[:, :, :n].contiguous(), v[:, :, :n].contiguous()
+        tp = time_events(lambda: R.retention_parallel_fwd(qn, kn, vn), 20, 5)
+        tc = time_events(lambda: R.retention_chunkwise_fwd(qn, kn, vn, chunk=w["chunk"]), 20, 5)
+        pf = parallel_alg_flops(w["B"], w["H"], n, w["dk"], w["dv"])
+        cross.append({"N": n, "parallel_ms": tp, "chunkwise_ms": tc, "parallel_tflops": pf / (tp * 1e-3) / 1e12,
+                      "parallel_mfma_frac": pf / (tp * 1e-3) / 1e12 / BF16_PEAK_TFLOPS})
+    also.append({
+        "key": name,
+        "workload": "long-context chunkwise: B=1 H=8 N=65536 d_k=d_v=128 bf16, chunk 128",
+        "tokens_per_s": w["B"] * w["N"] / (ms5 * 1e-3), "ms": ms5, "kernel_ms": k5,
+        "roofline": {"bound": "hbm", "kernel": "chunk_bf16_kernel<128, 128, 128, two-pass>",
+                     "achieved": by5 / (k5 * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": by5 / (k5 * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": measured_traffic(name),
+                     "alg_bytes_per_launch": by5, "tflops": fl5 / (k5 * 1e-3) / 1e12},
+        "parallel_crossover": cross,
+    })
+    del q, k, v
+    torch.cuda.empty_cache()
 
-        # ---------------- long context + parallel crossover
-        w = W.WORKLOADS["longctx_bf16"]
-        q, k, v, _ = W.make_workload("longctx_bf16", device=dev)
-        kw5 = dict(chunk=w["chunk"])
-        ms5 = time_events(lambda: R.retention_chunkwise_fwd(q, k, v, **kw5), 10, 3)
-        ph5 = time_phases(R, q, k, v, kw5, 5)
-        by5 = chunk_alg_bytes(w["B"], w["H"], w["N"], w["dk"], w["dv"])
-        fl5 = chunk_alg_flops(w["B"], w["H"], w["N"], w["dk"], w["dv"], w["chunk"])
-        cross = []
-        for n in w["parallel_lengths"]:
-            qn, kn, vn = q[:, :, :n].contiguous(), k[:, :, :n].contiguous(), v[:, :, :n].contiguous()
-            tp = time_events(lambda: R.retention_parallel_fwd(qn, kn, vn), 20, 5)
-            tc = time_events(lambda: R.retention_chunkwise_fwd(qn, kn, vn, chunk=w["chunk"]), 20, 5)
-            pf = parallel_alg_flops(w["B"], w["H"], n, w["dk"], w["dv"])
-            cross.append({"N": n, "parallel_ms": tp, "chunkwise_ms": tc,
-                          "parallel_tflops": pf / (tp * 1e-3) / 1e12})
-        also.append({
-            "workload": "long-context chunkwise: B=1 H=8 N=65536 d_k=d_v=128 bf16, chunk 128",
-            "tokens_per_s": w["B"] * w["N"] / (ms5 * 1e-3), "ms": ms5,
-            "phase_ms": {"segment_states": ph5[0], "segment_scan": ph5[1], "main": ph5[2]},
-            "alg_bytes_per_launch": by5, "traffic": measured_traffic("longctx_bf16"),
-            "step_gbs": by5 / (ms5 * 1e-3) / 1e9, "step_hbm_frac": by5 / (ms5 * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "step_tflops": fl5 / (ms5 * 1e-3) / 1e12,
-            "parallel_crossover": cross,
-        })
-        del q, k, v
-        torch.cuda.empty_cache()
+    # ---------------- backward of the multi-scale workload
+    w = W.WORKLOADS["msr_bf16_rotary"]
+    bstep = backward_step(R, W, "msr_bf16_rotary", dev)
+    msb, spb = time_graph(bstep, 100, 10)
+    flb = 3 * chunk_alg_flops(w["B"], w["H"], w["N"], w["dk"], w["dv"], w["chunk"])
+    byb = bwd_alg_bytes(w["B"], w["H"], w["N"], w["dk"], w["dv"])
+    also.append({
+        "workload": "backward of the multi-scale workload (dq, dk, dv; rotation; B=2 H=8 N=2048 d=64 "
+                    "bf16, chunk 64): a row kernel (rotated K, Q), then the three chunkwise passes in one "
+                    "launch (dq, dk rotated back as they are stored)",
+        "ms": msb, "ms_spread": spb, "tokens_per_s": w["B"] * w["N"] / (msb * 1e-3),
+        "tflops": flb / (msb * 1e-3) / 1e12, "mfma_frac": flb / (msb * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "gbs": byb / (msb * 1e-3) / 1e9, "alg_bytes": byb, "alg_flops": flb,
+    })
+    del bstep
+    torch.cuda.empty_cache()
 
-        # ---------------- backward of the main workload
-        w = W.WORKLOADS["msr_bf16_rotary"]
-        bstep = backward_step(R, W, "msr_bf16_rotary", dev)
-        msb, spb = time_graph(bstep, 100, 10)
-        flb = 3 * chunk_alg_flops(w["B"], w["H"], w["N"], w["dk"], w["dv"], w["chunk"])
-        byb = bwd_alg_bytes(w["B"], w["H"], w["N"], w["dk"], w["dv"])
-        also.append({
-            "workload": "backward of the multi-scale workload (dq, dk, dv; rotation; B=2 H=8 N=2048 d=64 "
-                        "bf16, chunk 64): a row kernel (rotated K, Q), then the three chunkwise passes in one "
-                        "launch (dq, dk rotated back as they are stored)",
-            "ms": msb, "ms_spread": spb, "tokens_per_s": w["B"] * w["N"] / (msb * 1e-3),
-            "tflops": flb / (msb * 1e-3) / 1e12, "mfma_frac": flb / (msb * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-            "gbs": byb / (msb * 1e-3) / 1e9, "alg_bytes": byb, "alg_flops": flb,
-            "forward_graph_ms": ms,
-        })
-        torch.cuda.empty_cache()
+    # ---------------- backward of the long-context workload
+    w = W.WORKLOADS["longctx_bf16"]
+    bstep = backward_step(R, W, "longctx_bf16", dev)
+    msl = time_events(bstep, 5, 2)
+    fll = 3 * chunk_alg_flops(w["B"], w["H"], w["N"], w["dk"], w["dv"], w["chunk"])
+    also.append({
+        "workload": "backward of the long-context workload (B=1 H=8 N=65536 d=128 bf16, chunk 128)",
+        "ms": msl, "tokens_per_s": w["B"] * w["N"] / (msl * 1e-3), "tflops": fll / (msl * 1e-3) / 1e12,
+        "mfma_frac": fll / (msl * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+    })
+    del bstep
+    torch.cuda.empty_cache()
 
-        # ---------------- backward of the long-context workload
-        w = W.WORKLOADS["longctx_bf16"]
-        bstep = backward_step(R, W, "longctx_bf16", dev)
-        msl = time_events(bstep, 5, 2)
-        fll = 3 * chunk_alg_flops(w["B"], w["H"], w["N"], w["dk"], w["dv"], w["chunk"])
-        also.append({
-            "workload": "backward of the long-context workload (B=1 H=8 N=65536 d=128 bf16, chunk 128)",
-            "ms": msl, "tokens_per_s": w["B"] * w["N"] / (msl * 1e-3), "tflops": fll / (msl * 1e-3) / 1e12,
-            "mfma_frac": fll / (msl * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-        })
-        del bstep
-        torch.cuda.empty_cache()
+    # ---------------- backward of the 7B-shaped layer
+    w = W.WORKLOADS["layer7b_bf16"]
+    bstep = backward_step(R, W, "layer7b_bf16", dev)
+    ms7 = time_events(bstep, 3, 1)
+    fl7 = (4 * chunk_alg_flops(w["B"], w["H"], w["N"], w["dv"] // 2, w["dk"], w["chunk"]) +
+           chunk_alg_flops(w["B"], w["H"], w["N"], w["dk"], w["dv"], w["chunk"]))
+    also.append({
+        "workload": "backward of the 7B-shaped layer (B=4 H=16 N=8192 d_k=256 d_v=512 bf16, chunk 128): "
+                    "passes 1 and 2 over the two halves of d_v, pass 3 at full width",
+        "ms": ms7, "tokens_per_s": w["B"] * w["N"] / (ms7 * 1e-3), "tflops": fl7 / (ms7 * 1e-3) / 1e12,
+        "mfma_frac": fl7 / (ms7 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+    })
+    del bstep
+    torch.cuda.empty_cache()
 
-        # ---------------- backward of the 7B-shaped layer
-        w = W.WORKLOADS["layer7b_bf16"]
-        bstep = backward_step(R, W, "layer7b_bf16", dev)
-        ms7 = time_events(bstep, 3, 1)
-        fl7 = (4 * chunk_alg_flops(w["B"], w["H"], w["N"], w["dv"] // 2, w["dk"], w["chunk"]) +
-               chunk_alg_flops(w["B"], w["H"], w["N"], w["dk"], w["dv"], w["chunk"]))
-        also.append({
-            "workload": "backward of the 7B-shaped layer (B=4 H=16 N=8192 d_k=256 d_v=512 bf16, chunk 128): "
-                        "passes 1 and 2 over the two halves of d_v, pass 3 at full width",
-            "ms": ms7, "tokens_per_s": w["B"] * w["N"] / (ms7 * 1e-3), "tflops": fl7 / (ms7 * 1e-3) / 1e12,
-            "mfma_frac": fl7 / (ms7 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, "forward_ms": ms3,
-        })
-        del bstep
-        torch.cuda.empty_cache()
+    # ---------------- output stage of the 7B-shaped layer
+    e = EPI_SHAPE
+    estep = epilogue_step(R, W, dev)
+    mse = time_events(estep, 10, 3)
+    fle = 2.0 * e["B"] * e["N"] * e["H"] * e["dv"] * e["d_out"]
+    also.append({
+        "workload": "output stage of the 7B-shaped layer: GroupNorm (16 heads of 512) + gate + W_O "
+                    "(8192 -> 4096) over 32768 tokens, bf16",
+        "ms": mse, "tokens_per_s": e["B"] * e["N"] / (mse * 1e-3), "tflops": fle / (mse * 1e-3) / 1e12,
+        "mfma_frac": fle / (mse * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, "alg_flops": fle,
+    })
+    del estep
+    torch.cuda.empty_cache()
 
-        # ---------------- output stage of the 7B-shaped layer
-        e = EPI_SHAPE
-        estep = epilogue_step(R, W, dev)
-        mse = time_events(estep, 10, 3)
-        fle = 2.0 * e["B"] * e["N"] * e["H"] * e["dv"] * e["d_out"]
-        also.append({
-            "workload": "output stage of the 7B-shaped layer: GroupNorm (16 heads of 512) + gate + W_O "
-                        "(8192 -> 4096) over 32768 tokens, bf16",
-            "ms": mse, "tokens_per_s": e["B"] * e["N"] / (mse * 1e-3), "tflops": fle / (mse * 1e-3) / 1e12,
-            "mfma_frac": fle / (mse * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, "alg_flops": fle,
-        })
-        del estep
-        torch.cuda.empty_cache()
+    # ---------------- decode step + output stage (one token per sequence through the layer's W_O)
+    w = W.WORKLOADS["decode_bf16"]
+    s0, qs, ks, vs = W.make_decode_workload(device=dev, steps=8)
+    _, w_o, gw, gb, gt = W.make_epilogue(w["B"], w["H"], 1, w["dv"], 4096, 8, device=dev)
+    gt = gt[:, 0, :].contiguous()
+    yd = torch.empty((w["B"], 4096), dtype=torch.bfloat16, device=dev)
+    od = torch.empty((w["B"], w["H"], w["dv"]), dtype=torch.bfloat16, device=dev)
+    itd = [0]
 
-        # ---------------- decode step + output stage (one token per sequence through the layer's W_O)
-        w = W.WORKLOADS["decode_bf16"]
-        s0, qs, ks, vs = W.make_decode_workload(device=dev, steps=8)
-        _, w_o, gw, gb, gt = W.make_epilogue(w["B"], w["H"], 1, w["dv"], 4096, 8, device=dev)
-        gt = gt[:, 0, :].contiguous()
-        yd = torch.empty((w["B"], 4096), dtype=torch.bfloat16, device=dev)
-        od = torch.empty((w["B"], w["H"], w["dv"]), dtype=torch.bfloat16, device=dev)
-        itd = [0]
+    def dstep():
+        t = itd[0] % 8
+        itd[0] += 1
+        R.retention_recurrent_step_msr(qs[t], ks[t], vs[t], s0, w_o, gate=gt, gn_weight=gw, gn_bias=gb, o=od,
+                                       out=yd)
 
-        def dstep():
-            t = itd[0] % 8
-            itd[0] += 1
-            R.retention_recurrent_step_msr(qs[t], ks[t], vs[t], s0, w_o, gate=gt, gn_weight=gw, gn_bias=gb, o=od,
-                                           out=yd)
+    msd, spd = time_graph(dstep, 100, 10)
+    itd[0] = 0
 
-        msd, spd = time_graph(dstep, 100, 10)
-        itd[0] = 0
+    def ostep():
+        R.retention_msr_epilogue(od.view(w["B"], w["H"], 1, w["dv"]), w_o, gn_weight=gw, gn_bias=gb,
+                                 gate=gt.view(w["B"], 1, -1), out=yd.view(w["B"], 1, 4096))
 
-        def ostep():
-            R.retention_msr_epilogue(od.view(w["B"], w["H"], 1, w["dv"]), w_o, gn_weight=gw, gn_bias=gb,
-                                     gate=gt.view(w["B"], 1, -1), out=yd.view(w["B"], 1, 4096))
+    mso, _ = time_graph(ostep, 100, 10)
+    wbytes = 4096 * w["H"] * w["dv"] * 2
+    also.append({
+        "workload": "decode step + output stage: 64 sequences x H=16 (state 256x512) -> GroupNorm, gate, "
+                    "W_O 8192 -> 4096, bf16",
+        "ms_per_token_step": msd, "spread": spd, "output_stage_ms": mso,
+        "output_stage_w_o_gbs": wbytes / (mso * 1e-3) / 1e9,
+    })
+    del s0, qs, ks, vs, w_o, gw, gb, gt, yd, od
+    torch.cuda.empty_cache()
 
-        mso, _ = time_graph(ostep, 100, 10)
-        wbytes = 4096 * w["H"] * w["dv"] * 2
-        also.append({
-            "workload": "decode step + output stage: 64 sequences x H=16 (state 256x512) -> GroupNorm, gate, "
-                        "W_O 8192 -> 4096, bf16",
-            "ms_per_token_step": msd, "spread": spd, "output_stage_ms": mso,
-            "output_stage_w_o_gbs": wbytes / (mso * 1e-3) / 1e9,
-        })
-        del s0, qs, ks, vs, w_o, gw, gb, gt, yd, od
-        torch.cuda.empty_cache()
-
-        # ---------------- single-head fp32
-        q, k, v, _ = W.make_workload("single_head_f32", device=dev)
-        ms1 = time_events(lambda: R.retention_chunkwise_fwd(q, k, v, chunk=64), 50, 5)
-        msp = time_events(lambda: R.retention_parallel_fwd(q, k, v), 50, 5)
-        also.append({"workload": "single-head fp32 B=1 H=1 N=256 d=64", "chunkwise_ms": ms1, "parallel_ms": msp})
-        result["also"] = also
-
-    print(json.dumps(result))
+    # ---------------- single-head fp32 (warm and cold caches)
+    name = "single_head_f32"
+    q, k, v, _ = W.make_workload(name, device=dev)
+    kw1 = dict(chunk=64)
+    ms1 = time_events(lambda: R.retention_chunkwise_fwd(q, k, v, **kw1), 50, 5)
+    msp = time_events(lambda: R.retention_parallel_fwd(q, k, v), 50, 5)
+    c1_warm, _ = time_kernel(R, q, k, v, kw1, 20)
+    c1_cold, _ = time_kernel(R, q, k, v, kw1, 10, evict=evict)
+    also.append({"key": name, "workload": "single-head fp32 B=1 H=1 N=256 d=64", "chunkwise_ms": ms1,
+                 "parallel_ms": msp, "main_kernel_ms_warm": c1_warm, "main_kernel_ms_cold": c1_cold})
+    del q, k, v, scratch
+    torch.cuda.empty_cache()
+    return also
 
 
 if __name__ == "__main__":

@@ -158,6 +158,39 @@ size_t retention_chunkwise_workspace_size(int B, int H, int N, int dk, int dv, r
                                           int chunk, int segments);
 
 /*
+ * The plan retention_chunkwise_fwd follows for these sizes (a diagnostic for
+ * callers and tests; the pages define no such call): the kernel's token tile,
+ * value-tile width and count, how each (batch, head) sequence is cut into
+ * segments and grouped for the state look-back, and the byte offsets of the
+ * workspace regions the segmented kernels index. "Chains" are the
+ * B * H * value_tiles independent (batch, head, value tile) sequences.
+ *   ticket counters  [0, flags_off): one 8-byte counter per chain, 128 bytes apart
+ *   segment flags    [flags_off, gflags_off): chain * segments + segment, 128 bytes apart
+ *   group flags      [gflags_off, agg_off): chain * groups + group, 128 bytes apart
+ *   segment states   [agg_off, gagg_off): bf16 path: chain * segments + segment,
+ *                    dk * dv_tile floats each; float32 path: [B, H, segments, dk, dv]
+ *   group states     [gagg_off, workspace_bytes): chain * groups + group, dk * dv_tile floats
+ * with groups = ceil(segments / group_len). A plan with segments == 1 uses no
+ * workspace (workspace_bytes == 0). Returns the status retention_chunkwise_fwd
+ * would return for these sizes (RET_OK, RET_ERR_SHAPE, RET_ERR_DTYPE or
+ * RET_ERR_UNSUPPORTED); `plan` (host memory, not NULL) is filled on RET_OK.
+ */
+typedef struct {
+    int tile;           /* tokens per kernel chunk tile (16, 32, 64 or 128) */
+    int dv_tile;        /* value columns per workgroup */
+    int value_tiles;    /* dv / dv_tile */
+    int segments;       /* segments per (batch, head) sequence */
+    int segment_len;    /* tokens per segment (a multiple of tile) */
+    int group_len;      /* segments per look-back group */
+    int segments_max;   /* segments the workspace holds per chain */
+    int reserved;
+    uint64_t flags_off, gflags_off, agg_off, gagg_off, workspace_bytes;
+} ret_chunk_plan_t;
+
+ret_status_t retention_chunkwise_plan(int B, int H, int N, int dk, int dv, ret_dtype_t dtype, int chunk,
+                                      int segments, ret_chunk_plan_t* plan);
+
+/*
  * Backward of retention_chunkwise_fwd (whose result is that of the parallel
  * form, which is how training evaluates retention: "RetNet Guide" section "1.
  * The Parallel Representation for High-Throughput Pretraining"; "Retentive

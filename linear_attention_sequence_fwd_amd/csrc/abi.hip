@@ -71,7 +71,7 @@ ret_status_t check_common(int B, int H, int N, int dk, int dv, ret_dtype_t dtype
 int bf16_dvt(int dk, int dv, int chunk) {
     if (dk != 64 && dk != 128 && dk != 256) return 0;
     if (dv % 64 != 0) return 0;
-    if (chunk == 64 && dk == 256) return 64;
+    if (chunk == 32 || (chunk == 64 && dk == 256)) return 64;
     return (dv % 128 == 0) ? 128 : 64;
 }
 
@@ -109,12 +109,14 @@ ret_status_t plan_chunk(int B, int H, int N, int dk, int dv, ret_dtype_t dtype, 
     // of 128, bf16) keep the 128-token tile inside the chunk and exchange the
     // state between chunks: one segment per chunk.
     const bool large = chunk > 128;
-    const bool small_ok = (chunk == 16 || chunk == 32) && dtype == RET_F32;  // the float32 kernel takes any chunk
     if (large ? (dtype != RET_BF16 || chunk % 128 != 0 || chunk > kMaxLargeChunk)
-              : (chunk != 64 && chunk != 128 && !small_ok))
+              : (chunk != 16 && chunk != 32 && chunk != 64 && chunk != 128))
         return RET_ERR_UNSUPPORTED;
     if (segments < 0) return RET_ERR_SHAPE;
-    p.tile = large ? 128 : chunk;
+    // bf16 chunks of 16 tokens run as 32-token tiles: the matrix-core contraction
+    // over tokens is 32 deep (the chunk length moves only the points where the
+    // state is carried, not the result); the float32 kernel takes any chunk
+    p.tile = large ? 128 : (chunk == 16 && dtype == RET_BF16 ? 32 : chunk);
     p.dvt = (dtype == RET_BF16) ? bf16_dvt(dk, dv, p.tile) : f32_chunk_dvt(dk, dv, p.tile);
     if (p.dvt == 0) return RET_ERR_UNSUPPORTED;
     p.nvt = dv / p.dvt;
@@ -189,6 +191,7 @@ void fill_chunk_args(ret::ChunkArgs& a, const void* q, const void* k, const void
     a.pos0 = pos0;
     a.rev = 0;
     a.orot = 0;
+    a.rescale = 1;
 }
 
 // Workspace of the backward: one forward-workspace region per pass first (each
@@ -277,6 +280,30 @@ size_t retention_chunkwise_workspace_size(int B, int H, int N, int dk, int dv, r
     ChunkPlan p;
     if (plan_chunk(B, H, N, dk, dv, dtype, chunk, segments, p) != RET_OK) return 0;
     return p.ws_bytes;
+}
+
+ret_status_t retention_chunkwise_plan(int B, int H, int N, int dk, int dv, ret_dtype_t dtype, int chunk,
+                                      int segments, ret_chunk_plan_t* out) {
+    if (!out) return RET_ERR_NULL;
+    ret_status_t s = check_common(B, H, N, dk, dv, dtype, nullptr);
+    if (s != RET_OK) return s;
+    ChunkPlan p;
+    s = plan_chunk(B, H, N, dk, dv, dtype, chunk, segments, p);
+    if (s != RET_OK) return s;
+    out->tile = p.tile;
+    out->dv_tile = p.dvt;
+    out->value_tiles = p.nvt;
+    out->segments = p.nseg;
+    out->segment_len = p.seg_len;
+    out->group_len = p.grp;
+    out->segments_max = p.nseg_max;
+    out->reserved = 0;
+    out->flags_off = p.flags_off;
+    out->gflags_off = p.gflags_off;
+    out->agg_off = p.agg_off;
+    out->gagg_off = p.gagg_off;
+    out->workspace_bytes = p.ws_bytes;
+    return RET_OK;
 }
 
 static ret_status_t chunkwise_impl(const void* q, const void* k, const void* v, void* o, int B, int H, int N,

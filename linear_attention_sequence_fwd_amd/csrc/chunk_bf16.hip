@@ -84,7 +84,7 @@ struct ChunkGeo {
     // thread, the value blocks go to the threads the key blocks leave free
     // (threads VOFF..), so staging work is spread over every wave.
     static constexpr int VOFF = (KB + VB <= NTHR) ? KB : 0;
-    static_assert(C == 64 || C == 128, "chunk");
+    static_assert(C == 32 || C == 64 || C == 128, "chunk");
     static_assert(DK % 64 == 0 && DVT % 64 == 0, "tile sizes");
     static_assert(MG * MT == TM && NG * NT == NTV, "state split");
 };
@@ -202,7 +202,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
         for (int u = 0; u < G::KPT; ++u) {
             const int idx = tid + u * G::NTHR;
             int tb, cb;
-            block_coords<DK, G::BWK>(idx < G::KB ? idx : 0, tb, cb);
+            block_coords<DK, G::BWK, C / 8>(idx < G::KB ? idx : 0, tb, cb);
 #pragma unroll
             for (int p = 0; p < G::BWK / 2; ++p) thk[u][p] = hp.theta[cb * (G::BWK / 2) + p];
         }
@@ -439,7 +439,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
             const int idx = tid_it + u * G::NTHR;
             if (idx < G::KB) {
                 int tb, cb;
-                block_coords<DK, G::BWK>(idx, tb, cb);
+                block_coords<DK, G::BWK, C / 8>(idx, tb, cb);
                 if (hp.has_theta) {  // rows past the end are zero: rotating them is harmless
 #pragma unroll
                     for (int q = 0; q < 8; ++q) rotate_key_row(krb[u].w[q], u, cb, t0, staged_token(tb, q));
@@ -465,7 +465,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
             const int idx = value_thread<G>(tid_it) + u * G::NTHR;
             if (idx < G::VB) {
                 int tb, cb;
-                block_coords<DVT, G::BWV>(idx, tb, cb);
+                block_coords<DVT, G::BWV, C / 8>(idx, tb, cb);
 #pragma unroll
                 for (int c = 0; c < G::BWV; ++c)
                     *reinterpret_cast<uint4*>(&vbuf[swz<UC>(cb * G::BWV + c, tb)]) = block_column(vrb[u], c);
@@ -528,7 +528,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
             const int idx = tid_it + u * G::NTHR;
             if (idx < G::KB) {
                 int tb, cb;
-                block_coords<DK, G::BWK>(idx, tb, cb);
+                block_coords<DK, G::BWK, C / 8>(idx, tb, cb);
                 if (hp.has_theta) {  // rows past the end are zero: rotating them is harmless
 #pragma unroll
                     for (int q = 0; q < 8; ++q) rotate_key_row(krb[u].w[q], u, cb, t0, staged_token(tb, q));
@@ -551,7 +551,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
             const int idx = value_thread<G>(tid_it) + u * G::NTHR;
             if (idx < G::VB) {
                 int tb, cb;
-                block_coords<DVT, G::BWV>(idx, tb, cb);
+                block_coords<DVT, G::BWV, C / 8>(idx, tb, cb);
                 float f[8];
 #pragma unroll
                 for (int q = 0; q < 8; ++q) f[q] = fast_exp2(-static_cast<float>(staged_token(tb, q) + 1) * lg2c);
@@ -710,7 +710,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
                 const int idx = tid_it + u * G::NTHR;
                 if (idx < G::KB) {
                     int tb, cb;
-                    block_coords<DK, G::BWK>(idx, tb, cb);
+                    block_coords<DK, G::BWK, C / 8>(idx, tb, cb);
 #pragma unroll
                     for (int q = 0; q < 8; ++q) {
                         const int row = staged_token(tb, q);
@@ -1082,12 +1082,14 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
         // group predecessors: entry i is segment seg-1-i with weight g^i
         const float fq = accumulate(sin, pos, [&](int i) { return slot(seg - 1 - i); }, 1.0f, gseg);
         if (pos == grp_sz - 1 && seg < a.nseg - 1) {  // close the group: A_q = T_s + g * (its predecessors)
+            // a failed wait publishes NaN, so every later segment and the final state see it
+            const float poison = failed ? NAN : 0.0f;
             unsigned long long* dst = gslot(q);
 #pragma unroll
             for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
                 for (int nt = 0; nt < G::NT; ++nt)
-                    store_coherent(dst + (mt * G::NT + nt) * 128, sacc[mt][nt] + gseg * sin[mt][nt]);
+                    store_coherent(dst + (mt * G::NT + nt) * 128, sacc[mt][nt] + gseg * sin[mt][nt] + poison);
             wait_stores();
             __syncthreads();
             if (tid == 0)
@@ -1120,6 +1122,15 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
         prefetch_first(true);
         if (seg == 0) {
             load_state(a.state_in);
+            if (a.state_in && a.state_out) {
+                // state_out may alias state_in: the last segment stores the final state only
+                // after this second read of it is done (its flag slot is otherwise unused)
+                wait_stores();
+                __syncthreads();
+                if (tid == 0)
+                    __hip_atomic_store(flags + static_cast<size_t>(a.nseg - 1) * kFlagStride, f_agg, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
         } else if (seg < a.nseg - 1) {  // T_s stays in sacc while the look-back may close a group
             f32x4 sin[G::MT][G::NT];
             look_back(sin);
@@ -1134,6 +1145,15 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
         have_state = seg > 0 || a.state_in != nullptr;
         if (have_state) write_state_copy(l16, grp);
         run_chunks(std::false_type{});
+        if (seg == a.nseg - 1 && a.state_in && a.state_out) {
+            __syncthreads();  // the look-back status slot overlays the state copy, written by every wave above
+            if (wait_published(flags, a.nseg - 1, a.nseg - 1, f_agg, f_agg)) {
+#pragma unroll
+                for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < G::NT; ++nt) sacc[mt][nt] = f32x4{NAN, NAN, NAN, NAN};
+            }
+        }
         write_final_state(sacc);
     } else if constexpr (MODE == kLocalPass) {
         // ---- every segment runs from a zero state, outputs held back
@@ -1298,6 +1318,14 @@ static hipError_t run_chunk_bf16(const ChunkArgs& a, const HeadParams& hp, hipSt
     record_empty_phase(st, ev);
     record_empty_phase(st, ev ? ev + 2 : nullptr);
     hipEvent_t* e = ev ? ev + 4 : nullptr;
+    if (chunk_wide_supported(DK, DVT, C, a.nseg, hp.has_theta != 0)) {
+        const int R = chunk_wide_rescale(hp, a.H);
+        if (R > 0) {
+            ChunkArgs aw = a;
+            aw.rescale = R;
+            return launch_chunk_wide(aw, hp, st, e);
+        }
+    }
     if (fast_form_ok(hp, a.H, C))
         launch_chunk_form<DK, DVT, C, true>(a, hp, st, e);
     else
@@ -1315,6 +1343,9 @@ static hipError_t run_chunk_bf16_multi(const ChunkCalls& cs, const HeadParams& h
 }
 
 #define RET_CHUNK_SHAPES \
+    RET_CASE(64, 64, 32)   \
+    RET_CASE(128, 64, 32)  \
+    RET_CASE(256, 64, 32)  \
     RET_CASE(64, 64, 64)   \
     RET_CASE(64, 128, 64)  \
     RET_CASE(128, 64, 64)  \

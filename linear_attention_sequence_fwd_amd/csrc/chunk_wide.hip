@@ -1,0 +1,564 @@
+// Chunkwise retention forward for wide heads (d_k of 128 or 256, value tiles of
+// 128 columns, 128-token chunks) on gfx950 (MI355X) matrix cores: bf16 inputs,
+// float32 accumulation and state, no rotation.
+//
+// "RetNet Guide: Retentive Networks & The Impossible Triangle", section "3. The
+// Chunkwise Recurrent Representation": inside a chunk of L tokens
+//     O = ((Q K^T) (.) D) V + zeta (.) (Q S),     zeta_i = gamma^(i+1)
+//     S <- gamma^L S + K^T (xi (.) V),            xi_j   = gamma^(L-1-j)
+// (xi is the in-chunk key decay that the page's printed carry leaves out).
+//
+// Rescaled form over decay groups. Chunks are taken in groups of R (R C
+// tokens); tau counts tokens from the start of the group. With
+//     V3 = gamma^-(tau+1) V    (each value row scaled once, at staging)
+// and A = gamma^-e S, where e is the number of group tokens already folded in,
+// every decay factor moves out of the contractions:
+//     O   = gamma^(tau_i + 1) (Q A + mask(Q K^T) V3)     (row i at group offset tau_i)
+//     A  <- A + K^T V3
+// and only at the end of a group is A scaled back to S (A <- gamma^e A), so the
+// float32 state is touched by the vector ALU once per R chunks. The host picks
+// the largest R in {8, 4, 2, 1} with gamma^(R C) >= 2^-64 for every head,
+// which keeps every factor far inside the float32 range.
+//
+// One workgroup of four waves (one per SIMD, each with the SIMD's whole
+// register file) owns one (batch, head, value tile) and walks its chunks in
+// order. Wave w owns query blocks w and 7-w (16 tokens each), so every wave
+// carries the same causal work, and every state fragment read from LDS feeds
+// two matrix instructions (one per block). The float32 state is split over the
+// waves by d_k rows: wave w holds rows [w d_k/4, (w+1) d_k/4) of all 128
+// columns in MFMA accumulators. Per chunk, on v_mfma_f32_16x16x32_bf16:
+//   G3  O^T  = A^T Q^T                    (bf16 copy of A^T in LDS)
+//   G1  P^T  = K Q^T, causal select on the diagonal tiles
+//   G2  O^T += V3^T P^T                   (V3^T by transposing LDS reads)
+//   G4  A   += K^T V3                     (K^T by transposing LDS reads)
+//
+// LDS (bf16, 16-byte units XOR-swizzled by row against bank conflicts): two
+// key-sized buffers that trade roles every chunk (this chunk's keys; the state
+// copy, which G3 reads first, after which the next chunk's keys are loaded
+// into it straight from HBM), and V3 of the chunk. Values come through
+// registers one chunk ahead (they are scaled on the way in); queries go from
+// HBM straight into MFMA operand registers. Buffer loads make rows past the
+// end of the sequence read as zero, and output stores past it are dropped.
+
+#include "common.hpp"
+#include "kernels.hpp"
+#include "tiles.hpp"
+
+#include <cmath>
+#include <type_traits>
+
+namespace ret {
+
+namespace {
+
+constexpr int kWideC = 128;            // tokens per chunk
+constexpr int kWideDvt = 128;          // value columns per workgroup
+constexpr int kWideThreads = 256;      // four waves
+constexpr int kBufFlags = 0x00020000;  // buffer resource word 3 for gfx9-family raw buffers
+constexpr int kPipeDepth = 4;          // steps between an LDS read and its use
+
+template <int DK>
+struct WideGeo {
+    static constexpr int UK = DK / 8;                      // 16-byte units per key row
+    static constexpr int UV = kWideDvt / 8;                // 16-byte units per value row (of the tile)
+    static constexpr int KSQ = DK / 32;                    // 32-wide contraction steps over d_k
+    static constexpr int NTV = kWideDvt / 16;              // 16-column tiles of the value tile
+    static constexpr int MT = DK / 64;                     // 16-row state tiles per wave
+    static constexpr int VU = kWideC * UV / kWideThreads;  // value units per thread
+    static constexpr int VROWS = kWideThreads / UV;        // value rows per load step
+    static constexpr int KBLK = kWideC * DK * 2 / 1024 / 4;  // 1 KiB key blocks per wave
+    static_assert(DK == 128 || DK == 256, "key width");
+};
+
+template <int V>
+using Ic = std::integral_constant<int, V>;
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufFlags);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ void buf_store8(uint2 v, __amdgpu_buffer_rsrc_t r, int off) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, v), r,
+                                          off, 0, 0);
+}
+
+// Eight bf16 (one 16-byte unit) times f, rounded back to bf16.
+__device__ __forceinline__ uint4 scale8_bf16(uint4 x, float f) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) o[p] = pack2_bf16(lo_bf16(w[p]) * f, hi_bf16(w[p]) * f);
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// s_waitcnt with at most VM vector memory operations and no LDS operation
+// outstanding (gfx9 fields: vmcnt in bits 3:0 and 15:14, expcnt 6:4 left at
+// its maximum, lgkmcnt 11:8).
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));
+}
+
+// s_waitcnt lgkmcnt(0), vector memory operations left outstanding.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(Ic<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// A software pipeline over NS steps of LDS reads feeding matrix instructions:
+// the fragments of step j are read during step j - D, and a scheduling
+// barrier closes every step, so each read is issued D steps ahead of its use
+// whatever the register pressure (with one wave per SIMD nothing else hides
+// the LDS latency). read(Ic<j>) returns step j's fragments, use(Ic<j>, frags)
+// issues its matrix instructions, side(Ic<j>) any other work placed in step j
+// (global loads and stores spread over the matrix work, so that they never
+// queue up behind one another and stall the wave).
+template <int NS, int D, typename Read, typename Use, typename Side>
+__device__ __forceinline__ void pipelined(Read&& read, Use&& use, Side&& side) {
+    using Frag = decltype(read(Ic<0>{}));
+    Frag fr[D];
+    static_for<0, (D < NS ? D : NS)>([&](auto i) { fr[decltype(i)::value] = read(i); });
+    static_for<0, NS>([&](auto i) {
+        constexpr int j = decltype(i)::value;
+        const Frag cur = fr[j % D];
+        if constexpr (j + D < NS) fr[j % D] = read(Ic<j + D>{});
+        side(i);
+        use(i, cur);
+        __builtin_amdgcn_sched_barrier(0);
+    });
+}
+
+// Calls f(Ic<i>) for the items i of M that fall on step J of NS when the M
+// items are spread evenly over the steps.
+template <int M, int NS, int J, typename F>
+__device__ __forceinline__ void spread(F&& f) {
+    static_for<0, M>([&](auto i) {
+        if constexpr (decltype(i)::value * NS / M == J) f(i);
+    });
+}
+
+}  // namespace
+
+template <int DK>
+__global__ __attribute__((amdgpu_flat_work_group_size(kWideThreads, kWideThreads), amdgpu_waves_per_eu(1, 1)))
+void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
+    using G = WideGeo<DK>;
+    constexpr int C = kWideC;
+    constexpr int UK = G::UK;
+    // separate objects, so the compiler can tell reads of one from the loads into the other
+    __shared__ __attribute__((aligned(16))) u16 pb0[C * DK];
+    __shared__ __attribute__((aligned(16))) u16 pb1[C * DK];
+    __shared__ __attribute__((aligned(16))) u16 vbuf[C * kWideDvt];
+
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    // Per-lane indices. Inside the chunk loop they are refreshed from an opaque
+    // copy of the thread index every chunk, so per-lane addresses and factors
+    // are recomputed there (a few ALU operations under the matrix work) rather
+    // than hoisted out of the loop and held in registers for its whole length.
+    int tid = threadIdx.x;
+    int lane = tid & 63;
+    int l16 = lane & 15;
+    int grp = lane >> 4;
+    auto refresh_lane = [&]() __attribute__((always_inline)) {
+        int t = threadIdx.x;
+        asm volatile("" : "+v"(t));
+        tid = t;
+        lane = t & 63;
+        l16 = t & 15;
+        grp = (t & 63) >> 4;
+    };
+
+    // (batch, head, value tile); the value tiles of one head run on one XCD
+    const int chain = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int vt = chain % a.nvt;
+    const int bh = chain / a.nvt;
+    const int h = bh % a.H;
+    const float gam = hp.gamma[h];
+    const double lg2 = log2_gamma(gam);
+    const float lg2f = static_cast<float>(lg2);
+    const int N = a.N;
+    const int nch = (N + C - 1) / C;
+    const int R = a.rescale;
+    const float g_group = gamma_pow(lg2, static_cast<double>(R) * C);  // gamma^(R C)
+
+    const size_t tok0 = static_cast<size_t>(bh) * N;
+    const char* Kg = reinterpret_cast<const char*>(a.k + tok0 * DK);
+    const char* Qg = reinterpret_cast<const char*>(a.q + tok0 * DK);
+    const char* Vg = reinterpret_cast<const char*>(a.v + tok0 * a.dv + vt * kWideDvt);
+    char* Og = reinterpret_cast<char*>(a.o + tok0 * a.dv + vt * kWideDvt);
+    const int ldv = a.dv * 2;    // value / output row stride, bytes
+    constexpr int ldk = DK * 2;  // key / query row stride, bytes
+    constexpr int tile_bytes = kWideDvt * 2;
+    const int d0 = wave * (DK / 4);  // this wave's state rows
+
+    uint4 vst[G::VU];           // the next chunk's values (scaled to V3 in registers before staging)
+    uint4 qf[2][G::KSQ];        // queries of blocks wave and 7-wave: row 16 blk + l16, d_k 32 s + 8 grp
+    f32x4 sacc[G::MT][G::NTV];  // A: rows d0 + 16 mt + 4 grp + r, columns 16 nt + l16
+    f32x4 oacc[2][G::NTV];      // O^T: [block][column tile]
+    uint4 pf[2][4];             // P^T as bf16 B operands: [block][32-key step]
+
+    // Buffer resources of a chunk (t: first token, L valid rows): loads past
+    // the last valid row read as zero, stores past it are dropped.
+    auto key_rsrc = [&](int t, int L) __attribute__((always_inline)) {
+        return make_rsrc(Kg + static_cast<size_t>(t) * ldk, L * ldk);
+    };
+    auto q_rsrc = [&](int t, int L) __attribute__((always_inline)) {
+        return make_rsrc(Qg + static_cast<size_t>(t) * ldk, L * ldk);
+    };
+    auto value_rsrc = [&](int t, int L) __attribute__((always_inline)) {
+        return make_rsrc(Vg + static_cast<size_t>(t) * ldv, L > 0 ? (L - 1) * ldv + tile_bytes : 0);
+    };
+    auto out_rsrc = [&](int t, int L) __attribute__((always_inline)) {
+        return make_rsrc(Og + static_cast<size_t>(t) * ldv, (L - 1) * ldv + tile_bytes);
+    };
+    // Key block i (1 KiB) of this wave's share, straight into LDS: each wave
+    // instruction fills 1 KiB of consecutive LDS (lane l the 16-byte unit at
+    // 16 l), so each lane fetches the unit the swizzled layout puts there.
+    auto load_key_block = [&](__amdgpu_buffer_rsrc_t rk, u16* dst, int i) __attribute__((always_inline)) {
+        const int blk = wave * G::KBLK + i;
+        const int e = blk * 512 + lane * 8;  // element offset of this lane's unit
+        const int row = e / DK;
+        const int unit = ((e % DK) >> 3) ^ (row & 15);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_ptr)(dst + blk * 512), 16, row * ldk + unit * 16, 0,
+                                                 0, 0);
+    };
+    auto load_value_unit = [&](__amdgpu_buffer_rsrc_t rv, int j) __attribute__((always_inline)) {
+        vst[j] = buf_load16(rv, (tid / G::UV + j * G::VROWS) * ldv + (tid % G::UV) * 16);
+    };
+    // query unit q = b * KSQ + s
+    auto load_q_unit = [&](__amdgpu_buffer_rsrc_t rq, int q) __attribute__((always_inline)) {
+        const int b = q / G::KSQ, s = q % G::KSQ;
+        const int blk = b ? 7 - wave : wave;
+        qf[b][s] = buf_load16(rq, (16 * blk + l16) * ldk + grp * 16 + s * 64);
+    };
+    // value unit j to V3 (tau0: group offset of the chunk's first token)
+    auto scale_value_unit = [&](int j, int tau0) __attribute__((always_inline)) {
+        const int row = tid / G::UV + j * G::VROWS;
+        vst[j] = scale8_bf16(vst[j], fast_exp2(-static_cast<float>(tau0 + row + 1) * lg2f));
+    };
+    auto write_values = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < G::VU; ++j)
+            *reinterpret_cast<uint4*>(&vbuf[swz<G::UV>(tid / G::UV + j * G::VROWS, tid % G::UV)]) = vst[j];
+    };
+    // bf16 copy of the state (A^T, row = value column) for G3
+    auto write_state_copy = [&](u16* dst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < G::NTV; ++nt) {
+                const int d = d0 + mt * 16 + grp * 4;
+                const int c = nt * 16 + l16;
+                const uint2 w = make_uint2(pack2_bf16(sacc[mt][nt][0], sacc[mt][nt][1]),
+                                           pack2_bf16(sacc[mt][nt][2], sacc[mt][nt][3]));
+                *reinterpret_cast<uint2*>(&dst[swz<UK>(c, d >> 3) + (d & 7)]) = w;
+            }
+    };
+    // Transposing-read fragment (8 tokens of 32-token step t, rows 4 grp + {0..3, 16..19})
+    // of 16 consecutive columns from a row-major tile: lane (l16, grp) points at
+    // token 4 grp + l16/4 (+16), columns col0 + 4 (l16 % 4) .. +3.
+    auto tr_frag = [&](const u16* buf, auto width_tag, int col0, int t) __attribute__((always_inline)) {
+        constexpr int W = decltype(width_tag)::value;  // row width in elements
+        const int tok = 4 * grp + (l16 >> 2);
+        const int c = col0 + 4 * (l16 & 3);
+        const int base = swz<W / 8>(tok, c >> 3) + (c & 7);
+        const uint2 lo = lds_read_tr16x4(&buf[base + (32 * t) * W]);
+        const uint2 hi = lds_read_tr16x4(&buf[base + (32 * t + 16) * W]);
+        return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    };
+
+    // G1 and G2 for the wave owning blocks W and 7-W. The next chunk's keys go
+    // into LDS during G1.
+    auto g12 = [&](const u16* __restrict__ kb, u16* __restrict__ next_kb, __amdgpu_buffer_rsrc_t rk, auto wtag)
+                   __attribute__((always_inline)) {
+        constexpr int B0 = decltype(wtag)::value, B1 = 7 - B0;
+        constexpr int T0 = B0 / 2 + 1, T1 = B1 / 2 + 1;
+        const FragAddr<UK> fk(l16, grp);  // K rows 16 kt + l16, d_k 32 s + 8 grp
+        // G1, step j: 32-key step t = j / KSQ (key tiles 2t, 2t+1), d_k step s = j % KSQ
+        struct KF {
+            uint4 a, b;
+        };
+        f32x4 p[4];  // tile 2t of block 7-W, tile 2t+1 of it, tile 2t of block W, tile 2t+1 of it
+        constexpr int NS1 = T1 * G::KSQ;
+        pipelined<NS1, kPipeDepth>(
+            [&](auto j) __attribute__((always_inline)) {
+                constexpr int t = decltype(j)::value / G::KSQ, s = decltype(j)::value % G::KSQ;
+                KF f;
+                f.a = *reinterpret_cast<const uint4*>(&kb[fk.at(2 * t, s)]);
+                if constexpr (2 * t + 1 <= B1) f.b = *reinterpret_cast<const uint4*>(&kb[fk.at(2 * t + 1, s)]);
+                return f;
+            },
+            [&](auto j, const KF& f) __attribute__((always_inline)) {
+                constexpr int t = decltype(j)::value / G::KSQ, s = decltype(j)::value % G::KSQ;
+                constexpr bool two1 = 2 * t + 1 <= B1, one0 = t < T0, two0 = 2 * t + 1 <= B0;
+                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                p[0] = mfma16x16x32(f.a, qf[1][s], s == 0 ? zero : p[0]);
+                if constexpr (two1) p[1] = mfma16x16x32(f.b, qf[1][s], s == 0 ? zero : p[1]);
+                if constexpr (one0) p[2] = mfma16x16x32(f.a, qf[0][s], s == 0 ? zero : p[2]);
+                if constexpr (two0) p[3] = mfma16x16x32(f.b, qf[0][s], s == 0 ? zero : p[3]);
+                if constexpr (s == G::KSQ - 1) {
+                    f32x4 r[4] = {p[0], two1 ? p[1] : zero, p[2], two0 ? p[3] : zero};
+                    // causal select on diagonal tiles: key 16 kt + 4 grp + q vs token 16 blk + l16
+                    auto mask = [&](f32x4& x, bool diag) __attribute__((always_inline)) {
+                        if (diag) {
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) x[q] = (4 * grp + q <= l16) ? x[q] : 0.0f;
+                        }
+                    };
+                    mask(r[0], 2 * t == B1);
+                    mask(r[1], 2 * t + 1 == B1);
+                    pf[1][t] = make_uint4(pack2_bf16(r[0][0], r[0][1]), pack2_bf16(r[0][2], r[0][3]),
+                                          pack2_bf16(r[1][0], r[1][1]), pack2_bf16(r[1][2], r[1][3]));
+                    if constexpr (one0) {
+                        mask(r[2], 2 * t == B0);
+                        mask(r[3], 2 * t + 1 == B0);
+                        pf[0][t] = make_uint4(pack2_bf16(r[2][0], r[2][1]), pack2_bf16(r[2][2], r[2][3]),
+                                              pack2_bf16(r[3][0], r[3][1]), pack2_bf16(r[3][2], r[3][3]));
+                    }
+                }
+            },
+            [&](auto j) __attribute__((always_inline)) {
+                spread<G::KBLK, NS1, decltype(j)::value>([&](auto i) { load_key_block(rk, next_kb, i); });
+            });
+        // G2, step j: 32-key step t = j / NTV, column tile nt = j % NTV
+        constexpr int NS2 = T1 * G::NTV;
+        pipelined<NS2, kPipeDepth>(
+            [&](auto j) __attribute__((always_inline)) {
+                constexpr int t = decltype(j)::value / G::NTV, nt = decltype(j)::value % G::NTV;
+                return tr_frag(vbuf, Ic<kWideDvt>{}, 16 * nt, t);
+            },
+            [&](auto j, const uint4& vf) __attribute__((always_inline)) {
+                constexpr int t = decltype(j)::value / G::NTV, nt = decltype(j)::value % G::NTV;
+                oacc[1][nt] = mfma16x16x32(vf, pf[1][t], oacc[1][nt]);
+                if constexpr (t < T0) oacc[0][nt] = mfma16x16x32(vf, pf[0][t], oacc[0][nt]);
+            },
+            [](auto) {});
+    };
+    // G4: A += K^T V3 on this wave's state tiles. Step j: 32-key step t =
+    // j / NTV, column tile nt = j % NTV; the first step of each t also brings
+    // that step's key fragments. Riding along: the chunk's outputs (scaled by
+    // z, rounded and stored), the next chunk's query loads and the scaling of
+    // its values (tau_next: their group offset).
+    auto g4 = [&](const u16* kb, __amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rq, const float (&z)[2],
+                  int tau_next) __attribute__((always_inline)) {
+        struct F4 {
+            uint4 v;
+            uint4 k[G::MT];
+        };
+        uint4 kt[G::MT];
+        constexpr int NS4 = 4 * G::NTV;
+        pipelined<NS4, kPipeDepth>(
+            [&](auto j) __attribute__((always_inline)) {
+                constexpr int t = decltype(j)::value / G::NTV, nt = decltype(j)::value % G::NTV;
+                F4 f;
+                f.v = tr_frag(vbuf, Ic<kWideDvt>{}, 16 * nt, t);
+                if constexpr (nt == 0) {
+#pragma unroll
+                    for (int mt = 0; mt < G::MT; ++mt) f.k[mt] = tr_frag(kb, Ic<DK>{}, d0 + 16 * mt, t);
+                }
+                return f;
+            },
+            [&](auto j, const F4& f) __attribute__((always_inline)) {
+                constexpr int nt = decltype(j)::value % G::NTV;
+                if constexpr (nt == 0) {
+#pragma unroll
+                    for (int mt = 0; mt < G::MT; ++mt) kt[mt] = f.k[mt];
+                }
+#pragma unroll
+                for (int mt = 0; mt < G::MT; ++mt) sacc[mt][nt] = mfma16x16x32(kt[mt], f.v, sacc[mt][nt]);
+            },
+            [&](auto j) __attribute__((always_inline)) {
+                constexpr int J = decltype(j)::value;
+                spread<2 * G::NTV, NS4, J>([&](auto i) {
+                    constexpr int b = decltype(i)::value / G::NTV, nt = decltype(i)::value % G::NTV;
+                    const int blk = b ? 7 - wave : wave;
+                    const f32x4 o = oacc[b][nt];
+                    const uint2 w = make_uint2(pack2_bf16(o[0] * z[b], o[1] * z[b]), pack2_bf16(o[2] * z[b], o[3] * z[b]));
+                    buf_store8(w, ro, (16 * blk + l16) * ldv + grp * 8 + nt * 32);
+                });
+                spread<2 * G::KSQ, NS4, J>([&](auto i) { load_q_unit(rq, i); });
+                spread<G::VU, NS4, J>([&](auto i) { scale_value_unit(decltype(i)::value, tau_next); });
+            });
+    };
+
+    // ---- start: the first chunk's values, keys and queries; the initial state
+    {
+        const int L0 = min(C, N);
+        const __amdgpu_buffer_rsrc_t rv = value_rsrc(0, L0), rk = key_rsrc(0, L0), rq = q_rsrc(0, L0);
+#pragma unroll
+        for (int j = 0; j < G::VU; ++j) load_value_unit(rv, j);
+#pragma unroll
+        for (int i = 0; i < G::KBLK; ++i) load_key_block(rk, pb0, i);
+#pragma unroll
+        for (int i = 0; i < 2 * G::KSQ; ++i) load_q_unit(rq, i);
+        // the per-chunk wait before barrier A counts the operations issued after
+        // a chunk's key loads in the loop; the first chunk's are waited for here
+        wait_vm_lgkm0<0>();
+#pragma unroll
+        for (int j = 0; j < G::VU; ++j) scale_value_unit(j, 0);
+    }
+    bool have_state = a.state_in != nullptr;
+    if (have_state) {
+        const float* s_in = a.state_in + static_cast<size_t>(bh) * DK * a.dv;
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < G::NTV; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int d = d0 + mt * 16 + grp * 4 + r;
+                    const int c = vt * kWideDvt + nt * 16 + l16;
+                    sacc[mt][nt][r] = s_in[static_cast<size_t>(d) * a.dv + c];
+                }
+        write_state_copy(pb1);  // read after barrier A
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < G::NTV; ++nt) sacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    int tau0 = 0;  // group offset of the current chunk's first token
+    // One chunk: its keys in kb (loaded during the previous chunk), the state
+    // copy in sb, its values scaled in vst.
+    auto chunk = [&](int ch, u16* __restrict__ kb, u16* __restrict__ sb) __attribute__((always_inline)) {
+        const int t0 = ch * C;
+        const int L = min(C, N - t0);
+        const bool has_next = ch + 1 < nch;
+        const int t1 = has_next ? t0 + C : t0;  // past the end: a discarded re-read
+        const int L1 = has_next ? min(C, N - t1) : L;
+        refresh_lane();
+
+        write_values();
+        // A: this chunk's keys have landed (issued after them, in program order:
+        // the previous chunk's output stores and the queries, both during its G4;
+        // every chunk issues the same operations, past the end as re-reads);
+        // V3 and the state copy are written
+        wait_vm_lgkm0<2 * G::KSQ + 2 * G::NTV>();
+        __builtin_amdgcn_s_barrier();
+
+        // ---- G3: O^T = A^T Q^T (the state before this chunk); the next chunk's values load meanwhile
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int nt = 0; nt < G::NTV; ++nt) oacc[b][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const __amdgpu_buffer_rsrc_t rv = value_rsrc(t1, L1);
+        if (have_state) {
+            const FragAddr<UK> fs(l16, grp);  // A^T rows 16 nt + l16, d_k 32 s + 8 grp
+            // step j: d_k step s = j / NTV, column tile nt = j % NTV
+            constexpr int NS3 = G::KSQ * G::NTV;
+            pipelined<NS3, kPipeDepth>(
+                [&](auto j) __attribute__((always_inline)) {
+                    constexpr int s = decltype(j)::value / G::NTV, nt = decltype(j)::value % G::NTV;
+                    return *reinterpret_cast<const uint4*>(&sb[fs.at(nt, s)]);
+                },
+                [&](auto j, const uint4& af) __attribute__((always_inline)) {
+                    constexpr int s = decltype(j)::value / G::NTV, nt = decltype(j)::value % G::NTV;
+                    oacc[0][nt] = mfma16x16x32(af, qf[0][s], oacc[0][nt]);
+                    oacc[1][nt] = mfma16x16x32(af, qf[1][s], oacc[1][nt]);
+                },
+                [&](auto j) __attribute__((always_inline)) {
+                    spread<G::VU, NS3, decltype(j)::value>([&](auto i) { load_value_unit(rv, i); });
+                });
+        } else {
+#pragma unroll
+            for (int j = 0; j < G::VU; ++j) load_value_unit(rv, j);
+        }
+        // every wave has read the state copy: the next chunk's keys go there
+        wait_lgkm0();
+        __builtin_amdgcn_s_barrier();
+
+        // ---- G1, G2 (the wave's blocks decide the causal extent)
+        const __amdgpu_buffer_rsrc_t rk = key_rsrc(t1, L1);
+        switch (wave) {
+            case 0: g12(kb, sb, rk, Ic<0>{}); break;
+            case 1: g12(kb, sb, rk, Ic<1>{}); break;
+            case 2: g12(kb, sb, rk, Ic<2>{}); break;
+            default: g12(kb, sb, rk, Ic<3>{}); break;
+        }
+
+        // ---- G4, with the outputs O = gamma^(tau + 1) O^T stored as bf16 meanwhile
+        float z[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+            z[b] = fast_exp2(static_cast<float>(tau0 + 16 * (b ? 7 - wave : wave) + l16 + 1) * lg2f);
+        tau0 += L;
+        const bool group_end = tau0 >= R * C || !has_next;
+        g4(kb, out_rsrc(t0, L), q_rsrc(t1, L1), z, group_end ? 0 : tau0);
+
+        // ---- end of a decay group (or of the sequence): A back to S
+        if (group_end) {
+            // (no float64 in the loop: its exp2 constants would be held in registers)
+            const float ge = tau0 == R * C ? g_group : fast_exp2(static_cast<float>(tau0) * lg2f);
+#pragma unroll
+            for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < G::NTV; ++nt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sacc[mt][nt][r] *= ge;
+            tau0 = 0;
+        }
+        // B: every read of the keys and V3 done
+        wait_lgkm0();
+        __builtin_amdgcn_s_barrier();
+        write_state_copy(kb);
+        have_state = true;
+    };
+    for (int ch = 0; ch < nch; ch += 2) {
+        chunk(ch, pb0, pb1);
+        if (ch + 1 < nch) chunk(ch + 1, pb1, pb0);
+    }
+    // the last chunk's discarded re-reads (into LDS among them) end before the workgroup does
+    wait_vm_lgkm0<0>();
+
+    if (a.state_out) {
+        float* s_dst = a.state_out + static_cast<size_t>(bh) * DK * a.dv;
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < G::NTV; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int d = d0 + mt * 16 + grp * 4 + r;
+                    const int c = vt * kWideDvt + nt * 16 + l16;
+                    s_dst[static_cast<size_t>(d) * a.dv + c] = sacc[mt][nt][r];
+                }
+    }
+}
+
+// Chunks per decay group: the largest R in {8, 4, 2, 1} with gamma^(R C) >=
+// 2^-64 for every head (0: the rescaled form does not fit these gammas).
+int chunk_wide_rescale(const HeadParams& hp, int H) {
+    double worst = 0.0;
+    for (int h = 0; h < H; ++h) worst = std::fmin(worst, std::log2(static_cast<double>(hp.gamma[h])));
+    for (int R = 8; R >= 1; R /= 2)
+        if (worst * R * kWideC >= -64.0) return R;
+    return 0;
+}
+
+bool chunk_wide_supported(int dk, int dvt, int chunk, int nseg, bool rotation) {
+    return !rotation && nseg == 1 && dvt == kWideDvt && chunk == kWideC && (dk == 128 || dk == 256);
+}
+
+hipError_t launch_chunk_wide(const ChunkArgs& a, const HeadParams& hp, hipStream_t st, hipEvent_t* ev) {
+    const dim3 grid(a.B * a.H * a.nvt), block(kWideThreads);
+    if (a.dk == 256)
+        launch_timed(chunk_wide_kernel<256>, grid, block, 0, st, ev, a, hp);
+    else
+        launch_timed(chunk_wide_kernel<128>, grid, block, 0, st, ev, a, hp);
+    return hipGetLastError();
+}
+
+}  // namespace ret

@@ -35,6 +35,7 @@ struct ChunkArgs {
     int rev;      // rows in reverse token order (chunk_bf16_multi_kernel only; no rotation then)
     int orot;     // rotate each output row by minus theta at its token's position before rounding
                   // (chunk_bf16_multi_kernel only, where chunk_orot_fits; output columns are the pairs)
+    int rescale;  // chunks per decay group of chunk_wide_kernel (set by launch_chunk_bf16)
 };
 
 // Ticket counters of the segmented bf16 chunk kernel: one per chain, each on a
@@ -160,6 +161,11 @@ hipError_t launch_states(const StateJobs& sj, const HeadParams& hp, hipStream_t 
 // (hipExtLaunchKernelGGL); a phase that does not run records its pair back to
 // back.
 hipError_t launch_chunk_bf16(const ChunkArgs& a, const HeadParams& hp, int dvt, hipStream_t st, hipEvent_t* ev);
+// The wide-head kernel (chunk_wide.hip): single pass, d_k 128 or 256, value
+// tiles of 128 columns, 128-token chunks, no rotation, gammas with gamma^128 >= 2^-64.
+bool chunk_wide_supported(int dk, int dvt, int chunk, int nseg, bool rotation);
+int chunk_wide_rescale(const HeadParams& hp, int H);
+hipError_t launch_chunk_wide(const ChunkArgs& a, const HeadParams& hp, hipStream_t st, hipEvent_t* ev);
 hipError_t launch_chunk_bf16_multi(const ChunkCalls& cs, const HeadParams& hp, int dvt, hipStream_t st);
 hipError_t launch_chunk_f32(const ChunkArgs& a, const HeadParams& hp, int dvt, hipStream_t st, hipEvent_t* ev);
 hipError_t launch_parallel_bf16(const ParallelArgs& a, const HeadParams& hp, int dvt, hipStream_t st);

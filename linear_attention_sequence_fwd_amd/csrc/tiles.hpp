@@ -55,11 +55,14 @@ __device__ __forceinline__ uint32_t elem16(const uint32_t (&x)[NW32], int e) {
 // column blocks (each row it touches as BW*2 contiguous bytes per lane), and
 // the transposed LDS writes of the 8 lanes that share a column block land in
 // different units of the same row.
-template <int D, int BW>
+// TB is the number of token blocks (tokens / 8) of the tile: consecutive
+// indices walk min(8, TB) of them (a 32-token chunk has only four).
+template <int D, int BW, int TB = 8>
 __device__ __forceinline__ void block_coords(int idx, int& tb, int& cb) {
-    const int rest = idx >> 3;
+    constexpr int S = TB < 8 ? TB : 8;
+    const int rest = idx / S;
     cb = rest % (D / BW);
-    tb = (idx & 7) + 8 * (rest / (D / BW));
+    tb = (idx % S) + S * (rest / (D / BW));
 }
 
 // Token order inside staged 32-token groups. Staging block tb covers tokens
@@ -96,7 +99,7 @@ __device__ __forceinline__ void load_blocks(BlockRows<BW> (&r)[PT], const u16* b
         const int idx = tid + u * NTHR;
         const bool in_blk = NBLK % NTHR == 0 || idx < NBLK;
         int tb, cb;
-        block_coords<D, BW>(in_blk ? idx : 0, tb, cb);
+        block_coords<D, BW, NBLK / (D / BW)>(in_blk ? idx : 0, tb, cb);
         const int tok0 = staged_token(tb, 0);
 #pragma unroll
         for (int q = Q0; q < Q1; ++q) {

@@ -118,8 +118,8 @@ def test_gamma_and_theta_validation(lib):
 
 
 def test_unsupported_sets(lib):
-    assert chunk(lib, chunk=16) == UNSUP  # bf16 tiles are 64 or 128 tokens (the float32 kernel takes 16 and 32)
-    assert chunk(lib, chunk=32) == UNSUP
+    assert chunk(lib, chunk=48) == UNSUP  # chunks: 16, 32, 64, 128 and (bf16) multiples of 128
+    assert chunk(lib, chunk=8) == UNSUP
     assert chunk(lib, chunk=48) == UNSUP
     assert chunk(lib, chunk=100) == UNSUP
     assert chunk(lib, dk=96) == UNSUP          # bf16 dk outside {64,128,256}
@@ -205,7 +205,7 @@ def test_backward_validation(lib):
     assert bwd(lib, dk=256, dv=512, chunk=128) == WS
     assert bwd(lib, dv=1024) == UNSUP
     assert bwd(lib, dk=512, dv=64) == UNSUP
-    assert bwd(lib, chunk=32) == UNSUP
+    assert bwd(lib, chunk=48) == UNSUP
     assert bwd(lib, dtype=F32, dk=64, dv=200) == UNSUP  # not a multiple of 8 / 16
     # the state gradient divides by gamma: tiny gammas are outside the set only then
     tiny, _keep2 = floats(0.9, 1e-7)
@@ -293,8 +293,79 @@ def test_large_chunk_workspace_holds_every_chunk(lib):
 
 
 def test_small_chunks(lib):
-    # 16- and 32-token chunks in float32 only
-    assert lib.retention_chunkwise_workspace_size(1, 2, 4096, 64, 64, F32, 16, 0) > 0
-    assert lib.retention_chunkwise_workspace_size(1, 2, 4096, 64, 64, F32, 32, 0) > 0
-    assert lib.retention_chunkwise_workspace_size(1, 2, 4096, 64, 64, BF16, 32, 0) == 0
-    assert lib.retention_chunkwise_workspace_size(1, 2, 4096, 64, 64, BF16, 16, 0) == 0
+    # 16- and 32-token chunks in both dtypes; bf16 runs a 16-token chunk as 32-token tiles
+    for dt in (F32, BF16):
+        assert lib.retention_chunkwise_workspace_size(1, 2, 4096, 64, 64, dt, 16, 0) > 0
+        assert lib.retention_chunkwise_workspace_size(1, 2, 4096, 64, 64, dt, 32, 0) > 0
+    st, p = plan(lib, 1, 2, 4096, 64, 64, BF16, 16, 0)
+    assert st == OK and p.tile == 32
+    st, p = plan(lib, 1, 2, 4096, 64, 64, F32, 16, 0)
+    assert st == OK and p.tile == 16
+
+
+# ------------------------------------------------------------ workspace plans
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("tile", ctypes.c_int), ("dv_tile", ctypes.c_int), ("value_tiles", ctypes.c_int),
+                ("segments", ctypes.c_int), ("segment_len", ctypes.c_int), ("group_len", ctypes.c_int),
+                ("segments_max", ctypes.c_int), ("reserved", ctypes.c_int),
+                ("flags_off", ctypes.c_uint64), ("gflags_off", ctypes.c_uint64), ("agg_off", ctypes.c_uint64),
+                ("gagg_off", ctypes.c_uint64), ("workspace_bytes", ctypes.c_uint64)]
+
+
+CTL_STRIDE = FLAG_STRIDE = 16 * 8  # bytes between two counters / two flags (one 128-byte line each)
+
+
+def plan(lib, B, H, N, dk, dv, dtype, chunk, segments):
+    p = Plan()
+    st = lib.retention_chunkwise_plan(B, H, N, dk, dv, dtype, chunk, segments, ctypes.byref(p))
+    return st, p
+
+
+def plan_grid():
+    for dtype in (F32, BF16):
+        for B, H in ((1, 1), (1, 8), (2, 3), (4, 16), (64, 16)):
+            for N in (1, 63, 128, 1000, 2048, 65536, 200000):
+                for dk, dv in ((64, 64), (128, 128), (256, 128), (256, 512), (64, 192)):
+                    for chunk in (16, 32, 64, 128, 256, 1024, 8192):
+                        for segments in (0, 1, 3, 64, 300):
+                            yield dtype, B, H, N, dk, dv, chunk, segments
+
+
+def test_every_plan_indexes_inside_its_workspace(lib):
+    """Every offset the segmented kernels form lies inside the workspace the
+    call requires: ticket counters, segment and group flags, published
+    segment states and group aggregates (the fault class of a plan whose
+    workspace held fewer segments than its kernel indexed)."""
+    checked = 0
+    for dtype, B, H, N, dk, dv, C, seg in plan_grid():
+        st, p = plan(lib, B, H, N, dk, dv, dtype, C, seg)
+        size = lib.retention_chunkwise_workspace_size(B, H, N, dk, dv, dtype, C, seg)
+        if st != OK:
+            assert st in (SHAPE, UNSUP) and size == 0, (dtype, B, H, N, dk, dv, C, seg, st)
+            continue
+        checked += 1
+        case = (dtype, B, H, N, dk, dv, C, seg)
+        assert size == p.workspace_bytes, case
+        assert p.value_tiles * p.dv_tile == dv and p.segment_len % p.tile == 0, case
+        assert p.segments == -(-N // p.segment_len), case  # every token belongs to a segment
+        assert (p.segments - 1) * p.segment_len < N, case   # no empty segment
+        assert 1 <= p.segments <= p.segments_max, case
+        if p.segments == 1:
+            continue
+        chains = B * H * p.value_tiles
+        groups = -(-p.segments // p.group_len)
+        assert p.workspace_bytes > 0, case
+        assert 0 < p.flags_off <= p.gflags_off <= p.agg_off <= p.gagg_off <= p.workspace_bytes, case
+        # one 8-byte ticket counter per chain at chain * 128 bytes
+        assert (chains - 1) * CTL_STRIDE + 8 <= p.flags_off, case
+        if dtype == BF16:
+            assert p.flags_off + ((chains - 1) * p.segments + p.segments - 1) * FLAG_STRIDE + 8 <= p.gflags_off, case
+            assert p.gflags_off + ((chains - 1) * groups + groups - 1) * FLAG_STRIDE + 8 <= p.agg_off, case
+            slot = dk * p.dv_tile * 4
+            assert p.agg_off + chains * p.segments * slot <= p.gagg_off, case
+            assert p.gagg_off + chains * groups * slot <= p.workspace_bytes, case
+        else:  # float32 pre-pass and scan: [B, H, segments, dk, dv]
+            assert p.agg_off + B * H * p.segments * dk * dv * 4 <= p.gagg_off, case
+    assert checked > 1000

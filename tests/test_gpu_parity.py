@@ -364,7 +364,9 @@ def test_longctx_full_sampled_heads():
     o, s = R.retention_chunkwise_fwd(q, k, v, chunk=w["chunk"], return_state=True)
     torch.cuda.synchronize()
     assert torch.isfinite(o).all()
-    _sampled_heads_check(q, k, v, o, s, w["H"], heads=[(0, 0), (0, 7)])
+    # every head: this is the workload that runs the two-pass look-back at scale (32 segments in
+    # groups), so each chain's flags, slots and decay factors are checked
+    _sampled_heads_check(q, k, v, o, s, w["H"], heads=[(0, h) for h in range(w["H"])])
 
 
 def test_longctx_parallel_crossover_lengths_sampled():
@@ -405,7 +407,8 @@ def test_decode_full_512_steps_sampled_heads():
                                         to64(vs_c[t, b:b + 1, h:h + 1]), St, g[h:h + 1])
             refs[(b, h)].append(o_ref[0, 0])
         got = torch.stack(outs[(b, h)]).cpu().numpy().astype(np.float64)
-        assert_close(got, np.stack(refs[(b, h)]), BF16_TOL, f"o over 512 steps, head {(b, h)}", per_head_axes=0)
+        # every step on its own (a wrong step would be diluted in a norm over all 512)
+        assert_close(got, np.stack(refs[(b, h)]), BF16_TOL, f"o over 512 steps, head {(b, h)}", per_head_axes=1)
         assert_close(to64(state[b, h]), St[0, 0], BF16_TOL, f"final state head {(b, h)}", per_head_axes=0)
 
 
@@ -443,6 +446,26 @@ def test_repeatable_bitwise(shape):
     for o, s in runs[1:]:
         assert torch.equal(o, runs[0][0]) and torch.equal(s, runs[0][1])
     assert torch.equal(c, d)
+
+
+@pytest.mark.parametrize("N,C,seg", [(500, 128, 3), (2000, 128, 3), (1500, 64, 5)],
+                         ids=lambda x: str(x))
+def test_state_in_out_alias_segmented(N, C, seg):
+    """state_out aliases state_in in a segmented call. With segments longer than
+    two chunks (2000 tokens in 3 segments of 768) the two-pass form runs, whose
+    first segment reads the initial state a second time while the last one may
+    already be done: the final state must not be stored before that read."""
+    B, H, dk, dv = 1, 2, 128, 128
+    q, k, v = _inputs(B, H, N, dk, dv, torch.bfloat16, seed=N + seg)
+    s0 = torch.randn((B, H, dk, dv), generator=torch.Generator().manual_seed(9)) * 0.1
+    ref, ref_s = orc.recurrent(to64(q), to64(k), to64(v), orc.head_gammas(H), state0=to64(s0))
+    for _ in range(3):
+        state = s0.to(DEV).clone()
+        o = R.retention_chunkwise_fwd(q.to(DEV), k.to(DEV), v.to(DEV), chunk=C, state_in=state, state_out=state,
+                                      segments=seg)
+        torch.cuda.synchronize()
+        assert_close(to64(o), ref, BF16_TOL, "O")
+        assert_close(to64(state), ref_s, BF16_TOL, "aliased final state")
 
 
 def test_state_in_out_alias_and_handoff():
@@ -840,10 +863,16 @@ def test_backward_and_output_stage_graph_replay():
 # ------------------------------------------------------------ small chunks
 
 SMALL_CHUNK_CASES = [
-    # B, H, N, dk, dv, chunk, dtype, rotary, state_in, segments (float32: its kernel takes any chunk)
+    # B, H, N, dk, dv, chunk, dtype, rotary, state_in, segments (float32: its kernel takes any chunk;
+    # bf16: 32-token tiles, a 16-token chunk runs on them)
     (1, 2, 150, 64, 64, 16, torch.float32, True, True, 0),
     (2, 1, 130, 32, 64, 32, torch.float32, False, True, 2),
     (1, 3, 300, 64, 128, 32, torch.float32, True, False, 0),
+    (1, 2, 333, 64, 64, 32, torch.bfloat16, True, True, 0),
+    (2, 3, 200, 128, 192, 32, torch.bfloat16, False, True, 1),
+    (1, 2, 1000, 256, 64, 32, torch.bfloat16, True, False, 5),
+    (1, 1, 97, 64, 128, 16, torch.bfloat16, False, True, 0),
+    (2, 2, 4100, 128, 64, 16, torch.bfloat16, True, True, 0),
 ]
 
 
