@@ -149,6 +149,28 @@ ret_status_t retention_chunkwise_fwd_timed(const void* q, const void* k, const v
                                            void* stream, void* const* events);
 
 /*
+ * retention_chunkwise_fwd for callers that cannot allocate memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same call without a workspace argument. The workspace of the segmented
+ * form lives in a device array of the library, RETENTION_NOALLOC_SCRATCH_BYTES
+ * bytes per GPU, held until the process ends; its address is looked up once
+ * per device (the current device of the calling thread, which must be the
+ * device of the tensors and the stream). The call allocates nothing.
+ * Returns RET_ERR_WORKSPACE when these sizes need more workspace than that
+ * (retention_chunkwise_workspace_size tells), RET_ERR_HIP if the array's
+ * address cannot be obtained; otherwise the results and status codes of
+ * retention_chunkwise_fwd. Every call on one GPU shares that array: calls
+ * that overlap on one GPU (concurrent streams, several host threads) race and
+ * must be serialised by the caller.
+ */
+#define RETENTION_NOALLOC_SCRATCH_BYTES (32u << 20)
+ret_status_t retention_chunkwise_fwd_noalloc(const void* q, const void* k, const void* v, void* o,
+                                             int B, int H, int N, int dk, int dv, ret_dtype_t dtype,
+                                             int chunk, const float* gamma, const float* theta,
+                                             int64_t pos0, const float* state_in, float* state_out,
+                                             int segments, void* stream);
+
+/*
  * Bytes of workspace retention_chunkwise_fwd needs for these sizes and this
  * `segments` request. For chunk <= 128 the value does not depend on N (the
  * segment count is bounded independently of the sequence length). Returns 0

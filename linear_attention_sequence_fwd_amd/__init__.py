@@ -75,6 +75,9 @@ def load_library(path=None):
     lib.retention_chunkwise_fwd.restype = i32
     lib.retention_chunkwise_fwd_timed.argtypes = lib.retention_chunkwise_fwd.argtypes + [vp]
     lib.retention_chunkwise_fwd_timed.restype = i32
+    lib.retention_chunkwise_fwd_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, fp, fp,
+                                                    i64, vp, vp, i32, vp]
+    lib.retention_chunkwise_fwd_noalloc.restype = i32
     lib.retention_chunkwise_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
     lib.retention_chunkwise_workspace_size.restype = sz
     lib.retention_recurrent_step.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, fp, fp, vp, vp]
@@ -269,6 +272,23 @@ def retention_chunkwise_fwd(q, k, v, chunk=64, gamma=None, theta=None, pos0=0, s
         st = lib.retention_chunkwise_fwd_timed(*args, ctypes.cast(evs, ctypes.c_void_p))
         _raise(st, "retention_chunkwise_fwd_timed")
     return (out, state_out) if return_state else out
+
+
+def retention_chunkwise_fwd_noalloc(q, k, v, out, chunk=64, gamma=None, theta=None, pos0=0, state_in=None,
+                                    state_out=None, segments=0, stream=None):
+    """retention_chunkwise_fwd without a workspace (the library's device array
+    serves instead; calls on one GPU must not overlap). `out` (and state_out,
+    when wanted) are the caller's device tensors."""
+    _check_dev(q, k, v, out, state_in, state_out)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    _g, g = _host_floats(gamma, H, "gamma")
+    _t, th = _host_floats(theta, dk // 2, "theta")
+    st = load_library().retention_chunkwise_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, dk, dv, _dtype_code(q), int(chunk), g, th, int(pos0),
+        _ptr(state_in), _ptr(state_out), int(segments), _stream(stream))
+    _raise(st, "retention_chunkwise_fwd_noalloc")
+    return out
 
 
 def retention_chunkwise_fwd_timed(q, k, v, events, **kw):

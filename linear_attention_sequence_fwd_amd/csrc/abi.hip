@@ -6,6 +6,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kernels.hpp"
 
 namespace ret {
@@ -341,6 +343,56 @@ ret_status_t retention_chunkwise_fwd(const void* q, const void* k, const void* v
                                      int segments, void* workspace, size_t workspace_bytes, void* stream) {
     return chunkwise_impl(q, k, v, o, B, H, N, dk, dv, dtype, chunk, gamma, theta, pos0, state_in, state_out,
                           segments, workspace, workspace_bytes, stream, nullptr);
+}
+
+// ---- allocation-free variant: the workspace is a device array of the library
+//
+// `scratch` holds the segmented form's workspace for retention_chunkwise_fwd_noalloc.
+// Static device storage starts zero-filled when the library's code object is
+// loaded, which is the state the workspace needs before its first use; every
+// call leaves it ready for the next one (counters carry a launch generation),
+// so nothing is cleared per call. In host code `scratch` names a host-side
+// stand-in: its device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[RETENTION_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices];  // device address of `scratch` per device (null until looked up)
+
+// The calling thread's current device's copy of `scratch`, or null.
+void* device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        scratch_ptr[dev] = p;
+    }
+    return scratch_ptr[dev];
+}
+}  // namespace
+
+ret_status_t retention_chunkwise_fwd_noalloc(const void* q, const void* k, const void* v, void* o, int B, int H,
+                                             int N, int dk, int dv, ret_dtype_t dtype, int chunk, const float* gamma,
+                                             const float* theta, int64_t pos0, const float* state_in,
+                                             float* state_out, int segments, void* stream) {
+    if (!q || !k || !v || !o) return RET_ERR_NULL;
+    ret_status_t s = check_common(B, H, N, dk, dv, dtype, theta);
+    if (s != RET_OK) return s;
+    if (segments < 0) return RET_ERR_SHAPE;
+    ChunkPlan p;
+    s = plan_chunk(B, H, N, dk, dv, dtype, chunk, segments, p);
+    if (s != RET_OK) return s;
+    if (p.ws_bytes > RETENTION_NOALLOC_SCRATCH_BYTES) return RET_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (p.ws_bytes > 0) {
+        ws = device_scratch();
+        if (!ws) return RET_ERR_HIP;
+    }
+    return chunkwise_impl(q, k, v, o, B, H, N, dk, dv, dtype, chunk, gamma, theta, pos0, state_in, state_out,
+                          segments, ws, p.ws_bytes, stream, nullptr);
 }
 
 ret_status_t retention_chunkwise_fwd_timed(const void* q, const void* k, const void* v, void* o, int B, int H,
