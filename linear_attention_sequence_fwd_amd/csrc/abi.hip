@@ -732,6 +732,10 @@ ret_status_t retention_parallel_fwd(const void* q, const void* k, const void* v,
     a.nvt = dv / dvt;
     a.pos0 = pos0;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dtype == RET_BF16 && ret::parallel_wide_supported(dk, dv, theta != nullptr)) {
+        a.nvt = dv / 128;  // the single-wave-per-SIMD kernel's 128-column value tiles
+        return ret::launch_parallel_wide(a, hp, st) == hipSuccess ? RET_OK : RET_ERR_HIP;
+    }
     const hipError_t e = (dtype == RET_BF16) ? ret::launch_parallel_bf16(a, hp, dvt, st)
                                              : ret::launch_parallel_f32(a, hp, dvt, st);
     return e == hipSuccess ? RET_OK : RET_ERR_HIP;

@@ -169,6 +169,10 @@ hipError_t launch_chunk_wide(const ChunkArgs& a, const HeadParams& hp, hipStream
 hipError_t launch_chunk_bf16_multi(const ChunkCalls& cs, const HeadParams& hp, int dvt, hipStream_t st);
 hipError_t launch_chunk_f32(const ChunkArgs& a, const HeadParams& hp, int dvt, hipStream_t st, hipEvent_t* ev);
 hipError_t launch_parallel_bf16(const ParallelArgs& a, const HeadParams& hp, int dvt, hipStream_t st);
+// The single-wave-per-SIMD parallel kernel (parallel_wide.hip): no rotation,
+// d_k 64 or 128, value tiles of 128 columns (a.nvt = dv / 128).
+bool parallel_wide_supported(int dk, int dv, bool rotation);
+hipError_t launch_parallel_wide(const ParallelArgs& a, const HeadParams& hp, hipStream_t st);
 hipError_t launch_parallel_f32(const ParallelArgs& a, const HeadParams& hp, int dvt, hipStream_t st);
 hipError_t launch_recurrent_step(const StepArgs& a, const HeadParams& hp, hipStream_t st);
 int recurrent_step_tiles(int B, int H, int dv);

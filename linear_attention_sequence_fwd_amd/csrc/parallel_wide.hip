@@ -1,0 +1,313 @@
+// Parallel retention form O = ((Q K^T) (.) D) V for heads without rotation, on
+// gfx950 (MI355X) matrix cores: bf16 inputs, float32 accumulation.
+//
+// "RetNet Guide: Retentive Networks & The Impossible Triangle", section "1. The
+// Parallel Representation for High-Throughput Pretraining": D[n][m] =
+// gamma^(n-m) for n >= m and 0 otherwise.
+//
+// One workgroup of four waves (one per SIMD, each with the SIMD's register
+// file) owns 128 query rows of one (batch, head, 128-column value tile) and
+// walks the key blocks of 128 tokens from its diagonal block backwards. Wave w
+// owns query blocks w and 7-w (16 rows each), so every wave carries the same
+// causal work on the diagonal block, and every key or value fragment read from
+// LDS feeds two matrix instructions. Per key block, on v_mfma_f32_16x16x32_bf16:
+//   G1  P^T = K Q^T, times D in registers, rounded to bf16 B operands
+//   G2  O^T += V^T P^T       (V^T by transposing LDS reads)
+// Keys and values of the next key block go from HBM straight into LDS (two
+// buffers each) while the current block is multiplied. D is a per-lane factor
+// times a per-tile factor, every exponent kept >= 0; the walk stops at the
+// first key block whose entries of D all underflow float32, since it and every
+// earlier block then add exactly zero. Query blocks are dispatched
+// longest-first.
+
+#include "common.hpp"
+#include "kernels.hpp"
+#include "tiles.hpp"
+#include "wide.hpp"
+
+namespace ret {
+
+namespace {
+
+using namespace wide;
+
+constexpr int kParBQ = 128;       // query rows per workgroup, keys per key block
+constexpr int kParDvt = 128;      // value columns per workgroup
+constexpr int kParThreads = 256;  // four waves
+constexpr int kParPipe = 4;       // steps between an LDS read and its use
+
+template <int DK>
+struct ParWGeo {
+    static constexpr int UK = DK / 8;                         // 16-byte units per key row
+    static constexpr int UV = kParDvt / 8;                    // 16-byte units per value row (of the tile)
+    static constexpr int KSQ = DK / 32;                       // 32-wide contraction steps over d_k
+    static constexpr int NTV = kParDvt / 16;                  // 16-column tiles of the value tile
+    static constexpr int KBLK = kParBQ * DK * 2 / 1024 / 4;   // 1 KiB key blocks per wave
+    static constexpr int VBLK = kParBQ * kParDvt * 2 / 1024 / 4;  // 1 KiB value blocks per wave
+    static_assert(DK == 64 || DK == 128, "key width");
+};
+
+}  // namespace
+
+template <int DK>
+__global__ __attribute__((amdgpu_flat_work_group_size(kParThreads, kParThreads), amdgpu_waves_per_eu(1, 1)))
+void parallel_wide_kernel(ParallelArgs a, HeadParams hp) {
+    using G = ParWGeo<DK>;
+    constexpr int BQ = kParBQ;
+    constexpr int UK = G::UK;
+    __shared__ __attribute__((aligned(16))) u16 kb0[BQ * DK];
+    __shared__ __attribute__((aligned(16))) u16 kb1[BQ * DK];
+    __shared__ __attribute__((aligned(16))) u16 vb0[BQ * kParDvt];
+    __shared__ __attribute__((aligned(16))) u16 vb1[BQ * kParDvt];
+
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int lane = threadIdx.x & 63;
+    const int l16 = lane & 15;
+    const int grp = lane >> 4;
+
+    const int nqb = (a.N + BQ - 1) / BQ;
+    const int BH = a.B * a.H;
+    const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int vt = lb % a.nvt;
+    const int bh = (lb / a.nvt) % BH;
+    const int qb = nqb - 1 - lb / (a.nvt * BH);
+    const int h = bh % a.H;
+    const float gam = hp.gamma[h];
+    const double lg2 = log2_gamma(gam);
+    const float lg2f = static_cast<float>(lg2);
+
+    const size_t tok0 = static_cast<size_t>(bh) * a.N;
+    const char* Kg = reinterpret_cast<const char*>(a.k + tok0 * DK);
+    const char* Qg = reinterpret_cast<const char*>(a.q + tok0 * DK);
+    const char* Vg = reinterpret_cast<const char*>(a.v + tok0 * a.dv + vt * kParDvt);
+    char* Og = reinterpret_cast<char*>(a.o + tok0 * a.dv + vt * kParDvt);
+    const int ldv = a.dv * 2;    // value / output row stride, bytes
+    constexpr int ldk = DK * 2;  // key / query row stride, bytes
+    constexpr int tile_bytes = kParDvt * 2;
+    const int q0 = qb * BQ;
+    const int Lq = min(BQ, a.N - q0);
+
+    // Key block i (1 KiB) of this wave's share of key block `kb`, straight into
+    // LDS: each wave instruction fills 1 KiB of consecutive LDS (lane l the
+    // 16-byte unit at 16 l), so each lane fetches the unit the swizzled layout
+    // puts there. Rows past the sequence end read as zero.
+    auto load_keys = [&](int kbk, u16* dst, int i) __attribute__((always_inline)) {
+        const int k0 = kbk * BQ;
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(Kg + static_cast<size_t>(k0) * ldk, min(BQ, a.N - k0) * ldk);
+        const int blk = wave * G::KBLK + i;
+        const int e = blk * 512 + lane * 8;
+        const int row = e / DK;
+        const int unit = ((e % DK) >> 3) ^ (row & ((UK < 16 ? UK : 16) - 1));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)(dst + blk * 512), 16, row * ldk + unit * 16, 0,
+                                                 0, 0);
+    };
+    auto load_values = [&](int kbk, u16* dst, int i) __attribute__((always_inline)) {
+        const int k0 = kbk * BQ;
+        const int L = min(BQ, a.N - k0);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(Vg + static_cast<size_t>(k0) * ldv, (L - 1) * ldv + tile_bytes);
+        const int blk = wave * G::VBLK + i;
+        const int e = blk * 512 + lane * 8;
+        const int row = e / kParDvt;
+        const int unit = ((e % kParDvt) >> 3) ^ (row & 15);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)(dst + blk * 512), 16, row * ldv + unit * 16, 0,
+                                                 0, 0);
+    };
+    // Transposing-read fragment of V (8 keys of 32-key step t, rows 4 grp + {0..3, 16..19})
+    // of value columns 16 nt .. +15: lane (l16, grp) points at key 4 grp + l16/4 (+16),
+    // columns 16 nt + 4 (l16 % 4) .. +3.
+    auto v_frag = [&](const u16* buf, int nt, int t) __attribute__((always_inline)) {
+        const int tok = 4 * grp + (l16 >> 2);
+        const int c = 16 * nt + 4 * (l16 & 3);
+        const int base = swz<G::UV>(tok, c >> 3) + (c & 7);
+        const uint2 lo = lds_read_tr16x4(&buf[base + (32 * t) * kParDvt]);
+        const uint2 hi = lds_read_tr16x4(&buf[base + (32 * t + 16) * kParDvt]);
+        return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    };
+
+    // queries of blocks wave and 7-wave: row 16 blk + l16, d_k 32 s + 8 grp
+    uint4 qf[2][G::KSQ];
+    {
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qg + static_cast<size_t>(q0) * ldk, Lq * ldk);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int s = 0; s < G::KSQ; ++s)
+                qf[b][s] = buf_load16(rq, (16 * (b ? 7 - wave : wave) + l16) * ldk + grp * 16 + s * 64);
+    }
+    f32x4 oacc[2][G::NTV];  // O^T: [block][column tile]
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int nt = 0; nt < G::NTV; ++nt) oacc[b][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint4 pf[2][4];  // P^T (times D) as bf16 B operands: [block][32-key step]
+
+    // D = gamma^((q0 + 16 blk + l16) - (k0 + 16 kt + 4 grp + r)):
+    //   diagonal tile (q0 = k0, kt = blk): dlane[r] = gamma^(l16 - 4 grp - r)
+    //     (negative exponents only in masked entries, which are selected away);
+    //   other tiles: dlane15[r] gamma^(16 (blk - kt) + (q0 - k0) - 15), the tile exponent >= 1.
+    float dlane[4], dlane15[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        dlane[r] = fast_exp2(static_cast<float>(l16 - 4 * grp - r) * lg2f);
+        dlane15[r] = fast_exp2(static_cast<float>(l16 - 4 * grp - r + 15) * lg2f);
+    }
+
+    // key blocks with any entry of D above float32 underflow: block qb - m has
+    // its largest decay gamma^(128 m - 127)
+    int nkb = qb + 1;
+    if (lg2 < 0.0) {
+        const double span = 160.0 / (-lg2);  // gamma^span < 2^-160
+        const int mmax = static_cast<int>((span + BQ - 1) / BQ) + 1;
+        nkb = min(nkb, mmax + 1);
+    }
+
+    // G1 for the wave owning blocks W and 7-W against the key block in kb
+    // (delta = q0 - k0); DIAG: the diagonal block (causal tiles only). Riding
+    // along: the next key block's keys and values into the other buffers
+    // (next < 0: none), early enough to land before the next step.
+    auto g1 = [&](const u16* __restrict__ kb, u16* __restrict__ nkbuf, u16* __restrict__ nvbuf, int next, int delta,
+                  auto wtag, auto diag_tag) __attribute__((always_inline)) {
+        constexpr int B0 = decltype(wtag)::value, B1 = 7 - B0;
+        constexpr bool DIAG = decltype(diag_tag)::value;
+        constexpr int T1 = DIAG ? B1 / 2 + 1 : 4;
+        constexpr int T0 = DIAG ? B0 / 2 + 1 : 4;
+        const FragAddr<UK> fk(l16, grp);  // K rows 16 kt + l16, d_k 32 s + 8 grp
+        struct KF {
+            uint4 a, b;
+        };
+        f32x4 p[4];  // tile 2t of block 7-W, tile 2t+1 of it, tile 2t of block W, tile 2t+1 of it
+        constexpr int NS1 = T1 * G::KSQ;
+        pipelined<NS1, kParPipe>(
+            [&](auto j) __attribute__((always_inline)) {
+                constexpr int t = decltype(j)::value / G::KSQ, s = decltype(j)::value % G::KSQ;
+                KF f;
+                f.a = *reinterpret_cast<const uint4*>(&kb[fk.at(2 * t, s)]);
+                if constexpr (!DIAG || 2 * t + 1 <= B1)
+                    f.b = *reinterpret_cast<const uint4*>(&kb[fk.at(2 * t + 1, s)]);
+                return f;
+            },
+            [&](auto j, const KF& f) __attribute__((always_inline)) {
+                constexpr int t = decltype(j)::value / G::KSQ, s = decltype(j)::value % G::KSQ;
+                constexpr bool two1 = !DIAG || 2 * t + 1 <= B1, one0 = t < T0, two0 = !DIAG || 2 * t + 1 <= B0;
+                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                p[0] = mfma16x16x32(f.a, qf[1][s], s == 0 ? zero : p[0]);
+                if constexpr (two1) p[1] = mfma16x16x32(f.b, qf[1][s], s == 0 ? zero : p[1]);
+                if constexpr (one0) p[2] = mfma16x16x32(f.a, qf[0][s], s == 0 ? zero : p[2]);
+                if constexpr (two0) p[3] = mfma16x16x32(f.b, qf[0][s], s == 0 ? zero : p[3]);
+                if constexpr (s == G::KSQ - 1) {
+                    f32x4 r[4] = {p[0], two1 ? p[1] : zero, p[2], two0 ? p[3] : zero};
+                    // D on tile kt of block blk: the diagonal tile with the causal select
+                    auto decay = [&](f32x4& x, int blk, int kt, bool present) __attribute__((always_inline)) {
+                        if (!present) return;
+                        if (DIAG && kt == blk) {
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) x[q] = (4 * grp + q <= l16) ? x[q] * dlane[q] : 0.0f;
+                        } else {
+                            const float tf = fast_exp2(static_cast<float>(16 * (blk - kt) + delta - 15) * lg2f);
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) x[q] *= dlane15[q] * tf;
+                        }
+                    };
+                    // off the diagonal one instantiation serves every wave: its blocks at run time
+                    const int blk1 = DIAG ? B1 : 7 - wave, blk0 = DIAG ? B0 : wave;
+                    decay(r[0], blk1, 2 * t, true);
+                    decay(r[1], blk1, 2 * t + 1, two1);
+                    pf[1][t] = make_uint4(pack2_bf16(r[0][0], r[0][1]), pack2_bf16(r[0][2], r[0][3]),
+                                          pack2_bf16(r[1][0], r[1][1]), pack2_bf16(r[1][2], r[1][3]));
+                    if constexpr (one0) {
+                        decay(r[2], blk0, 2 * t, true);
+                        decay(r[3], blk0, 2 * t + 1, two0);
+                        pf[0][t] = make_uint4(pack2_bf16(r[2][0], r[2][1]), pack2_bf16(r[2][2], r[2][3]),
+                                              pack2_bf16(r[3][0], r[3][1]), pack2_bf16(r[3][2], r[3][3]));
+                    }
+                }
+            },
+            [&](auto j) __attribute__((always_inline)) {
+                constexpr int J = decltype(j)::value;
+                if (next >= 0) {
+                    spread<G::KBLK, NS1, J>([&](auto i) { load_keys(next, nkbuf, i); });
+                    spread<G::VBLK, NS1, J>([&](auto i) { load_values(next, nvbuf, i); });
+                }
+            });
+    };
+    // G2 for the wave owning blocks W and 7-W: step j = 32-key step t = j / NTV,
+    // column tile nt = j % NTV.
+    auto g2 = [&](const u16* __restrict__ vb, auto wtag, auto diag_tag) __attribute__((always_inline)) {
+        constexpr int B0 = decltype(wtag)::value, B1 = 7 - B0;
+        constexpr bool DIAG = decltype(diag_tag)::value;
+        constexpr int T1 = DIAG ? B1 / 2 + 1 : 4;
+        constexpr int T0 = DIAG ? B0 / 2 + 1 : 4;
+        constexpr int NS2 = T1 * G::NTV;
+        pipelined<NS2, kParPipe>(
+            [&](auto j) __attribute__((always_inline)) {
+                constexpr int t = decltype(j)::value / G::NTV, nt = decltype(j)::value % G::NTV;
+                return v_frag(vb, nt, t);
+            },
+            [&](auto j, const uint4& vf) __attribute__((always_inline)) {
+                constexpr int t = decltype(j)::value / G::NTV, nt = decltype(j)::value % G::NTV;
+                oacc[1][nt] = mfma16x16x32(vf, pf[1][t], oacc[1][nt]);
+                if constexpr (t < T0) oacc[0][nt] = mfma16x16x32(vf, pf[0][t], oacc[0][nt]);
+            },
+            [](auto) {});
+    };
+    auto step = [&](int m, u16* __restrict__ kb, u16* __restrict__ vb, u16* __restrict__ nk, u16* __restrict__ nv)
+                    __attribute__((always_inline)) {
+        // this key block has landed (nothing else is in flight) and every wave
+        // has finished with the other buffers
+        wait_vm_lgkm0<0>();
+        __builtin_amdgcn_s_barrier();
+        const int next = m + 1 < nkb ? qb - m - 1 : -1;
+        const int delta = m * BQ;
+        if (m == 0) {
+            switch (wave) {
+                case 0: g1(kb, nk, nv, next, delta, Ic<0>{}, Ic<1>{}); g2(vb, Ic<0>{}, Ic<1>{}); break;
+                case 1: g1(kb, nk, nv, next, delta, Ic<1>{}, Ic<1>{}); g2(vb, Ic<1>{}, Ic<1>{}); break;
+                case 2: g1(kb, nk, nv, next, delta, Ic<2>{}, Ic<1>{}); g2(vb, Ic<2>{}, Ic<1>{}); break;
+                default: g1(kb, nk, nv, next, delta, Ic<3>{}, Ic<1>{}); g2(vb, Ic<3>{}, Ic<1>{}); break;
+            }
+        } else {
+            // off the diagonal every wave does the same work
+            g1(kb, nk, nv, next, delta, Ic<0>{}, Ic<0>{});
+            g2(vb, Ic<0>{}, Ic<0>{});
+        }
+    };
+
+    // the diagonal key block first
+#pragma unroll
+    for (int i = 0; i < G::KBLK; ++i) load_keys(qb, kb0, i);
+#pragma unroll
+    for (int i = 0; i < G::VBLK; ++i) load_values(qb, vb0, i);
+    for (int m = 0; m < nkb; m += 2) {
+        step(m, kb0, vb0, kb1, vb1);
+        if (m + 1 < nkb) step(m + 1, kb1, vb1, kb0, vb0);
+    }
+
+    // O = O^T transposed back: lane (l16, grp) holds rows 16 blk + l16, columns 16 nt + 4 grp .. +3
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(Og + static_cast<size_t>(q0) * ldv, (Lq - 1) * ldv + tile_bytes);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int blk = b ? 7 - wave : wave;
+#pragma unroll
+        for (int nt = 0; nt < G::NTV; ++nt) {
+            const f32x4 o = oacc[b][nt];
+            buf_store8(make_uint2(pack2_bf16(o[0], o[1]), pack2_bf16(o[2], o[3])), ro,
+                       (16 * blk + l16) * ldv + grp * 8 + nt * 32);
+        }
+    }
+}
+
+bool parallel_wide_supported(int dk, int dv, bool rotation) {
+    return !rotation && (dk == 64 || dk == 128) && dv % kParDvt == 0;
+}
+
+hipError_t launch_parallel_wide(const ParallelArgs& a, const HeadParams& hp, hipStream_t st) {
+    const int nqb = (a.N + kParBQ - 1) / kParBQ;
+    const dim3 grid(nqb * a.B * a.H * a.nvt), block(kParThreads);
+    if (a.dk == 128)
+        hipLaunchKernelGGL(parallel_wide_kernel<128>, grid, block, 0, st, a, hp);
+    else
+        hipLaunchKernelGGL(parallel_wide_kernel<64>, grid, block, 0, st, a, hp);
+    return hipGetLastError();
+}
+
+}  // namespace ret
