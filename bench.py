@@ -54,37 +54,56 @@ def decode_alg_bytes(B, H, dk, dv, elt=2):
 
 
 PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
-SOURCE_DIRS = ("linear_attention_sequence_fwd_amd/csrc", "include")
+CSRC = "linear_attention_sequence_fwd_amd/csrc"
+# the source file of each workload's dominant kernel; with the shared headers it
+# decides that kernel's code (the traffic of the others is not affected by it)
+KERNEL_SOURCES = {
+    "layer7b_bf16": "chunk_wide.hip",
+    "msr_bf16_rotary": "chunk_bf16.hip",
+    "longctx_bf16": "chunk_bf16.hip",
+    "decode_bf16": "decode.hip",
+}
+SHARED_HEADERS = ("common.hpp", "tiles.hpp", "wide.hpp", "kernels.hpp")
 
 
-def source_fingerprint():
-    """sha256 (first 16 hex digits) over the kernel sources, in name order."""
+def source_fingerprint(workload):
+    """sha256 (first 16 hex digits) over the workload's kernel source and the shared headers."""
     import hashlib
 
-    root = os.path.dirname(os.path.abspath(__file__))
+    root = os.path.join(os.path.dirname(os.path.abspath(__file__)), CSRC)
     h = hashlib.sha256()
-    for d in SOURCE_DIRS:
-        for name in sorted(os.listdir(os.path.join(root, d))):
-            if name.endswith((".hip", ".hpp", ".h")):
-                h.update(name.encode())
-                with open(os.path.join(root, d, name), "rb") as f:
-                    h.update(f.read())
+    for name in (KERNEL_SOURCES[workload],) + SHARED_HEADERS:
+        h.update(name.encode())
+        with open(os.path.join(root, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(workload):
     """HBM bytes per launch of the workload's dominant kernel from the committed
-    counter summary (profiles/hbm_traffic.json: scaled FETCH_SIZE + WRITE_SIZE),
-    or None when the kernel sources changed since the counters were taken."""
+    counter summary (profiles/hbm_traffic.json: FETCH_SIZE and WRITE_SIZE, each
+    scaled by what it reads for a plain copy of known size), or None when that
+    kernel's sources changed since the counters were taken."""
     path = os.path.join(PROFILES, "hbm_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_fingerprint") != source_fingerprint() or workload not in rec.get("workloads", {}):
+    w = rec.get("workloads", {}).get(workload)
+    if w is None or workload not in KERNEL_SOURCES or w.get("source_fingerprint") != source_fingerprint(workload):
         return None
-    w = rec["workloads"][workload]
     return w["read_bytes"] + w["write_bytes"]
+
+
+def measured_dram(workload):
+    """The same launch's bytes at the DRAM controllers (32-byte TCC_EA0 read and
+    write requests to DRAM, which MALL hits do not reach), or None like
+    measured_traffic."""
+    if measured_traffic(workload) is None:
+        return None
+    with open(os.path.join(PROFILES, "hbm_traffic.json")) as f:
+        w = json.load(f)["workloads"][workload]
+    return w.get("dram_read_bytes", 0) + w.get("dram_write_bytes", 0) if "dram_read_bytes" in w else None
 
 
 def time_events(fn, steps, warmup):
@@ -349,6 +368,18 @@ def run_only(name, steps, warmup, dev):
         print(json.dumps({"workload": "copy 1 GiB -> 1 GiB", "ms_per_call": ms, "bytes_read": src.numel() * 4,
                           "bytes_written": dst.numel() * 4}))
         return
+    if name == "parallel":
+        # the parallel form on the long-context heads at the longest crossover length
+        w = W.WORKLOADS["longctx_bf16"]
+        n = max(w["parallel_lengths"])
+        q, k, v, _ = W.make_workload("longctx_bf16", device=dev)
+        qn, kn, vn = q[:, :, :n].contiguous(), k[:, :, :n].contiguous(), v[:, :, :n].contiguous()
+        del q, k, v
+        out = torch.empty_like(vn)
+        ms = time_events(lambda: R.retention_parallel_fwd(qn, kn, vn, out=out), steps, warmup)
+        print(json.dumps({"workload": f"parallel form, B=1 H=8 N={n} d_k=d_v=128 bf16", "ms_per_call": ms,
+                          "steps": steps}))
+        return
     key = {"msr": "msr_bf16_rotary", "layer7b": "layer7b_bf16", "decode": "decode_bf16",
            "longctx": "longctx_bf16", "single": "single_head_f32", "bwd": "msr_bf16_rotary",
            "epi": "layer7b_bf16", "decmsr": "decode_bf16"}[name]
@@ -535,7 +566,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["msr", "layer7b", "decode", "longctx", "single", "copy", "bwd", "epi",
+    ap.add_argument("--only", choices=["msr", "layer7b", "decode", "longctx", "single", "copy", "bwd", "epi", "parallel",
                                        "decmsr"],
                     help="time one workload only (no CPU baseline); for profilers")
     ap.add_argument("--sweep", choices=["decode-batch", "chunk"], help="print one JSON line per point of a sweep")
@@ -605,6 +636,7 @@ def main():
             "frac": tflops / BF16_PEAK_TFLOPS,
             "traffic": measured_traffic(name),
             "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x copy calibration + WRITE_SIZE)",
+            "dram_traffic": measured_dram(name),
             "alg_flops_per_launch": flops,
             "alg_bytes_per_launch": nbytes,
             "kernel_ms": kernel_ms,
@@ -670,7 +702,8 @@ def run_also(R, W, torch, dev):
                      "achieved": by2 / (warm_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": by2 / (warm_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "frac_cold": by2 / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(name), "alg_bytes_per_launch": by2},
+                     "traffic": measured_traffic(name), "dram_traffic": measured_dram(name),
+                     "alg_bytes_per_launch": by2},
     })
     del q, k, v, out, ws
     torch.cuda.empty_cache()
@@ -695,7 +728,8 @@ def run_also(R, W, torch, dev):
         "ms_per_step": ms4, "state_updates_per_s": w["B"] * w["H"] / (ms4 * 1e-3),
         "roofline": {"bound": "hbm", "kernel": "recurrent_step_kernel", "achieved": by4 / (ms4 * 1e-3) / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": by4 / (ms4 * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(name), "alg_bytes_per_launch": by4},
+                     "traffic": measured_traffic(name), "dram_traffic": measured_dram(name),
+                     "alg_bytes_per_launch": by4},
     })
     del s0, qs, ks, vs, state, o
     torch.cuda.empty_cache()
@@ -724,6 +758,7 @@ def run_also(R, W, torch, dev):
         "roofline": {"bound": "hbm", "kernel": "chunk_bf16_kernel<128, 128, 128, two-pass>",
                      "achieved": by5 / (k5 * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": by5 / (k5 * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": measured_traffic(name),
+                     "dram_traffic": measured_dram(name),
                      "alg_bytes_per_launch": by5, "tflops": fl5 / (k5 * 1e-3) / 1e12},
         "parallel_crossover": cross,
     })
