@@ -317,7 +317,11 @@ size_t retention_msr_epilogue_workspace_size(int B, int H, int N, int dv, int d_
  * Guide" section "2. The Recurrent Representation for Constant-Memory O(1)
  * Decoding": the listing's recurrent step normalises and projects each
  * token's output). With few tokens the projection splits its contraction over
- * workgroups so the whole of W_O streams from HBM in parallel.
+ * workgroups so the whole of W_O streams from HBM in parallel. When one
+ * workgroup of the step owns a whole (sequence, head) row (B*H >= 256, or d_v
+ * not a multiple of 128), the step also normalises and gates that row, and no separate
+ * GroupNorm pass runs; o and y are the same either way up to float32 rounding
+ * order in the statistics.
  * Arguments as in the two calls; workspace:
  * retention_msr_epilogue_workspace_size(B, H, 1, dv, d_out, RET_BF16) bytes.
  * Implemented set: bf16, and each call's own set.

@@ -624,6 +624,51 @@ ret_status_t retention_chunkwise_bwd(const void* q, const void* k, const void* v
     return finish_states();
 }
 
+namespace {
+
+// y = z W_O^T for the output stage, z being the bf16 [B*N, H*dv] block at the start
+// of the workspace and the split-K partial sums (when any) after it.
+ret_status_t msr_projection(const void* w_o, void* y, int B, int H, int N, int dv, int d_out, void* workspace,
+                            hipStream_t st) {
+    ret::GemmArgs g;
+    g.a = static_cast<const ret::u16*>(workspace);
+    g.b = static_cast<const ret::u16*>(w_o);
+    g.c = static_cast<ret::u16*>(y);
+    g.M = B * N;
+    g.N = d_out;
+    g.K = H * dv;
+    g.splits = ret::gemm_splits(g.M, g.N, g.K);
+    g.part = g.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                     round256(static_cast<size_t>(B) * N * H * dv * sizeof(uint16_t)))
+                          : nullptr;
+    return ret::launch_gemm_bt(g, st) == hipSuccess ? RET_OK : RET_ERR_HIP;
+}
+
+ret::StepArgs step_args(const void* q, const void* k, const void* v, void* o, float* state, const int64_t* pos, int B,
+                        int H, int dk, int dv, ret_dtype_t dtype) {
+    ret::StepArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.state = state;
+    a.pos = pos;
+    a.B = B;
+    a.H = H;
+    a.dk = dk;
+    a.dv = dv;
+    a.bf16 = dtype == RET_BF16;
+    a.ntile = ret::recurrent_step_tiles(B, H, dv);
+    a.gate = nullptr;
+    a.gn_w = nullptr;
+    a.gn_b = nullptr;
+    a.z = nullptr;
+    a.eps = 0.f;
+    return a;
+}
+
+}  // namespace
+
 size_t retention_msr_epilogue_workspace_size(int B, int H, int N, int dv, int d_out, ret_dtype_t dtype) {
     if (B < 1 || H < 1 || N < 1 || dv < 1 || d_out < 1 || dtype != RET_BF16) return 0;
     if (dv != 64 && dv != 128 && dv != 256 && dv != 512) return 0;
@@ -661,19 +706,7 @@ ret_status_t retention_msr_epilogue(const void* o, const void* gate, const float
     a.dv = dv;
     a.eps = eps;
     if (ret::launch_groupnorm_gate(a, st) != hipSuccess) return RET_ERR_HIP;
-    ret::GemmArgs g;
-    g.a = a.z;
-    g.b = static_cast<const ret::u16*>(w_o);
-    g.c = static_cast<ret::u16*>(y);
-    g.M = B * N;
-    g.N = d_out;
-    g.K = H * dv;
-    g.splits = ret::gemm_splits(g.M, g.N, g.K);
-    g.part = g.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                                     round256(static_cast<size_t>(B) * N * H * dv * sizeof(uint16_t)))
-                          : nullptr;
-    if (ret::launch_gemm_bt(g, st) != hipSuccess) return RET_ERR_HIP;
-    return RET_OK;
+    return msr_projection(w_o, y, B, H, N, dv, d_out, workspace, st);
 }
 
 ret_status_t retention_recurrent_step_msr(const void* q, const void* k, const void* v, float* state, int B, int H,
@@ -698,10 +731,23 @@ ret_status_t retention_recurrent_step_msr(const void* q, const void* k, const vo
     const size_t need = retention_msr_epilogue_workspace_size(B, H, 1, dv, d_out, dtype);
     if (need == 0) return RET_ERR_UNSUPPORTED;
     if (workspace == nullptr || workspace_bytes < need) return RET_ERR_WORKSPACE;
-    s = retention_recurrent_step(q, k, v, o, state, B, H, dk, dv, dtype, gamma, theta, pos, stream);
-    if (s != RET_OK) return s;
-    return retention_msr_epilogue(o, gate, gn_weight, gn_bias, eps, w_o, y, B, H, 1, dv, d_out, dtype, workspace,
-                                  workspace_bytes, stream);
+    if (ret::recurrent_step_tiles(B, H, dv) != 1) {  // rows split over workgroups: the general output stage
+        s = retention_recurrent_step(q, k, v, o, state, B, H, dk, dv, dtype, gamma, theta, pos, stream);
+        if (s != RET_OK) return s;
+        return retention_msr_epilogue(o, gate, gn_weight, gn_bias, eps, w_o, y, B, H, 1, dv, d_out, dtype,
+                                      workspace, workspace_bytes, stream);
+    }
+    // each workgroup of the step owns a whole (sequence, head) row: it also writes the
+    // normalised, gated row into the workspace, and only the projection follows
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    ret::StepArgs a = step_args(q, k, v, o, state, pos, B, H, dk, dv, dtype);
+    a.gate = static_cast<const ret::u16*>(gate);
+    a.gn_w = gn_weight;
+    a.gn_b = gn_bias;
+    a.z = static_cast<ret::u16*>(workspace);
+    a.eps = eps;
+    if (ret::launch_recurrent_step(a, hp, st) != hipSuccess) return RET_ERR_HIP;
+    return msr_projection(w_o, y, B, H, 1, dv, d_out, workspace, st);
 }
 
 ret_status_t retention_parallel_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N,
@@ -756,19 +802,7 @@ ret_status_t retention_recurrent_step(const void* q, const void* k, const void* 
         return RET_ERR_ALIGN;
     if (dv % 4 != 0 || dv > 1024 || dk > 4096) return RET_ERR_UNSUPPORTED;
 
-    ret::StepArgs a;
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.o = o;
-    a.state = state;
-    a.pos = pos;
-    a.B = B;
-    a.H = H;
-    a.dk = dk;
-    a.dv = dv;
-    a.bf16 = dtype == RET_BF16;
-    a.ntile = ret::recurrent_step_tiles(B, H, dv);
+    const ret::StepArgs a = step_args(q, k, v, o, state, pos, B, H, dk, dv, dtype);
     const hipError_t e = ret::launch_recurrent_step(a, hp, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? RET_OK : RET_ERR_HIP;
 }

@@ -36,6 +36,45 @@ __device__ __forceinline__ float load_elem(const void* p, size_t i) {
     return static_cast<const float*>(p)[i];
 }
 
+// Sum of v over the workgroup (every thread gets it); `scratch` holds one float
+// per wave and is free again when the function returns.
+__device__ __forceinline__ float block_sum(float v, float* scratch) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    __syncthreads();  // earlier readers of scratch are done
+    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < kStepThreads / 64; ++w) t += scratch[w];
+    return t;
+}
+
+// GroupNorm of one head's bf16 output row, held by threads 0 .. tpr-1 (four
+// channels each, tpr = dv / 4), then the gain, bias and gate: the multi-scale
+// output stage's first half for a workgroup that owns the whole row.
+__device__ __forceinline__ void step_groupnorm_gate(const StepArgs& a, const f32v4& o, int b, int h, int tpr,
+                                                    float* scratch) {
+    const bool mine = static_cast<int>(threadIdx.x) < tpr;
+    const float inv = 1.0f / a.dv;
+    const float mean = block_sum(mine ? (o[0] + o[1]) + (o[2] + o[3]) : 0.f, scratch) * inv;
+    const f32v4 d = o - mean;
+    const float var = block_sum(mine ? (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]) : 0.f, scratch) * inv;
+    const float rstd = rsqrtf(var + a.eps);
+    if (!mine) return;
+    const int c = h * a.dv + 4 * static_cast<int>(threadIdx.x);  // channel in the layer's H*dv
+    const size_t zi = static_cast<size_t>(b) * a.H * a.dv + c;
+    f32v4 w = {1.f, 1.f, 1.f, 1.f}, bias = {0.f, 0.f, 0.f, 0.f}, g = {1.f, 1.f, 1.f, 1.f};
+    if (a.gn_w) w = *reinterpret_cast<const f32v4*>(a.gn_w + c);
+    if (a.gn_b) bias = *reinterpret_cast<const f32v4*>(a.gn_b + c);
+    if (a.gate) {
+        const uint2 gw = *reinterpret_cast<const uint2*>(a.gate + zi);
+        g = f32v4{lo_bf16(gw.x), hi_bf16(gw.x), lo_bf16(gw.y), hi_bf16(gw.y)};
+    }
+    const f32v4 z = (d * rstd * w + bias) * g;
+    *reinterpret_cast<uint2*>(a.z + zi) = make_uint2(pack2_bf16(z[0], z[1]), pack2_bf16(z[2], z[3]));
+}
+
 template <bool BF16, int UNROLL>
 __global__ __launch_bounds__(kStepThreads) void recurrent_step_kernel(StepArgs a, HeadParams hp) {
     __shared__ float qs[kStepMaxDk];
@@ -108,16 +147,22 @@ __global__ __launch_bounds__(kStepThreads) void recurrent_step_kernel(StepArgs a
     __syncthreads();
 
     // ---- reduce over row groups and write o
+    f32v4 o = {0.f, 0.f, 0.f, 0.f};
     if (tid < tpr) {
-        f32v4 o = red[tid];
+        o = red[tid];
         for (int g = 1; g < rgs; ++g) o += red[g * tpr + tid];
         const size_t o0 = static_cast<size_t>(bh) * a.dv + c0 + 4 * tid;
         if (BF16) {
             u16* op = static_cast<u16*>(a.o) + o0;
-            *reinterpret_cast<uint2*>(op) = make_uint2(pack2_bf16(o[0], o[1]), pack2_bf16(o[2], o[3]));
+            const uint2 w = make_uint2(pack2_bf16(o[0], o[1]), pack2_bf16(o[2], o[3]));
+            *reinterpret_cast<uint2*>(op) = w;
+            o = f32v4{lo_bf16(w.x), hi_bf16(w.x), lo_bf16(w.y), hi_bf16(w.y)};  // what a reader of o sees
         } else {
             *reinterpret_cast<f32v4*>(static_cast<float*>(a.o) + o0) = o;
         }
+    }
+    if constexpr (BF16) {
+        if (a.z) step_groupnorm_gate(a, o, b, h, tpr, reinterpret_cast<float*>(red));
     }
 }
 
@@ -134,7 +179,7 @@ int recurrent_step_tiles(int B, int H, int dv) {
 
 hipError_t launch_recurrent_step(const StepArgs& a, const HeadParams& hp, hipStream_t st) {
     if (a.dk > kStepMaxDk || a.dv % 4 != 0 || a.ntile < 1 || a.dv % (4 * a.ntile) != 0 ||
-        a.dv / a.ntile / 4 > kStepThreads)
+        a.dv / a.ntile / 4 > kStepThreads || (a.z && (a.ntile != 1 || !a.bf16)))
         return hipErrorInvalidValue;
     dim3 grid(a.B * a.H * a.ntile), block(kStepThreads);
     // narrow tiles have more row groups per workgroup and so fewer rows per thread

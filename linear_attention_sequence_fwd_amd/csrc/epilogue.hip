@@ -21,6 +21,11 @@
 //     double-buffered in LDS and filled by direct global-to-LDS loads (the
 //     next step's loads are in flight while the current one is multiplied);
 //     output staged through LDS for 16-byte stores.
+//   gemm_split_kernel + reduce_splits_kernel: the same product for at most 64
+//     rows, its K range split over workgroups (about one per compute unit)
+//     with three LDS stages, then the float32 partials summed in split order.
+// A decode step whose workgroups own whole rows normalises and gates in the
+// step kernel itself (decode.hip), and only the projection runs here.
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -202,10 +207,9 @@ __device__ __forceinline__ void gemm_step(f32x4 (&acc)[WM / 16][WN / 16], const 
     __syncthreads();
 }
 
-// NWM x NWN waves; wave tile (BM / NWM) x (BN / NWN). With SPLIT, workgroup
-// b multiplies K range (b / tiles) of g.splits equal ranges for tile b % tiles
-// and writes float32 partial sums (reduced by reduce_splits_kernel).
-template <int BM, int BN, int NWM, int NWN, bool SPLIT>
+// NWM x NWN waves; wave tile (BM / NWM) x (BN / NWN); the whole K range per
+// workgroup (few rows take gemm_split_kernel instead).
+template <int BM, int BN, int NWM, int NWN>
 __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bt_kernel(GemmArgs g) {
     constexpr int GM = BM;
     constexpr int NW = NWM * NWN;
@@ -224,8 +228,7 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bt_kernel(GemmArgs g) {
     // tile order: consecutive ids on one XCD, grouped by kGroupM row tiles so
     // that the workgroups running together share row and column panels in L2
     const int tiles_m = (g.M + GM - 1) / GM, tiles_n = g.N / BN;
-    const int split = SPLIT ? static_cast<int>(blockIdx.x) / (tiles_m * tiles_n) : 0;
-    const int id = SPLIT ? static_cast<int>(blockIdx.x) % (tiles_m * tiles_n) : xcd_logical_block(blockIdx.x, gridDim.x);
+    const int id = xcd_logical_block(blockIdx.x, gridDim.x);
     const int per_group = kGroupM * tiles_n;
     const int first_m = (id / per_group) * kGroupM;
     const int gsize = min(tiles_m - first_m, kGroupM);
@@ -239,8 +242,8 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bt_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int KT = g.K / GK / (SPLIT ? g.splits : 1);  // K steps of this workgroup
-    const int kb = split * KT * GK;                     // first K index
+    const int KT = g.K / GK;  // K steps
+    const int kb = 0;         // first K index
     panel_fill<GM, NW>(a0, g.a, m0, g.M, g.K, kb, wave, lane);
     panel_fill<BN, NW>(b0, g.b, n0, g.N, g.K, kb, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
@@ -252,26 +255,13 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bt_kernel(GemmArgs g) {
             gemm_step<BM, BN, WM, WN, NW>(acc, a1, b1, a0, b0, kt + 2 < KT, g, m0, n0, kb + (kt + 2) * GK, wm, wn,
                                           wave, lane);
     }
-    if constexpr (SPLIT) {  // four consecutive float32 columns of one row per lane
-        float* part = g.part + static_cast<size_t>(split) * g.M * g.N;
-#pragma unroll
-        for (int i = 0; i < TI; ++i) {
-            const int row = m0 + wm * WM + i * 16 + l16;
-            if (row < g.M)
-#pragma unroll
-                for (int j = 0; j < TJ; ++j)
-                    *reinterpret_cast<f32x4*>(part + static_cast<size_t>(row) * g.N + n0 + wn * WN + j * 16 +
-                                              4 * grp) = acc[i][j];
-        }
-        return;
-    }
 
     // acc[i][j][r]: output row m0 + wm*WM + i*16 + l16, column n0 + wn*WN + j*16 + 4*grp + r:
     // four consecutive columns of one row per lane. Stage SLICE-row slices
     // through LDS and store rows with 16-byte writes.
     constexpr int LDC = BN + 8;
     constexpr int SLICE = GM < 32 ? GM : 32;
-    static_assert(SPLIT || SLICE * LDC <= GM * GK, "slice fits one A stage");
+    static_assert(SLICE * LDC <= GM * GK, "slice fits one A stage");
     u16* cs = a0;
 #pragma unroll
     for (int sl = 0; sl < GM / SLICE; ++sl) {
@@ -302,18 +292,129 @@ __global__ __launch_bounds__(NWM * NWN * 64) void gemm_bt_kernel(GemmArgs g) {
     }
 }
 
-// c[m][n] = bf16(sum over splits of part[split][m][n]), 8 outputs per thread.
-__global__ __launch_bounds__(256) void reduce_splits_kernel(GemmArgs g) {
-    const long long e = (static_cast<long long>(blockIdx.x) * 256 + threadIdx.x) * 8;
-    if (e >= static_cast<long long>(g.M) * g.N) return;
-    f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < g.splits; ++s) {
-        const f32x4* p = reinterpret_cast<const f32x4*>(g.part + static_cast<size_t>(s) * g.M * g.N + e);
-        lo += p[0];
-        hi += p[1];
+// ---------------------------------------------------------------- split-K GEMM for few rows
+//
+// At most 64 rows (a decode step's tokens) the product streams W_O once and is
+// bound by how many bytes are in flight, so this kernel keeps three LDS stages:
+// step kt multiplies stage kt % 3 while the loads of step kt + 2 fill stage
+// (kt + 2) % 3, and waits only for stage kt + 1 before its barrier.
+
+// One step: multiply (as, bs) into the accumulators while (af, bf) fill from K
+// index kfill; then wait until the loads issued before this step's (the next
+// stage) have landed and synchronise. The stages are restrict arguments: that is
+// what lets the compiler tell the direct loads into one stage from the reads of
+// another, so it adds no waits of its own.
+template <int WM, int WN, int NW>
+__device__ __forceinline__ void split_step(f32x4 (&acc)[WM / 16][WN / 16], const u16* __restrict__ as,
+                                           const u16* __restrict__ bs, u16* __restrict__ af, u16* __restrict__ bf,
+                                           const GemmArgs& g, int m0, int n0, int kfill, int wm, int wn, int wave,
+                                           int lane) {
+    constexpr int TI = WM / 16, TJ = WN / 16;
+    constexpr int kIssued = (64 + 128) / 8 / NW;  // direct loads per thread and step
+    const int l16 = lane & 15, grp = lane >> 4;
+    panel_fill<64, NW>(af, g.a, m0, g.M, g.K, kfill, wave, lane);
+    panel_fill<128, NW>(bf, g.b, n0, g.N, g.K, kfill, wave, lane);
+#pragma unroll
+    for (int ks = 0; ks < GK / 32; ++ks) {
+        uint4 bq[TJ];
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) bq[j] = panel_read(bs, wn * WN + j * 16 + l16, ks * 4 + grp);
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+            const uint4 aq = panel_read(as, wm * WM + i * 16 + l16, ks * 4 + grp);
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16x16x32(bq[j], aq, acc[i][j]);
+        }
     }
-    *reinterpret_cast<uint4*>(g.c + e) =
-        make_uint4(pack2_bf16(lo[0], lo[1]), pack2_bf16(lo[2], lo[3]), pack2_bf16(hi[0], hi[1]), pack2_bf16(hi[2], hi[3]));
+    __builtin_amdgcn_s_waitcnt((kIssued & 15) | ((kIssued >> 4) << 14) | (7 << 4));  // next stage in, LDS done
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// 64 x 128 output tile, K range (b / tiles) of g.splits equal ranges for tile
+// b % tiles, float32 partial sums into g.part (summed by reduce_splits_kernel).
+template <int NWM, int NWN>
+__global__ __launch_bounds__(NWM * NWN * 64) void gemm_split_kernel(GemmArgs g) {
+    constexpr int BM = 64, BN = 128, NW = NWM * NWN;
+    constexpr int WM = BM / NWM, WN = BN / NWN;
+    constexpr int TI = WM / 16, TJ = WN / 16;
+    constexpr int kIssued = (BM + BN) / 8 / NW;
+    static_assert(kIssued * 8 * NW == BM + BN, "panel split");
+    __shared__ __attribute__((aligned(1024))) u16 a0[BM * GK];
+    __shared__ __attribute__((aligned(1024))) u16 a1[BM * GK];
+    __shared__ __attribute__((aligned(1024))) u16 a2[BM * GK];
+    __shared__ __attribute__((aligned(1024))) u16 b0[BN * GK];
+    __shared__ __attribute__((aligned(1024))) u16 b1[BN * GK];
+    __shared__ __attribute__((aligned(1024))) u16 b2[BN * GK];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / NWN, wn = wave % NWN;
+    const int l16 = lane & 15, grp = lane >> 4;
+    const int tiles_m = (g.M + BM - 1) / BM, tiles_n = g.N / BN;
+    const int split = static_cast<int>(blockIdx.x) / (tiles_m * tiles_n);
+    const int id = static_cast<int>(blockIdx.x) % (tiles_m * tiles_n);
+    const int m0 = (id % tiles_m) * BM, n0 = (id / tiles_m) * BN;
+
+    f32x4 acc[TI][TJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int KT = g.K / GK / g.splits;  // K steps of this workgroup
+    const int kb = split * KT * GK;      // first K index
+    auto kof = [&](int kt) { return kb + min(kt, KT - 1) * GK; };  // past the last step: a re-read
+    panel_fill<BM, NW>(a0, g.a, m0, g.M, g.K, kof(0), wave, lane);
+    panel_fill<BN, NW>(b0, g.b, n0, g.N, g.K, kof(0), wave, lane);
+    panel_fill<BM, NW>(a1, g.a, m0, g.M, g.K, kof(1), wave, lane);
+    panel_fill<BN, NW>(b1, g.b, n0, g.N, g.K, kof(1), wave, lane);
+    __builtin_amdgcn_s_waitcnt((kIssued & 15) | ((kIssued >> 4) << 14) | (7 << 4));  // stage 0 in
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // whole groups of three steps without exits, then the remaining zero to two
+    int kt = 0;
+    for (; kt + 3 <= KT; kt += 3) {
+        split_step<WM, WN, NW>(acc, a0, b0, a2, b2, g, m0, n0, kof(kt + 2), wm, wn, wave, lane);
+        split_step<WM, WN, NW>(acc, a1, b1, a0, b0, g, m0, n0, kof(kt + 3), wm, wn, wave, lane);
+        split_step<WM, WN, NW>(acc, a2, b2, a1, b1, g, m0, n0, kof(kt + 4), wm, wn, wave, lane);
+    }
+    if (kt < KT) split_step<WM, WN, NW>(acc, a0, b0, a2, b2, g, m0, n0, kof(kt + 2), wm, wn, wave, lane);
+    if (kt + 1 < KT) split_step<WM, WN, NW>(acc, a1, b1, a0, b0, g, m0, n0, kof(kt + 3), wm, wn, wave, lane);
+    __builtin_amdgcn_s_waitcnt(0);  // the last fills (re-reads) end before the workgroup's LDS is released
+
+    float* part = g.part + static_cast<size_t>(split) * g.M * g.N;  // four consecutive columns of a row per lane
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+        const int row = m0 + wm * WM + i * 16 + l16;
+        if (row < g.M)
+#pragma unroll
+            for (int j = 0; j < TJ; ++j)
+                *reinterpret_cast<f32x4*>(part + static_cast<size_t>(row) * g.N + n0 + wn * WN + j * 16 + 4 * grp) =
+                    acc[i][j];
+    }
+}
+
+// c[m][n] = bf16(sum over splits of part[split][m][n]) in split order, 4 outputs
+// per thread; the loads of eight splits go out before their sums.
+__global__ __launch_bounds__(256) void reduce_splits_kernel(GemmArgs g) {
+    const long long e = (static_cast<long long>(blockIdx.x) * 256 + threadIdx.x) * 4;
+    const long long mn = static_cast<long long>(g.M) * g.N;
+    if (e >= mn) return;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < g.splits; s0 += 8) {
+        f32x4 t[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)  // past the last split: a re-read of it, not added
+            t[u] = __builtin_nontemporal_load(
+                reinterpret_cast<const f32x4*>(g.part + static_cast<size_t>(min(s0 + u, g.splits - 1)) * mn + e));
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (s0 + u < g.splits) acc += t[u];
+    }
+    *reinterpret_cast<uint2*>(g.c + e) = make_uint2(pack2_bf16(acc[0], acc[1]), pack2_bf16(acc[2], acc[3]));
 }
 
 }  // namespace
@@ -341,18 +442,18 @@ hipError_t launch_gemm_bt(const GemmArgs& g, hipStream_t st) {
     if (splits > 1) {  // few rows (a decode step's tokens): split K, then sum the partials
         if (!g.part || g.splits != splits) return hipErrorInvalidValue;
         const unsigned tiles = static_cast<unsigned>((g.M + 63) / 64) * (g.N / 128);
-        hipLaunchKernelGGL((gemm_bt_kernel<64, 128, kWavesM, kWavesN, true>), dim3(tiles * splits),
-                           dim3(kWavesM * kWavesN * 64), 0, st, g);
-        const long long n8 = static_cast<long long>(g.M) * g.N / 8;
-        hipLaunchKernelGGL(reduce_splits_kernel, dim3(static_cast<unsigned>((n8 + 255) / 256)), dim3(256), 0, st, g);
+        hipLaunchKernelGGL((gemm_split_kernel<kWavesM, kWavesN>), dim3(tiles * splits), dim3(kWavesM * kWavesN * 64),
+                           0, st, g);
+        const long long n4 = static_cast<long long>(g.M) * g.N / 4;
+        hipLaunchKernelGGL(reduce_splits_kernel, dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, st, g);
         return hipGetLastError();
     }
     const long long tiles_m = (g.M + 255) / 256;
     if (g.N % 256 == 0)
-        hipLaunchKernelGGL((gemm_bt_kernel<256, 256, kWavesM, kWavesN, false>),
+        hipLaunchKernelGGL((gemm_bt_kernel<256, 256, kWavesM, kWavesN>),
                            dim3(static_cast<unsigned>(tiles_m * (g.N / 256))), dim3(kWavesM * kWavesN * 64), 0, st, g);
     else
-        hipLaunchKernelGGL((gemm_bt_kernel<256, 128, kWavesM, kWavesN, false>),
+        hipLaunchKernelGGL((gemm_bt_kernel<256, 128, kWavesM, kWavesN>),
                            dim3(static_cast<unsigned>(tiles_m * (g.N / 128))), dim3(kWavesM * kWavesN * 64), 0, st, g);
     return hipGetLastError();
 }

@@ -82,6 +82,14 @@ struct StepArgs {
     int B, H, dk, dv;
     int bf16;
     int ntile;  // column tiles per (sequence, head), see recurrent_step_tiles
+    // Optional GroupNorm-and-gate epilogue (bf16, ntile == 1 only; z == nullptr: none):
+    // z[b, h*dv + c] = ((o - mean) / sqrt(var + eps) * gn_w + gn_b) * gate over the
+    // head's dv channels of the bf16 o, as groupnorm_gate_kernel computes it.
+    const u16* gate;     // [B, H*dv] bf16 or nullptr (ones)
+    const float* gn_w;   // [H*dv] or nullptr (ones)
+    const float* gn_b;   // [H*dv] or nullptr (zeros)
+    u16* z;              // [B, H*dv] bf16 out
+    float eps;
 };
 
 // Row transforms of the backward (backward.hip): one job per tensor.

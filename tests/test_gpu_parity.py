@@ -741,13 +741,26 @@ def test_msr_epilogue_few_rows_split_k(B, H, dv, d_out):
     _epi_check(B, H, 1, dv, d_out, True, True, seed=114 + B)
 
 
-@pytest.mark.parametrize("rot", [False, True])
-def test_recurrent_step_msr_matches_oracle(rot):
-    B, H, dk, dv, d_out = 5, 4, 64, 128, 256
+STEP_MSR_CASES = [
+    # B, H, dk, dv, d_out, rotation. Rows split over step workgroups (B*H < 256 and d_v a
+    # multiple of 128) take the separate GroupNorm pass, the others normalise in the step;
+    # at most 64 sequences the projection splits K, 65 run the whole-K GEMM.
+    (5, 4, 64, 128, 256, False),      # GroupNorm pass, split K
+    (5, 4, 64, 128, 256, True),
+    (1, 1, 64, 64, 128, False),       # in-step GroupNorm, one head
+    (3, 6, 64, 64, 384, True),        # in-step GroupNorm, d_v 64
+    (64, 16, 256, 512, 4096, False),  # the decode workload's shape
+    (64, 8, 128, 256, 512, True),
+    (65, 2, 64, 128, 256, False),     # GroupNorm pass, whole-K GEMM
+]
+
+
+@pytest.mark.parametrize("B,H,dk,dv,d_out,rot", STEP_MSR_CASES)
+def test_recurrent_step_msr_matches_oracle(B, H, dk, dv, d_out, rot):
     s0, qs, ks, vs = W.make_decode(B, H, dk, dv, torch.bfloat16, 1, 0.05, seed=120)
     _, w_o, gw, gb, gt = W.make_epilogue(B, H, 1, dv, d_out, 121)
     theta = W.rotary_theta(dk) if rot else None
-    pos = torch.tensor([3, 70, 0, 1_000_003, 9], dtype=torch.int64)
+    pos = torch.tensor([3, 70, 0, 1_000_003, 9] * ((B + 4) // 5), dtype=torch.int64)[:B]
     g = orc.head_gammas(H)
     o_ref, s_ref = orc.decode_step(to64(qs[0]), to64(ks[0]), to64(vs[0]), to64(s0), g,
                                    theta=None if theta is None else to64(theta), pos=pos.numpy() if rot else None)
@@ -765,6 +778,25 @@ def test_recurrent_step_msr_matches_oracle(rot):
                               gate=to64(gt))[:, 0, :]
     assert_close(to64(y), y_on_o, BF16_TOL, "y (on the step's o)", per_head_axes=0)
     assert_close(to64(y), y_ref, BF16_TOL, "y", per_head_axes=0)
+
+
+def test_recurrent_step_msr_repeats_bitwise():
+    """Consecutive steps reuse the output stage's tickets and partial tiles: the
+    same inputs give the same outputs bit for bit, call after call."""
+    B, H, dk, dv, d_out = 64, 16, 256, 512, 4096
+    s0, qs, ks, vs = W.make_decode(B, H, dk, dv, torch.bfloat16, 1, 0.05, seed=123)
+    _, w_o, gw, gb, gt = W.make_epilogue(B, H, 1, dv, d_out, 124)
+    args = [x.to(DEV) for x in (qs[0], ks[0], vs[0])]
+    kw = dict(gate=gt[:, 0, :].contiguous().to(DEV), gn_weight=gw.to(DEV), gn_bias=gb.to(DEV))
+    w_o = w_o.to(DEV)
+    outs = []
+    for _ in range(4):
+        state = s0.to(DEV)
+        y, o = R.retention_recurrent_step_msr(*args, state, w_o, **kw)
+        outs.append((y.clone(), o.clone(), state))
+    torch.cuda.synchronize()
+    for y, o, st in outs[1:]:
+        assert torch.equal(y, outs[0][0]) and torch.equal(o, outs[0][1]) and torch.equal(st, outs[0][2])
 
 
 # ------------------------------------------------------------ large chunks
