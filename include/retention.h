@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define RETENTION_ABI_VERSION 3
+#define RETENTION_ABI_VERSION 4
 #define RETENTION_MAX_HEADS 128 /* H limit (per-head constants travel in kernel arguments) */
 #define RETENTION_MAX_DK 256
 
@@ -77,7 +77,23 @@ typedef enum {
 ret_status_t retention_parallel_fwd(const void* q, const void* k, const void* v, void* o,
                                     int B, int H, int N, int dk, int dv, ret_dtype_t dtype,
                                     const float* gamma, const float* theta, int64_t pos0,
-                                    void* stream);
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of workspace retention_parallel_fwd can use for these sizes (0: it
+ * uses none). Causal work grows with a query block's position, so when the
+ * query blocks alone would leave compute units idle (bf16 without rotation,
+ * d_k 64 or 128, at most 512 blocks of 128 queries over heads and value
+ * tiles), the key walk of every query block longer than half the longest is
+ * split over two workgroups, whose float32 partial outputs meet in this
+ * workspace and the later of the two adds them. The workspace follows the
+ * chunkwise forward's contract: zero-filled before its first use, left ready
+ * by every call, calls sharing it ordered on one stream. With a NULL
+ * workspace the call runs every query block's walk in one workgroup (same
+ * result up to float32 rounding order); a workspace smaller than this size is
+ * RET_ERR_WORKSPACE.
+ */
+size_t retention_parallel_workspace_size(int B, int H, int N, int dk, int dv, ret_dtype_t dtype);
 
 /*
  * Chunkwise recurrent form ("RetNet Guide" section "3. The Chunkwise Recurrent

@@ -15,6 +15,7 @@ __all__ = [
     "HostFloats",
     "load_library",
     "retention_parallel_fwd",
+    "retention_parallel_workspace_size",
     "retention_chunkwise_fwd",
     "retention_chunkwise_fwd_timed",
     "retention_chunkwise_workspace_size",
@@ -68,8 +69,10 @@ def load_library(path=None):
         )
     lib = ctypes.CDLL(path)
     vp, i32, i64, sz, fp = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
-    lib.retention_parallel_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, fp, fp, i64, vp]
+    lib.retention_parallel_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, fp, fp, i64, vp, sz, vp]
     lib.retention_parallel_fwd.restype = i32
+    lib.retention_parallel_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.retention_parallel_workspace_size.restype = sz
     lib.retention_chunkwise_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, fp, fp, i64,
                                             vp, vp, i32, vp, sz, vp]
     lib.retention_chunkwise_fwd.restype = i32
@@ -182,8 +185,19 @@ def _raise(status, what):
         raise RetentionError(status, what)
 
 
-def retention_parallel_fwd(q, k, v, gamma=None, theta=None, pos0=0, out=None, stream=None):
-    """O = ((Q K^T) (.) D) V for q, k [B,H,N,dk] and v [B,H,N,dv] (bf16 or fp32)."""
+def retention_parallel_workspace_size(B, H, N, dk, dv, dtype):
+    torch = _torch()
+    code = RET_BF16 if dtype == torch.bfloat16 else RET_F32
+    return int(load_library().retention_parallel_workspace_size(B, H, N, dk, dv, code))
+
+
+def retention_parallel_fwd(q, k, v, gamma=None, theta=None, pos0=0, out=None, workspace=None, balanced=True,
+                           stream=None):
+    """O = ((Q K^T) (.) D) V for q, k [B,H,N,dk] and v [B,H,N,dv] (bf16 or fp32).
+
+    With balanced (the default) and no workspace given, a cached zero-filled
+    workspace lets the library split the longest causal walks over two
+    workgroups; balanced=False runs every query block's walk whole."""
     torch = _torch()
     _check_dev(q, k, v)
     B, H, N, dk = q.shape
@@ -191,10 +205,15 @@ def retention_parallel_fwd(q, k, v, gamma=None, theta=None, pos0=0, out=None, st
     if out is None:
         out = torch.empty((B, H, N, dv), dtype=v.dtype, device=v.device)
     _check_dev(out)
+    if workspace is None and balanced:
+        nbytes = retention_parallel_workspace_size(B, H, N, dk, dv, q.dtype)
+        if nbytes:
+            workspace = _cached_workspace(nbytes, v.device, stream, kind="parallel")
     _g, g = _host_floats(gamma, H, "gamma")
     _t, th = _host_floats(theta, dk // 2, "theta")
     st = load_library().retention_parallel_fwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, dk, dv, _dtype_code(q), g, th, int(pos0), _stream(stream)
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, dk, dv, _dtype_code(q), g, th, int(pos0), _ptr(workspace),
+        workspace.numel() if workspace is not None else 0, _stream(stream)
     )
     _raise(st, "retention_parallel_fwd")
     return out

@@ -750,16 +750,24 @@ ret_status_t retention_recurrent_step_msr(const void* q, const void* k, const vo
     return msr_projection(w_o, y, B, H, 1, dv, d_out, workspace, st);
 }
 
+size_t retention_parallel_workspace_size(int B, int H, int N, int dk, int dv, ret_dtype_t dtype) {
+    if (B < 1 || H < 1 || N < 1 || dk < 1 || dv < 1 || dtype != RET_BF16 || H > RETENTION_MAX_HEADS) return 0;
+    if (!ret::parallel_wide_supported(dk, dv, false)) return 0;
+    if (static_cast<long long>(N) * B * H > 2147483647LL) return 0;
+    return ret::parallel_wide_workspace(B, H, N, dv);
+}
+
 ret_status_t retention_parallel_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N,
                                     int dk, int dv, ret_dtype_t dtype, const float* gamma, const float* theta,
-                                    int64_t pos0, void* stream) {
+                                    int64_t pos0, void* workspace, size_t workspace_bytes, void* stream) {
     if (!q || !k || !v || !o) return RET_ERR_NULL;
     ret_status_t s = check_common(B, H, N, dk, dv, dtype, theta);
     if (s != RET_OK) return s;
     HeadParams hp;
     s = fill_head_params(hp, H, dk, gamma, theta);
     if (s != RET_OK) return s;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return RET_ERR_ALIGN;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace))
+        return RET_ERR_ALIGN;
     const int dvt = (dtype == RET_BF16) ? bf16_dvt(dk, dv, 128) : f32_parallel_dvt(dk, dv);
     if (dvt == 0) return RET_ERR_UNSUPPORTED;
     const long long nqb = (N + 63) / 64;
@@ -777,9 +785,17 @@ ret_status_t retention_parallel_fwd(const void* q, const void* k, const void* v,
     a.dv = dv;
     a.nvt = dv / dvt;
     a.pos0 = pos0;
+    a.split_t = 0;
+    a.part = nullptr;
+    a.ctr = nullptr;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (dtype == RET_BF16 && ret::parallel_wide_supported(dk, dv, theta != nullptr)) {
         a.nvt = dv / 128;  // the single-wave-per-SIMD kernel's 128-column value tiles
+        const size_t need = ret::parallel_wide_workspace(B, H, N, dv);
+        if (workspace && need > 0) {  // the balanced schedule; without a workspace every walk runs whole
+            if (workspace_bytes < need) return RET_ERR_WORKSPACE;
+            ret::parallel_wide_bind(a, workspace);
+        }
         return ret::launch_parallel_wide(a, hp, st) == hipSuccess ? RET_OK : RET_ERR_HIP;
     }
     const hipError_t e = (dtype == RET_BF16) ? ret::launch_parallel_bf16(a, hp, dvt, st)

@@ -70,6 +70,13 @@ struct ParallelArgs {
     int B, H, N, dk, dv;
     int nvt;
     long long pos0;
+    // balanced schedule of parallel_wide_kernel (split_t == 0: none): the key walks of
+    // query blocks longer than split_t blocks go to two workgroups, whose float32
+    // partials meet in `part` ([split block][2][128 x 128]) under ticket `ctr`
+    // ([split block], at most 256)
+    int split_t;
+    float* part;
+    unsigned* ctr;
 };
 
 struct StepArgs {
@@ -180,6 +187,12 @@ hipError_t launch_parallel_bf16(const ParallelArgs& a, const HeadParams& hp, int
 // The single-wave-per-SIMD parallel kernel (parallel_wide.hip): no rotation,
 // d_k 64 or 128, value tiles of 128 columns (a.nvt = dv / 128).
 bool parallel_wide_supported(int dk, int dv, bool rotation);
+// split threshold of parallel_wide_kernel for these sizes (0: no split) and the
+// workspace bytes it then needs
+int parallel_wide_split(int B, int H, int N, int dv);
+size_t parallel_wide_workspace(int B, int H, int N, int dv);
+// point a's split schedule at a workspace of parallel_wide_workspace bytes
+void parallel_wide_bind(ParallelArgs& a, void* workspace);
 hipError_t launch_parallel_wide(const ParallelArgs& a, const HeadParams& hp, hipStream_t st);
 hipError_t launch_parallel_f32(const ParallelArgs& a, const HeadParams& hp, int dvt, hipStream_t st);
 hipError_t launch_recurrent_step(const StepArgs& a, const HeadParams& hp, hipStream_t st);

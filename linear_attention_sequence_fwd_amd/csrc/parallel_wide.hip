@@ -18,7 +18,14 @@
 // times a per-tile factor, every exponent kept >= 0; the walk stops at the
 // first key block whose entries of D all underflow float32, since it and every
 // earlier block then add exactly zero. Query blocks are dispatched
-// longest-first.
+// longest-first. The causal work of a query block grows with its position, so
+// when the blocks alone would leave compute units idle the walk of every block
+// longer than T key blocks is split: one workgroup takes the T blocks from the
+// diagonal, another the rest, each writes its float32 partial of O to the
+// workspace, and the later of the two (by a ticket) adds the other's and
+// stores O. Retention has no softmax normaliser, so the two partials simply
+// add; a sum of two float32 values does not depend on their order, so the
+// result repeats bit for bit whichever finishes first.
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -59,6 +66,7 @@ void parallel_wide_kernel(ParallelArgs a, HeadParams hp) {
     __shared__ __attribute__((aligned(16))) u16 kb1[BQ * DK];
     __shared__ __attribute__((aligned(16))) u16 vb0[BQ * kParDvt];
     __shared__ __attribute__((aligned(16))) u16 vb1[BQ * kParDvt];
+    __shared__ unsigned s_ticket;
 
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     const int lane = threadIdx.x & 63;
@@ -67,10 +75,40 @@ void parallel_wide_kernel(ParallelArgs a, HeadParams hp) {
 
     const int nqb = (a.N + BQ - 1) / BQ;
     const int BH = a.B * a.H;
-    const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+    // Block order as dispatched: the hardware deals consecutive blocks to the eight XCDs
+    // in turn, so each XCD receives every eighth entry of the longest-first order (an even
+    // share of long and short walks), and with (batch, head, value tile) the fastest index
+    // a multiple of eight of them keeps each head's keys and values in one XCD's L2.
+    const int lb = static_cast<int>(blockIdx.x);
     const int vt = lb % a.nvt;
     const int bh = (lb / a.nvt) % BH;
-    const int qb = nqb - 1 - lb / (a.nvt * BH);
+    // Position li of this workgroup in its (batch, head, value tile)'s longest-first
+    // order. Unsplit (T = 0): query block nqb - 1 - li, whole walk. Split: first the
+    // diagonal parts of blocks nqb-1 .. T (T key blocks each), then blocks T-1 .. nqb-T
+    // alone (walks T .. nqb-T+1), then per length w = nqb-T .. 1 the block w-1 alone
+    // and the rest of block w+T-1 (key blocks T .. w+T-1 back from its diagonal).
+    const int T = a.split_t;
+    const int S = T > 0 ? nqb - T : 0;  // split query blocks
+    const int li = lb / (a.nvt * BH);
+    int qb, m_lo, m_hi, part;  // walk m_lo <= m < m_hi blocks back from the diagonal; part 0: whole
+    if (S == 0 || li < S) {
+        qb = nqb - 1 - li;
+        m_lo = 0;
+        m_hi = S == 0 ? qb + 1 : T;
+        part = S == 0 ? 0 : 1;
+    } else {
+        const int r = li - S, c1 = 2 * T - nqb;
+        if (r < c1) {
+            qb = T - 1 - r;
+            part = 0;
+        } else {
+            const int w = nqb - T - (r - c1) / 2;
+            part = ((r - c1) & 1) ? 2 : 0;
+            qb = part ? w + T - 1 : w - 1;
+        }
+        m_lo = part ? T : 0;
+        m_hi = qb + 1;
+    }
     const int h = bh % a.H;
     const float gam = hp.gamma[h];
     const double lg2 = log2_gamma(gam);
@@ -154,7 +192,7 @@ void parallel_wide_kernel(ParallelArgs a, HeadParams hp) {
 
     // key blocks with any entry of D above float32 underflow: block qb - m has
     // its largest decay gamma^(128 m - 127)
-    int nkb = qb + 1;
+    int nkb = m_hi;
     if (lg2 < 0.0) {
         const double span = 160.0 / (-lg2);  // gamma^span < 2^-160
         const int mmax = static_cast<int>((span + BQ - 1) / BQ) + 1;
@@ -272,14 +310,42 @@ void parallel_wide_kernel(ParallelArgs a, HeadParams hp) {
         }
     };
 
-    // the diagonal key block first
+    // the first key block of the walk (the diagonal one unless this is the rest of a split walk)
+    if (m_lo < nkb) {
 #pragma unroll
-    for (int i = 0; i < G::KBLK; ++i) load_keys(qb, kb0, i);
+        for (int i = 0; i < G::KBLK; ++i) load_keys(qb - m_lo, kb0, i);
 #pragma unroll
-    for (int i = 0; i < G::VBLK; ++i) load_values(qb, vb0, i);
-    for (int m = 0; m < nkb; m += 2) {
+        for (int i = 0; i < G::VBLK; ++i) load_values(qb - m_lo, vb0, i);
+    }
+    for (int m = m_lo; m < nkb; m += 2) {
         step(m, kb0, vb0, kb1, vb1);
         if (m + 1 < nkb) step(m + 1, kb1, vb1, kb0, vb0);
+    }
+
+    if (part != 0) {  // half of a split walk: publish the partial, the later half adds and stores
+        // a partial in register order: (wave, block, column tile) a 1 KiB run, lane l its
+        // 16 bytes at 16 l (the two halves share the order, so they add element by element)
+        const size_t si = (static_cast<size_t>(bh) * a.nvt + vt) * S + (qb - T);
+        constexpr int kPartBytes = BQ * kParDvt * 4;
+        const __amdgpu_buffer_rsrc_t mine = make_rsrc(a.part + (si * 2 + (part - 1)) * (BQ * kParDvt), kPartBytes);
+        const __amdgpu_buffer_rsrc_t other = make_rsrc(a.part + (si * 2 + (2 - part)) * (BQ * kParDvt), kPartBytes);
+        auto at = [&](int b, int nt) { return (((wave * 2 + b) * G::NTV + nt) * 64 + lane) * 16; };
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int nt = 0; nt < G::NTV; ++nt) store_coherent16(oacc[b][nt], mine, at(b, nt));
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial is out
+        __syncthreads();
+        if (threadIdx.x == 0)
+            s_ticket = __hip_atomic_fetch_add(a.ctr + si, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (s_ticket == 0) return;  // the other half finishes later and stores O
+        if (threadIdx.x == 0)        // both halves have counted: ready for the next call
+            __hip_atomic_store(a.ctr + si, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int nt = 0; nt < G::NTV; ++nt) oacc[b][nt] += load_coherent16(other, at(b, nt));
     }
 
     // O = O^T transposed back: lane (l16, grp) holds rows 16 blk + l16, columns 16 nt + 4 grp .. +3
@@ -300,9 +366,43 @@ bool parallel_wide_supported(int dk, int dv, bool rotation) {
     return !rotation && (dk == 64 || dk == 128) && dv % kParDvt == 0;
 }
 
+// Split the long walks when the query blocks (over heads and value tiles) are at
+// most two per compute unit: beyond that the longest-first dispatch keeps the
+// units busy by itself. T = ceil(nqb / 2): no workgroup walks more than T blocks.
+int parallel_wide_split(int B, int H, int N, int dv) {
+    const long long nqb = (static_cast<long long>(N) + kParBQ - 1) / kParBQ;
+    const long long blocks = nqb * B * H * (dv / kParDvt);
+    if (nqb < 2 || blocks > 512) return 0;
+    return static_cast<int>((nqb + 1) / 2);
+}
+
+// Workspace: the tickets first, in a region of fixed size (at most 512 query blocks,
+// of which at most half split: 256 tickets), so that calls of any sizes sharing a
+// workspace find theirs where earlier calls left tickets at zero, never partials;
+// then two float32 128 x 128 partials per split block.
+constexpr size_t kParTicketBytes = 256 * sizeof(unsigned);
+
+size_t parallel_wide_workspace(int B, int H, int N, int dv) {
+    const int T = parallel_wide_split(B, H, N, dv);
+    if (T == 0) return 0;
+    const size_t nqb = (static_cast<size_t>(N) + kParBQ - 1) / kParBQ;
+    const size_t nsplit = (nqb - T) * B * H * (dv / kParDvt);
+    return kParTicketBytes + nsplit * 2 * kParBQ * kParDvt * sizeof(float);
+}
+
+void parallel_wide_bind(ParallelArgs& a, void* workspace) {
+    a.split_t = parallel_wide_split(a.B, a.H, a.N, a.dv);
+    a.ctr = static_cast<unsigned*>(workspace);
+    a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kParTicketBytes);
+}
+
 hipError_t launch_parallel_wide(const ParallelArgs& a, const HeadParams& hp, hipStream_t st) {
     const int nqb = (a.N + kParBQ - 1) / kParBQ;
-    const dim3 grid(nqb * a.B * a.H * a.nvt), block(kParThreads);
+    if (a.split_t != 0 && (a.split_t != parallel_wide_split(a.B, a.H, a.N, a.dv) || !a.part || !a.ctr ||
+                           static_cast<size_t>(nqb - a.split_t) * a.B * a.H * a.nvt > kParTicketBytes / sizeof(unsigned)))
+        return hipErrorInvalidValue;
+    const int per = nqb + (a.split_t ? nqb - a.split_t : 0);  // workgroups per (batch, head, value tile)
+    const dim3 grid(per * a.B * a.H * a.nvt), block(kParThreads);
     if (a.dk == 128)
         hipLaunchKernelGGL(parallel_wide_kernel<128>, grid, block, 0, st, a, hp);
     else

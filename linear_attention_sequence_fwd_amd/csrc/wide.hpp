@@ -52,6 +52,19 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 // s_waitcnt lgkmcnt(0), vector memory operations left outstanding.
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
+// 16 bytes through device-coherent buffer accesses (cache policy sc1: past the
+// XCD's L2 to the device's point of coherence), for what one workgroup publishes
+// for another of the same launch. Whole 16-byte units at consecutive lane
+// addresses keep every access a full segment.
+constexpr int kCoherent = 16;  // sc1
+__device__ __forceinline__ void store_coherent16(const f32x4& v, __amdgpu_buffer_rsrc_t r, int off) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v), r,
+                                           off, 0, kCoherent);
+}
+__device__ __forceinline__ f32x4 load_coherent16(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherent));
+}
+
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
     if constexpr (B < E) {

@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.retention_abi_version() == 3
+    assert lib.retention_abi_version() == 4
     for s in range(9):
         assert len(lib.retention_status_string(s)) > 0
     assert lib.retention_status_string(123) == b"unknown status"
@@ -68,10 +68,11 @@ def chunk(lib, **kw):
 
 
 def par(lib, **kw):
-    a = dict(q=A, k=A, v=A, o=A, B=1, H=2, N=100, dk=64, dv=64, dtype=BF16, gamma=None, theta=None, pos0=0)
+    a = dict(q=A, k=A, v=A, o=A, B=1, H=2, N=100, dk=64, dv=64, dtype=BF16, gamma=None, theta=None, pos0=0,
+             ws=None, ws_bytes=0)
     a.update(kw)
     return lib.retention_parallel_fwd(a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], a["N"], a["dk"], a["dv"],
-                                      a["dtype"], a["gamma"], a["theta"], a["pos0"], None)
+                                      a["dtype"], a["gamma"], a["theta"], a["pos0"], a["ws"], a["ws_bytes"], None)
 
 
 def step(lib, **kw):
@@ -154,6 +155,27 @@ def test_workspace_contract(lib):
     # requested segments are honoured up to 512 (batch x heads x value tiles) chains, ignored beyond
     assert lib.retention_chunkwise_workspace_size(4, 128, 4096, 64, 64, BF16, 64, 4) > 0
     assert lib.retention_chunkwise_workspace_size(5, 128, 4096, 64, 64, BF16, 64, 4) == 0
+
+
+def test_parallel_workspace_contract(lib):
+    """The parallel form asks for a workspace only where it splits long causal walks: bf16 without
+    rotation at d_k 64 / 128, d_v a multiple of 128, at most 512 query blocks of 128 over heads
+    and value tiles. 4096 tokens, 8 heads of 128: 32 blocks a head, walks longer than 16 split,
+    so 16 x 8 split blocks, each with two 128 x 128 float32 partials, after a fixed region of 256
+    tickets (at most 512 blocks, at most half of them split)."""
+    need = lib.retention_parallel_workspace_size(1, 8, 4096, 128, 128, BF16)
+    assert need == 1024 + 16 * 8 * 2 * 128 * 128 * 4  # 256 tickets first, whatever the sizes
+    assert lib.retention_parallel_workspace_size(1, 8, 4096, 64, 256, BF16) == 1024 + 16 * 16 * 2 * 128 * 128 * 4
+    assert lib.retention_parallel_workspace_size(1, 8, 4096, 128, 128, F32) == 0      # the f32 kernel
+    assert lib.retention_parallel_workspace_size(1, 8, 4096, 256, 128, BF16) == 0     # d_k 256: another kernel
+    assert lib.retention_parallel_workspace_size(1, 8, 4096, 128, 64, BF16) == 0      # d_v 64: another kernel
+    assert lib.retention_parallel_workspace_size(1, 8, 128, 128, 128, BF16) == 0      # one query block a head
+    assert lib.retention_parallel_workspace_size(4, 16, 4096, 128, 128, BF16) == 0    # 2048 blocks: no split
+    assert lib.retention_parallel_workspace_size(1, 16, 4096, 128, 128, BF16) > 0     # 512 blocks: split
+    assert lib.retention_parallel_workspace_size(0, 8, 4096, 128, 128, BF16) == 0
+    # a workspace, when given, must be large enough and aligned; none is also valid (whole walks)
+    assert par(lib, H=8, N=4096, dk=128, dv=128, ws=A, ws_bytes=need - 1) == WS
+    assert par(lib, H=8, N=4096, dk=128, dv=128, ws=A + 8, ws_bytes=need) == ALIGN
 
 
 @pytest.mark.parametrize("cfg", [(1, 8, 64, 64, BF16, 64), (1, 8, 128, 128, BF16, 128), (2, 8, 64, 64, F32, 64),
