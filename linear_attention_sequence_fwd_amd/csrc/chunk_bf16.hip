@@ -39,6 +39,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "tiles.hpp"
+#include "wide.hpp"
 
 #include <cmath>
 #include <type_traits>
@@ -135,24 +136,6 @@ __device__ __forceinline__ int wave_row_block(int w) {
 constexpr unsigned kMaxLookbackSpins = 1u << 20;
 
 constexpr int imax(int x, int y) { return x > y ? x : y; }
-
-// A float4 per lane as two 8-byte halves, each half of the wavefront stored
-// contiguously (p[0..63] low halves, p[64..127] high halves), so every
-// instruction writes or reads 512 contiguous bytes.
-__device__ __forceinline__ void store_coherent(unsigned long long* p, const f32x4& v) {
-    const f32x2 lo = {v[0], v[1]}, hi = {v[2], v[3]};
-    __hip_atomic_store(p, __builtin_bit_cast(unsigned long long, lo), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(p + 64, __builtin_bit_cast(unsigned long long, hi), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ f32x4 load_coherent(unsigned long long* p) {
-    const f32x2 lo =
-        __builtin_bit_cast(f32x2, __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    const f32x2 hi =
-        __builtin_bit_cast(f32x2, __hip_atomic_load(p + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    return f32x4{lo[0], lo[1], hi[0], hi[1]};
-}
 
 // Wait until this thread's global stores have completed.
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -968,24 +951,26 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
     }
 
     // Published states are stored in accumulator order: thread (wave, lane)
-    // keeps its (mt, nt) tile as one float4, split into two 8-byte halves that
-    // are each contiguous over the wavefront, so every access is a coalesced
-    // load or store by the thread that uses the value.
+    // keeps its (mt, nt) tile as one float4 at ((wave, mt, nt) * 64 + lane) * 16
+    // bytes of the slot, so each wave instruction moves 1 KiB of consecutive
+    // bytes through 16-byte device-coherent accesses by the thread that uses
+    // the value.
     constexpr int kSlot = DK * DVT;
+    const int eoff = (wave * G::MT * G::NT * 64 + lane) * 16;
+    auto at = [&](int mt, int nt) __attribute__((always_inline)) { return eoff + (mt * G::NT + nt) * 1024; };
     auto slot = [&](int j) __attribute__((always_inline)) {
-        return reinterpret_cast<unsigned long long*>(a.agg + (static_cast<size_t>(chain) * a.nseg + j) * kSlot) +
-               wave * (G::MT * G::NT * 128) + lane;
+        return wide::make_rsrc(a.agg + (static_cast<size_t>(chain) * a.nseg + j) * kSlot, kSlot * 4);
     };
     unsigned long long* flags = a.flags + static_cast<size_t>(chain) * a.nseg * kFlagStride;
     const unsigned long long f_agg =
         (static_cast<unsigned long long>(gen + 1) << 32) | (static_cast<unsigned long long>(chain) << 1);
     const unsigned long long f_inc = f_agg | 1ull;
     auto publish = [&](const f32x4 (&st)[G::MT][G::NT], unsigned long long flag) __attribute__((always_inline)) {
-        unsigned long long* dst = slot(seg);
+        const __amdgpu_buffer_rsrc_t dst = slot(seg);
 #pragma unroll
         for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < G::NT; ++nt) store_coherent(dst + (mt * G::NT + nt) * 128, st[mt][nt]);
+            for (int nt = 0; nt < G::NT; ++nt) wide::store_coherent16(st[mt][nt], dst, at(mt, nt));
         wait_stores();
         __syncthreads();
         if (tid == 0)
@@ -1001,8 +986,7 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
     const int ngroups = (a.nseg + a.grp - 1) / a.grp;
     unsigned long long* gflags = a.gflags + static_cast<size_t>(chain) * ngroups * kFlagStride;
     auto gslot = [&](int q) __attribute__((always_inline)) {
-        return reinterpret_cast<unsigned long long*>(a.gagg + (static_cast<size_t>(chain) * ngroups + q) * kSlot) +
-               wave * (G::MT * G::NT * 128) + lane;
+        return wide::make_rsrc(a.gagg + (static_cast<size_t>(chain) * ngroups + q) * kSlot, kSlot * 4);
     };
     // Wait (wave 0, then the whole workgroup) until flags fl[lo .. hi] all read as
     // published (want_lo for index 0 of the chain's segments, else want).
@@ -1047,12 +1031,11 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
                 if (i0 + u < n) {
-                    unsigned long long* sp = src(i0 + u);
+                    const __amdgpu_buffer_rsrc_t sp = src(i0 + u);
 #pragma unroll
                     for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
-                        for (int nt = 0; nt < G::NT; ++nt)
-                            t[u][mt][nt] = load_coherent(sp + (mt * G::NT + nt) * 128);
+                        for (int nt = 0; nt < G::NT; ++nt) t[u][mt][nt] = wide::load_coherent16(sp, at(mt, nt));
                 }
             }
 #pragma unroll
@@ -1084,12 +1067,12 @@ __device__ __forceinline__ void chunk_body(const ChunkArgs& a, const HeadParams&
         if (pos == grp_sz - 1 && seg < a.nseg - 1) {  // close the group: A_q = T_s + g * (its predecessors)
             // a failed wait publishes NaN, so every later segment and the final state see it
             const float poison = failed ? NAN : 0.0f;
-            unsigned long long* dst = gslot(q);
+            const __amdgpu_buffer_rsrc_t dst = gslot(q);
 #pragma unroll
             for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
                 for (int nt = 0; nt < G::NT; ++nt)
-                    store_coherent(dst + (mt * G::NT + nt) * 128, sacc[mt][nt] + gseg * sin[mt][nt] + poison);
+                    wide::store_coherent16(sacc[mt][nt] + gseg * sin[mt][nt] + poison, dst, at(mt, nt));
             wait_stores();
             __syncthreads();
             if (tid == 0)
