@@ -5,12 +5,15 @@
 // Parallel Representation for High-Throughput Pretraining": D[n][m] =
 // gamma^(n-m) for n >= m and 0 otherwise.
 //
-// One workgroup of four waves (one per SIMD, each with the SIMD's register
-// file) owns 128 query rows of one (batch, head, 128-column value tile) and
-// walks the key blocks of 128 tokens from its diagonal block backwards. Wave w
-// owns query blocks w and 7-w (16 rows each), so every wave carries the same
-// causal work on the diagonal block, and every key or value fragment read from
-// LDS feeds two matrix instructions. Per key block, on v_mfma_f32_16x16x32_bf16:
+// One workgroup of eight waves (two per SIMD) owns 128 query rows of one
+// (batch, head, 128-column value tile) and walks the key blocks of 128 tokens
+// from its diagonal block backwards; wave w owns query rows 16 w .. 16 w + 15.
+// Each wave fits in half a SIMD's register file, so while one wave waits for
+// its LDS operands the other issues matrix instructions (one wave per SIMD
+// owning two row blocks, every fragment feeding two instructions, measured
+// 15% slower: it cannot hide the LDS latency alone). On the diagonal block
+// wave w has w + 1 causal tiles; every other block is the same work for all.
+// Per key block, on v_mfma_f32_16x16x32_bf16:
 //   G1  P^T = K Q^T, times D in registers, rounded to bf16 B operands
 //   G2  O^T += V^T P^T       (V^T by transposing LDS reads)
 // Keys and values of the next key block go from HBM straight into LDS (two
@@ -40,7 +43,7 @@ using namespace wide;
 
 constexpr int kParBQ = 128;       // query rows per workgroup, keys per key block
 constexpr int kParDvt = 128;      // value columns per workgroup
-constexpr int kParThreads = 256;  // four waves
+constexpr int kParThreads = 512;  // eight waves, two per SIMD
 constexpr int kParPipe = 4;       // steps between an LDS read and its use
 
 template <int DK>
@@ -49,15 +52,15 @@ struct ParWGeo {
     static constexpr int UV = kParDvt / 8;                    // 16-byte units per value row (of the tile)
     static constexpr int KSQ = DK / 32;                       // 32-wide contraction steps over d_k
     static constexpr int NTV = kParDvt / 16;                  // 16-column tiles of the value tile
-    static constexpr int KBLK = kParBQ * DK * 2 / 1024 / 4;   // 1 KiB key blocks per wave
-    static constexpr int VBLK = kParBQ * kParDvt * 2 / 1024 / 4;  // 1 KiB value blocks per wave
+    static constexpr int KBLK = kParBQ * DK * 2 / 1024 / 8;   // 1 KiB key blocks per wave
+    static constexpr int VBLK = kParBQ * kParDvt * 2 / 1024 / 8;  // 1 KiB value blocks per wave
     static_assert(DK == 64 || DK == 128, "key width");
 };
 
 }  // namespace
 
 template <int DK>
-__global__ __attribute__((amdgpu_flat_work_group_size(kParThreads, kParThreads), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kParThreads, kParThreads), amdgpu_waves_per_eu(2, 2)))
 void parallel_wide_kernel(ParallelArgs a, HeadParams hp) {
     using G = ParWGeo<DK>;
     constexpr int BQ = kParBQ;
@@ -163,21 +166,16 @@ void parallel_wide_kernel(ParallelArgs a, HeadParams hp) {
     };
 
     // queries of blocks wave and 7-wave: row 16 blk + l16, d_k 32 s + 8 grp
-    uint4 qf[2][G::KSQ];
+    uint4 qf[G::KSQ];
     {
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qg + static_cast<size_t>(q0) * ldk, Lq * ldk);
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int s = 0; s < G::KSQ; ++s)
-                qf[b][s] = buf_load16(rq, (16 * (b ? 7 - wave : wave) + l16) * ldk + grp * 16 + s * 64);
+        for (int s = 0; s < G::KSQ; ++s) qf[s] = buf_load16(rq, (16 * wave + l16) * ldk + grp * 16 + s * 64);
     }
-    f32x4 oacc[2][G::NTV];  // O^T: [block][column tile]
+    f32x4 oacc[G::NTV];  // O^T: [column tile]
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int nt = 0; nt < G::NTV; ++nt) oacc[b][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    uint4 pf[2][4];  // P^T (times D) as bf16 B operands: [block][32-key step]
+    for (int nt = 0; nt < G::NTV; ++nt) oacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint4 pf[4];  // P^T (times D) as bf16 B operands: [32-key step]
 
     // D = gamma^((q0 + 16 blk + l16) - (k0 + 16 kt + 4 grp + r)):
     //   diagonal tile (q0 = k0, kt = blk): dlane[r] = gamma^(l16 - 4 grp - r)
@@ -199,42 +197,37 @@ void parallel_wide_kernel(ParallelArgs a, HeadParams hp) {
         nkb = min(nkb, mmax + 1);
     }
 
-    // G1 for the wave owning blocks W and 7-W against the key block in kb
-    // (delta = q0 - k0); DIAG: the diagonal block (causal tiles only). Riding
-    // along: the next key block's keys and values into the other buffers
-    // (next < 0: none), early enough to land before the next step.
+    // G1 for the wave owning block W against the key block in kb (delta = q0 - k0);
+    // DIAG: the diagonal block (causal tiles only). Riding along: the next key
+    // block's keys and values into the other buffers (next < 0: none).
     auto g1 = [&](const u16* __restrict__ kb, u16* __restrict__ nkbuf, u16* __restrict__ nvbuf, int next, int delta,
                   auto wtag, auto diag_tag) __attribute__((always_inline)) {
-        constexpr int B0 = decltype(wtag)::value, B1 = 7 - B0;
+        constexpr int B0 = decltype(wtag)::value;
         constexpr bool DIAG = decltype(diag_tag)::value;
-        constexpr int T1 = DIAG ? B1 / 2 + 1 : 4;
         constexpr int T0 = DIAG ? B0 / 2 + 1 : 4;
-        const FragAddr<UK> fk(l16, grp);  // K rows 16 kt + l16, d_k 32 s + 8 grp
+        const FragAddr<UK> fk(l16, grp);
         struct KF {
             uint4 a, b;
         };
-        f32x4 p[4];  // tile 2t of block 7-W, tile 2t+1 of it, tile 2t of block W, tile 2t+1 of it
-        constexpr int NS1 = T1 * G::KSQ;
+        f32x4 p[2];
+        constexpr int NS1 = T0 * G::KSQ;
         pipelined<NS1, kParPipe>(
             [&](auto j) __attribute__((always_inline)) {
                 constexpr int t = decltype(j)::value / G::KSQ, s = decltype(j)::value % G::KSQ;
                 KF f;
                 f.a = *reinterpret_cast<const uint4*>(&kb[fk.at(2 * t, s)]);
-                if constexpr (!DIAG || 2 * t + 1 <= B1)
+                if constexpr (!DIAG || 2 * t + 1 <= B0)
                     f.b = *reinterpret_cast<const uint4*>(&kb[fk.at(2 * t + 1, s)]);
                 return f;
             },
             [&](auto j, const KF& f) __attribute__((always_inline)) {
                 constexpr int t = decltype(j)::value / G::KSQ, s = decltype(j)::value % G::KSQ;
-                constexpr bool two1 = !DIAG || 2 * t + 1 <= B1, one0 = t < T0, two0 = !DIAG || 2 * t + 1 <= B0;
+                constexpr bool two = !DIAG || 2 * t + 1 <= B0;
                 const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-                p[0] = mfma16x16x32(f.a, qf[1][s], s == 0 ? zero : p[0]);
-                if constexpr (two1) p[1] = mfma16x16x32(f.b, qf[1][s], s == 0 ? zero : p[1]);
-                if constexpr (one0) p[2] = mfma16x16x32(f.a, qf[0][s], s == 0 ? zero : p[2]);
-                if constexpr (two0) p[3] = mfma16x16x32(f.b, qf[0][s], s == 0 ? zero : p[3]);
+                p[0] = mfma16x16x32(f.a, qf[s], s == 0 ? zero : p[0]);
+                if constexpr (two) p[1] = mfma16x16x32(f.b, qf[s], s == 0 ? zero : p[1]);
                 if constexpr (s == G::KSQ - 1) {
-                    f32x4 r[4] = {p[0], two1 ? p[1] : zero, p[2], two0 ? p[3] : zero};
-                    // D on tile kt of block blk: the diagonal tile with the causal select
+                    f32x4 r[2] = {p[0], two ? p[1] : zero};
                     auto decay = [&](f32x4& x, int blk, int kt, bool present) __attribute__((always_inline)) {
                         if (!present) return;
                         if (DIAG && kt == blk) {
@@ -246,18 +239,11 @@ void parallel_wide_kernel(ParallelArgs a, HeadParams hp) {
                             for (int q = 0; q < 4; ++q) x[q] *= dlane15[q] * tf;
                         }
                     };
-                    // off the diagonal one instantiation serves every wave: its blocks at run time
-                    const int blk1 = DIAG ? B1 : 7 - wave, blk0 = DIAG ? B0 : wave;
-                    decay(r[0], blk1, 2 * t, true);
-                    decay(r[1], blk1, 2 * t + 1, two1);
-                    pf[1][t] = make_uint4(pack2_bf16(r[0][0], r[0][1]), pack2_bf16(r[0][2], r[0][3]),
-                                          pack2_bf16(r[1][0], r[1][1]), pack2_bf16(r[1][2], r[1][3]));
-                    if constexpr (one0) {
-                        decay(r[2], blk0, 2 * t, true);
-                        decay(r[3], blk0, 2 * t + 1, two0);
-                        pf[0][t] = make_uint4(pack2_bf16(r[2][0], r[2][1]), pack2_bf16(r[2][2], r[2][3]),
-                                              pack2_bf16(r[3][0], r[3][1]), pack2_bf16(r[3][2], r[3][3]));
-                    }
+                    const int blk0 = DIAG ? B0 : wave;
+                    decay(r[0], blk0, 2 * t, true);
+                    decay(r[1], blk0, 2 * t + 1, two);
+                    pf[t] = make_uint4(pack2_bf16(r[0][0], r[0][1]), pack2_bf16(r[0][2], r[0][3]),
+                                       pack2_bf16(r[1][0], r[1][1]), pack2_bf16(r[1][2], r[1][3]));
                 }
             },
             [&](auto j) __attribute__((always_inline)) {
@@ -268,14 +254,11 @@ void parallel_wide_kernel(ParallelArgs a, HeadParams hp) {
                 }
             });
     };
-    // G2 for the wave owning blocks W and 7-W: step j = 32-key step t = j / NTV,
-    // column tile nt = j % NTV.
     auto g2 = [&](const u16* __restrict__ vb, auto wtag, auto diag_tag) __attribute__((always_inline)) {
-        constexpr int B0 = decltype(wtag)::value, B1 = 7 - B0;
+        constexpr int B0 = decltype(wtag)::value;
         constexpr bool DIAG = decltype(diag_tag)::value;
-        constexpr int T1 = DIAG ? B1 / 2 + 1 : 4;
         constexpr int T0 = DIAG ? B0 / 2 + 1 : 4;
-        constexpr int NS2 = T1 * G::NTV;
+        constexpr int NS2 = T0 * G::NTV;
         pipelined<NS2, kParPipe>(
             [&](auto j) __attribute__((always_inline)) {
                 constexpr int t = decltype(j)::value / G::NTV, nt = decltype(j)::value % G::NTV;
@@ -283,8 +266,7 @@ void parallel_wide_kernel(ParallelArgs a, HeadParams hp) {
             },
             [&](auto j, const uint4& vf) __attribute__((always_inline)) {
                 constexpr int t = decltype(j)::value / G::NTV, nt = decltype(j)::value % G::NTV;
-                oacc[1][nt] = mfma16x16x32(vf, pf[1][t], oacc[1][nt]);
-                if constexpr (t < T0) oacc[0][nt] = mfma16x16x32(vf, pf[0][t], oacc[0][nt]);
+                oacc[nt] = mfma16x16x32(vf, pf[t], oacc[nt]);
             },
             [](auto) {});
     };
@@ -301,7 +283,11 @@ void parallel_wide_kernel(ParallelArgs a, HeadParams hp) {
                 case 0: g1(kb, nk, nv, next, delta, Ic<0>{}, Ic<1>{}); g2(vb, Ic<0>{}, Ic<1>{}); break;
                 case 1: g1(kb, nk, nv, next, delta, Ic<1>{}, Ic<1>{}); g2(vb, Ic<1>{}, Ic<1>{}); break;
                 case 2: g1(kb, nk, nv, next, delta, Ic<2>{}, Ic<1>{}); g2(vb, Ic<2>{}, Ic<1>{}); break;
-                default: g1(kb, nk, nv, next, delta, Ic<3>{}, Ic<1>{}); g2(vb, Ic<3>{}, Ic<1>{}); break;
+                case 3: g1(kb, nk, nv, next, delta, Ic<3>{}, Ic<1>{}); g2(vb, Ic<3>{}, Ic<1>{}); break;
+                case 4: g1(kb, nk, nv, next, delta, Ic<4>{}, Ic<1>{}); g2(vb, Ic<4>{}, Ic<1>{}); break;
+                case 5: g1(kb, nk, nv, next, delta, Ic<5>{}, Ic<1>{}); g2(vb, Ic<5>{}, Ic<1>{}); break;
+                case 6: g1(kb, nk, nv, next, delta, Ic<6>{}, Ic<1>{}); g2(vb, Ic<6>{}, Ic<1>{}); break;
+                default: g1(kb, nk, nv, next, delta, Ic<7>{}, Ic<1>{}); g2(vb, Ic<7>{}, Ic<1>{}); break;
             }
         } else {
             // off the diagonal every wave does the same work
@@ -329,11 +315,9 @@ void parallel_wide_kernel(ParallelArgs a, HeadParams hp) {
         constexpr int kPartBytes = BQ * kParDvt * 4;
         const __amdgpu_buffer_rsrc_t mine = make_rsrc(a.part + (si * 2 + (part - 1)) * (BQ * kParDvt), kPartBytes);
         const __amdgpu_buffer_rsrc_t other = make_rsrc(a.part + (si * 2 + (2 - part)) * (BQ * kParDvt), kPartBytes);
-        auto at = [&](int b, int nt) { return (((wave * 2 + b) * G::NTV + nt) * 64 + lane) * 16; };
+        auto at = [&](int nt) { return ((wave * G::NTV + nt) * 64 + lane) * 16; };
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int nt = 0; nt < G::NTV; ++nt) store_coherent16(oacc[b][nt], mine, at(b, nt));
+        for (int nt = 0; nt < G::NTV; ++nt) store_coherent16(oacc[nt], mine, at(nt));
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial is out
         __syncthreads();
         if (threadIdx.x == 0)
@@ -343,22 +327,16 @@ void parallel_wide_kernel(ParallelArgs a, HeadParams hp) {
         if (threadIdx.x == 0)        // both halves have counted: ready for the next call
             __hip_atomic_store(a.ctr + si, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int nt = 0; nt < G::NTV; ++nt) oacc[b][nt] += load_coherent16(other, at(b, nt));
+        for (int nt = 0; nt < G::NTV; ++nt) oacc[nt] += load_coherent16(other, at(nt));
     }
 
     // O = O^T transposed back: lane (l16, grp) holds rows 16 blk + l16, columns 16 nt + 4 grp .. +3
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(Og + static_cast<size_t>(q0) * ldv, (Lq - 1) * ldv + tile_bytes);
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        const int blk = b ? 7 - wave : wave;
-#pragma unroll
-        for (int nt = 0; nt < G::NTV; ++nt) {
-            const f32x4 o = oacc[b][nt];
-            buf_store8(make_uint2(pack2_bf16(o[0], o[1]), pack2_bf16(o[2], o[3])), ro,
-                       (16 * blk + l16) * ldv + grp * 8 + nt * 32);
-        }
+    for (int nt = 0; nt < G::NTV; ++nt) {
+        const f32x4 o = oacc[nt];
+        buf_store8(make_uint2(pack2_bf16(o[0], o[1]), pack2_bf16(o[2], o[3])), ro,
+                   (16 * wave + l16) * ldv + grp * 8 + nt * 32);
     }
 }
 
