@@ -20,13 +20,14 @@
 // the largest R in {8, 4, 2, 1} with gamma^(R C) >= 2^-64 for every head,
 // which keeps every factor far inside the float32 range.
 //
-// One workgroup of four waves (one per SIMD, each with the SIMD's whole
-// register file) owns one (batch, head, value tile) and walks its chunks in
-// order. Wave w owns query blocks w and 7-w (16 tokens each), so every wave
-// carries the same causal work, and every state fragment read from LDS feeds
-// two matrix instructions (one per block). The float32 state is split over the
-// waves by d_k rows: wave w holds rows [w d_k/4, (w+1) d_k/4) of all 128
-// columns in MFMA accumulators. Per chunk, on v_mfma_f32_16x16x32_bf16:
+// One workgroup of eight waves (two per SIMD, each in half the SIMD's register
+// file) owns one (batch, head, value tile) and walks its chunks in order. Wave
+// w owns query block w (16 tokens), so on the causal tiles wave w has w + 1;
+// while one wave of a SIMD waits for its LDS operands the other issues matrix
+// instructions (four waves owning two blocks each, every fragment feeding two
+// instructions, measured 6% slower). The float32 state is split over the waves
+// by d_k rows: wave w holds rows [w d_k/8, (w+1) d_k/8) of all 128 columns in
+// MFMA accumulators. Per chunk, on v_mfma_f32_16x16x32_bf16:
 //   G3  O^T  = A^T Q^T                    (bf16 copy of A^T in LDS)
 //   G1  P^T  = K Q^T, causal select on the diagonal tiles
 //   G2  O^T += V3^T P^T                   (V3^T by transposing LDS reads)
@@ -55,7 +56,7 @@ using namespace wide;
 
 constexpr int kWideC = 128;            // tokens per chunk
 constexpr int kWideDvt = 128;          // value columns per workgroup
-constexpr int kWideThreads = 256;      // four waves
+constexpr int kWideThreads = 512;      // eight waves, two per SIMD
 constexpr int kPipeDepth = 4;          // steps between an LDS read and its use
 
 template <int DK>
@@ -64,17 +65,17 @@ struct WideGeo {
     static constexpr int UV = kWideDvt / 8;                // 16-byte units per value row (of the tile)
     static constexpr int KSQ = DK / 32;                    // 32-wide contraction steps over d_k
     static constexpr int NTV = kWideDvt / 16;              // 16-column tiles of the value tile
-    static constexpr int MT = DK / 64;                     // 16-row state tiles per wave
+    static constexpr int MT = DK / 128;                    // 16-row state tiles per wave
     static constexpr int VU = kWideC * UV / kWideThreads;  // value units per thread
     static constexpr int VROWS = kWideThreads / UV;        // value rows per load step
-    static constexpr int KBLK = kWideC * DK * 2 / 1024 / 4;  // 1 KiB key blocks per wave
+    static constexpr int KBLK = kWideC * DK * 2 / 1024 / 8;  // 1 KiB key blocks per wave
     static_assert(DK == 128 || DK == 256, "key width");
 };
 
 }  // namespace
 
 template <int DK>
-__global__ __attribute__((amdgpu_flat_work_group_size(kWideThreads, kWideThreads), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kWideThreads, kWideThreads), amdgpu_waves_per_eu(2, 2)))
 void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
     using G = WideGeo<DK>;
     constexpr int C = kWideC;
@@ -123,13 +124,13 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
     const int ldv = a.dv * 2;    // value / output row stride, bytes
     constexpr int ldk = DK * 2;  // key / query row stride, bytes
     constexpr int tile_bytes = kWideDvt * 2;
-    const int d0 = wave * (DK / 4);  // this wave's state rows
+    const int d0 = wave * (DK / 8);  // this wave's state rows
 
     uint4 vst[G::VU];           // the next chunk's values (scaled to V3 in registers before staging)
-    uint4 qf[2][G::KSQ];        // queries of blocks wave and 7-wave: row 16 blk + l16, d_k 32 s + 8 grp
+    uint4 qf[G::KSQ];           // queries of block wave: row 16 wave + l16, d_k 32 s + 8 grp
     f32x4 sacc[G::MT][G::NTV];  // A: rows d0 + 16 mt + 4 grp + r, columns 16 nt + l16
-    f32x4 oacc[2][G::NTV];      // O^T: [block][column tile]
-    uint4 pf[2][4];             // P^T as bf16 B operands: [block][32-key step]
+    f32x4 oacc[G::NTV];         // O^T: [column tile]
+    uint4 pf[4];                // P^T as bf16 B operands: [32-key step]
 
     // Buffer resources of a chunk (t: first token, L valid rows): loads past
     // the last valid row read as zero, stores past it are dropped.
@@ -159,11 +160,9 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
     auto load_value_unit = [&](__amdgpu_buffer_rsrc_t rv, int j) __attribute__((always_inline)) {
         vst[j] = buf_load16(rv, (tid / G::UV + j * G::VROWS) * ldv + (tid % G::UV) * 16);
     };
-    // query unit q = b * KSQ + s
-    auto load_q_unit = [&](__amdgpu_buffer_rsrc_t rq, int q) __attribute__((always_inline)) {
-        const int b = q / G::KSQ, s = q % G::KSQ;
-        const int blk = b ? 7 - wave : wave;
-        qf[b][s] = buf_load16(rq, (16 * blk + l16) * ldk + grp * 16 + s * 64);
+    // query unit s
+    auto load_q_unit = [&](__amdgpu_buffer_rsrc_t rq, int s) __attribute__((always_inline)) {
+        qf[s] = buf_load16(rq, (16 * wave + l16) * ldk + grp * 16 + s * 64);
     };
     // value unit j to V3 (tau0: group offset of the chunk's first token)
     auto scale_value_unit = [&](int j, int tau0) __attribute__((always_inline)) {
@@ -201,37 +200,34 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
         return make_uint4(lo.x, lo.y, hi.x, hi.y);
     };
 
-    // G1 and G2 for the wave owning blocks W and 7-W. The next chunk's keys go
-    // into LDS during G1.
+    // G1 and G2 for the wave owning block W. The next chunk's keys go into LDS during G1.
     auto g12 = [&](const u16* __restrict__ kb, u16* __restrict__ next_kb, __amdgpu_buffer_rsrc_t rk, auto wtag)
                    __attribute__((always_inline)) {
-        constexpr int B0 = decltype(wtag)::value, B1 = 7 - B0;
-        constexpr int T0 = B0 / 2 + 1, T1 = B1 / 2 + 1;
+        constexpr int B0 = decltype(wtag)::value;
+        constexpr int T0 = B0 / 2 + 1;
         const FragAddr<UK> fk(l16, grp);  // K rows 16 kt + l16, d_k 32 s + 8 grp
         // G1, step j: 32-key step t = j / KSQ (key tiles 2t, 2t+1), d_k step s = j % KSQ
         struct KF {
             uint4 a, b;
         };
-        f32x4 p[4];  // tile 2t of block 7-W, tile 2t+1 of it, tile 2t of block W, tile 2t+1 of it
-        constexpr int NS1 = T1 * G::KSQ;
+        f32x4 p[2];  // tiles 2t and 2t+1
+        constexpr int NS1 = T0 * G::KSQ;
         pipelined<NS1, kPipeDepth>(
             [&](auto j) __attribute__((always_inline)) {
                 constexpr int t = decltype(j)::value / G::KSQ, s = decltype(j)::value % G::KSQ;
                 KF f;
                 f.a = *reinterpret_cast<const uint4*>(&kb[fk.at(2 * t, s)]);
-                if constexpr (2 * t + 1 <= B1) f.b = *reinterpret_cast<const uint4*>(&kb[fk.at(2 * t + 1, s)]);
+                if constexpr (2 * t + 1 <= B0) f.b = *reinterpret_cast<const uint4*>(&kb[fk.at(2 * t + 1, s)]);
                 return f;
             },
             [&](auto j, const KF& f) __attribute__((always_inline)) {
                 constexpr int t = decltype(j)::value / G::KSQ, s = decltype(j)::value % G::KSQ;
-                constexpr bool two1 = 2 * t + 1 <= B1, one0 = t < T0, two0 = 2 * t + 1 <= B0;
+                constexpr bool two = 2 * t + 1 <= B0;
                 const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-                p[0] = mfma16x16x32(f.a, qf[1][s], s == 0 ? zero : p[0]);
-                if constexpr (two1) p[1] = mfma16x16x32(f.b, qf[1][s], s == 0 ? zero : p[1]);
-                if constexpr (one0) p[2] = mfma16x16x32(f.a, qf[0][s], s == 0 ? zero : p[2]);
-                if constexpr (two0) p[3] = mfma16x16x32(f.b, qf[0][s], s == 0 ? zero : p[3]);
+                p[0] = mfma16x16x32(f.a, qf[s], s == 0 ? zero : p[0]);
+                if constexpr (two) p[1] = mfma16x16x32(f.b, qf[s], s == 0 ? zero : p[1]);
                 if constexpr (s == G::KSQ - 1) {
-                    f32x4 r[4] = {p[0], two1 ? p[1] : zero, p[2], two0 ? p[3] : zero};
+                    f32x4 r[2] = {p[0], two ? p[1] : zero};
                     // causal select on diagonal tiles: key 16 kt + 4 grp + q vs token 16 blk + l16
                     auto mask = [&](f32x4& x, bool diag) __attribute__((always_inline)) {
                         if (diag) {
@@ -239,23 +235,17 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
                             for (int q = 0; q < 4; ++q) x[q] = (4 * grp + q <= l16) ? x[q] : 0.0f;
                         }
                     };
-                    mask(r[0], 2 * t == B1);
-                    mask(r[1], 2 * t + 1 == B1);
-                    pf[1][t] = make_uint4(pack2_bf16(r[0][0], r[0][1]), pack2_bf16(r[0][2], r[0][3]),
-                                          pack2_bf16(r[1][0], r[1][1]), pack2_bf16(r[1][2], r[1][3]));
-                    if constexpr (one0) {
-                        mask(r[2], 2 * t == B0);
-                        mask(r[3], 2 * t + 1 == B0);
-                        pf[0][t] = make_uint4(pack2_bf16(r[2][0], r[2][1]), pack2_bf16(r[2][2], r[2][3]),
-                                              pack2_bf16(r[3][0], r[3][1]), pack2_bf16(r[3][2], r[3][3]));
-                    }
+                    mask(r[0], 2 * t == B0);
+                    mask(r[1], 2 * t + 1 == B0);
+                    pf[t] = make_uint4(pack2_bf16(r[0][0], r[0][1]), pack2_bf16(r[0][2], r[0][3]),
+                                       pack2_bf16(r[1][0], r[1][1]), pack2_bf16(r[1][2], r[1][3]));
                 }
             },
             [&](auto j) __attribute__((always_inline)) {
                 spread<G::KBLK, NS1, decltype(j)::value>([&](auto i) { load_key_block(rk, next_kb, i); });
             });
         // G2, step j: 32-key step t = j / NTV, column tile nt = j % NTV
-        constexpr int NS2 = T1 * G::NTV;
+        constexpr int NS2 = T0 * G::NTV;
         pipelined<NS2, kPipeDepth>(
             [&](auto j) __attribute__((always_inline)) {
                 constexpr int t = decltype(j)::value / G::NTV, nt = decltype(j)::value % G::NTV;
@@ -263,8 +253,7 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
             },
             [&](auto j, const uint4& vf) __attribute__((always_inline)) {
                 constexpr int t = decltype(j)::value / G::NTV, nt = decltype(j)::value % G::NTV;
-                oacc[1][nt] = mfma16x16x32(vf, pf[1][t], oacc[1][nt]);
-                if constexpr (t < T0) oacc[0][nt] = mfma16x16x32(vf, pf[0][t], oacc[0][nt]);
+                oacc[nt] = mfma16x16x32(vf, pf[t], oacc[nt]);
             },
             [](auto) {});
     };
@@ -273,7 +262,7 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
     // that step's key fragments. Riding along: the chunk's outputs (scaled by
     // z, rounded and stored), the next chunk's query loads and the scaling of
     // its values (tau_next: their group offset).
-    auto g4 = [&](const u16* kb, __amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rq, const float (&z)[2],
+    auto g4 = [&](const u16* kb, __amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rq, float z,
                   int tau_next) __attribute__((always_inline)) {
         struct F4 {
             uint4 v;
@@ -303,14 +292,13 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
             },
             [&](auto j) __attribute__((always_inline)) {
                 constexpr int J = decltype(j)::value;
-                spread<2 * G::NTV, NS4, J>([&](auto i) {
-                    constexpr int b = decltype(i)::value / G::NTV, nt = decltype(i)::value % G::NTV;
-                    const int blk = b ? 7 - wave : wave;
-                    const f32x4 o = oacc[b][nt];
-                    const uint2 w = make_uint2(pack2_bf16(o[0] * z[b], o[1] * z[b]), pack2_bf16(o[2] * z[b], o[3] * z[b]));
-                    buf_store8(w, ro, (16 * blk + l16) * ldv + grp * 8 + nt * 32);
+                spread<G::NTV, NS4, J>([&](auto i) {
+                    constexpr int nt = decltype(i)::value;
+                    const f32x4 o = oacc[nt];
+                    const uint2 w = make_uint2(pack2_bf16(o[0] * z, o[1] * z), pack2_bf16(o[2] * z, o[3] * z));
+                    buf_store8(w, ro, (16 * wave + l16) * ldv + grp * 8 + nt * 32);
                 });
-                spread<2 * G::KSQ, NS4, J>([&](auto i) { load_q_unit(rq, i); });
+                spread<G::KSQ, NS4, J>([&](auto i) { load_q_unit(rq, i); });
                 spread<G::VU, NS4, J>([&](auto i) { scale_value_unit(decltype(i)::value, tau_next); });
             });
     };
@@ -324,7 +312,7 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
 #pragma unroll
         for (int i = 0; i < G::KBLK; ++i) load_key_block(rk, pb0, i);
 #pragma unroll
-        for (int i = 0; i < 2 * G::KSQ; ++i) load_q_unit(rq, i);
+        for (int i = 0; i < G::KSQ; ++i) load_q_unit(rq, i);
         // the per-chunk wait before barrier A counts the operations issued after
         // a chunk's key loads in the loop; the first chunk's are waited for here
         wait_vm_lgkm0<0>();
@@ -368,14 +356,12 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
         // the previous chunk's output stores and the queries, both during its G4;
         // every chunk issues the same operations, past the end as re-reads);
         // V3 and the state copy are written
-        wait_vm_lgkm0<2 * G::KSQ + 2 * G::NTV>();
+        wait_vm_lgkm0<G::KSQ + G::NTV>();
         __builtin_amdgcn_s_barrier();
 
         // ---- G3: O^T = A^T Q^T (the state before this chunk); the next chunk's values load meanwhile
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int nt = 0; nt < G::NTV; ++nt) oacc[b][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < G::NTV; ++nt) oacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
         const __amdgpu_buffer_rsrc_t rv = value_rsrc(t1, L1);
         if (have_state) {
             const FragAddr<UK> fs(l16, grp);  // A^T rows 16 nt + l16, d_k 32 s + 8 grp
@@ -388,8 +374,7 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
                 },
                 [&](auto j, const uint4& af) __attribute__((always_inline)) {
                     constexpr int s = decltype(j)::value / G::NTV, nt = decltype(j)::value % G::NTV;
-                    oacc[0][nt] = mfma16x16x32(af, qf[0][s], oacc[0][nt]);
-                    oacc[1][nt] = mfma16x16x32(af, qf[1][s], oacc[1][nt]);
+                    oacc[nt] = mfma16x16x32(af, qf[s], oacc[nt]);
                 },
                 [&](auto j) __attribute__((always_inline)) {
                     spread<G::VU, NS3, decltype(j)::value>([&](auto i) { load_value_unit(rv, i); });
@@ -408,14 +393,15 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
             case 0: g12(kb, sb, rk, Ic<0>{}); break;
             case 1: g12(kb, sb, rk, Ic<1>{}); break;
             case 2: g12(kb, sb, rk, Ic<2>{}); break;
-            default: g12(kb, sb, rk, Ic<3>{}); break;
+            case 3: g12(kb, sb, rk, Ic<3>{}); break;
+            case 4: g12(kb, sb, rk, Ic<4>{}); break;
+            case 5: g12(kb, sb, rk, Ic<5>{}); break;
+            case 6: g12(kb, sb, rk, Ic<6>{}); break;
+            default: g12(kb, sb, rk, Ic<7>{}); break;
         }
 
         // ---- G4, with the outputs O = gamma^(tau + 1) O^T stored as bf16 meanwhile
-        float z[2];
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-            z[b] = fast_exp2(static_cast<float>(tau0 + 16 * (b ? 7 - wave : wave) + l16 + 1) * lg2f);
+        const float z = fast_exp2(static_cast<float>(tau0 + 16 * wave + l16 + 1) * lg2f);
         tau0 += L;
         const bool group_end = tau0 >= R * C || !has_next;
         g4(kb, out_rsrc(t0, L), q_rsrc(t1, L1), z, group_end ? 0 : tau0);
