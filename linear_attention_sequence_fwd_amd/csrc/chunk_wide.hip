@@ -22,7 +22,8 @@
 //
 // One workgroup of eight waves (two per SIMD, each in half the SIMD's register
 // file) owns one (batch, head, value tile) and walks its chunks in order. Wave
-// w owns query block w (16 tokens), so on the causal tiles wave w has w + 1;
+// w owns one query block of 16 tokens (w, or 11 - w for w >= 4, so that the two
+// waves of a SIMD carry blocks b and 7 - b and every SIMD the same causal work);
 // while one wave of a SIMD waits for its LDS operands the other issues matrix
 // instructions (four waves owning two blocks each, every fragment feeding two
 // instructions, measured 6% slower). The float32 state is split over the waves
@@ -125,6 +126,10 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
     constexpr int ldk = DK * 2;  // key / query row stride, bytes
     constexpr int tile_bytes = kWideDvt * 2;
     const int d0 = wave * (DK / 8);  // this wave's state rows
+    // this wave's query block: waves w and w + 4 share a SIMD (a workgroup's waves
+    // are dealt to the SIMDs in turn), so they take blocks w and 7 - w and every
+    // SIMD carries the same causal work
+    const int qblk = wave < 4 ? wave : 11 - wave;
 
     uint4 vst[G::VU];           // the next chunk's values (scaled to V3 in registers before staging)
     uint4 qf[G::KSQ];           // queries of block wave: row 16 wave + l16, d_k 32 s + 8 grp
@@ -162,7 +167,7 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
     };
     // query unit s
     auto load_q_unit = [&](__amdgpu_buffer_rsrc_t rq, int s) __attribute__((always_inline)) {
-        qf[s] = buf_load16(rq, (16 * wave + l16) * ldk + grp * 16 + s * 64);
+        qf[s] = buf_load16(rq, (16 * qblk + l16) * ldk + grp * 16 + s * 64);
     };
     // value unit j to V3 (tau0: group offset of the chunk's first token)
     auto scale_value_unit = [&](int j, int tau0) __attribute__((always_inline)) {
@@ -296,7 +301,7 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
                     constexpr int nt = decltype(i)::value;
                     const f32x4 o = oacc[nt];
                     const uint2 w = make_uint2(pack2_bf16(o[0] * z, o[1] * z), pack2_bf16(o[2] * z, o[3] * z));
-                    buf_store8(w, ro, (16 * wave + l16) * ldv + grp * 8 + nt * 32);
+                    buf_store8(w, ro, (16 * qblk + l16) * ldv + grp * 8 + nt * 32);
                 });
                 spread<G::KSQ, NS4, J>([&](auto i) { load_q_unit(rq, i); });
                 spread<G::VU, NS4, J>([&](auto i) { scale_value_unit(decltype(i)::value, tau_next); });
@@ -389,7 +394,7 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
 
         // ---- G1, G2 (the wave's blocks decide the causal extent)
         const __amdgpu_buffer_rsrc_t rk = key_rsrc(t1, L1);
-        switch (wave) {
+        switch (qblk) {
             case 0: g12(kb, sb, rk, Ic<0>{}); break;
             case 1: g12(kb, sb, rk, Ic<1>{}); break;
             case 2: g12(kb, sb, rk, Ic<2>{}); break;
@@ -401,7 +406,7 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
         }
 
         // ---- G4, with the outputs O = gamma^(tau + 1) O^T stored as bf16 meanwhile
-        const float z = fast_exp2(static_cast<float>(tau0 + 16 * wave + l16 + 1) * lg2f);
+        const float z = fast_exp2(static_cast<float>(tau0 + 16 * qblk + l16 + 1) * lg2f);
         tau0 += L;
         const bool group_end = tau0 >= R * C || !has_next;
         g4(kb, out_rsrc(t0, L), q_rsrc(t1, L1), z, group_end ? 0 : tau0);
