@@ -194,6 +194,7 @@ void fill_chunk_args(ret::ChunkArgs& a, const void* q, const void* k, const void
     a.rev = 0;
     a.orot = 0;
     a.rescale = 1;
+    a.ldqk = 0;
 }
 
 // Workspace of the backward: one forward-workspace region per pass first (each
@@ -500,11 +501,18 @@ ret_status_t retention_chunkwise_bwd(const void* q, const void* k, const void* v
         char* dob = doa + static_cast<size_t>(B) * H * N * hv * 2;
         char* va = ws + b.vh;
         char* vb = va + static_cast<size_t>(B) * H * N * hv * 2;
+        // 128-token chunks with key widths of 128 or 256 (passes 1 and 2 keyed by hv, pass 3 by
+        // dk, equal) and value widths that are multiples of 128: every pass runs on the wide
+        // chunkwise kernel, all in one launch, when together they fill the chip; the split
+        // passes then read their halves of dO and V in place
+        const long long wide_chains = (b.split ? 4LL : 2LL) * B * H * (dk / 128) + 1LL * B * H * (dv / 128);
+        const bool wide = chunk == 128 && hv == dk && (dk == 128 || dk == 256) && dv % 128 == 0 &&
+                          ret::chunk_wide_rescale(hp, H) > 0 && wide_chains >= kTargetBlocks;
         if (rot) {
             rj.j[rj.n++] = {q, qf, nullptr, dk, 0, 1, 0, 0, 0, nullptr};
             rj.j[rj.n++] = {k, kr, nullptr, dk, 0, 1, 0, 0, 0, nullptr};
         }
-        if (b.split) {
+        if (b.split && !wide) {
             rj.j[rj.n++] = {d_o, doa, nullptr, hv, 0, 0, 0, dv, 0, nullptr};
             rj.j[rj.n++] = {d_o, dob, nullptr, hv, 0, 0, 0, dv, hv, nullptr};
             rj.j[rj.n++] = {v, va, nullptr, hv, 0, 0, 0, dv, 0, nullptr};
@@ -516,6 +524,55 @@ ret_status_t retention_chunkwise_bwd(const void* q, const void* k, const void* v
         if (s != RET_OK) return s;
         const void* kp = rot ? kr : k;  // K'
         const void* qp = rot ? qf : q;  // Q'
+        HeadParams hp_passes = hp;
+        hp_passes.has_theta = 0;
+        if (wide) {
+            ChunkPlan pw;
+            memset(&pw, 0, sizeof(pw));
+            pw.tile = 128;
+            pw.dvt = 128;
+            pw.nseg = 1;
+            pw.seg_len = N;
+            pw.grp = 1;
+            auto call = [&](ret::ChunkArgs& a, const void* aq, const void* ak, const void* av, void* ao, int vw,
+                            const float* sin, float* sout, int rev, int ldqk) {
+                pw.nvt = vw / 128;
+                fill_chunk_args(a, aq, ak, av, ao, B, H, N, dk, vw, chunk, 0, sin, sout, pw, nullptr);
+                a.rev = rev;
+                a.ldqk = ldqk;
+            };
+            // column block `half` of a [B,H,N,dv] bf16 tensor, read with row stride dv
+            auto half_of = [&](const void* t, int half) {
+                return static_cast<const void*>(static_cast<const char*>(t) + static_cast<size_t>(half) * hv * 2);
+            };
+            ret::ChunkCalls cw;
+            memset(&cw, 0, sizeof(cw));
+            const size_t xh = static_cast<size_t>(B) * H * hv * dk;  // floats in one half of a split state
+            if (b.split) {
+                call(cw.a[0], half_of(d_o, 0), half_of(v, 0), kp, d_q, dk, sx1, nullptr, 0, dv);
+                call(cw.a[1], half_of(d_o, 1), half_of(v, 1), kp, ws + b.t1, dk, sx1 ? sx1 + xh : nullptr, nullptr, 0,
+                     dv);
+                call(cw.a[2], half_of(v, 0), half_of(d_o, 0), qp, d_k, dk, sx2, nullptr, 1, dv);
+                call(cw.a[3], half_of(v, 1), half_of(d_o, 1), qp, ws + b.t2, dk, sx2 ? sx2 + xh : nullptr, nullptr, 1,
+                     dv);
+                cw.n = 4;
+            } else {
+                call(cw.a[0], d_o, v, kp, d_q, dk, sx1, nullptr, 0, 0);
+                call(cw.a[1], v, d_o, qp, d_k, dk, sx2, nullptr, 1, 0);
+                cw.n = 2;
+            }
+            call(cw.a[cw.n++], kp, qp, d_o, d_v, dv, sx3, d_state_in, 1, 0);
+            if (ret::launch_chunk_wide_multi(cw, hp_passes, st) != hipSuccess) return RET_ERR_HIP;
+            if (b.split || rot) {  // dQ = R^-1 (dQ'_a + dQ'_b), dK likewise (in place)
+                memset(&rj.j, 0, sizeof(rj.j));
+                rj.nzero = 0;
+                rj.n = 2;
+                rj.j[0] = {d_q, d_q, nullptr, dk, 0, rot ? -1 : 0, 0, 0, 0, b.split ? ws + b.t1 : nullptr};
+                rj.j[1] = {d_k, d_k, nullptr, dk, 0, rot ? -1 : 0, 0, 0, 0, b.split ? ws + b.t2 : nullptr};
+                if (ret::launch_rows(rj, hp, bf16, st) != hipSuccess) return RET_ERR_HIP;
+            }
+            return finish_states();
+        }
         ChunkPlan p1, p3;  // key width hv (passes 1, 2) and dk (pass 3)
         s = plan_chunk(B, H, N, hv, dk, dtype, chunk, 0, p1);
         if (s != RET_OK) return s;
@@ -538,8 +595,6 @@ ret_status_t retention_chunkwise_bwd(const void* q, const void* k, const void* v
         // with rotation and no dv split the first two passes rotate their outputs back when the
         // frequencies fit in LDS beside their tiles; otherwise a row kernel does it afterwards
         const bool orot = rot && !b.split && ret::chunk_orot_fits(dv, p1.dvt, p1.tile);
-        HeadParams hp_passes = hp;
-        hp_passes.has_theta = 0;
         ret::ChunkCalls cs;
         ret::ChunkArgs a3;
         const size_t xh = static_cast<size_t>(B) * H * hv * dk;  // floats in one half of a split state

@@ -75,9 +75,13 @@ struct WideGeo {
 
 }  // namespace
 
-template <int DK>
-__global__ __attribute__((amdgpu_flat_work_group_size(kWideThreads, kWideThreads), amdgpu_waves_per_eu(2, 2)))
-void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
+namespace {
+
+// One call's chain `chain` (batch x head x value tile). MULTI only tells the
+// two kernels' copies apart (each kernel its own specialization, as each
+// holds its own LDS).
+template <int DK, bool MULTI>
+__device__ __forceinline__ void chunk_wide_body(const ChunkArgs& a, const HeadParams& hp, const int chain) {
     using G = WideGeo<DK>;
     constexpr int C = kWideC;
     constexpr int UK = G::UK;
@@ -104,8 +108,6 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
         grp = (t & 63) >> 4;
     };
 
-    // (batch, head, value tile); the value tiles of one head run on one XCD
-    const int chain = xcd_logical_block(blockIdx.x, gridDim.x);
     const int vt = chain % a.nvt;
     const int bh = chain / a.nvt;
     const int h = bh % a.H;
@@ -118,12 +120,13 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
     const float g_group = gamma_pow(lg2, static_cast<double>(R) * C);  // gamma^(R C)
 
     const size_t tok0 = static_cast<size_t>(bh) * N;
-    const char* Kg = reinterpret_cast<const char*>(a.k + tok0 * DK);
-    const char* Qg = reinterpret_cast<const char*>(a.q + tok0 * DK);
+    const int ldqk = a.ldqk > 0 ? a.ldqk : DK;  // query / key row stride, elements
+    const char* Kg = reinterpret_cast<const char*>(a.k + tok0 * ldqk);
+    const char* Qg = reinterpret_cast<const char*>(a.q + tok0 * ldqk);
     const char* Vg = reinterpret_cast<const char*>(a.v + tok0 * a.dv + vt * kWideDvt);
     char* Og = reinterpret_cast<char*>(a.o + tok0 * a.dv + vt * kWideDvt);
     const int ldv = a.dv * 2;    // value / output row stride, bytes
-    constexpr int ldk = DK * 2;  // key / query row stride, bytes
+    const int ldk = ldqk * 2;  // key / query row stride, bytes
     constexpr int tile_bytes = kWideDvt * 2;
     const int d0 = wave * (DK / 8);  // this wave's state rows
     // this wave's query block: waves w and w + 4 share a SIMD (a workgroup's waves
@@ -137,37 +140,43 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
     f32x4 oacc[G::NTV];         // O^T: [column tile]
     uint4 pf[4];                // P^T as bf16 B operands: [32-key step]
 
-    // Buffer resources of a chunk (t: first token, L valid rows): loads past
-    // the last valid row read as zero, stores past it are dropped.
+    // Rows of one chunk in memory (t: first token of the pass, L valid rows): a
+    // buffer resource over the L rows. In reverse token order (a.rev) pass row r
+    // of the chunk is row L - 1 - r of the resource. Rows past L fall outside it
+    // either way (a negative offset reads as out of range), so they load as zero
+    // and their stores are dropped.
+    const bool rev = a.rev != 0;
+    auto first_row = [&](int t, int L) __attribute__((always_inline)) { return rev ? N - t - L : t; };
+    auto mrow = [&](int L, int row) __attribute__((always_inline)) { return rev ? L - 1 - row : row; };
     auto key_rsrc = [&](int t, int L) __attribute__((always_inline)) {
-        return make_rsrc(Kg + static_cast<size_t>(t) * ldk, L * ldk);
+        return make_rsrc(Kg + static_cast<size_t>(first_row(t, L)) * ldk, (L - 1) * ldk + DK * 2);
     };
     auto q_rsrc = [&](int t, int L) __attribute__((always_inline)) {
-        return make_rsrc(Qg + static_cast<size_t>(t) * ldk, L * ldk);
+        return make_rsrc(Qg + static_cast<size_t>(first_row(t, L)) * ldk, (L - 1) * ldk + DK * 2);
     };
     auto value_rsrc = [&](int t, int L) __attribute__((always_inline)) {
-        return make_rsrc(Vg + static_cast<size_t>(t) * ldv, L > 0 ? (L - 1) * ldv + tile_bytes : 0);
+        return make_rsrc(Vg + static_cast<size_t>(first_row(t, L)) * ldv, (L - 1) * ldv + tile_bytes);
     };
     auto out_rsrc = [&](int t, int L) __attribute__((always_inline)) {
-        return make_rsrc(Og + static_cast<size_t>(t) * ldv, (L - 1) * ldv + tile_bytes);
+        return make_rsrc(Og + static_cast<size_t>(first_row(t, L)) * ldv, (L - 1) * ldv + tile_bytes);
     };
     // Key block i (1 KiB) of this wave's share, straight into LDS: each wave
     // instruction fills 1 KiB of consecutive LDS (lane l the 16-byte unit at
     // 16 l), so each lane fetches the unit the swizzled layout puts there.
-    auto load_key_block = [&](__amdgpu_buffer_rsrc_t rk, u16* dst, int i) __attribute__((always_inline)) {
+    auto load_key_block = [&](__amdgpu_buffer_rsrc_t rk, int L, u16* dst, int i) __attribute__((always_inline)) {
         const int blk = wave * G::KBLK + i;
         const int e = blk * 512 + lane * 8;  // element offset of this lane's unit
-        const int row = e / DK;
+        const int row = e / DK;              // LDS row = pass row of the chunk
         const int unit = ((e % DK) >> 3) ^ (row & 15);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_ptr)(dst + blk * 512), 16, row * ldk + unit * 16, 0,
-                                                 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_ptr)(dst + blk * 512), 16,
+                                                 mrow(L, row) * ldk + unit * 16, 0, 0, 0);
     };
-    auto load_value_unit = [&](__amdgpu_buffer_rsrc_t rv, int j) __attribute__((always_inline)) {
-        vst[j] = buf_load16(rv, (tid / G::UV + j * G::VROWS) * ldv + (tid % G::UV) * 16);
+    auto load_value_unit = [&](__amdgpu_buffer_rsrc_t rv, int L, int j) __attribute__((always_inline)) {
+        vst[j] = buf_load16(rv, mrow(L, tid / G::UV + j * G::VROWS) * ldv + (tid % G::UV) * 16);
     };
     // query unit s
-    auto load_q_unit = [&](__amdgpu_buffer_rsrc_t rq, int s) __attribute__((always_inline)) {
-        qf[s] = buf_load16(rq, (16 * qblk + l16) * ldk + grp * 16 + s * 64);
+    auto load_q_unit = [&](__amdgpu_buffer_rsrc_t rq, int L, int s) __attribute__((always_inline)) {
+        qf[s] = buf_load16(rq, mrow(L, 16 * qblk + l16) * ldk + grp * 16 + s * 64);
     };
     // value unit j to V3 (tau0: group offset of the chunk's first token)
     auto scale_value_unit = [&](int j, int tau0) __attribute__((always_inline)) {
@@ -206,7 +215,7 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
     };
 
     // G1 and G2 for the wave owning block W. The next chunk's keys go into LDS during G1.
-    auto g12 = [&](const u16* __restrict__ kb, u16* __restrict__ next_kb, __amdgpu_buffer_rsrc_t rk, auto wtag)
+    auto g12 = [&](const u16* __restrict__ kb, u16* __restrict__ next_kb, __amdgpu_buffer_rsrc_t rk, int Lk, auto wtag)
                    __attribute__((always_inline)) {
         constexpr int B0 = decltype(wtag)::value;
         constexpr int T0 = B0 / 2 + 1;
@@ -247,7 +256,7 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
                 }
             },
             [&](auto j) __attribute__((always_inline)) {
-                spread<G::KBLK, NS1, decltype(j)::value>([&](auto i) { load_key_block(rk, next_kb, i); });
+                spread<G::KBLK, NS1, decltype(j)::value>([&](auto i) { load_key_block(rk, Lk, next_kb, i); });
             });
         // G2, step j: 32-key step t = j / NTV, column tile nt = j % NTV
         constexpr int NS2 = T0 * G::NTV;
@@ -267,7 +276,7 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
     // that step's key fragments. Riding along: the chunk's outputs (scaled by
     // z, rounded and stored), the next chunk's query loads and the scaling of
     // its values (tau_next: their group offset).
-    auto g4 = [&](const u16* kb, __amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rq, float z,
+    auto g4 = [&](const u16* kb, __amdgpu_buffer_rsrc_t ro, int Lo, __amdgpu_buffer_rsrc_t rq, int Lq, float z,
                   int tau_next) __attribute__((always_inline)) {
         struct F4 {
             uint4 v;
@@ -301,9 +310,9 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
                     constexpr int nt = decltype(i)::value;
                     const f32x4 o = oacc[nt];
                     const uint2 w = make_uint2(pack2_bf16(o[0] * z, o[1] * z), pack2_bf16(o[2] * z, o[3] * z));
-                    buf_store8(w, ro, (16 * qblk + l16) * ldv + grp * 8 + nt * 32);
+                    buf_store8(w, ro, mrow(Lo, 16 * qblk + l16) * ldv + grp * 8 + nt * 32);
                 });
-                spread<G::KSQ, NS4, J>([&](auto i) { load_q_unit(rq, i); });
+                spread<G::KSQ, NS4, J>([&](auto i) { load_q_unit(rq, Lq, i); });
                 spread<G::VU, NS4, J>([&](auto i) { scale_value_unit(decltype(i)::value, tau_next); });
             });
     };
@@ -313,11 +322,11 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
         const int L0 = min(C, N);
         const __amdgpu_buffer_rsrc_t rv = value_rsrc(0, L0), rk = key_rsrc(0, L0), rq = q_rsrc(0, L0);
 #pragma unroll
-        for (int j = 0; j < G::VU; ++j) load_value_unit(rv, j);
+        for (int j = 0; j < G::VU; ++j) load_value_unit(rv, L0, j);
 #pragma unroll
-        for (int i = 0; i < G::KBLK; ++i) load_key_block(rk, pb0, i);
+        for (int i = 0; i < G::KBLK; ++i) load_key_block(rk, L0, pb0, i);
 #pragma unroll
-        for (int i = 0; i < G::KSQ; ++i) load_q_unit(rq, i);
+        for (int i = 0; i < G::KSQ; ++i) load_q_unit(rq, L0, i);
         // the per-chunk wait before barrier A counts the operations issued after
         // a chunk's key loads in the loop; the first chunk's are waited for here
         wait_vm_lgkm0<0>();
@@ -382,11 +391,11 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
                     oacc[nt] = mfma16x16x32(af, qf[s], oacc[nt]);
                 },
                 [&](auto j) __attribute__((always_inline)) {
-                    spread<G::VU, NS3, decltype(j)::value>([&](auto i) { load_value_unit(rv, i); });
+                    spread<G::VU, NS3, decltype(j)::value>([&](auto i) { load_value_unit(rv, L1, i); });
                 });
         } else {
 #pragma unroll
-            for (int j = 0; j < G::VU; ++j) load_value_unit(rv, j);
+            for (int j = 0; j < G::VU; ++j) load_value_unit(rv, L1, j);
         }
         // every wave has read the state copy: the next chunk's keys go there
         wait_lgkm0();
@@ -395,21 +404,21 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
         // ---- G1, G2 (the wave's blocks decide the causal extent)
         const __amdgpu_buffer_rsrc_t rk = key_rsrc(t1, L1);
         switch (qblk) {
-            case 0: g12(kb, sb, rk, Ic<0>{}); break;
-            case 1: g12(kb, sb, rk, Ic<1>{}); break;
-            case 2: g12(kb, sb, rk, Ic<2>{}); break;
-            case 3: g12(kb, sb, rk, Ic<3>{}); break;
-            case 4: g12(kb, sb, rk, Ic<4>{}); break;
-            case 5: g12(kb, sb, rk, Ic<5>{}); break;
-            case 6: g12(kb, sb, rk, Ic<6>{}); break;
-            default: g12(kb, sb, rk, Ic<7>{}); break;
+            case 0: g12(kb, sb, rk, L1, Ic<0>{}); break;
+            case 1: g12(kb, sb, rk, L1, Ic<1>{}); break;
+            case 2: g12(kb, sb, rk, L1, Ic<2>{}); break;
+            case 3: g12(kb, sb, rk, L1, Ic<3>{}); break;
+            case 4: g12(kb, sb, rk, L1, Ic<4>{}); break;
+            case 5: g12(kb, sb, rk, L1, Ic<5>{}); break;
+            case 6: g12(kb, sb, rk, L1, Ic<6>{}); break;
+            default: g12(kb, sb, rk, L1, Ic<7>{}); break;
         }
 
         // ---- G4, with the outputs O = gamma^(tau + 1) O^T stored as bf16 meanwhile
         const float z = fast_exp2(static_cast<float>(tau0 + 16 * qblk + l16 + 1) * lg2f);
         tau0 += L;
         const bool group_end = tau0 >= R * C || !has_next;
-        g4(kb, out_rsrc(t0, L), q_rsrc(t1, L1), z, group_end ? 0 : tau0);
+        g4(kb, out_rsrc(t0, L), L, q_rsrc(t1, L1), L1, z, group_end ? 0 : tau0);
 
         // ---- end of a decay group (or of the sequence): A back to S
         if (group_end) {
@@ -451,6 +460,27 @@ void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
     }
 }
 
+}  // namespace
+
+template <int DK>
+__global__ __attribute__((amdgpu_flat_work_group_size(kWideThreads, kWideThreads), amdgpu_waves_per_eu(2, 2)))
+void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
+    // (batch, head, value tile); the value tiles of one head run on one XCD
+    const int chain = xcd_logical_block(blockIdx.x, gridDim.x);
+    chunk_wide_body<DK, false>(a, hp, chain);
+}
+
+// Several calls of one key width in one launch (the backward's passes):
+// workgroups [first[c], first[c+1]) of the XCD-ordered block index serve call c.
+template <int DK>
+__global__ __attribute__((amdgpu_flat_work_group_size(kWideThreads, kWideThreads), amdgpu_waves_per_eu(2, 2)))
+void chunk_wide_multi_kernel(ChunkCalls cs, HeadParams hp) {
+    const int b = xcd_logical_block(blockIdx.x, gridDim.x);
+    int c = 0;
+    while (c + 1 < cs.n && b >= cs.first[c + 1]) ++c;
+    chunk_wide_body<DK, true>(cs.a[c], hp, b - cs.first[c]);
+}
+
 // Chunks per decay group: the largest R in {8, 4, 2, 1} with gamma^(R C) >=
 // 2^-64 for every head (0: the rescaled form does not fit these gammas).
 int chunk_wide_rescale(const HeadParams& hp, int H) {
@@ -463,6 +493,29 @@ int chunk_wide_rescale(const HeadParams& hp, int H) {
 
 bool chunk_wide_supported(int dk, int dvt, int chunk, int nseg, bool rotation) {
     return !rotation && nseg == 1 && dvt == kWideDvt && chunk == kWideC && (dk == 128 || dk == 256);
+}
+
+hipError_t launch_chunk_wide_multi(const ChunkCalls& in, const HeadParams& hp, hipStream_t st) {
+    if (in.n < 1 || in.n > kMaxChunkCalls) return hipErrorInvalidValue;
+    ChunkCalls cs = in;
+    const int R = chunk_wide_rescale(hp, cs.a[0].H);
+    if (R == 0) return hipErrorInvalidValue;
+    cs.first[0] = 0;
+    for (int i = 0; i < cs.n; ++i) {
+        ChunkArgs& b = cs.a[i];
+        if (b.dk != cs.a[0].dk || b.H != cs.a[0].H || !chunk_wide_supported(b.dk, b.dv / b.nvt, b.chunk, b.nseg, false) ||
+            b.orot)
+            return hipErrorInvalidValue;
+        b.rescale = R;
+        cs.first[i + 1] = cs.first[i] + b.B * b.H * b.nvt;
+    }
+    cs.interleave = 0;
+    const dim3 grid(cs.first[cs.n]), block(kWideThreads);
+    if (cs.a[0].dk == 256)
+        hipLaunchKernelGGL(chunk_wide_multi_kernel<256>, grid, block, 0, st, cs, hp);
+    else
+        hipLaunchKernelGGL(chunk_wide_multi_kernel<128>, grid, block, 0, st, cs, hp);
+    return hipGetLastError();
 }
 
 hipError_t launch_chunk_wide(const ChunkArgs& a, const HeadParams& hp, hipStream_t st, hipEvent_t* ev) {

@@ -36,6 +36,8 @@ struct ChunkArgs {
     int orot;     // rotate each output row by minus theta at its token's position before rounding
                   // (chunk_bf16_multi_kernel only, where chunk_orot_fits; output columns are the pairs)
     int rescale;  // chunks per decay group of chunk_wide_kernel (set by launch_chunk_bf16)
+    int ldqk;     // row stride of q and k in elements (0: dk; chunk_wide kernels only, which then
+                  // read a dk-wide column block of wider rows)
 };
 
 // Ticket counters of the segmented bf16 chunk kernel: one per chain, each on a
@@ -181,6 +183,9 @@ hipError_t launch_chunk_bf16(const ChunkArgs& a, const HeadParams& hp, int dvt, 
 bool chunk_wide_supported(int dk, int dvt, int chunk, int nseg, bool rotation);
 int chunk_wide_rescale(const HeadParams& hp, int H);
 hipError_t launch_chunk_wide(const ChunkArgs& a, const HeadParams& hp, hipStream_t st, hipEvent_t* ev);
+// several unrotated calls of one key width (128 or 256), chunk 128, 128-column value tiles,
+// one segment each, in one launch (a.rev honoured); rescale is filled in here
+hipError_t launch_chunk_wide_multi(const ChunkCalls& cs, const HeadParams& hp, hipStream_t st);
 hipError_t launch_chunk_bf16_multi(const ChunkCalls& cs, const HeadParams& hp, int dvt, hipStream_t st);
 hipError_t launch_chunk_f32(const ChunkArgs& a, const HeadParams& hp, int dvt, hipStream_t st, hipEvent_t* ev);
 hipError_t launch_parallel_bf16(const ParallelArgs& a, const HeadParams& hp, int dvt, hipStream_t st);

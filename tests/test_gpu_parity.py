@@ -627,6 +627,22 @@ def test_chunkwise_backward_small(case):
     _bwd_check(*case, seed=71)
 
 
+# 128-token chunks, key widths of 128 or 256 and enough (batch, head, value tile) chains over the
+# passes to fill the chip: every pass runs on the wide chunkwise kernel in one launch (the dK and dV
+# passes in reverse token order), with ragged last chunks, initial states and state gradients
+WIDE_BWD_CASES = [
+    # B, H, N, dk, dv, chunk, dtype, rotary, state_in, d_state_out
+    (2, 48, 300, 128, 128, 128, torch.bfloat16, True, True, True),    # unsplit; rotation undone afterwards
+    (2, 32, 257, 128, 256, 128, torch.bfloat16, False, True, True),   # passes 1, 2 over halves of dv
+    (2, 16, 260, 256, 512, 128, torch.bfloat16, True, False, True),   # the 7B-shaped layer's widths
+]
+
+
+@pytest.mark.parametrize("case", WIDE_BWD_CASES, ids=lambda c: "B{}H{}N{}dk{}dv{}rot{}".format(*c[:5], c[7]))
+def test_chunkwise_backward_wide_passes(case):
+    _bwd_check(*case, seed=79)
+
+
 @pytest.mark.parametrize("pos0", [1_000_000_007, 3 * 2**31 + 5])
 @pytest.mark.parametrize("dk,dv,C", [(64, 64, 64), (128, 128, 128), (256, 256, 128)])
 def test_chunkwise_backward_rotation_far_positions(pos0, dk, dv, C):
