@@ -17,45 +17,164 @@ namespace ret {
 
 constexpr int kF32Threads = 256;
 
-__device__ __forceinline__ void rotate_row_f32(float* row, int dk, const HeadParams& hp, double position) {
-    for (int j = 0; j < dk / 2; ++j) {
-        float c, s;
-        rot_cs(position, hp.theta[j], c, s);
-        const float re = row[2 * j], im = row[2 * j + 1];
-        row[2 * j] = re * c - im * s;
-        row[2 * j + 1] = re * s + im * c;
+// Register micro-tiles: every product below is evaluated as 4 x 4 blocks of
+// outputs per thread, with the operands read from LDS as 16-byte rows of four
+// contraction steps, so each pair of 16-byte reads feeds 16 multiply-adds
+// (a thread walking one output at a time waits a full LDS round trip per
+// multiply-add). Rows are float4-aligned: every width is a multiple of 4.
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float at4(const float4& x, int i) { return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w; }
+
+// acc[r][s] += sum over the four steps e of a[r].e * b[e].s
+__device__ __forceinline__ void mma4(float (&acc)[4][4], const float4 (&a)[4], const float4 (&b)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(at4(a[r], e), at4(b[e], c), acc[r][c]);
+}
+
+// acc[r][s] += sum over the four steps e of a[r].e * b[s].e (both operands row-major along the steps)
+__device__ __forceinline__ void mma4_nt(float (&acc)[4][4], const float4 (&a)[4], const float4 (&b)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(at4(a[r], e), at4(b[c], e), acc[r][c]);
+}
+
+// Scores with the decay mask of one (query block, key block) pair into P[R][R]
+// (pitch R): P[i][j] = (q_i . k_j) gamma^(dq + i - j) for kept entries
+// (i < Lq, j < Lk, and j <= i when dq == 0), else 0 (a select, so a non-finite
+// key never leaks into a dropped entry). Thread tile: rows 4 ti + r, keys
+// tj + (R/4) s (keys strided, so the 16 lanes reading key rows hit different
+// banks with a key pitch of 4 mod 8 words).
+__device__ __forceinline__ void scores_f32(float* P, const float* sq, const float* sk, int R, int DK, int KP, int Lq,
+                                           int Lk, int dq, float lg2f) {
+    const int R4 = R / 4;
+    for (int tile = threadIdx.x; tile < R4 * R4; tile += kF32Threads) {
+        const int ti = tile / R4, tj = tile % R4;
+        float acc[4][4] = {};
+        for (int d = 0; d < DK; d += 4) {
+            float4 a[4], b[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a[r] = ld4(sq + (4 * ti + r) * DK + d);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) b[c] = ld4(sk + (tj + R4 * c) * KP + d);
+            mma4_nt(acc, a, b);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int i = 4 * ti + r, j = tj + R4 * c;
+                const bool keep = i < Lq && j < Lk && (dq > 0 || j <= i);
+                P[i * R + j] = keep ? acc[r][c] * exp2f(static_cast<float>(dq + i - j) * lg2f) : 0.0f;
+            }
     }
 }
 
-// Stage rows [t0, t0 + L) of a [*, ld] float matrix (columns c0 .. c0 + w) into
-// LDS as [C][pitch], zero-filling rows >= L; optionally rotate each row. Key
-// rows use pitch w + 1 so that lanes reading one column of consecutive rows
-// hit different banks.
-__device__ __forceinline__ void stage_rows(float* dst, const float* src, int ld, int c0, int w, int pitch, int t0,
-                                           int L, int C, bool rotate, const HeadParams& hp, long long pos0) {
+// Rotate pair j of LDS row r (absolute position `position`) in place.
+__device__ __forceinline__ void rotate_pair_f32(float* row, int j, const HeadParams& hp, double position) {
+    float c, s;
+    rot_cs(position, hp.theta[j], c, s);
+    const float re = row[2 * j], im = row[2 * j + 1];
+    row[2 * j] = re * c - im * s;
+    row[2 * j + 1] = re * s + im * c;
+}
+
+// One LDS staging copy: rows [0, R) of a [*, ld] float matrix (columns c0 ..
+// c0 + w, w a multiple of 4, 16-byte aligned) into LDS as [R][pitch]; rows >= L
+// (or every row when src is null) become zeros; with `rotate`, each valid row
+// r is then rotated at absolute position pos0 + r.
+struct RowCopy {
+    float* dst;
+    const float* src;
+    int ld, c0, w, pitch, R, L;
+    bool rotate;
+    long long pos0;
+};
+
+// Runs NC copies together: each thread issues its 16-byte loads of every copy
+// (four per copy per batch) before storing any of them, so the HBM round
+// trips of the copies overlap. Rotation (one thread per (row, pair)) follows
+// after a barrier.
+template <int NC>
+__device__ __forceinline__ void copy_rows(const RowCopy (&cs)[NC], const HeadParams& hp) {
+    constexpr int kBatch = 4;
     const int tid = threadIdx.x;
-    for (int idx = tid; idx < C * w; idx += kF32Threads) {
-        const int r = idx / w, c = idx % w;
-        dst[r * pitch + c] = r < L ? src[static_cast<size_t>(t0 + r) * ld + c0 + c] : 0.0f;
+    int n4max = 0;
+#pragma unroll
+    for (int k = 0; k < NC; ++k) n4max = max(n4max, cs[k].R * (cs[k].w / 4));
+    for (int b0 = 0; b0 < n4max; b0 += kBatch * kF32Threads) {
+        float4 x[NC][kBatch];
+#pragma unroll
+        for (int k = 0; k < NC; ++k) {
+            const int w4 = cs[k].w / 4, n4 = cs[k].R * w4;
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int idx = b0 + tid + u * kF32Threads;
+                const int r = idx / w4, c = idx % w4;
+                x[k][u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                if (cs[k].src && idx < n4 && r < cs[k].L)
+                    x[k][u] = *reinterpret_cast<const float4*>(cs[k].src + static_cast<size_t>(r) * cs[k].ld +
+                                                               cs[k].c0 + 4 * c);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NC; ++k) {
+            const int w4 = cs[k].w / 4, n4 = cs[k].R * w4;
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int idx = b0 + tid + u * kF32Threads;
+                if (idx < n4) {
+                    float* d = cs[k].dst + (idx / w4) * cs[k].pitch + 4 * (idx % w4);
+                    d[0] = x[k][u].x;
+                    d[1] = x[k][u].y;
+                    d[2] = x[k][u].z;
+                    d[3] = x[k][u].w;
+                }
+            }
+        }
     }
-    if (rotate) {
+    bool any_rot = false;
+#pragma unroll
+    for (int k = 0; k < NC; ++k) any_rot |= cs[k].rotate;
+    if (any_rot) {
         __syncthreads();
-        for (int r = tid; r < L; r += kF32Threads)
-            rotate_row_f32(dst + r * pitch, w, hp, static_cast<double>(pos0 + t0 + r));
+#pragma unroll
+        for (int k = 0; k < NC; ++k) {
+            if (!cs[k].rotate) continue;
+            const int pairs = cs[k].w / 2;
+            for (int idx = tid; idx < cs[k].L * pairs; idx += kF32Threads) {
+                const int r = idx / pairs;
+                rotate_pair_f32(cs[k].dst + r * cs[k].pitch, idx % pairs, hp, static_cast<double>(cs[k].pos0 + r));
+            }
+        }
     }
+}
+
+// Rows [t0, t0 + L) of a [*, ld] float matrix as a chunk of C staged rows
+// (key rows use pitch w + 4 so that lanes reading key rows hit different banks).
+__device__ __forceinline__ RowCopy chunk_rows(float* dst, const float* src, int ld, int c0, int w, int pitch, int t0,
+                                              int L, int C, bool rotate, long long pos0) {
+    return RowCopy{dst, src + static_cast<size_t>(t0) * ld, ld, c0, w, pitch, C, L, rotate, pos0 + t0};
 }
 
 template <bool STATE_ONLY>
 __global__ __launch_bounds__(kF32Threads) void chunk_f32_kernel(ChunkArgs a, HeadParams hp, int dvt) {
     extern __shared__ __attribute__((aligned(16))) float smem[];
     const int C = a.chunk, DK = a.dk;
-    const int KP = DK + 1;            // padded key row pitch
+    const int KP = DK + 4;            // padded key row pitch (float4-aligned)
     float* sq = smem;                 // [C][DK]
     float* sk = sq + C * DK;          // [C][KP]
     float* sv = sk + C * KP;          // [C][dvt]
     float* ss = sv + C * dvt;         // [DK][dvt]
     float* sp = ss + DK * dvt;        // [C][C]
     float* sx = sp + C * C;           // [C] key decay xi_j of the current chunk
+    float* sz = sx + C;               // [C] query decay zeta_i = gamma^(i+1)
 
     const int tid = threadIdx.x;
     const int nseg_grid = STATE_ONLY ? a.nseg - 1 : a.nseg;
@@ -83,52 +202,92 @@ __global__ __launch_bounds__(kF32Threads) void chunk_f32_kernel(ChunkArgs a, Hea
         else if (a.state_in)
             s_src = a.state_in + static_cast<size_t>(bh) * DK * a.dv;
     }
-    for (int idx = tid; idx < DK * dvt; idx += kF32Threads) {
-        const int d = idx / dvt, c = idx % dvt;
-        ss[idx] = s_src ? s_src[static_cast<size_t>(d) * a.dv + c0 + c] : 0.0f;
+    {
+        const RowCopy cs[1] = {RowCopy{ss, s_src, a.dv, c0, dvt, dvt, DK, DK, false, 0}};
+        copy_rows(cs, hp);
     }
     bool have_state = s_src != nullptr;
 
     for (int t0 = t_begin; t0 < t_end; t0 += C) {
         const int L = min(C, t_end - t0);
         __syncthreads();
-        if (!STATE_ONLY) stage_rows(sq, Q, DK, 0, DK, DK, t0, L, C, hp.has_theta, hp, a.pos0);
-        stage_rows(sk, K, DK, 0, DK, KP, t0, L, C, hp.has_theta, hp, a.pos0);
-        stage_rows(sv, V, a.dv, c0, dvt, dvt, t0, L, C, false, hp, a.pos0);
-        for (int j = tid; j < L; j += kF32Threads) sx[j] = exp2f(static_cast<float>(L - 1 - j) * lg2f);
+        const RowCopy ck = chunk_rows(sk, K, DK, 0, DK, KP, t0, L, C, hp.has_theta, a.pos0);
+        const RowCopy cv = chunk_rows(sv, V, a.dv, c0, dvt, dvt, t0, L, C, false, a.pos0);
+        if (STATE_ONLY) {
+            const RowCopy cs[2] = {ck, cv};
+            copy_rows(cs, hp);
+        } else {
+            const RowCopy cs[3] = {chunk_rows(sq, Q, DK, 0, DK, DK, t0, L, C, hp.has_theta, a.pos0), ck, cv};
+            copy_rows(cs, hp);
+        }
+        for (int j = tid; j < L; j += kF32Threads) {
+            sx[j] = exp2f(static_cast<float>(L - 1 - j) * lg2f);
+            sz[j] = static_cast<float>(gamma_pow(lg2, j + 1.0));
+        }
         __syncthreads();
+        const int V4 = dvt / 4;
         if (!STATE_ONLY) {
-            // scores with decay mask (select, so a non-finite future key never leaks)
-            for (int idx = tid; idx < L * L; idx += kF32Threads) {
-                const int i = idx / L, j = idx % L;
-                float p = 0.0f;
-                if (j <= i) {
-                    float acc = 0.0f;
-                    for (int d = 0; d < DK; ++d) acc = fmaf(sq[i * DK + d], sk[j * KP + d], acc);
-                    p = acc * exp2f(static_cast<float>(i - j) * lg2f);
-                }
-                sp[i * C + j] = p;
-            }
+            scores_f32(sp, sq, sk, C, DK, KP, L, L, 0, lg2f);
             __syncthreads();
-            for (int idx = tid; idx < L * dvt; idx += kF32Threads) {
-                const int i = idx / dvt, c = idx % dvt;
-                float inner = 0.0f;
-                for (int j = 0; j <= i; ++j) inner = fmaf(sp[i * C + j], sv[j * dvt + c], inner);
-                float cross = 0.0f;
-                if (have_state) {
-                    for (int d = 0; d < DK; ++d) cross = fmaf(sq[i * DK + d], ss[d * dvt + c], cross);
-                    cross *= gamma_pow(lg2, i + 1.0);
+            // O = P V + zeta (.) (Q S): thread tile rows 4 ti + r, columns 4 tc + s
+            for (int tile = tid; tile < (C / 4) * V4; tile += kF32Threads) {
+                const int ti = tile / V4, tc = tile % V4;
+                float inner[4][4] = {}, cross[4][4] = {};
+                // P is zero right of the diagonal and past L, V past L
+                const int jend = min(4 * ti + 4, (L + 3) & ~3);
+                for (int j = 0; j < jend; j += 4) {
+                    float4 pa[4], vb[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) pa[r] = ld4(sp + (4 * ti + r) * C + j);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) vb[e] = ld4(sv + (j + e) * dvt + 4 * tc);
+                    mma4(inner, pa, vb);
                 }
-                O[static_cast<size_t>(t0 + i) * a.dv + c0 + c] = inner + cross;
+                if (have_state) {
+                    for (int d = 0; d < DK; d += 4) {
+                        float4 qa[4], sb[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) qa[r] = ld4(sq + (4 * ti + r) * DK + d);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) sb[e] = ld4(ss + (d + e) * dvt + 4 * tc);
+                        mma4(cross, qa, sb);
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 4 * ti + r;
+                    if (i < L) {
+                        const float z = sz[i];
+                        const float4 o = make_float4(inner[r][0] + cross[r][0] * z, inner[r][1] + cross[r][1] * z,
+                                                     inner[r][2] + cross[r][2] * z, inner[r][3] + cross[r][3] * z);
+                        *reinterpret_cast<float4*>(O + static_cast<size_t>(t0 + i) * a.dv + c0 + 4 * tc) = o;
+                    }
+                }
             }
             __syncthreads();
         }
+        // S <- gamma^L S + K^T (xi (.) V): thread tile state rows 4 td + r, columns 4 tc + s
         const float gL = gamma_pow(lg2, L);
-        for (int idx = tid; idx < DK * dvt; idx += kF32Threads) {
-            const int d = idx / dvt, c = idx % dvt;
-            float acc = 0.0f;
-            for (int j = 0; j < L; ++j) acc = fmaf(sk[j * KP + d] * sx[j], sv[j * dvt + c], acc);
-            ss[idx] = gL * ss[idx] + acc;
+        for (int tile = tid; tile < (DK / 4) * V4; tile += kF32Threads) {
+            const int td = tile / V4, tc = tile % V4;
+            float acc[4][4] = {};
+            for (int j = 0; j < L; ++j) {
+                const float4 kr = ld4(sk + j * KP + 4 * td);
+                const float4 vr = ld4(sv + j * dvt + 4 * tc);
+                const float x = sx[j];
+                const float kx[4] = {kr.x * x, kr.y * x, kr.z * x, kr.w * x};
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(kx[r], at4(vr, c), acc[r][c]);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float4* row = reinterpret_cast<float4*>(ss + (4 * td + r) * dvt + 4 * tc);
+                const float4 o = *row;
+                *row = make_float4(gL * o.x + acc[r][0], gL * o.y + acc[r][1], gL * o.z + acc[r][2],
+                                   gL * o.w + acc[r][3]);
+            }
         }
         have_state = true;
     }
@@ -148,9 +307,9 @@ __global__ __launch_bounds__(kF32Threads) void chunk_f32_kernel(ChunkArgs a, Hea
 }
 
 size_t chunk_f32_lds_bytes(int C, int dk, int dvt) {
-    return sizeof(float) * (static_cast<size_t>(C) * dk + static_cast<size_t>(C) * (dk + 1) +
+    return sizeof(float) * (static_cast<size_t>(C) * dk + static_cast<size_t>(C) * (dk + 4) +
                             static_cast<size_t>(C) * dvt + static_cast<size_t>(dk) * dvt +
-                            static_cast<size_t>(C) * C + C);
+                            static_cast<size_t>(C) * C + 2 * static_cast<size_t>(C));
 }
 
 hipError_t launch_chunk_f32(const ChunkArgs& a, const HeadParams& hp, int dvt, hipStream_t st, hipEvent_t* ev) {
@@ -182,7 +341,7 @@ constexpr int kParF32Block = 64;
 __global__ __launch_bounds__(kF32Threads) void parallel_f32_kernel(ParallelArgs a, HeadParams hp, int dvt) {
     extern __shared__ __attribute__((aligned(16))) float smem[];
     const int BQ = kParF32Block, DK = a.dk;
-    const int KP = DK + 1;       // padded key row pitch
+    const int KP = DK + 4;       // padded key row pitch (float4-aligned)
     float* sq = smem;            // [BQ][DK]
     float* sk = sq + BQ * DK;    // [BQ][KP]
     float* sv = sk + BQ * KP;    // [BQ][dvt]
@@ -208,58 +367,59 @@ __global__ __launch_bounds__(kF32Threads) void parallel_f32_kernel(ParallelArgs 
     const int q0 = qb * BQ;
     const int Lq = min(BQ, a.N - q0);
 
-    constexpr int kMaxOut = BQ * 64 / kF32Threads;  // outputs per thread (dvt <= 64)
-    float out[kMaxOut];
-#pragma unroll
-    for (int u = 0; u < kMaxOut; ++u) out[u] = 0.0f;
+    // output tile of this thread: rows 4 ti + r, columns 4 tc + s (dvt <= 64: at most 256 tiles)
+    const int V4 = dvt / 4;
+    const int ti = tid / V4, tc = tid % V4;
+    const bool owns = tid < (BQ / 4) * V4;
+    float out[4][4] = {};
 
-    stage_rows(sq, Q, DK, 0, DK, DK, q0, Lq, BQ, hp.has_theta, hp, a.pos0);
+    {
+        const RowCopy cs[1] = {chunk_rows(sq, Q, DK, 0, DK, DK, q0, Lq, BQ, hp.has_theta, a.pos0)};
+        copy_rows(cs, hp);
+    }
     for (int kb = qb; kb >= 0; --kb) {
         const int k0 = kb * BQ;
         const int Lk = min(BQ, a.N - k0);
         // every D entry of this block (and all earlier ones) below float32 underflow
         if (lg2 < 0.0 && (static_cast<double>(q0 - k0) - (BQ - 1)) * (-lg2) > 160.0) break;
         __syncthreads();
-        stage_rows(sk, K, DK, 0, DK, KP, k0, Lk, BQ, hp.has_theta, hp, a.pos0);
-        stage_rows(sv, V, a.dv, c0, dvt, dvt, k0, Lk, BQ, false, hp, a.pos0);
+        {
+            const RowCopy cs[2] = {chunk_rows(sk, K, DK, 0, DK, KP, k0, Lk, BQ, hp.has_theta, a.pos0),
+                                   chunk_rows(sv, V, a.dv, c0, dvt, dvt, k0, Lk, BQ, false, a.pos0)};
+            copy_rows(cs, hp);
+        }
         __syncthreads();
         // one exponent per entry, (q0 + i) - (k0 + j) >= 0 for every kept entry,
         // so no factor overflows for small gamma
-        for (int idx = tid; idx < BQ * BQ; idx += kF32Threads) {
-            const int i = idx / BQ, j = idx % BQ;
-            float p = 0.0f;
-            if (i < Lq && j < Lk && (kb < qb || j <= i)) {
-                float acc = 0.0f;
-                for (int d = 0; d < DK; ++d) acc = fmaf(sq[i * DK + d], sk[j * KP + d], acc);
-                p = acc * exp2f(static_cast<float>((q0 - k0) + i - j) * lg2f);
-            }
-            sp[idx] = p;
-        }
+        scores_f32(sp, sq, sk, BQ, DK, KP, Lq, Lk, q0 - k0, lg2f);
         __syncthreads();
+        if (owns) {
+            // P is zero past Lk and right of the diagonal, V past Lk
+            const int jend = kb == qb ? min(4 * ti + 4, (Lk + 3) & ~3) : (Lk + 3) & ~3;
+            for (int j = 0; j < jend; j += 4) {
+                float4 pa[4], vb[4];
 #pragma unroll
-        for (int u = 0; u < kMaxOut; ++u) {
-            const int idx = tid + u * kF32Threads;
-            if (idx < BQ * dvt) {
-                const int i = idx / dvt, c = idx % dvt;
-                float acc = out[u];
-                for (int j = 0; j < Lk; ++j) acc = fmaf(sp[i * BQ + j], sv[j * dvt + c], acc);
-                out[u] = acc;
+                for (int r = 0; r < 4; ++r) pa[r] = ld4(sp + (4 * ti + r) * BQ + j);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vb[e] = ld4(sv + (j + e) * dvt + 4 * tc);
+                mma4(out, pa, vb);
             }
         }
     }
+    if (owns) {
 #pragma unroll
-    for (int u = 0; u < kMaxOut; ++u) {
-        const int idx = tid + u * kF32Threads;
-        if (idx < BQ * dvt) {
-            const int i = idx / dvt, c = idx % dvt;
-            if (i < Lq) O[static_cast<size_t>(q0 + i) * a.dv + c0 + c] = out[u];
+        for (int r = 0; r < 4; ++r) {
+            const int i = 4 * ti + r;
+            if (i < Lq)
+                *reinterpret_cast<float4*>(O + static_cast<size_t>(q0 + i) * a.dv + c0 + 4 * tc) =
+                    make_float4(out[r][0], out[r][1], out[r][2], out[r][3]);
         }
     }
 }
 
 size_t parallel_f32_lds_bytes(int dk, int dvt) {
     const size_t BQ = kParF32Block;
-    return sizeof(float) * (BQ * dk + BQ * (dk + 1) + BQ * dvt + BQ * BQ);
+    return sizeof(float) * (BQ * dk + BQ * (dk + 4) + BQ * dvt + BQ * BQ);
 }
 
 hipError_t launch_parallel_f32(const ParallelArgs& a, const HeadParams& hp, int dvt, hipStream_t st) {
