@@ -1297,18 +1297,21 @@ bool fast_form_ok(const HeadParams& hp, int H, int chunk) {
 
 template <int DK, int DVT, int C>
 static hipError_t run_chunk_bf16(const ChunkArgs& a, const HeadParams& hp, hipStream_t st, hipEvent_t* ev) {
-    // the segmented form is a single launch: the pre-pass and scan phases are empty
-    record_empty_phase(st, ev);
-    record_empty_phase(st, ev ? ev + 2 : nullptr);
-    hipEvent_t* e = ev ? ev + 4 : nullptr;
-    if (chunk_wide_supported(DK, DVT, C, a.nseg, hp.has_theta != 0)) {
+    // Unrotated heads of width 128 or 256 in 128-token chunks run on the wide
+    // kernel, segmented (state pass, scan, segment pass) when the plan cuts the
+    // sequence; it takes its six phase events itself.
+    if (chunk_wide_supported(DK, DVT, C, 1, hp.has_theta != 0) && (a.nseg == 1 || a.agg != nullptr)) {
         const int R = chunk_wide_rescale(hp, a.H);
         if (R > 0) {
             ChunkArgs aw = a;
             aw.rescale = R;
-            return launch_chunk_wide(aw, hp, st, e);
+            return launch_chunk_wide(aw, hp, st, ev);
         }
     }
+    // the segmented form of this kernel is a single launch: the pre-pass and scan phases are empty
+    record_empty_phase(st, ev);
+    record_empty_phase(st, ev ? ev + 2 : nullptr);
+    hipEvent_t* e = ev ? ev + 4 : nullptr;
     if (fast_form_ok(hp, a.H, C))
         launch_chunk_form<DK, DVT, C, true>(a, hp, st, e);
     else

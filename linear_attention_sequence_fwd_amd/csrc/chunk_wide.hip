@@ -60,6 +60,11 @@ constexpr int kWideDvt = 128;          // value columns per workgroup
 constexpr int kWideThreads = 512;      // eight waves, two per SIMD
 constexpr int kPipeDepth = 4;          // steps between an LDS read and its use
 
+// What one workgroup computes for its chain (batch x head x value tile):
+constexpr int kWideWhole = 0;      // outputs and end state of the whole sequence
+constexpr int kWideStatePass = 1;  // the end state of segment `seg` from a zero state (no outputs)
+constexpr int kWideSegPass = 2;    // outputs of segment `seg` from its start state (after the scan)
+
 template <int DK>
 struct WideGeo {
     static constexpr int UK = DK / 8;                      // 16-byte units per key row
@@ -77,11 +82,16 @@ struct WideGeo {
 
 namespace {
 
-// One call's chain `chain` (batch x head x value tile). MULTI only tells the
-// two kernels' copies apart (each kernel its own specialization, as each
-// holds its own LDS).
-template <int DK, bool MULTI>
-__device__ __forceinline__ void chunk_wide_body(const ChunkArgs& a, const HeadParams& hp, const int chain) {
+// One call's chain `chain` (batch x head x value tile), over the whole
+// sequence or one segment of it (MODE). MULTI only tells the kernels' copies
+// apart (each kernel its own specialization, as each holds its own LDS).
+// Segmented calls keep their states in the workspace as float32
+// [B*H][nseg][d_k][d_v]: slot s + 1 receives segment s's end state from zero
+// (state pass), the scan turns slot s into segment s's start state, and the
+// segment pass starts from it.
+template <int DK, bool MULTI, int MODE = kWideWhole>
+__device__ __forceinline__ void chunk_wide_body(const ChunkArgs& a, const HeadParams& hp, const int chain,
+                                                const int seg) {
     using G = WideGeo<DK>;
     constexpr int C = kWideC;
     constexpr int UK = G::UK;
@@ -115,7 +125,9 @@ __device__ __forceinline__ void chunk_wide_body(const ChunkArgs& a, const HeadPa
     const double lg2 = log2_gamma(gam);
     const float lg2f = static_cast<float>(lg2);
     const int N = a.N;
-    const int nch = (N + C - 1) / C;
+    const int t_begin = MODE == kWideWhole ? 0 : seg * a.seg_len;  // tokens [t_begin, t_end) of this pass
+    const int t_end = MODE == kWideWhole ? N : min(N, t_begin + a.seg_len);
+    const int nch = (t_end - t_begin + C - 1) / C;
     const int R = a.rescale;
     const float g_group = gamma_pow(lg2, static_cast<double>(R) * C);  // gamma^(R C)
 
@@ -319,23 +331,30 @@ __device__ __forceinline__ void chunk_wide_body(const ChunkArgs& a, const HeadPa
 
     // ---- start: the first chunk's values, keys and queries; the initial state
     {
-        const int L0 = min(C, N);
-        const __amdgpu_buffer_rsrc_t rv = value_rsrc(0, L0), rk = key_rsrc(0, L0), rq = q_rsrc(0, L0);
+        const int L0 = min(C, t_end - t_begin);
+        const __amdgpu_buffer_rsrc_t rv = value_rsrc(t_begin, L0), rk = key_rsrc(t_begin, L0);
 #pragma unroll
         for (int j = 0; j < G::VU; ++j) load_value_unit(rv, L0, j);
 #pragma unroll
         for (int i = 0; i < G::KBLK; ++i) load_key_block(rk, L0, pb0, i);
+        if constexpr (MODE != kWideStatePass) {
+            const __amdgpu_buffer_rsrc_t rq = q_rsrc(t_begin, L0);
 #pragma unroll
-        for (int i = 0; i < G::KSQ; ++i) load_q_unit(rq, L0, i);
-        // the per-chunk wait before barrier A counts the operations issued after
-        // a chunk's key loads in the loop; the first chunk's are waited for here
-        wait_vm_lgkm0<0>();
+            for (int i = 0; i < G::KSQ; ++i) load_q_unit(rq, L0, i);
+            // the per-chunk wait before barrier A counts the operations issued after
+            // a chunk's key loads in the loop; the first chunk's are waited for here
+            wait_vm_lgkm0<0>();
 #pragma unroll
-        for (int j = 0; j < G::VU; ++j) scale_value_unit(j, 0);
+            for (int j = 0; j < G::VU; ++j) scale_value_unit(j, 0);
+        }
     }
-    bool have_state = a.state_in != nullptr;
+    const float* s_in = nullptr;
+    if constexpr (MODE == kWideSegPass)
+        s_in = a.agg + (static_cast<size_t>(bh) * a.nseg + seg) * DK * a.dv;
+    else if constexpr (MODE == kWideWhole)
+        s_in = a.state_in ? a.state_in + static_cast<size_t>(bh) * DK * a.dv : nullptr;
+    bool have_state = s_in != nullptr;
     if (have_state) {
-        const float* s_in = a.state_in + static_cast<size_t>(bh) * DK * a.dv;
 #pragma unroll
         for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
@@ -358,11 +377,11 @@ __device__ __forceinline__ void chunk_wide_body(const ChunkArgs& a, const HeadPa
     // One chunk: its keys in kb (loaded during the previous chunk), the state
     // copy in sb, its values scaled in vst.
     auto chunk = [&](int ch, u16* __restrict__ kb, u16* __restrict__ sb) __attribute__((always_inline)) {
-        const int t0 = ch * C;
-        const int L = min(C, N - t0);
+        const int t0 = t_begin + ch * C;
+        const int L = min(C, t_end - t0);
         const bool has_next = ch + 1 < nch;
         const int t1 = has_next ? t0 + C : t0;  // past the end: a discarded re-read
-        const int L1 = has_next ? min(C, N - t1) : L;
+        const int L1 = has_next ? min(C, t_end - t1) : L;
         refresh_lane();
 
         write_values();
@@ -438,15 +457,89 @@ __device__ __forceinline__ void chunk_wide_body(const ChunkArgs& a, const HeadPa
         write_state_copy(kb);
         have_state = true;
     };
-    for (int ch = 0; ch < nch; ch += 2) {
-        chunk(ch, pb0, pb1);
-        if (ch + 1 < nch) chunk(ch + 1, pb1, pb0);
+    // State pass: per chunk only G4 (A += K^T V3) and the group-end scaling;
+    // the next chunk's keys go into the other key buffer and its values into
+    // registers during G4, and are scaled at the start of that chunk.
+    auto state_chunk = [&](int ch, u16* __restrict__ kb, u16* __restrict__ nkb) __attribute__((always_inline)) {
+        const int t0 = t_begin + ch * C;
+        const int L = min(C, t_end - t0);
+        const bool has_next = ch + 1 < nch;
+        const int t1 = has_next ? t0 + C : t0;  // past the end: a discarded re-read
+        const int L1 = has_next ? min(C, t_end - t1) : L;
+        refresh_lane();
+#pragma unroll
+        for (int j = 0; j < G::VU; ++j) scale_value_unit(j, tau0);
+        write_values();
+        // A: this chunk's keys have landed (nothing else is in flight), V3 is written
+        wait_vm_lgkm0<0>();
+        __builtin_amdgcn_s_barrier();
+        const __amdgpu_buffer_rsrc_t rk = key_rsrc(t1, L1), rv = value_rsrc(t1, L1);
+        struct F4 {
+            uint4 v;
+            uint4 k[G::MT];
+        };
+        uint4 kt[G::MT];
+        constexpr int NS4 = 4 * G::NTV;
+        pipelined<NS4, kPipeDepth>(
+            [&](auto j) __attribute__((always_inline)) {
+                constexpr int t = decltype(j)::value / G::NTV, nt = decltype(j)::value % G::NTV;
+                F4 f;
+                f.v = tr_frag(vbuf, Ic<kWideDvt>{}, 16 * nt, t);
+                if constexpr (nt == 0) {
+#pragma unroll
+                    for (int mt = 0; mt < G::MT; ++mt) f.k[mt] = tr_frag(kb, Ic<DK>{}, d0 + 16 * mt, t);
+                }
+                return f;
+            },
+            [&](auto j, const F4& f) __attribute__((always_inline)) {
+                constexpr int nt = decltype(j)::value % G::NTV;
+                if constexpr (nt == 0) {
+#pragma unroll
+                    for (int mt = 0; mt < G::MT; ++mt) kt[mt] = f.k[mt];
+                }
+#pragma unroll
+                for (int mt = 0; mt < G::MT; ++mt) sacc[mt][nt] = mfma16x16x32(kt[mt], f.v, sacc[mt][nt]);
+            },
+            [&](auto j) __attribute__((always_inline)) {
+                constexpr int J = decltype(j)::value;
+                spread<G::KBLK, NS4, J>([&](auto i) { load_key_block(rk, L1, nkb, i); });
+                spread<G::VU, NS4, J>([&](auto i) { load_value_unit(rv, L1, decltype(i)::value); });
+            });
+        tau0 += L;
+        if (tau0 >= R * C || !has_next) {
+            const float ge = tau0 == R * C ? g_group : fast_exp2(static_cast<float>(tau0) * lg2f);
+#pragma unroll
+            for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < G::NTV; ++nt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sacc[mt][nt][r] *= ge;
+            tau0 = 0;
+        }
+        // B: every read of the keys and V3 done
+        wait_lgkm0();
+        __builtin_amdgcn_s_barrier();
+    };
+    if constexpr (MODE == kWideStatePass) {
+        for (int ch = 0; ch < nch; ch += 2) {
+            state_chunk(ch, pb0, pb1);
+            if (ch + 1 < nch) state_chunk(ch + 1, pb1, pb0);
+        }
+    } else {
+        for (int ch = 0; ch < nch; ch += 2) {
+            chunk(ch, pb0, pb1);
+            if (ch + 1 < nch) chunk(ch + 1, pb1, pb0);
+        }
     }
     // the last chunk's discarded re-reads (into LDS among them) end before the workgroup does
     wait_vm_lgkm0<0>();
 
-    if (a.state_out) {
-        float* s_dst = a.state_out + static_cast<size_t>(bh) * DK * a.dv;
+    float* s_dst = nullptr;
+    if constexpr (MODE == kWideStatePass)
+        s_dst = a.agg + (static_cast<size_t>(bh) * a.nseg + seg + 1) * DK * a.dv;
+    else if (a.state_out && (MODE == kWideWhole || seg == a.nseg - 1))
+        s_dst = a.state_out + static_cast<size_t>(bh) * DK * a.dv;
+    if (s_dst) {
 #pragma unroll
         for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
@@ -467,7 +560,25 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kWideThreads, kWideThreads
 void chunk_wide_kernel(ChunkArgs a, HeadParams hp) {
     // (batch, head, value tile); the value tiles of one head run on one XCD
     const int chain = xcd_logical_block(blockIdx.x, gridDim.x);
-    chunk_wide_body<DK, false>(a, hp, chain);
+    chunk_wide_body<DK, false>(a, hp, chain, 0);
+}
+
+// Segmented calls (few chains: the sequence is cut into a.nseg segments so the
+// grid fills the chip): workgroup b serves chain b % chains, segment b / chains.
+template <int DK>
+__global__ __attribute__((amdgpu_flat_work_group_size(kWideThreads, kWideThreads), amdgpu_waves_per_eu(2, 2)))
+void chunk_wide_state_kernel(ChunkArgs a, HeadParams hp) {
+    const int chains = a.B * a.H * a.nvt;
+    const int b = blockIdx.x;
+    chunk_wide_body<DK, false, kWideStatePass>(a, hp, b % chains, b / chains);
+}
+
+template <int DK>
+__global__ __attribute__((amdgpu_flat_work_group_size(kWideThreads, kWideThreads), amdgpu_waves_per_eu(2, 2)))
+void chunk_wide_seg_kernel(ChunkArgs a, HeadParams hp) {
+    const int chains = a.B * a.H * a.nvt;
+    const int b = blockIdx.x;
+    chunk_wide_body<DK, false, kWideSegPass>(a, hp, b % chains, b / chains);
 }
 
 // Several calls of one key width in one launch (the backward's passes):
@@ -478,7 +589,7 @@ void chunk_wide_multi_kernel(ChunkCalls cs, HeadParams hp) {
     const int b = xcd_logical_block(blockIdx.x, gridDim.x);
     int c = 0;
     while (c + 1 < cs.n && b >= cs.first[c + 1]) ++c;
-    chunk_wide_body<DK, true>(cs.a[c], hp, b - cs.first[c]);
+    chunk_wide_body<DK, true>(cs.a[c], hp, b - cs.first[c], 0);
 }
 
 // Chunks per decay group: the largest R in {8, 4, 2, 1} with gamma^(R C) >=
@@ -518,12 +629,37 @@ hipError_t launch_chunk_wide_multi(const ChunkCalls& in, const HeadParams& hp, h
     return hipGetLastError();
 }
 
+// ev: six events (start / stop of the state pass, the scan and the segment or
+// whole pass), or null.
 hipError_t launch_chunk_wide(const ChunkArgs& a, const HeadParams& hp, hipStream_t st, hipEvent_t* ev) {
-    const dim3 grid(a.B * a.H * a.nvt), block(kWideThreads);
+    const int chains = a.B * a.H * a.nvt;
+    const dim3 block(kWideThreads);
+    if (a.nseg <= 1) {
+        record_empty_phase(st, ev);
+        record_empty_phase(st, ev ? ev + 2 : nullptr);
+        const dim3 grid(chains);
+        if (a.dk == 256)
+            launch_timed(chunk_wide_kernel<256>, grid, block, 0, st, ev ? ev + 4 : nullptr, a, hp);
+        else
+            launch_timed(chunk_wide_kernel<128>, grid, block, 0, st, ev ? ev + 4 : nullptr, a, hp);
+        return hipGetLastError();
+    }
+    // segments: end states from zero, their scan (float32 [B*H][nseg][d_k][d_v] in the
+    // workspace's state region), then every segment's outputs from its start state
+    if (!a.agg || a.rev || a.seg_len % kWideC != 0) return hipErrorInvalidValue;
+    const dim3 gs(chains * (a.nseg - 1)), gm(chains * a.nseg);
     if (a.dk == 256)
-        launch_timed(chunk_wide_kernel<256>, grid, block, 0, st, ev, a, hp);
+        launch_timed(chunk_wide_state_kernel<256>, gs, block, 0, st, ev, a, hp);
     else
-        launch_timed(chunk_wide_kernel<128>, grid, block, 0, st, ev, a, hp);
+        launch_timed(chunk_wide_state_kernel<128>, gs, block, 0, st, ev, a, hp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_segment_scan(a, hp, st, ev ? ev + 2 : nullptr);
+    if (e != hipSuccess) return e;
+    if (a.dk == 256)
+        launch_timed(chunk_wide_seg_kernel<256>, gm, block, 0, st, ev ? ev + 4 : nullptr, a, hp);
+    else
+        launch_timed(chunk_wide_seg_kernel<128>, gm, block, 0, st, ev ? ev + 4 : nullptr, a, hp);
     return hipGetLastError();
 }
 
