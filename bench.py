@@ -60,7 +60,7 @@ CSRC = "linear_attention_sequence_fwd_amd/csrc"
 KERNEL_SOURCES = {
     "layer7b_bf16": "chunk_wide.hip",
     "msr_bf16_rotary": "chunk_bf16.hip",
-    "longctx_bf16": "chunk_bf16.hip",
+    "longctx_bf16": "chunk_wide.hip",
     "decode_bf16": "decode.hip",
 }
 SHARED_HEADERS = ("common.hpp", "tiles.hpp", "wide.hpp", "kernels.hpp")
@@ -96,8 +96,9 @@ def measured_traffic(workload):
 
 
 def measured_dram(workload):
-    """The same launch's bytes at the DRAM controllers (32-byte TCC_EA0 read and
-    write requests to DRAM, which MALL hits do not reach), or None like
+    """The same launch's bytes requested from memory (32-byte TCC_EA0 read and
+    write requests to DRAM: what left the L2s; these counters cannot tell
+    whether the memory-side cache served a request), or None like
     measured_traffic."""
     if measured_traffic(workload) is None:
         return None
@@ -522,11 +523,13 @@ def sweep_decode_batch(dev):
         torch.cuda.empty_cache()
 
 
-def time_kernel(R, q, k, v, kw, reps, evict=None):
+def time_kernel(R, q, k, v, kw, reps, evict=None, phases=False):
     """Durations (ms) of the chunkwise call's main kernel from the events the
     library records around its execution, one call at a time; with `evict`
-    (a callable that writes 1 GiB) the caches are flushed before each call.
-    Returns (median, {p10, p50, p90})."""
+    (a callable that writes 1 GiB) the caches are flushed before each call;
+    with `phases`, the sum of its three phases (segment state pass, scan, main
+    pass; a phase that does not run has zero length). Returns (median,
+    {p10, p50, p90})."""
     import numpy as np
     import torch
 
@@ -538,7 +541,7 @@ def time_kernel(R, q, k, v, kw, reps, evict=None):
         R.retention_chunkwise_fwd(q, k, v, events=evs, **kw)
         torch.cuda.synchronize()
         if i >= 2:
-            ts.append(evs[4].elapsed_time(evs[5]))
+            ts.append(sum(evs[j].elapsed_time(evs[j + 1]) for j in ((0, 2, 4) if phases else (4,))))
     ts = np.array(ts)
     return float(np.median(ts)), {f"p{p}": float(np.percentile(ts, p)) for p in (10, 50, 90)}
 
@@ -740,7 +743,7 @@ def run_also(R, W, torch, dev):
     q, k, v, _ = W.make_workload(name, device=dev)
     kw5 = dict(chunk=w["chunk"])
     ms5 = time_events(lambda: R.retention_chunkwise_fwd(q, k, v, **kw5), 10, 3)
-    k5, _ = time_kernel(R, q, k, v, kw5, 5)
+    k5, _ = time_kernel(R, q, k, v, kw5, 5, phases=True)
     by5 = chunk_alg_bytes(w["B"], w["H"], w["N"], w["dk"], w["dv"])
     fl5 = chunk_alg_flops(w["B"], w["H"], w["N"], w["dk"], w["dv"], w["chunk"])
     cross = []
@@ -755,7 +758,8 @@ def run_also(R, W, torch, dev):
         "key": name,
         "workload": "long-context chunkwise: B=1 H=8 N=65536 d_k=d_v=128 bf16, chunk 128",
         "tokens_per_s": w["B"] * w["N"] / (ms5 * 1e-3), "ms": ms5, "kernel_ms": k5,
-        "roofline": {"bound": "hbm", "kernel": "chunk_bf16_kernel<128, 128, 128, two-pass>",
+        "roofline": {"bound": "hbm", "kernel": "chunk_wide_state_kernel<128> + segment_scan_kernel + "
+                               "chunk_wide_seg_kernel<128> (32 segments; kernel_ms sums the three)",
                      "achieved": by5 / (k5 * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": by5 / (k5 * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": measured_traffic(name),
                      "dram_traffic": measured_dram(name),
