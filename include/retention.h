@@ -119,8 +119,10 @@ size_t retention_parallel_workspace_size(int B, int H, int N, int dk, int dv, re
  *            the end states of the segments before it, with factor
  *            gamma^(segment length) per segment. bf16 does this in one launch
  *            (workgroups publish segment states and look back at their
- *            predecessors' through the workspace); float32 runs three
- *            kernels (segment end states, their scan, the segments).
+ *            predecessors' through the workspace), except for unrotated
+ *            heads with dk of 128 or 256 in 128-token chunks, which run
+ *            three kernels like float32 (segment end states, their scan,
+ *            the segments).
  * workspace: device buffer of at least retention_chunkwise_workspace_size(...)
  *            bytes (may be NULL when that size is 0). It must be zero-filled
  *            before its first use (one hipMemset after allocation); every
@@ -205,8 +207,10 @@ size_t retention_chunkwise_workspace_size(int B, int H, int N, int dk, int dv, r
  *   ticket counters  [0, flags_off): one 8-byte counter per chain, 128 bytes apart
  *   segment flags    [flags_off, gflags_off): chain * segments + segment, 128 bytes apart
  *   group flags      [gflags_off, agg_off): chain * groups + group, 128 bytes apart
- *   segment states   [agg_off, gagg_off): bf16 path: chain * segments + segment,
- *                    dk * dv_tile floats each; float32 path: [B, H, segments, dk, dv]
+ *   segment states   [agg_off, gagg_off): bf16 look-back: chain * segments + segment,
+ *                    dk * dv_tile floats each; the three-kernel form (float32, and
+ *                    bf16 unrotated dk 128/256 in 128-token tiles of 128 value
+ *                    columns): [B, H, segments, dk, dv] floats
  *   group states     [gagg_off, workspace_bytes): chain * groups + group, dk * dv_tile floats
  * with groups = ceil(segments / group_len). A plan with segments == 1 uses no
  * workspace (workspace_bytes == 0). Returns the status retention_chunkwise_fwd

@@ -388,6 +388,9 @@ def test_every_plan_indexes_inside_its_workspace(lib):
             slot = dk * p.dv_tile * 4
             assert p.agg_off + chains * p.segments * slot <= p.gagg_off, case
             assert p.gagg_off + chains * groups * slot <= p.workspace_bytes, case
+            if dk in (128, 256) and p.dv_tile == 128 and p.tile == 128:
+                # the wide kernel's three-kernel form (unrotated calls): [B, H, segments, dk, dv]
+                assert p.agg_off + B * H * p.segments * dk * dv * 4 <= p.gagg_off, case
         else:  # float32 pre-pass and scan: [B, H, segments, dk, dv]
             assert p.agg_off + B * H * p.segments * dk * dv * 4 <= p.gagg_off, case
     assert checked > 1000
