@@ -578,6 +578,32 @@ ret_status_t retention_chunkwise_bwd(const void* q, const void* k, const void* v
         if (s != RET_OK) return s;
         s = plan_chunk(B, H, N, dk, dv, dtype, chunk, 0, p3);
         if (s != RET_OK) return s;
+        // Keys and values of one width (128 or 256) in 128-token chunks whose plan cuts the
+        // sequence (few heads): the three passes run on the wide kernel's segmented form
+        // (their state passes, scans and segment passes, one launch each for all three),
+        // each pass with its own workspace region
+        if (!b.split && dk == dv && (dk == 128 || dk == 256) && chunk == 128 && p1.nseg > 1 && p1.tile == 128 &&
+            p1.dvt == 128 && ret::chunk_wide_rescale(hp, H) > 0) {
+            ret::ChunkCalls cw;
+            memset(&cw, 0, sizeof(cw));
+            fill_chunk_args(cw.a[0], d_o, v, kp, d_q, B, H, N, dv, dk, chunk, 0, sx1, nullptr, p1, ws);
+            fill_chunk_args(cw.a[1], v, d_o, qp, d_k, B, H, N, dv, dk, chunk, 0, sx2, nullptr, p1, ws + b.fwd_bytes);
+            fill_chunk_args(cw.a[2], kp, qp, d_o, d_v, B, H, N, dk, dv, chunk, 0, sx3, d_state_in, p3,
+                            ws + 2 * b.fwd_bytes);
+            cw.a[1].rev = 1;
+            cw.a[2].rev = 1;
+            cw.n = 3;
+            if (ret::launch_chunk_wide_multi(cw, hp_passes, st) != hipSuccess) return RET_ERR_HIP;
+            if (rot) {  // dQ = R^-1 dQ', dK likewise (in place)
+                memset(&rj.j, 0, sizeof(rj.j));
+                rj.nzero = 0;
+                rj.n = 2;
+                rj.j[0] = {d_q, d_q, nullptr, dk, 0, -1, 0, 0, 0, nullptr};
+                rj.j[1] = {d_k, d_k, nullptr, dk, 0, -1, 0, 0, 0, nullptr};
+                if (ret::launch_rows(rj, hp, bf16, st) != hipSuccess) return RET_ERR_HIP;
+            }
+            return finish_states();
+        }
         // Split passes whose tile matches pass 3's (hv == dk) share its launch
         // when the five passes together fill the chip without sequence
         // segments (one kernel form for all of them).

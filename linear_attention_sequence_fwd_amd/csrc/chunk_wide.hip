@@ -592,6 +592,20 @@ void chunk_wide_multi_kernel(ChunkCalls cs, HeadParams hp) {
     chunk_wide_body<DK, true>(cs.a[c], hp, b - cs.first[c], 0);
 }
 
+// Segmented calls of several passes (the backward's) in one launch per phase:
+// workgroups [first[c], first[c+1]) serve call c, chain local % chains,
+// segment local / chains.
+template <int DK, int MODE>
+__global__ __attribute__((amdgpu_flat_work_group_size(kWideThreads, kWideThreads), amdgpu_waves_per_eu(2, 2)))
+void chunk_wide_multi_seg_kernel(ChunkCalls cs, HeadParams hp) {
+    const int b = blockIdx.x;
+    int c = 0;
+    while (c + 1 < cs.n && b >= cs.first[c + 1]) ++c;
+    const int chains = cs.a[c].B * cs.a[c].H * cs.a[c].nvt;
+    const int local = b - cs.first[c];
+    chunk_wide_body<DK, true, MODE>(cs.a[c], hp, local % chains, local / chains);
+}
+
 // Chunks per decay group: the largest R in {8, 4, 2, 1} with gamma^(R C) >=
 // 2^-64 for every head (0: the rescaled form does not fit these gammas).
 int chunk_wide_rescale(const HeadParams& hp, int H) {
@@ -611,21 +625,46 @@ hipError_t launch_chunk_wide_multi(const ChunkCalls& in, const HeadParams& hp, h
     ChunkCalls cs = in;
     const int R = chunk_wide_rescale(hp, cs.a[0].H);
     if (R == 0) return hipErrorInvalidValue;
-    cs.first[0] = 0;
+    // every call whole (one pass per chain) or every call segmented (state pass,
+    // scan, segment pass per call, each phase one launch for all calls)
+    const bool seg = cs.a[0].nseg > 1;
     for (int i = 0; i < cs.n; ++i) {
         ChunkArgs& b = cs.a[i];
-        if (b.dk != cs.a[0].dk || b.H != cs.a[0].H || !chunk_wide_supported(b.dk, b.dv / b.nvt, b.chunk, b.nseg, false) ||
-            b.orot)
+        if (b.dk != cs.a[0].dk || b.H != cs.a[0].H || !chunk_wide_supported(b.dk, b.dv / b.nvt, b.chunk, 1, false) ||
+            b.orot || (b.nseg > 1) != seg || (seg && (!b.agg || b.seg_len % kWideC != 0)))
             return hipErrorInvalidValue;
         b.rescale = R;
-        cs.first[i + 1] = cs.first[i] + b.B * b.H * b.nvt;
     }
     cs.interleave = 0;
-    const dim3 grid(cs.first[cs.n]), block(kWideThreads);
+    const dim3 block(kWideThreads);
+    auto ranges = [&](int extra) {  // workgroups per call: chains x (nseg + extra)
+        cs.first[0] = 0;
+        for (int i = 0; i < cs.n; ++i)
+            cs.first[i + 1] = cs.first[i] + cs.a[i].B * cs.a[i].H * cs.a[i].nvt * (seg ? cs.a[i].nseg + extra : 1);
+        return dim3(cs.first[cs.n]);
+    };
+    if (!seg) {
+        const dim3 grid = ranges(0);
+        if (cs.a[0].dk == 256)
+            hipLaunchKernelGGL(chunk_wide_multi_kernel<256>, grid, block, 0, st, cs, hp);
+        else
+            hipLaunchKernelGGL(chunk_wide_multi_kernel<128>, grid, block, 0, st, cs, hp);
+        return hipGetLastError();
+    }
+    dim3 grid = ranges(-1);
     if (cs.a[0].dk == 256)
-        hipLaunchKernelGGL(chunk_wide_multi_kernel<256>, grid, block, 0, st, cs, hp);
+        hipLaunchKernelGGL((chunk_wide_multi_seg_kernel<256, kWideStatePass>), grid, block, 0, st, cs, hp);
     else
-        hipLaunchKernelGGL(chunk_wide_multi_kernel<128>, grid, block, 0, st, cs, hp);
+        hipLaunchKernelGGL((chunk_wide_multi_seg_kernel<128, kWideStatePass>), grid, block, 0, st, cs, hp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_segment_scan_multi(cs, hp, st);
+    if (e != hipSuccess) return e;
+    grid = ranges(0);
+    if (cs.a[0].dk == 256)
+        hipLaunchKernelGGL((chunk_wide_multi_seg_kernel<256, kWideSegPass>), grid, block, 0, st, cs, hp);
+    else
+        hipLaunchKernelGGL((chunk_wide_multi_seg_kernel<128, kWideSegPass>), grid, block, 0, st, cs, hp);
     return hipGetLastError();
 }
 

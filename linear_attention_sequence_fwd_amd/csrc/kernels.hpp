@@ -203,6 +203,7 @@ hipError_t launch_parallel_f32(const ParallelArgs& a, const HeadParams& hp, int 
 hipError_t launch_recurrent_step(const StepArgs& a, const HeadParams& hp, hipStream_t st);
 int recurrent_step_tiles(int B, int H, int dv);
 hipError_t launch_segment_scan(const ChunkArgs& a, const HeadParams& hp, hipStream_t st, hipEvent_t* ev);
+hipError_t launch_segment_scan_multi(const ChunkCalls& cs, const HeadParams& hp, hipStream_t st);
 
 // Launch `kernel` with the given configuration; with events, bracket its
 // execution with ev[0] / ev[1].

@@ -17,10 +17,8 @@ namespace ret {
 // end state of segment s-1 built from zero and is replaced by the state at
 // the start of segment s. One thread owns four consecutive state elements and
 // walks the segments in order; a wavefront covers 256 contiguous elements.
-__global__ __launch_bounds__(256) void segment_scan_kernel(float* ws, const float* state_in, int H, int nseg,
-                                                           int per_bh, int seg_len, HeadParams hp) {
-    const int bh = blockIdx.y;
-    const int e4 = blockIdx.x * blockDim.x + threadIdx.x;
+__device__ __forceinline__ void segment_scan_body(float* ws, const float* state_in, int H, int nseg, int per_bh,
+                                                  int seg_len, const HeadParams& hp, int bh, int e4) {
     if (e4 * 4 >= per_bh) return;
     const float gL = gamma_pow(log2_gamma(hp.gamma[bh % H]), seg_len);
     float4* w = reinterpret_cast<float4*>(ws + static_cast<size_t>(bh) * nseg * per_bh) + e4;
@@ -50,11 +48,37 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(float* ws, const floa
     }
 }
 
+__global__ __launch_bounds__(256) void segment_scan_kernel(float* ws, const float* state_in, int H, int nseg,
+                                                           int per_bh, int seg_len, HeadParams hp) {
+    segment_scan_body(ws, state_in, H, nseg, per_bh, seg_len, hp, blockIdx.y,
+                      blockIdx.x * blockDim.x + threadIdx.x);
+}
+
+// The scans of several calls in one launch (call blockIdx.z), each over its
+// own workspace slots.
+__global__ __launch_bounds__(256) void segment_scan_multi_kernel(ChunkCalls cs, HeadParams hp) {
+    const ChunkArgs& a = cs.a[blockIdx.z];
+    if (static_cast<int>(blockIdx.y) >= a.B * a.H) return;
+    segment_scan_body(a.agg, a.state_in, a.H, a.nseg, a.dk * a.dv, a.seg_len, hp, blockIdx.y,
+                      blockIdx.x * blockDim.x + threadIdx.x);
+}
+
 hipError_t launch_segment_scan(const ChunkArgs& a, const HeadParams& hp, hipStream_t st, hipEvent_t* ev) {
     const int per_bh = a.dk * a.dv;
     dim3 grid((per_bh / 4 + 255) / 256, a.B * a.H);
     launch_timed(segment_scan_kernel, grid, dim3(256), 0, st, ev, a.agg, a.state_in, a.H, a.nseg, per_bh,
                  a.seg_len, hp);
+    return hipGetLastError();
+}
+
+hipError_t launch_segment_scan_multi(const ChunkCalls& cs, const HeadParams& hp, hipStream_t st) {
+    int per_max = 0, bh_max = 0;
+    for (int i = 0; i < cs.n; ++i) {
+        per_max = max(per_max, cs.a[i].dk * cs.a[i].dv);
+        bh_max = max(bh_max, cs.a[i].B * cs.a[i].H);
+    }
+    const dim3 grid((per_max / 4 + 255) / 256, bh_max, cs.n);
+    hipLaunchKernelGGL(segment_scan_multi_kernel, grid, dim3(256), 0, st, cs, hp);
     return hipGetLastError();
 }
 
