@@ -792,7 +792,7 @@ def run_also(R, W, torch, dev):
     msl = time_events(bstep, 5, 2)
     fll = 3 * chunk_alg_flops(w["B"], w["H"], w["N"], w["dk"], w["dv"], w["chunk"])
     also.append({
-        "workload": "backward of the long-context workload (B=1 H=8 N=65536 d=128 bf16, chunk 128)",
+        "workload": "backward of the long-context workload (B=1 H=8 N=65536 d=128 bf16, chunk 128): the three passes on the segmented wide kernel (state passes, scans, segment passes: one launch each)",
         "ms": msl, "tokens_per_s": w["B"] * w["N"] / (msl * 1e-3), "tflops": fll / (msl * 1e-3) / 1e12,
         "mfma_frac": fll / (msl * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
     })
