@@ -128,6 +128,9 @@ F32_CASES = [
     (1, 3, 300, 64, 64, 128, False, False),
     (1, 2, 129, 128, 16, 64, True, True),
     (2, 1, 77, 32, 128, 128, False, True),
+    # widths that are multiples of 4 but not of 16 (the register micro-tiles step four columns)
+    (1, 2, 97, 36, 16, 32, True, True),
+    (1, 1, 70, 20, 32, 16, False, True),
 ]
 
 
