@@ -24,11 +24,12 @@
 // longest-first. The causal work of a query block grows with its position, so
 // when the blocks alone would leave compute units idle the walk of every block
 // longer than T key blocks is split: one workgroup takes the T blocks from the
-// diagonal, another the rest, each writes its float32 partial of O to the
-// workspace, and the later of the two (by a ticket) adds the other's and
-// stores O. Retention has no softmax normaliser, so the two partials simply
-// add; a sum of two float32 values does not depend on their order, so the
-// result repeats bit for bit whichever finishes first.
+// diagonal, another the rest. The first of the two to finish (by a ticket)
+// writes its float32 partial of O to the workspace and marks it written; the
+// second adds it to its own and stores O. Retention has no softmax
+// normaliser, so the two partials simply add; a sum of two float32 values does
+// not depend on their order, so the result repeats bit for bit whichever
+// finishes first.
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -45,6 +46,9 @@ constexpr int kParBQ = 128;       // query rows per workgroup, keys per key bloc
 constexpr int kParDvt = 128;      // value columns per workgroup
 constexpr int kParThreads = 512;  // eight waves, two per SIMD
 constexpr int kParPipe = 4;       // steps between an LDS read and its use
+// Bound of the second half's wait for the first half's partial (the first is
+// running: it took its ticket before writing). Past it O is stored as NaN.
+constexpr unsigned kMaxHandoverSpins = 1u << 20;
 
 template <int DK>
 struct ParWGeo {
@@ -308,26 +312,46 @@ void parallel_wide_kernel(ParallelArgs a, HeadParams hp) {
         if (m + 1 < nkb) step(m + 1, kb1, vb1, kb0, vb0);
     }
 
-    if (part != 0) {  // half of a split walk: publish the partial, the later half adds and stores
+    if (part != 0) {  // half of a split walk: the first to finish hands its partial over, the second stores O
         // a partial in register order: (wave, block, column tile) a 1 KiB run, lane l its
-        // 16 bytes at 16 l (the two halves share the order, so they add element by element)
+        // 16 bytes at 16 l (the two halves share the order, so they add element by element).
+        // The pair's ticket counts arrivals (+1 each) and the partial's completion (+2).
         const size_t si = (static_cast<size_t>(bh) * a.nvt + vt) * S + (qb - T);
         constexpr int kPartBytes = BQ * kParDvt * 4;
         const __amdgpu_buffer_rsrc_t mine = make_rsrc(a.part + (si * 2 + (part - 1)) * (BQ * kParDvt), kPartBytes);
         const __amdgpu_buffer_rsrc_t other = make_rsrc(a.part + (si * 2 + (2 - part)) * (BQ * kParDvt), kPartBytes);
         auto at = [&](int nt) { return ((wave * G::NTV + nt) * 64 + lane) * 16; };
-#pragma unroll
-        for (int nt = 0; nt < G::NTV; ++nt) store_coherent16(oacc[nt], mine, at(nt));
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial is out
-        __syncthreads();
         if (threadIdx.x == 0)
             s_ticket = __hip_atomic_fetch_add(a.ctr + si, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
-        if (s_ticket == 0) return;  // the other half finishes later and stores O
-        if (threadIdx.x == 0)        // both halves have counted: ready for the next call
-            __hip_atomic_store(a.ctr + si, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned t0 = s_ticket;
+        __syncthreads();  // every thread has read the ticket before s_ticket is reused
+        if (t0 == 0) {  // first: write the partial, then mark it complete
 #pragma unroll
-        for (int nt = 0; nt < G::NTV; ++nt) oacc[nt] += load_coherent16(other, at(nt));
+            for (int nt = 0; nt < G::NTV; ++nt) store_coherent16(oacc[nt], mine, at(nt));
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial is out
+            __syncthreads();
+            if (threadIdx.x == 0) __hip_atomic_fetch_add(a.ctr + si, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        // second: the other's partial is complete once the counter reads 4 (1 + 1 + 2)
+        if (threadIdx.x == 0) {
+            unsigned v = t0 + 1, spins = 0;
+            while (v < 4 && spins++ < kMaxHandoverSpins) {
+                __builtin_amdgcn_s_sleep(1);
+                v = __hip_atomic_load(a.ctr + si, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            s_ticket = v;
+            // ready for the next call (the first is done with the counter)
+            __hip_atomic_store(a.ctr + si, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        const bool ok = s_ticket >= 4;
+#pragma unroll
+        for (int nt = 0; nt < G::NTV; ++nt) {
+            const f32x4 x = load_coherent16(other, at(nt));
+            oacc[nt] += ok ? x : f32x4{NAN, NAN, NAN, NAN};
+        }
     }
 
     // O = O^T transposed back: lane (l16, grp) holds rows 16 blk + l16, columns 16 nt + 4 grp .. +3
