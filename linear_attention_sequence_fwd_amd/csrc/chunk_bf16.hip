@@ -1300,7 +1300,7 @@ static hipError_t run_chunk_bf16(const ChunkArgs& a, const HeadParams& hp, hipSt
     // Unrotated heads of width 128 or 256 in 128-token chunks run on the wide
     // kernel, segmented (state pass, scan, segment pass) when the plan cuts the
     // sequence; it takes its six phase events itself.
-    if (chunk_wide_supported(DK, DVT, C, 1, hp.has_theta != 0) && (a.nseg == 1 || a.agg != nullptr)) {
+    if (chunk_wide_supported(DK, DVT, C, hp.has_theta != 0) && (a.nseg == 1 || a.agg != nullptr)) {
         const int R = chunk_wide_rescale(hp, a.H);
         if (R > 0) {
             ChunkArgs aw = a;

@@ -616,8 +616,8 @@ int chunk_wide_rescale(const HeadParams& hp, int H) {
     return 0;
 }
 
-bool chunk_wide_supported(int dk, int dvt, int chunk, int nseg, bool rotation) {
-    return !rotation && nseg == 1 && dvt == kWideDvt && chunk == kWideC && (dk == 128 || dk == 256);
+bool chunk_wide_supported(int dk, int dvt, int chunk, bool rotation) {
+    return !rotation && dvt == kWideDvt && chunk == kWideC && (dk == 128 || dk == 256);
 }
 
 hipError_t launch_chunk_wide_multi(const ChunkCalls& in, const HeadParams& hp, hipStream_t st) {
@@ -630,7 +630,7 @@ hipError_t launch_chunk_wide_multi(const ChunkCalls& in, const HeadParams& hp, h
     const bool seg = cs.a[0].nseg > 1;
     for (int i = 0; i < cs.n; ++i) {
         ChunkArgs& b = cs.a[i];
-        if (b.dk != cs.a[0].dk || b.H != cs.a[0].H || !chunk_wide_supported(b.dk, b.dv / b.nvt, b.chunk, 1, false) ||
+        if (b.dk != cs.a[0].dk || b.H != cs.a[0].H || !chunk_wide_supported(b.dk, b.dv / b.nvt, b.chunk, false) ||
             b.orot || (b.nseg > 1) != seg || (seg && (!b.agg || b.seg_len % kWideC != 0)))
             return hipErrorInvalidValue;
         b.rescale = R;

@@ -178,13 +178,16 @@ hipError_t launch_states(const StateJobs& sj, const HeadParams& hp, hipStream_t 
 // (hipExtLaunchKernelGGL); a phase that does not run records its pair back to
 // back.
 hipError_t launch_chunk_bf16(const ChunkArgs& a, const HeadParams& hp, int dvt, hipStream_t st, hipEvent_t* ev);
-// The wide-head kernel (chunk_wide.hip): single pass, d_k 128 or 256, value
-// tiles of 128 columns, 128-token chunks, no rotation, gammas with gamma^128 >= 2^-64.
-bool chunk_wide_supported(int dk, int dvt, int chunk, int nseg, bool rotation);
+// The wide-head kernel (chunk_wide.hip): d_k 128 or 256, value tiles of 128
+// columns, 128-token chunks, no rotation, gammas with gamma^128 >= 2^-64. One
+// pass per chain, or with a.nseg > 1 three launches (segment end states, their
+// scan in a.agg, the segments); launch_chunk_wide records the six phase events.
+bool chunk_wide_supported(int dk, int dvt, int chunk, bool rotation);
 int chunk_wide_rescale(const HeadParams& hp, int H);
 hipError_t launch_chunk_wide(const ChunkArgs& a, const HeadParams& hp, hipStream_t st, hipEvent_t* ev);
 // several unrotated calls of one key width (128 or 256), chunk 128, 128-column value tiles,
-// one segment each, in one launch (a.rev honoured); rescale is filled in here
+// all whole (one launch) or all segmented (one launch per phase), a.rev honoured; rescale is
+// filled in here
 hipError_t launch_chunk_wide_multi(const ChunkCalls& cs, const HeadParams& hp, hipStream_t st);
 hipError_t launch_chunk_bf16_multi(const ChunkCalls& cs, const HeadParams& hp, int dvt, hipStream_t st);
 hipError_t launch_chunk_f32(const ChunkArgs& a, const HeadParams& hp, int dvt, hipStream_t st, hipEvent_t* ev);
