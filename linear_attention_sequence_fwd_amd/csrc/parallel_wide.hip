@@ -47,7 +47,9 @@ constexpr int kParDvt = 128;      // value columns per workgroup
 constexpr int kParThreads = 512;  // eight waves, two per SIMD
 constexpr int kParPipe = 4;       // steps between an LDS read and its use
 // Bound of the second half's wait for the first half's partial (the first is
-// running: it took its ticket before writing). Past it O is stored as NaN.
+// running: it took its ticket before writing). Past it O is stored as NaN and
+// the pair's counter is left undefined (the workspace then needs zero-filling
+// again); a wait can only run out if the first half stops making progress.
 constexpr unsigned kMaxHandoverSpins = 1u << 20;
 
 template <int DK>
