@@ -266,7 +266,7 @@ def _oracle_worker_init():
 
 
 def host_cores():
-    """Cores this process may use, capped at the 16 host cores a one-GPU machine shares out."""
+    """Cores this process may use, capped at 16 (the host cores that come with one MI355X)."""
     return max(1, min(len(os.sched_getaffinity(0)), 16))
 
 
